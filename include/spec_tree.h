@@ -1,0 +1,198 @@
+/*
+ * spec_tree.h -- C ABI of libspectree, the MI355X (gfx950) verification step of
+ * EAGLE-style tree speculative decoding.
+ *
+ * One verification step over a flattened draft tree is:
+ *   spec_tree_mask_build      parent links -> ancestor / child bitmasks, depths
+ *   spec_tree_attention       tree-masked split-KV GQA attention
+ *   spec_tree_softmax         per-node vocabulary softmax statistics (target, draft)
+ *   spec_tree_reject_sample   lossless tree rejection sampling (or greedy at T = 0)
+ *   spec_accept_path          longest accepted root-to-leaf path plus the bonus token
+ *
+ * Sources.  "EAGLE 演化史 (1 → 2 → 3) 与 DFlash 的回答" (zhangshuibai.github.io paper
+ * notes), section "Tree Verification 详解": part B (BFS flattening and the
+ * ancestor-only mask), part C (per-parent draft distribution, sibling fallthrough
+ * on the residual, unique longest accepted path), part D.2 (cost split), part G
+ * (worked example, bonus token at a leaf).  "Eagle vs DFlash: Best speculative
+ * decoding methods" (gingerlabs.ai), section "Target-model decoding is serial"
+ * (accept with probability min(1, p/q), resample from norm(max(0, p - q))).
+ * "EAGLE-4 Technical Deepdive" (blog.fal.ai), "EAGLE-4 verification trees and
+ * harness" (prefix + ancestors + self).  "The EAGLE Family: Speculating in Feature
+ * Space" (consciousengines.com), "Why predict features instead of tokens?"
+ * (next-token distribution = softmax of the LM-head output).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named in the argument lists are DEVICE pointers unless stated, owned
+ *    by the caller; arrays are row-major and contiguous.  The library never
+ *    allocates or frees memory and never reads device memory from the host.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronises the host.  Results are valid once the stream
+ *    reaches the call.
+ *  - The return value reports what the host can check without touching device
+ *    memory: SPEC_OK, or an error code below; on an error nothing is launched.
+ *  - `status` (device int32, nullable) receives data errors found on the device:
+ *    the first error code wins (atomic compare-and-swap from 0).  The caller zeroes
+ *    it (with a kernel, not a memset, if the call is captured in a graph); the
+ *    library never clears it.
+ *  - Trees: node 0 is the root (the last committed token, never tested itself);
+ *    nodes are flattened so that parent[i] < i (BFS order is one such order);
+ *    parent[0] = -1; 1 <= n_nodes[b] <= n_max <= 64; entries i >= n_nodes[b] are
+ *    padding and ignored.
+ *  - Workspaces are caller-provided device buffers of at least the size the
+ *    matching *_workspace_size query returns, zero-filled once before first use.
+ *    Each call leaves its workspace zero-filled where that matters, so one buffer
+ *    can be reused by consecutive calls of the same entry point on one stream.
+ *    Calls that run concurrently need separate workspaces.
+ *  - gfx950 only.  The library is stateless and reentrant across streams.
+ */
+#ifndef SPEC_TREE_H
+#define SPEC_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARG = -1, /* null pointer, size out of range, bad temperature  */
+  SPEC_ERR_UNSUPPORTED = -2, /* a shape or dtype this build does not implement    */
+  SPEC_ERR_BAD_TREE = -3,    /* device: parent[] does not describe a tree          */
+  SPEC_ERR_BAD_INPUT = -4,   /* device: token or page id out of range, NaN/+inf    */
+  SPEC_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
+  SPEC_ERR_HIP = -6          /* a HIP launch failed                                */
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Markers written into the per-node sampling outputs. */
+#define SPEC_NODE_NONE (-1)          /* no child accepted                          */
+#define SPEC_NODE_NOT_EVALUATED (-2) /* node not visited by the walk               */
+#define SPEC_NODE_BAD_REQUEST (-3)   /* request rejected (bad tree, token or row)  */
+
+/*
+ * Ancestor mask (tree notes, part B; fal.ai page, "verification trees").
+ * For each request b and node i < n_nodes[b]:
+ *   anc_mask[b,i]   bit j set iff node j is node i or one of its ancestors
+ *   child_mask[b,p] bit i set iff parent[b,i] == p
+ *   depth[b,i]      number of edges from the root (the caller's RoPE position of
+ *                   node i is ctx_len[b] + depth[b,i])
+ * parent, n_nodes: int32 [batch, n_max], [batch].  Outputs: uint64 [batch, n_max],
+ * uint64 [batch, n_max], int32 [batch, n_max].  Padding entries get anc = child = 0
+ * and depth = -1.  A request whose parent[] is not a tree gets all-zero masks,
+ * depth -1 everywhere, and SPEC_ERR_BAD_TREE in status.
+ * Host errors: batch < 1, n_max outside [1, 64], null pointers.
+ */
+int spec_tree_mask_build(const int32_t* parent, const int32_t* n_nodes, int32_t batch, int32_t n_max,
+                         uint64_t* anc_mask, uint64_t* child_mask, int32_t* depth, int32_t* status, void* stream);
+
+/*
+ * Tree-masked attention (tree notes, parts B and D.2).  For request b, node
+ * i < n_nodes[b] and query head h (KV head g = h / (hq / hkv)):
+ *   visible keys = logical positions [0, ctx_len[b]) plus ctx_len[b] + j for
+ *                  every bit j of anc_mask[b,i]
+ *   out[b,i,h,:] = softmax(scale * q . k) . v over the visible keys
+ * The tree's own K/V rows sit at logical positions ctx_len[b] + j (node j), so the
+ * caller writes them before this call.  Q and K carry RoPE already (node i at
+ * position ctx_len[b] + depth[b,i]).
+ *   q    [batch, n_max, hq, head_dim]           dtype
+ *   k, v contiguous: [batch, kv_capacity, hkv, head_dim] (block_table == NULL)
+ *        paged:      [n_pages, page_size, hkv, head_dim] with block_table int32
+ *                    [batch, kv_capacity] listing the pages of each request in
+ *                    logical order (kv_capacity = pages per request)
+ *   out  [batch, n_max, hq, head_dim]           dtype; padding rows are zero
+ * dtype SPEC_BF16 (fp32 accumulate) or SPEC_F32.  head_dim 64 or 128.
+ * Query rows per KV head G = n_max * hq / hkv: bf16 with G >= 16 runs on MFMA
+ * tiles, otherwise on a shuffle dot-product kernel.
+ * Device errors: ctx_len[b] + n_nodes[b] beyond the cache, a page id outside
+ * [0, n_pages), a bad tree -> SPEC_ERR_BAD_INPUT / SPEC_ERR_BAD_TREE; the
+ * affected request's rows are written as zeros.
+ * Host errors: null pointers, hq % hkv != 0, head_dim not 64/128, n_max outside
+ * [1, 64], page_size < 1 with a block table, workspace too small.
+ */
+size_t spec_tree_attention_workspace_size(int32_t batch, int32_t n_max, int32_t hq, int32_t hkv, int32_t head_dim,
+                                          int32_t max_kv_len);
+int spec_tree_attention(const void* q, const void* k, const void* v, int32_t dtype, const int32_t* block_table,
+                        int32_t page_size, int32_t kv_capacity, int32_t n_pages, const int32_t* ctx_len,
+                        const int32_t* n_nodes, const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq,
+                        int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
+ * Per-row vocabulary softmax statistics at temperature T ("The EAGLE Family",
+ * "Why predict features instead of tokens?"; tree notes, parts A and D.2).
+ *   row_max[r]    = max_x logits[r,x]
+ *   row_sumexp[r] = sum_x exp((logits[r,x] - row_max[r]) / T)      (T > 0)
+ *   row_argmax[r] = smallest x with logits[r,x] == row_max[r]       (nullable)
+ *   probs[r,x]    = exp((logits[r,x] - row_max[r]) / T) / row_sumexp (nullable,
+ *                   T > 0; meant for tests)
+ * logits: fp32 [rows, vocab].  -inf logits are probability 0.  A row holding NaN
+ * or +inf, or only -inf, gets row_max = NaN and SPEC_ERR_BAD_INPUT in status.
+ * T == 0 computes row_max and row_argmax only.
+ * Host errors: rows < 1, vocab < 1, T < 0 or NaN, null outputs, workspace.
+ */
+size_t spec_tree_softmax_workspace_size(int64_t rows, int32_t vocab);
+int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float temperature, float* row_max,
+                      float* row_sumexp, int32_t* row_argmax, float* probs, void* workspace, size_t workspace_bytes,
+                      int32_t* status, void* stream);
+
+/*
+ * Tree rejection sampling (gingerlabs page, "Target-model decoding is serial";
+ * tree notes, parts C and G).  Walks each request from the root.  At node n the
+ * children c (parent[c] == n) are tested in ascending index against the target
+ * distribution p_n = softmax(tgt_logits[n] / T) and the draft distribution at the
+ * parent q_n = softmax(dft_logits[n] / T_d): child c with token x is accepted when
+ * u_accept[c] < r(x) / q_n(x), where r starts as p_n and after each rejected
+ * sibling becomes norm(max(0, r - q_n)) (unchanged if that mass is zero).  The
+ * walk continues at an accepted child.  If every child is rejected the terminal
+ * token is drawn from r by inverse CDF with u_sample[n] (smallest token whose
+ * running sum exceeds u * total); at a leaf it is drawn from p_n the same way.
+ * q(x) == 0 gives ratio +inf when r(x) > 0, else 0.
+ * T == 0 is greedy: the first child whose token equals the target argmax is
+ * accepted, the terminal token is that argmax; draft inputs and uniforms may be
+ * NULL.
+ * Inputs: tgt_logits, dft_logits fp32 [batch, n_max, vocab]; the row statistics
+ * of spec_tree_softmax over the same rows (tgt_argmax needed only at T == 0);
+ * tokens, parent int32 [batch, n_max]; n_nodes int32 [batch]; u_accept, u_sample
+ * fp32 [batch, n_max] in (0, 1).
+ * Outputs int32 [batch, n_max]: accepted_child[b,n] = accepted child,
+ * SPEC_NODE_NONE, or SPEC_NODE_NOT_EVALUATED for nodes off the walk;
+ * term_token[b,n] = the terminal token of the last node of the walk, else
+ * SPEC_NODE_NOT_EVALUATED.  A request with a bad tree, a token outside
+ * [0, vocab) or an invalid logit row gets accepted_child[b,0] =
+ * SPEC_NODE_BAD_REQUEST and a device error code.
+ * Host errors: T < 0 or NaN, T > 0 with T_d <= 0, null required pointers, sizes,
+ * workspace.
+ */
+size_t spec_tree_reject_sample_workspace_size(int32_t batch, int32_t n_max, int32_t vocab);
+int spec_tree_reject_sample(const float* tgt_logits, const float* tgt_max, const float* tgt_sumexp,
+                            const int32_t* tgt_argmax, float temperature, const float* dft_logits,
+                            const float* dft_max, const float* dft_sumexp, float draft_temperature,
+                            const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
+                            const float* u_accept, const float* u_sample, int32_t batch, int32_t n_max, int32_t vocab,
+                            int32_t* accepted_child, int32_t* term_token, void* workspace, size_t workspace_bytes,
+                            int32_t* status, void* stream);
+
+/*
+ * Accepted path plus bonus token (tree notes, parts C and G; gingerlabs page, "A
+ * useful performance model": the accepted length counts drafted tokens, the bonus
+ * is emitted on top).  Follows accepted_child from node 0 until SPEC_NODE_NONE.
+ *   path_nodes [batch, n_max]  root first, then the accepted nodes; -1 padded
+ *   out_tokens [batch, n_max]  tokens of the accepted nodes, then the terminal
+ *                              token of the last node; -1 padded
+ *   accept_len [batch]         number of accepted nodes; -1 for a rejected request
+ * Host errors: null pointers, batch < 1, n_max outside [1, 64].
+ */
+int spec_accept_path(const int32_t* accepted_child, const int32_t* term_token, const int32_t* tokens,
+                     const int32_t* n_nodes, int32_t batch, int32_t n_max, int32_t* path_nodes, int32_t* out_tokens,
+                     int32_t* accept_len, int32_t* status, void* stream);
+
+/* Library version string (static storage). */
+const char* spec_tree_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_TREE_H */

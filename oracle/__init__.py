@@ -54,6 +54,12 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
+def set_threads(n: int) -> int:
+    """Use n OpenMP threads in the parallel loops; returns the count now in effect."""
+    lib().oracle_set_threads(ctypes.c_int(int(n)))
+    return int(lib().oracle_max_threads())
+
+
 def mask(parent, n_nodes):
     """Ancestor / child bitmasks and depths.  parent [B, n_max] int32, n_nodes [B]."""
     parent = _c(parent, np.int32)

@@ -32,6 +32,7 @@
  *   oracle_accept_path      pinned (worked example)
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -628,4 +629,10 @@ int oracle_accept_path(const int32_t* accepted_child, const int32_t* term_token,
     accept_len[b] = len;
   }
   return ORC_OK;
+}
+
+/* Thread plumbing for timing runs (no arithmetic). */
+int oracle_max_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
 }

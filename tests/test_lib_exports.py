@@ -1,0 +1,103 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports every
+function the public header declares, and rejects bad arguments before launching."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_verification_masked_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "spec_tree.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libspectree.so not built")
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding._SIGNATURES), "binding and header disagree"
+
+
+def test_version(lib):
+    assert "gfx950" in binding.spec_tree_version()
+
+
+def test_workspace_queries(lib):
+    assert binding.spec_tree_softmax_workspace_size(60, 128256) > 60 * 16 * 12
+    assert binding.spec_tree_softmax_workspace_size(0, 10) == 0
+    a = binding.spec_tree_attention_workspace_size(1, 60, 32, 8, 128, 4156)
+    assert a >= 60 * 32 * 130 * 4
+    assert binding.spec_tree_attention_workspace_size(1, 60, 30, 8, 128, 4156) == 0  # hq % hkv
+
+
+P = ctypes.c_void_p(16)  # never dereferenced: every call below fails host validation first
+
+
+def test_host_errors_mask_and_path(lib):
+    assert lib.spec_tree_mask_build(None, P, 1, 7, P, P, P, None, None) == -1
+    assert lib.spec_tree_mask_build(P, P, 1, 65, P, P, P, None, None) == -1
+    assert lib.spec_tree_mask_build(P, P, 0, 7, P, P, P, None, None) == -1
+    assert lib.spec_accept_path(P, P, P, P, 1, 0, P, P, P, None, None) == -1
+    assert lib.spec_accept_path(P, None, P, P, 1, 4, P, P, P, None, None) == -1
+
+
+def test_host_errors_softmax(lib):
+    f = lib.spec_tree_softmax
+    assert f(P, 4, 100, -1.0, P, P, P, None, P, 1 << 20, None, None) == -1       # T < 0
+    assert f(P, 4, 100, float("nan"), P, P, P, None, P, 1 << 20, None, None) == -1
+    assert f(P, 4, 100, 1.0, P, None, P, None, P, 1 << 20, None, None) == -1     # T > 0 needs sums
+    assert f(P, 4, 100, 1.0, P, P, P, None, P, 8, None, None) == -5              # workspace too small
+    assert f(P, 4, 100, 1.0, P, P, P, None, None, 0, None, None) == -5
+
+
+def test_host_errors_attention(lib):
+    f = lib.spec_tree_attention
+    base = dict(q=P, k=P, v=P, dtype=1, bt=None, ps=0, cap=100, npg=0, ctx=P, n=P, anc=P, B=1, nmax=8, hq=8, hkv=2,
+                D=128, maxlen=100, scale=0.1, out=P, ws=P, wsb=1 << 30, st=None, s=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+
+    assert call(hq=6, hkv=4) == -1
+    assert call(D=96) == -2
+    assert call(dtype=7) == -2
+    assert call(nmax=65) == -1
+    assert call(q=None) == -1
+    assert call(scale=0.0) == -1
+    assert call(bt=P, ps=0) == -1
+    assert call(wsb=16) == -5
+
+
+def test_host_errors_reject(lib):
+    f = lib.spec_tree_reject_sample
+    args = [P, P, P, P, 1.0, P, P, P, 1.0, P, P, P, P, P, 1, 8, 100, P, P, None, 0, None, None]
+    a = list(args)
+    a[4] = -0.5
+    assert f(*a) == -1
+    a = list(args)
+    a[8] = 0.0  # T_d must be positive when T > 0
+    assert f(*a) == -1
+    a = list(args)
+    a[4], a[3] = 0.0, None  # greedy needs the argmax
+    assert f(*a) == -1
+    a = list(args)
+    a[12] = None  # stochastic needs uniforms
+    assert f(*a) == -1
+    a = list(args)
+    a[15] = 65
+    assert f(*a) == -1

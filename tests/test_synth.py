@@ -78,7 +78,7 @@ def test_small_variants_of_the_large_workloads():
     c2 = synth.make_config(2, seed=1, ctx_override=64, vocab_override=2048)
     assert c2["parent"].shape == (1, 60) and c2["k"].dtype == np.uint16 and c2["hq"] == 32
     c3 = synth.make_config(3, seed=1, ctx_override=64, vocab_override=2048)
-    assert c3["parent"][0].tolist() == list(range(-1, 15)) and c3["T"] == 0.7
+    assert c3["parent"][0].tolist() == list(range(-1, 15)) and c3["T"] == float(np.float32(0.7))
     c4 = synth.make_config(4, seed=1, ctx_override=100, vocab_override=2048)
     assert c4["B"] == 8 and c4["block_table"] is not None and c4["page_size"] == 16
     used = c4["block_table"][c4["block_table"] >= 0]

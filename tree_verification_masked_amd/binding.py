@@ -1,0 +1,226 @@
+"""Thin ctypes binding over libspectree.so.
+
+Every function keeps the name of the C entry point it wraps, takes torch tensors
+that already live on the GPU, checks dtype / shape / contiguity, and passes raw
+device pointers plus the current HIP stream.  No arithmetic of the verification
+step happens here; PyTorch only provides device memory and streams.  If the
+library is missing the first call raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspectree.so")
+
+SPEC_OK = 0
+SPEC_F32 = 0
+SPEC_BF16 = 1
+NODE_NONE = -1
+NODE_NOT_EVALUATED = -2
+NODE_BAD_REQUEST = -3
+ERRORS = {
+    0: "SPEC_OK", -1: "SPEC_ERR_INVALID_ARG", -2: "SPEC_ERR_UNSUPPORTED", -3: "SPEC_ERR_BAD_TREE",
+    -4: "SPEC_ERR_BAD_INPUT", -5: "SPEC_ERR_WORKSPACE", -6: "SPEC_ERR_HIP",
+}
+
+_lib = None
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "spec_tree_mask_build": [_VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
+    "spec_tree_attention_workspace_size": [_I32, _I32, _I32, _I32, _I32, _I32],
+    "spec_tree_attention": [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
+                            _I32, _F32, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_softmax_workspace_size": [_I64, _I32],
+    "spec_tree_softmax": [_VP, _I64, _I32, _F32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_reject_sample_workspace_size": [_I32, _I32, _I32],
+    "spec_tree_reject_sample": [_VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
+                                _I32, _VP, _VP, _VP, _SZ, _VP, _VP],
+    "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
+    "spec_tree_version": [],
+}
+_RESTYPES = {
+    "spec_tree_attention_workspace_size": _SZ,
+    "spec_tree_softmax_workspace_size": _SZ,
+    "spec_tree_reject_sample_workspace_size": _SZ,
+    "spec_tree_version": ctypes.c_char_p,
+}
+
+
+class SpecTreeError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} returned {code} ({ERRORS.get(code, 'unknown')})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no CPU fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = _RESTYPES.get(name, ctypes.c_int)
+        _lib = handle
+    return _lib
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _check(t, dtype, shape=None, name="tensor"):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _call(name, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != SPEC_OK:
+        raise SpecTreeError(name, rc)
+    return rc
+
+
+def spec_tree_version() -> str:
+    return lib().spec_tree_version().decode()
+
+
+# ---------------------------------------------------------------- workspace sizes
+
+def spec_tree_attention_workspace_size(batch, n_max, hq, hkv, head_dim, max_kv_len) -> int:
+    return int(lib().spec_tree_attention_workspace_size(batch, n_max, hq, hkv, head_dim, max_kv_len))
+
+
+def spec_tree_softmax_workspace_size(rows, vocab) -> int:
+    return int(lib().spec_tree_softmax_workspace_size(rows, vocab))
+
+
+def spec_tree_reject_sample_workspace_size(batch, n_max, vocab) -> int:
+    return int(lib().spec_tree_reject_sample_workspace_size(batch, n_max, vocab))
+
+
+# ---------------------------------------------------------------- entry points
+# Masks travel as int64 tensors holding the uint64 bit patterns.
+
+def spec_tree_mask_build(parent, n_nodes, anc_mask, child_mask, depth, status=None, stream=None):
+    B, n_max = parent.shape
+    _check(parent, torch.int32, (B, n_max), "parent")
+    _check(n_nodes, torch.int32, (B,), "n_nodes")
+    _check(anc_mask, torch.int64, (B, n_max), "anc_mask")
+    _check(child_mask, torch.int64, (B, n_max), "child_mask")
+    _check(depth, torch.int32, (B, n_max), "depth")
+    _check(status, torch.int32, (1,), "status")
+    _call("spec_tree_mask_build", _ptr(parent), _ptr(n_nodes), B, n_max, _ptr(anc_mask), _ptr(child_mask),
+          _ptr(depth), _ptr(status), _stream(stream))
+
+
+def spec_tree_attention(q, k, v, ctx_len, n_nodes, anc_mask, out, workspace, *, hkv, max_kv_len,
+                        block_table=None, page_size=0, n_pages=0, scale=None, status=None, stream=None):
+    B, n_max, hq, D = q.shape
+    if q.dtype == torch.bfloat16:
+        dtype = SPEC_BF16
+    elif q.dtype == torch.float32:
+        dtype = SPEC_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t, nm in ((k, "k"), (v, "v"), (out, "out")):
+        _check(t, q.dtype, None, nm)
+    _check(out, q.dtype, (B, n_max, hq, D), "out")
+    _check(ctx_len, torch.int32, (B,), "ctx_len")
+    _check(n_nodes, torch.int32, (B,), "n_nodes")
+    _check(anc_mask, torch.int64, (B, n_max), "anc_mask")
+    _check(status, torch.int32, (1,), "status")
+    if block_table is None:
+        if k.shape[0] != B or k.shape[2] != hkv or k.shape[3] != D or k.shape != v.shape:
+            raise ValueError("k/v must be [B, kv_capacity, hkv, D]")
+        kv_capacity = k.shape[1]
+    else:
+        _check(block_table, torch.int32, None, "block_table")
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, pages_per_request]")
+        if k.shape[1] != page_size or k.shape[2] != hkv or k.shape[3] != D or k.shape != v.shape:
+            raise ValueError("paged k/v must be [n_pages, page_size, hkv, D]")
+        kv_capacity = block_table.shape[1]
+        n_pages = k.shape[0] if not n_pages else n_pages
+    if scale is None:
+        scale = D ** -0.5
+    _call("spec_tree_attention", _ptr(q), _ptr(k), _ptr(v), dtype, _ptr(block_table), page_size, kv_capacity,
+          n_pages, _ptr(ctx_len), _ptr(n_nodes), _ptr(anc_mask), B, n_max, hq, hkv, D, max_kv_len, scale, _ptr(out),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream))
+
+
+def spec_tree_softmax(logits, temperature, row_max, row_sumexp, row_argmax, workspace, probs=None, status=None,
+                      stream=None):
+    V = logits.shape[-1]
+    R = logits.numel() // V
+    _check(logits, torch.float32, None, "logits")
+    _check(row_max, torch.float32, None, "row_max")
+    _check(row_sumexp, torch.float32, None, "row_sumexp")
+    _check(row_argmax, torch.int32, None, "row_argmax")
+    _check(probs, torch.float32, None, "probs")
+    _check(status, torch.int32, (1,), "status")
+    for t in (row_max, row_sumexp, row_argmax):
+        if t is not None and t.numel() != R:
+            raise ValueError("row outputs must have one entry per logit row")
+    _call("spec_tree_softmax", _ptr(logits), R, V, float(temperature), _ptr(row_max), _ptr(row_sumexp),
+          _ptr(row_argmax), _ptr(probs), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status),
+          _stream(stream))
+
+
+def spec_tree_reject_sample(tgt_logits, tgt_max, tgt_sumexp, tgt_argmax, temperature, dft_logits, dft_max,
+                            dft_sumexp, draft_temperature, tokens, parent, n_nodes, u_accept, u_sample,
+                            accepted_child, term_token, workspace=None, status=None, stream=None):
+    B, n_max, V = tgt_logits.shape
+    _check(tgt_logits, torch.float32, (B, n_max, V), "tgt_logits")
+    _check(dft_logits, torch.float32, (B, n_max, V), "dft_logits")
+    for t, nm in ((tokens, "tokens"), (parent, "parent"), (accepted_child, "accepted_child"),
+                  (term_token, "term_token")):
+        _check(t, torch.int32, (B, n_max), nm)
+    _check(n_nodes, torch.int32, (B,), "n_nodes")
+    _check(u_accept, torch.float32, (B, n_max), "u_accept")
+    _check(u_sample, torch.float32, (B, n_max), "u_sample")
+    _check(status, torch.int32, (1,), "status")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("spec_tree_reject_sample", _ptr(tgt_logits), _ptr(tgt_max), _ptr(tgt_sumexp), _ptr(tgt_argmax),
+          float(temperature), _ptr(dft_logits), _ptr(dft_max), _ptr(dft_sumexp), float(draft_temperature),
+          _ptr(tokens), _ptr(parent), _ptr(n_nodes), _ptr(u_accept), _ptr(u_sample), B, n_max, V,
+          _ptr(accepted_child), _ptr(term_token), _ptr(workspace), ws_bytes, _ptr(status), _stream(stream))
+
+
+def spec_accept_path(accepted_child, term_token, tokens, n_nodes, path_nodes, out_tokens, accept_len, status=None,
+                     stream=None):
+    B, n_max = accepted_child.shape
+    for t, nm in ((accepted_child, "accepted_child"), (term_token, "term_token"), (tokens, "tokens"),
+                  (path_nodes, "path_nodes"), (out_tokens, "out_tokens")):
+        _check(t, torch.int32, (B, n_max), nm)
+    _check(n_nodes, torch.int32, (B,), "n_nodes")
+    _check(accept_len, torch.int32, (B,), "accept_len")
+    _check(status, torch.int32, (1,), "status")
+    _call("spec_accept_path", _ptr(accepted_child), _ptr(term_token), _ptr(tokens), _ptr(n_nodes), B, n_max,
+          _ptr(path_nodes), _ptr(out_tokens), _ptr(accept_len), _ptr(status), _stream(stream))

@@ -1,0 +1,129 @@
+"""One verification step on the GPU: device buffers plus the five library calls.
+
+``VerifyStep`` owns every buffer the step touches (inputs copied to the device
+once, outputs, workspaces, the status word) so that ``run()`` allocates nothing
+and only issues the library calls, in order, on one stream:
+
+    spec_tree_mask_build -> spec_tree_attention -> spec_tree_softmax (target)
+    -> spec_tree_softmax (draft, skipped at T = 0) -> spec_tree_reject_sample
+    -> spec_accept_path
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """Copy a synthetic input set (numpy, see synth.make_config) to the GPU."""
+    d = {}
+    for key in ("parent", "tokens", "n_nodes", "ctx_len", "block_table"):
+        if inp.get(key) is not None:
+            d[key] = torch.from_numpy(np.ascontiguousarray(inp[key], np.int32)).to(device)
+    for key in ("tgt_logits", "dft_logits", "u_accept", "u_sample"):
+        if inp.get(key) is not None:
+            d[key] = torch.from_numpy(np.ascontiguousarray(inp[key], np.float32)).to(device)
+    if inp.get("q") is not None:
+        for key in ("q", "k", "v"):
+            a = np.ascontiguousarray(inp[key])
+            if inp["bf16"]:
+                d[key] = torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+            else:
+                d[key] = torch.from_numpy(a.astype(np.float32)).to(device)
+    for key in ("B", "n_max", "V", "hq", "hkv", "d", "T", "Td", "bf16", "page_size", "n_pages", "kv_capacity"):
+        if key in inp:
+            d[key] = inp[key]
+    d["max_kv_len"] = int(np.max(inp["ctx_len"]) + inp["n_max"])
+    return d
+
+
+class VerifyStep:
+    def __init__(self, dev: dict, with_attention: bool = True):
+        self.d = dev
+        Bn, n_max, V = dev["B"], dev["n_max"], dev["V"]
+        cuda = dev["parent"].device
+        i32 = dict(dtype=torch.int32, device=cuda)
+        f32 = dict(dtype=torch.float32, device=cuda)
+        self.T, self.Td = float(dev["T"]), float(dev["Td"])
+        self.with_attention = with_attention and dev.get("q") is not None
+        self.status = torch.zeros(1, **i32)
+        self.anc = torch.zeros((Bn, n_max), dtype=torch.int64, device=cuda)
+        self.child = torch.zeros((Bn, n_max), dtype=torch.int64, device=cuda)
+        self.depth = torch.zeros((Bn, n_max), **i32)
+        if self.with_attention:
+            self.attn_out = torch.empty_like(dev["q"])
+            ws = B.spec_tree_attention_workspace_size(Bn, n_max, dev["hq"], dev["hkv"], dev["d"], dev["max_kv_len"])
+            self.attn_ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=cuda)
+        R = Bn * n_max
+        self.tmax, self.tsum, self.targ = torch.zeros(R, **f32), torch.zeros(R, **f32), torch.zeros(R, **i32)
+        self.dmax, self.dsum = torch.zeros(R, **f32), torch.zeros(R, **f32)
+        sm_ws = B.spec_tree_softmax_workspace_size(R, V)
+        self.sm_ws_t = torch.zeros(sm_ws, dtype=torch.uint8, device=cuda)
+        self.sm_ws_d = torch.zeros(sm_ws, dtype=torch.uint8, device=cuda)
+        rj = B.spec_tree_reject_sample_workspace_size(Bn, n_max, V)
+        self.rj_ws = torch.zeros(max(rj, 256), dtype=torch.uint8, device=cuda)
+        self.accepted_child = torch.zeros((Bn, n_max), **i32)
+        self.term_token = torch.zeros((Bn, n_max), **i32)
+        self.path_nodes = torch.zeros((Bn, n_max), **i32)
+        self.out_tokens = torch.zeros((Bn, n_max), **i32)
+        self.accept_len = torch.zeros(Bn, **i32)
+
+    # the individual stages -------------------------------------------------
+    def mask(self, stream=None):
+        d = self.d
+        B.spec_tree_mask_build(d["parent"], d["n_nodes"], self.anc, self.child, self.depth, self.status, stream)
+
+    def attention(self, stream=None, q=None, k=None, v=None, out=None):
+        d = self.d
+        B.spec_tree_attention(d["q"] if q is None else q, d["k"] if k is None else k, d["v"] if v is None else v,
+                              d["ctx_len"], d["n_nodes"], self.anc, self.attn_out if out is None else out,
+                              self.attn_ws, hkv=d["hkv"], max_kv_len=d["max_kv_len"],
+                              block_table=d.get("block_table"), page_size=d.get("page_size", 0),
+                              n_pages=d.get("n_pages", 0), status=self.status, stream=stream)
+
+    def softmax(self, stream=None, tgt=None, dft=None):
+        d = self.d
+        B.spec_tree_softmax(d["tgt_logits"] if tgt is None else tgt, self.T, self.tmax, self.tsum, self.targ,
+                            self.sm_ws_t, status=self.status, stream=stream)
+        if self.T > 0:
+            B.spec_tree_softmax(d["dft_logits"] if dft is None else dft, self.Td, self.dmax, self.dsum, None,
+                                self.sm_ws_d, status=self.status, stream=stream)
+
+    def reject(self, stream=None, tgt=None, dft=None):
+        d = self.d
+        greedy = self.T == 0
+        B.spec_tree_reject_sample(d["tgt_logits"] if tgt is None else tgt, self.tmax, self.tsum, self.targ, self.T,
+                                  None if greedy else (d["dft_logits"] if dft is None else dft),
+                                  None if greedy else self.dmax, None if greedy else self.dsum, self.Td,
+                                  d["tokens"], d["parent"], d["n_nodes"], None if greedy else d["u_accept"],
+                                  None if greedy else d["u_sample"], self.accepted_child, self.term_token,
+                                  self.rj_ws, self.status, stream)
+
+    def path(self, stream=None):
+        d = self.d
+        B.spec_accept_path(self.accepted_child, self.term_token, d["tokens"], d["n_nodes"], self.path_nodes,
+                           self.out_tokens, self.accept_len, self.status, stream)
+
+    def run(self, stream=None, replica=None):
+        """The whole step.  ``replica`` (optional dict) swaps in another copy of the
+        large inputs (q/k/v and logits) so that timed loops can rotate buffers."""
+        r = replica or {}
+        self.mask(stream)
+        if self.with_attention:
+            self.attention(stream, r.get("q"), r.get("k"), r.get("v"))
+        self.softmax(stream, r.get("tgt_logits"), r.get("dft_logits"))
+        self.reject(stream, r.get("tgt_logits"), r.get("dft_logits"))
+        self.path(stream)
+
+    def results(self) -> dict:
+        torch.cuda.synchronize()
+        out = {k: getattr(self, k).cpu().numpy() for k in
+               ("anc", "child", "depth", "tmax", "tsum", "targ", "dmax", "dsum", "accepted_child", "term_token",
+                "path_nodes", "out_tokens", "accept_len", "status")}
+        out["anc"] = out["anc"].view(np.uint64)
+        out["child"] = out["child"].view(np.uint64)
+        if self.with_attention:
+            out["attn"] = self.attn_out.float().cpu().numpy()
+        return out

@@ -331,7 +331,9 @@ def make_config(cfg: int, seed: int = 0, T: float | None = None, with_kv: bool =
             tgt[b, i] = tr
             dft[b, i] = dr
     urng = rng_for(seed, cfg, 9)
-    inp.update(dict(B=B, n_max=n_max, V=V, hq=hq, hkv=hkv, d=d, T=float(T_), Td=float(Td), bf16=bf16,
+    # temperatures are fp32 values (what the library receives), carried as Python floats
+    T_, Td = float(np.float32(T_)), float(np.float32(Td))
+    inp.update(dict(B=B, n_max=n_max, V=V, hq=hq, hkv=hkv, d=d, T=T_, Td=Td, bf16=bf16,
                     parent=parent, tokens=tokens, n_nodes=n_nodes, tgt_logits=tgt, dft_logits=dft,
                     u_accept=uniforms(urng, (B, n_max)), u_sample=uniforms(urng, (B, n_max)),
                     ctx_len=np.array(ctxs, np.int32)))
