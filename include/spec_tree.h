@@ -128,15 +128,35 @@ int spec_tree_attention(const void* q, const void* k, const void* v, int32_t dty
  *   row_argmax[r] = smallest x with logits[r,x] == row_max[r]       (nullable)
  *   probs[r,x]    = exp((logits[r,x] - row_max[r]) / T) / row_sumexp (nullable,
  *                   T > 0; meant for tests)
+ *   chunk_max[r,c], chunk_sum[r,c] (nullable, both or neither): for chunk c of
+ *                   spec_tree_softmax_chunk() tokens, the chunk's maximum m_c and
+ *                   sum_x exp((logits[r,x] - m_c) / T) in fp64 -- the rejection
+ *                   sampler uses them to draw bonus tokens at leaves without
+ *                   another pass over the row.  [rows, ceil(vocab / chunk)].
  * logits: fp32 [rows, vocab].  -inf logits are probability 0.  A row holding NaN
  * or +inf, or only -inf, gets row_max = NaN and SPEC_ERR_BAD_INPUT in status.
  * T == 0 computes row_max and row_argmax only.
  * Host errors: rows < 1, vocab < 1, T < 0 or NaN, null outputs, workspace.
  */
+int32_t spec_tree_softmax_chunk(void);
 size_t spec_tree_softmax_workspace_size(int64_t rows, int32_t vocab);
 int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float temperature, float* row_max,
-                      float* row_sumexp, int32_t* row_argmax, float* probs, void* workspace, size_t workspace_bytes,
-                      int32_t* status, void* stream);
+                      float* row_sumexp, int32_t* row_argmax, float* probs, float* chunk_max, double* chunk_sum,
+                      void* workspace, size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
+ * The same statistics for the target rows (temperature T, with argmax and chunk
+ * partials) and the draft rows (temperature T_d) of a step in one launch, so the
+ * two vocabulary passes share the GPU instead of running back to back.  Both
+ * arrays are fp32 [rows, vocab]; T > 0 and T_d > 0.  tgt_argmax, tgt_chunk_max
+ * and tgt_chunk_sum are nullable (the chunk pair both or neither).
+ */
+size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vocab);
+int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
+                           float draft_temperature, int64_t rows, int32_t vocab, float* tgt_max, float* tgt_sumexp,
+                           int32_t* tgt_argmax, float* tgt_chunk_max, double* tgt_chunk_sum, float* dft_max,
+                           float* dft_sumexp, void* workspace, size_t workspace_bytes, int32_t* status,
+                           void* stream);
 
 /*
  * Tree rejection sampling (gingerlabs page, "Target-model decoding is serial";
@@ -154,7 +174,8 @@ int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float te
  * accepted, the terminal token is that argmax; draft inputs and uniforms may be
  * NULL.
  * Inputs: tgt_logits, dft_logits fp32 [batch, n_max, vocab]; the row statistics
- * of spec_tree_softmax over the same rows (tgt_argmax needed only at T == 0);
+ * of spec_tree_softmax over the same rows (tgt_argmax needed only at T == 0;
+ * tgt_chunk_max / tgt_chunk_sum optional, both or neither, from the same call);
  * tokens, parent int32 [batch, n_max]; n_nodes int32 [batch]; u_accept, u_sample
  * fp32 [batch, n_max] in (0, 1).
  * Outputs int32 [batch, n_max]: accepted_child[b,n] = accepted child,
@@ -163,12 +184,19 @@ int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float te
  * SPEC_NODE_NOT_EVALUATED.  A request with a bad tree, a token outside
  * [0, vocab) or an invalid logit row gets accepted_child[b,0] =
  * SPEC_NODE_BAD_REQUEST and a device error code.
+ * T > 0 needs the workspace of spec_tree_reject_sample_workspace_size
+ * (zero-filled once; every call leaves it ready for the next).  Each node is
+ * evaluated in parallel and the last workgroup of a request walks the results;
+ * vocabularies of more than one chunk add a ratio-histogram launch and an
+ * exact-sum launch first, so no workgroup waits on another.  At T == 0 the
+ * workspace may be NULL.
  * Host errors: T < 0 or NaN, T > 0 with T_d <= 0, null required pointers, sizes,
  * workspace.
  */
 size_t spec_tree_reject_sample_workspace_size(int32_t batch, int32_t n_max, int32_t vocab);
 int spec_tree_reject_sample(const float* tgt_logits, const float* tgt_max, const float* tgt_sumexp,
-                            const int32_t* tgt_argmax, float temperature, const float* dft_logits,
+                            const int32_t* tgt_argmax, const float* tgt_chunk_max, const double* tgt_chunk_sum,
+                            float temperature, const float* dft_logits,
                             const float* dft_max, const float* dft_sumexp, float draft_temperature,
                             const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
                             const float* u_accept, const float* u_sample, int32_t batch, int32_t n_max, int32_t vocab,

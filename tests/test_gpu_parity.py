@@ -135,6 +135,40 @@ def test_softmax_parity(V, T):
         assert (pr[~big] < 1e-29).all()
 
 
+@pytest.mark.parametrize("V", [1000, 128256, 151936])
+def test_softmax_pair_and_chunk_partials(V):
+    """The fused target+draft launch equals two single launches; chunk partials match
+    their definition (chunk max exactly, chunk sum of exp((l - m_c)/T) within 1e-5)."""
+    say("softmax pair", V)
+    rng = np.random.default_rng(V)
+    R, T, Td = 7, float(np.float32(0.7)), 1.0
+    tgt = (rng.standard_normal((R, V)) * 3).astype(np.float32)
+    dft = (tgt + rng.standard_normal((R, V))).astype(np.float32)
+    ch = B.spec_tree_softmax_chunk()
+    nch = -(-V // ch)
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, dtype=dt, device="cuda")
+    tm, ts, ta, cm, cs, dm, ds = z(R), z(R), z(R, dt=torch.int32), z(R, nch), z(R, nch, dt=torch.float64), z(R), z(R)
+    ws = z(B.spec_tree_softmax_pair_workspace_size(R, V), dt=torch.uint8)
+    st = z(1, dt=torch.int32)
+    for _ in range(2):
+        B.spec_tree_softmax_pair(dev(tgt), T, dev(dft), Td, tm, ts, ta, cm, cs, dm, ds, ws, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    rt = oracle.softmax(tgt, T, want_probs=False)
+    rd = oracle.softmax(dft, Td, want_probs=False)
+    assert np.array_equal(tm.cpu().numpy().astype(np.float64), rt["max"])
+    assert np.array_equal(ta.cpu().numpy(), rt["argmax"])
+    np.testing.assert_allclose(ts.cpu().numpy(), rt["sumexp"], rtol=1e-5)
+    assert np.array_equal(dm.cpu().numpy().astype(np.float64), rd["max"])
+    np.testing.assert_allclose(ds.cpu().numpy(), rd["sumexp"], rtol=1e-5)
+    cmx, csm = cm.cpu().numpy(), cs.cpu().numpy()
+    for c in range(nch):
+        part = tgt[:, c * ch:(c + 1) * ch].astype(np.float64)
+        assert np.array_equal(cmx[:, c].astype(np.float64), part.max(axis=1))
+        ref = np.exp((part - part.max(axis=1, keepdims=True)) / T).sum(axis=1)
+        np.testing.assert_allclose(csm[:, c], ref, rtol=1e-5)
+
+
 def test_softmax_flags_bad_rows():
     say("softmax bad rows")
     logits = np.zeros((4, 300), np.float32)

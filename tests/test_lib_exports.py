@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding and header disagree"
@@ -57,11 +57,16 @@ def test_host_errors_mask_and_path(lib):
 
 def test_host_errors_softmax(lib):
     f = lib.spec_tree_softmax
-    assert f(P, 4, 100, -1.0, P, P, P, None, P, 1 << 20, None, None) == -1       # T < 0
-    assert f(P, 4, 100, float("nan"), P, P, P, None, P, 1 << 20, None, None) == -1
-    assert f(P, 4, 100, 1.0, P, None, P, None, P, 1 << 20, None, None) == -1     # T > 0 needs sums
-    assert f(P, 4, 100, 1.0, P, P, P, None, P, 8, None, None) == -5              # workspace too small
-    assert f(P, 4, 100, 1.0, P, P, P, None, None, 0, None, None) == -5
+    assert f(P, 4, 100, -1.0, P, P, P, None, None, None, P, 1 << 20, None, None) == -1       # T < 0
+    assert f(P, 4, 100, float("nan"), P, P, P, None, None, None, P, 1 << 20, None, None) == -1
+    assert f(P, 4, 100, 1.0, P, None, P, None, None, None, P, 1 << 20, None, None) == -1     # T > 0 needs sums
+    assert f(P, 4, 100, 1.0, P, P, P, None, None, None, P, 8, None, None) == -5              # workspace
+    assert f(P, 4, 100, 1.0, P, P, P, None, None, None, None, 0, None, None) == -5
+    g = lib.spec_tree_softmax_pair
+    assert g(P, 1.0, P, 0.0, 4, 100, P, P, P, None, None, P, P, P, 1 << 20, None, None) == -1  # T_d = 0
+    assert g(P, 1.0, None, 1.0, 4, 100, P, P, P, None, None, P, P, P, 1 << 20, None, None) == -1
+    assert g(P, 1.0, P, 1.0, 4, 100, P, P, P, None, None, P, P, P, 8, None, None) == -5
+    assert lib.spec_tree_softmax_chunk() == 4096
 
 
 def test_host_errors_attention(lib):
@@ -85,19 +90,30 @@ def test_host_errors_attention(lib):
 
 def test_host_errors_reject(lib):
     f = lib.spec_tree_reject_sample
-    args = [P, P, P, P, 1.0, P, P, P, 1.0, P, P, P, P, P, 1, 8, 100, P, P, None, 0, None, None]
+    #       tl mx se am cmx csm T    dl mx se Td   tok par nn ua us B  nmax V    acc term ws   wsb st   s
+    args = [P, P, P, P, None, None, 1.0, P, P, P, 1.0, P, P, P, P, P, 1, 8, 100, P, P, None, 0, None, None]
     a = list(args)
-    a[4] = -0.5
+    a[6] = -0.5
     assert f(*a) == -1
     a = list(args)
-    a[8] = 0.0  # T_d must be positive when T > 0
+    a[10] = 0.0  # T_d must be positive when T > 0
     assert f(*a) == -1
     a = list(args)
-    a[4], a[3] = 0.0, None  # greedy needs the argmax
+    a[6], a[3] = 0.0, None  # greedy needs the argmax
     assert f(*a) == -1
     a = list(args)
-    a[12] = None  # stochastic needs uniforms
+    a[14] = None  # stochastic needs uniforms
     assert f(*a) == -1
     a = list(args)
-    a[15] = 65
+    a[17] = 65
     assert f(*a) == -1
+    a = list(args)
+    a[4] = P  # chunk partials come as a pair
+    assert f(*a) == -1
+    assert f(*args) == -5  # T > 0 needs the workspace (per-node results)
+    a = list(args)
+    a[18] = 100000
+    assert f(*a) == -5
+    assert binding.spec_tree_reject_sample_workspace_size(1, 60, 4096) < 4096
+    assert binding.spec_tree_reject_sample_workspace_size(1, 65, 4096) == 0
+    assert binding.spec_tree_reject_sample_workspace_size(1, 60, 128256) > 60 * 4096 * 32

@@ -39,17 +39,23 @@ _SIGNATURES = {
     "spec_tree_attention_workspace_size": [_I32, _I32, _I32, _I32, _I32, _I32],
     "spec_tree_attention": [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                             _I32, _F32, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_softmax_chunk": [],
     "spec_tree_softmax_workspace_size": [_I64, _I32],
-    "spec_tree_softmax": [_VP, _I64, _I32, _F32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_softmax": [_VP, _I64, _I32, _F32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_softmax_pair_workspace_size": [_I64, _I32],
+    "spec_tree_softmax_pair": [_VP, _F32, _VP, _F32, _I64, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
+                               _VP],
     "spec_tree_reject_sample_workspace_size": [_I32, _I32, _I32],
-    "spec_tree_reject_sample": [_VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
-                                _I32, _VP, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_reject_sample": [_VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _I32,
+                                _I32, _I32, _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_version": [],
 }
 _RESTYPES = {
+    "spec_tree_softmax_chunk": _I32,
     "spec_tree_attention_workspace_size": _SZ,
     "spec_tree_softmax_workspace_size": _SZ,
+    "spec_tree_softmax_pair_workspace_size": _SZ,
     "spec_tree_reject_sample_workspace_size": _SZ,
     "spec_tree_version": ctypes.c_char_p,
 }
@@ -121,6 +127,14 @@ def spec_tree_softmax_workspace_size(rows, vocab) -> int:
     return int(lib().spec_tree_softmax_workspace_size(rows, vocab))
 
 
+def spec_tree_softmax_pair_workspace_size(rows, vocab) -> int:
+    return int(lib().spec_tree_softmax_pair_workspace_size(rows, vocab))
+
+
+def spec_tree_softmax_chunk() -> int:
+    return int(lib().spec_tree_softmax_chunk())
+
+
 def spec_tree_reject_sample_workspace_size(batch, n_max, vocab) -> int:
     return int(lib().spec_tree_reject_sample_workspace_size(batch, n_max, vocab))
 
@@ -175,8 +189,8 @@ def spec_tree_attention(q, k, v, ctx_len, n_nodes, anc_mask, out, workspace, *, 
           _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream))
 
 
-def spec_tree_softmax(logits, temperature, row_max, row_sumexp, row_argmax, workspace, probs=None, status=None,
-                      stream=None):
+def spec_tree_softmax(logits, temperature, row_max, row_sumexp, row_argmax, workspace, probs=None, chunk_max=None,
+                      chunk_sum=None, status=None, stream=None):
     V = logits.shape[-1]
     R = logits.numel() // V
     _check(logits, torch.float32, None, "logits")
@@ -184,18 +198,45 @@ def spec_tree_softmax(logits, temperature, row_max, row_sumexp, row_argmax, work
     _check(row_sumexp, torch.float32, None, "row_sumexp")
     _check(row_argmax, torch.int32, None, "row_argmax")
     _check(probs, torch.float32, None, "probs")
+    _check(chunk_max, torch.float32, None, "chunk_max")
+    _check(chunk_sum, torch.float64, None, "chunk_sum")
     _check(status, torch.int32, (1,), "status")
     for t in (row_max, row_sumexp, row_argmax):
         if t is not None and t.numel() != R:
             raise ValueError("row outputs must have one entry per logit row")
+    nch = -(-V // spec_tree_softmax_chunk())
+    for t in (chunk_max, chunk_sum):
+        if t is not None and t.numel() != R * nch:
+            raise ValueError("chunk outputs must be [rows, ceil(vocab / chunk)]")
     _call("spec_tree_softmax", _ptr(logits), R, V, float(temperature), _ptr(row_max), _ptr(row_sumexp),
-          _ptr(row_argmax), _ptr(probs), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status),
+          _ptr(row_argmax), _ptr(probs), _ptr(chunk_max), _ptr(chunk_sum), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream))
+
+
+def spec_tree_softmax_pair(tgt_logits, temperature, dft_logits, draft_temperature, tgt_max, tgt_sumexp, tgt_argmax,
+                           tgt_chunk_max, tgt_chunk_sum, dft_max, dft_sumexp, workspace, status=None, stream=None):
+    V = tgt_logits.shape[-1]
+    R = tgt_logits.numel() // V
+    _check(tgt_logits, torch.float32, None, "tgt_logits")
+    _check(dft_logits, torch.float32, tuple(tgt_logits.shape), "dft_logits")
+    for t, nm in ((tgt_max, "tgt_max"), (tgt_sumexp, "tgt_sumexp"), (dft_max, "dft_max"), (dft_sumexp, "dft_sumexp")):
+        _check(t, torch.float32, None, nm)
+        if t.numel() != R:
+            raise ValueError(f"{nm} must have one entry per row")
+    _check(tgt_argmax, torch.int32, None, "tgt_argmax")
+    _check(tgt_chunk_max, torch.float32, None, "tgt_chunk_max")
+    _check(tgt_chunk_sum, torch.float64, None, "tgt_chunk_sum")
+    _check(status, torch.int32, (1,), "status")
+    _call("spec_tree_softmax_pair", _ptr(tgt_logits), float(temperature), _ptr(dft_logits), float(draft_temperature),
+          R, V, _ptr(tgt_max), _ptr(tgt_sumexp), _ptr(tgt_argmax), _ptr(tgt_chunk_max), _ptr(tgt_chunk_sum),
+          _ptr(dft_max), _ptr(dft_sumexp), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status),
           _stream(stream))
 
 
 def spec_tree_reject_sample(tgt_logits, tgt_max, tgt_sumexp, tgt_argmax, temperature, dft_logits, dft_max,
                             dft_sumexp, draft_temperature, tokens, parent, n_nodes, u_accept, u_sample,
-                            accepted_child, term_token, workspace=None, status=None, stream=None):
+                            accepted_child, term_token, workspace=None, status=None, stream=None,
+                            tgt_chunk_max=None, tgt_chunk_sum=None):
     B, n_max, V = tgt_logits.shape
     _check(tgt_logits, torch.float32, (B, n_max, V), "tgt_logits")
     _check(dft_logits, torch.float32, (B, n_max, V), "dft_logits")
@@ -205,12 +246,15 @@ def spec_tree_reject_sample(tgt_logits, tgt_max, tgt_sumexp, tgt_argmax, tempera
     _check(n_nodes, torch.int32, (B,), "n_nodes")
     _check(u_accept, torch.float32, (B, n_max), "u_accept")
     _check(u_sample, torch.float32, (B, n_max), "u_sample")
+    _check(tgt_chunk_max, torch.float32, None, "tgt_chunk_max")
+    _check(tgt_chunk_sum, torch.float64, None, "tgt_chunk_sum")
     _check(status, torch.int32, (1,), "status")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("spec_tree_reject_sample", _ptr(tgt_logits), _ptr(tgt_max), _ptr(tgt_sumexp), _ptr(tgt_argmax),
-          float(temperature), _ptr(dft_logits), _ptr(dft_max), _ptr(dft_sumexp), float(draft_temperature),
-          _ptr(tokens), _ptr(parent), _ptr(n_nodes), _ptr(u_accept), _ptr(u_sample), B, n_max, V,
-          _ptr(accepted_child), _ptr(term_token), _ptr(workspace), ws_bytes, _ptr(status), _stream(stream))
+          _ptr(tgt_chunk_max), _ptr(tgt_chunk_sum), float(temperature), _ptr(dft_logits), _ptr(dft_max),
+          _ptr(dft_sumexp), float(draft_temperature), _ptr(tokens), _ptr(parent), _ptr(n_nodes), _ptr(u_accept),
+          _ptr(u_sample), B, n_max, V, _ptr(accepted_child), _ptr(term_token), _ptr(workspace), ws_bytes,
+          _ptr(status), _stream(stream))
 
 
 def spec_accept_path(accepted_child, term_token, tokens, n_nodes, path_nodes, out_tokens, accept_len, status=None,

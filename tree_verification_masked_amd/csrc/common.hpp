@@ -10,6 +10,9 @@
 namespace spectree {
 
 constexpr int kWave = 64;
+// Vocabulary chunk shared by the softmax statistics and the samplers: chunk c of a
+// row covers tokens [c * kChunk, (c + 1) * kChunk).
+constexpr int kChunk = 4096;
 
 // First data error wins; later errors leave the word unchanged.
 __device__ inline void report(int32_t* status, int32_t code) {
@@ -71,6 +74,31 @@ __device__ inline float exp_scaled(float d, ExpScale s) {
 }
 
 __device__ inline bool is_bad_logit(float x) { return isnan(x) || x == INFINITY; }
+
+// ---- publishing small results across workgroups (last-block merges) ----
+// Values meant for another workgroup are written with agent-scope atomic stores
+// (they bypass the non-coherent caches), the writer waits for its stores to
+// complete before bumping the counter, and the reader uses agent-scope atomic
+// loads.  This keeps the merge free of whole-L2 write-back / invalidate fences.
+template <typename T>
+__device__ inline void pub_store(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ inline T pub_load(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All of this thread's prior stores have completed (compiler fences keep the
+// surrounding memory operations on their side of the wait).
+__device__ inline void stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Returns the counter value before the increment.
+__device__ inline uint32_t pub_arrive(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 }  // namespace spectree
 

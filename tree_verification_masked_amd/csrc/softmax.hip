@@ -5,84 +5,101 @@
 // Tree-verification notes, parts A and D.2: one softmax per tree node, N x |V|
 // elements per verify, bound by memory bandwidth.
 //
-// One pass over the logits.  A row is cut into chunks of kChunk elements; each
-// workgroup reads one chunk with 16-byte loads (every element read once), keeps it
-// in registers, and produces the chunk's maximum, first argmax and
-// sum exp((l - m_chunk) / T) accumulated in fp64.  The last workgroup to finish a
-// row (device-scope counter in the workspace, reset by that workgroup) merges the
-// chunk partials in chunk order: m = max m_c, Z = sum_c s_c exp((m_c - m) / T).
+// One pass over the logits.  A row is cut into chunks of kChunk tokens; each
+// workgroup reads one chunk with 16-byte loads that are all in flight at once
+// (full chunks take a branch-free path), keeps it in registers, and writes the
+// chunk's maximum m_c, first argmax and s_c = sum exp((l - m_c) / T) accumulated in
+// fp64.  A second, small launch merges the chunk partials of each row in chunk
+// order:  m = max_c m_c,  Z = sum_c s_c exp((m_c - m) / T).  (Merging inside the
+// first launch would make every workgroup wait for its partials to become visible
+// device-wide before signalling; on MI355X that costs more than the extra launch.)
+// One launch can cover two logit arrays (target and draft rows, each with its own
+// temperature).
 #include "common.hpp"
 
 namespace spectree {
 
 constexpr int kSmThreads = 256;
-constexpr int kSmPerThread = 32;                      // fp32 elements held per thread
-constexpr int kChunk = kSmThreads * kSmPerThread;     // 8192 elements per workgroup
-
-struct SmWorkspace {
-  float* cmax;     // [rows, nch]
-  double* csum;    // [rows, nch]
-  int32_t* carg;   // [rows, nch]
-  int32_t* cbad;   // [rows, nch]
-  uint32_t* count; // [rows]
-};
+constexpr int kSmPerThread = kChunk / kSmThreads;  // 32 fp32 elements held per thread
 
 inline int sm_chunks(int32_t vocab) { return (vocab + kChunk - 1) / kChunk; }
-
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline size_t sm_layout(int64_t rows, int32_t vocab, char* base, SmWorkspace* w) {
+struct SmSet {
+  const float* logits;
+  int64_t rows;
+  double inv_t;
+  ExpScale es;
+  int greedy;
+  float* row_max;
+  float* row_sumexp;
+  int32_t* row_argmax;
+  float* cmax;      // [rows, nch]  chunk maxima (caller's array or workspace)
+  double* csum;     // [rows, nch]  chunk sums of exp((l - m_c)/T)
+  int32_t* carg;    // [rows, nch]  workspace
+  int32_t* cbad;    // [rows, nch]  workspace
+};
+
+// Workspace of one logit array: argmax / bad flags per chunk, and the chunk maxima
+// and sums unless the caller asked for them.
+inline size_t sm_set_bytes(int64_t rows, int32_t vocab) {
+  const size_t n = (size_t)rows * (size_t)sm_chunks(vocab);
+  return align256(n * 4) * 3 + align256(n * 8);
+}
+inline void sm_set_carve(char* base, int64_t rows, int32_t vocab, SmSet* s, float* cmax, double* csum) {
   const size_t n = (size_t)rows * (size_t)sm_chunks(vocab);
   size_t off = 0;
-  auto take = [&](size_t bytes) {
-    char* p = base ? base + off : nullptr;
-    off += align256(bytes);
-    return p;
-  };
-  char* p0 = take(n * sizeof(float));
-  char* p1 = take(n * sizeof(double));
-  char* p2 = take(n * sizeof(int32_t));
-  char* p3 = take(n * sizeof(int32_t));
-  char* p4 = take((size_t)rows * sizeof(uint32_t));
-  if (w) {
-    w->cmax = (float*)p0;
-    w->csum = (double*)p1;
-    w->carg = (int32_t*)p2;
-    w->cbad = (int32_t*)p3;
-    w->count = (uint32_t*)p4;
+  s->carg = (int32_t*)(base + off);
+  off += align256(n * 4);
+  s->cbad = (int32_t*)(base + off);
+  off += align256(n * 4);
+  s->cmax = cmax ? cmax : (float*)(base + off);
+  off += align256(n * 4);
+  s->csum = csum ? csum : (double*)(base + off);
+}
+
+__device__ inline void better(float& m, int& a, float om, int oa) {
+  if (om > m || (om == m && oa < a)) {
+    m = om;
+    a = oa;
   }
-  return off;
 }
 
 template <bool kVec>
-__global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(const float* __restrict__ logits, int32_t vocab,
-                                                                   int nch, double inv_t, ExpScale es, int greedy,
-                                                                   SmWorkspace ws, float* __restrict__ row_max,
-                                                                   float* __restrict__ row_sumexp,
-                                                                   int32_t* __restrict__ row_argmax, int32_t* status) {
-  const int chunk = (int)(blockIdx.x % (unsigned)nch);
-  const int64_t row = (int64_t)(blockIdx.x / (unsigned)nch);
+__global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSet B, int32_t vocab, int nch,
+                                                                   int32_t* status) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
-  const float* src = logits + row * (int64_t)vocab;
+  int64_t blk = blockIdx.x;
+  const int64_t blocks_a = A.rows * nch;
+  const bool second = blk >= blocks_a;
+  const SmSet& S = second ? B : A;
+  if (second) blk -= blocks_a;
+  const int chunk = (int)(blk % nch);
+  const int64_t row = blk / nch;
+  const float* src = S.logits + row * (int64_t)vocab;
   const int c0 = chunk * kChunk;
 
   // Element (k, v) of a thread is token c0 + (k * kSmThreads + tid) * 4 + v, so
   // consecutive threads read consecutive 16-byte pieces.
   float x[kSmPerThread];
+  if (kVec && c0 + kChunk <= vocab) {
 #pragma unroll
-  for (int k = 0; k < kSmPerThread / 4; ++k) {
-    const int t = c0 + (k * kSmThreads + tid) * 4;
-    if (kVec && t + 3 < vocab) {
-      const float4 f = *reinterpret_cast<const float4*>(src + t);
+    for (int k = 0; k < kSmPerThread / 4; ++k) {
+      const float4 f = *reinterpret_cast<const float4*>(src + c0 + (k * kSmThreads + tid) * 4);
       x[4 * k + 0] = f.x;
       x[4 * k + 1] = f.y;
       x[4 * k + 2] = f.z;
       x[4 * k + 3] = f.w;
-    } else {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) x[4 * k + v] = (t + v < vocab) ? src[t + v] : -INFINITY;
     }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSmPerThread / 4; ++k)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = c0 + (k * kSmThreads + tid) * 4 + v;
+        x[4 * k + v] = t < vocab ? src[t] : -INFINITY;
+      }
   }
   float m = -INFINITY;
   int am = 0x7fffffff;
@@ -92,36 +109,23 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(const float* 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float e = x[4 * k + v];
-      const int t = c0 + (k * kSmThreads + tid) * 4 + v;
       bad |= is_bad_logit(e) ? 1 : 0;
-      if (e > m) {  // tokens are visited in increasing order per thread
+      if (e > m) {  // a thread visits its tokens in increasing order
         m = e;
-        am = t;
+        am = c0 + (k * kSmThreads + tid) * 4 + v;
       }
     }
-  // block max / first argmax / bad flag
   __shared__ float s_m[kSmThreads / 64];
   __shared__ int s_a[kSmThreads / 64];
   __shared__ int s_b[kSmThreads / 64];
   __shared__ double s_s[kSmThreads / 64];
-  {
-    float wm = m;
-    int wa = am;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float om = __shfl_xor(wm, o);
-      const int oa = __shfl_xor(wa, o);
-      if (om > wm || (om == wm && oa < wa)) {
-        wm = om;
-        wa = oa;
-      }
-    }
-    const int wb = wave_or_i(bad);
-    if (lane == 0) {
-      s_m[wid] = wm;
-      s_a[wid] = wa;
-      s_b[wid] = wb;
-    }
+  for (int o = 32; o > 0; o >>= 1) better(m, am, __shfl_xor(m, o), __shfl_xor(am, o));
+  bad = wave_or_i(bad);
+  if (lane == 0) {
+    s_m[wid] = m;
+    s_a[wid] = am;
+    s_b[wid] = bad;
   }
   __syncthreads();
   float cm = s_m[0];
@@ -129,17 +133,14 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(const float* 
   int cb = s_b[0];
 #pragma unroll
   for (int w = 1; w < kSmThreads / 64; ++w) {
-    if (s_m[w] > cm || (s_m[w] == cm && s_a[w] < ca)) {
-      cm = s_m[w];
-      ca = s_a[w];
-    }
+    better(cm, ca, s_m[w], s_a[w]);
     cb |= s_b[w];
   }
   double csum = 0.0;
-  if (!greedy && cm > -INFINITY) {
+  if (!S.greedy && cm > -INFINITY) {
     double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < kSmPerThread; ++k) acc += (double)exp_scaled(x[k] - cm, es);
+    for (int k = 0; k < kSmPerThread; ++k) acc += (double)exp_scaled(x[k] - cm, S.es);
     acc = wave_sum_d(acc);
     if (lane == 0) s_s[wid] = acc;
     __syncthreads();
@@ -147,60 +148,46 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(const float* 
 #pragma unroll
     for (int w = 1; w < kSmThreads / 64; ++w) csum += s_s[w];
   }
-  const int64_t slot = row * nch + chunk;
-  __shared__ int s_last;
   if (tid == 0) {
-    ws.cmax[slot] = cm;
-    ws.csum[slot] = csum;
-    ws.carg[slot] = ca;
-    ws.cbad[slot] = cb;
-    __threadfence();  // partials visible device-wide before the counter moves
-    const uint32_t prev = atomicAdd(&ws.count[row], 1u);
-    s_last = (prev == (uint32_t)(nch - 1));
+    const int64_t slot = row * nch + chunk;
+    S.cmax[slot] = cm;
+    S.csum[slot] = csum;
+    S.carg[slot] = ca;
+    S.cbad[slot] = cb;
   }
-  __syncthreads();
-  if (!s_last) return;
-  // ---- last workgroup of this row: merge the chunk partials in chunk order ----
-  if (wid != 0) return;
-  __threadfence();  // acquire: every chunk's partials are visible past this point
+}
+
+// One wavefront per row: merge the chunk partials in chunk order.
+__global__ __launch_bounds__(256) void softmax_merge_kernel(SmSet A, SmSet B, int nch, int32_t* status) {
+  const int lane = threadIdx.x & 63;
+  int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= A.rows + B.rows) return;
+  const bool second = row >= A.rows;
+  const SmSet& S = second ? B : A;
+  if (second) row -= A.rows;
   float m_all = -INFINITY;
   int a_all = 0x7fffffff;
   int b_all = 0;
   for (int c = lane; c < nch; c += 64) {
-    const float mc = ws.cmax[row * nch + c];
-    const int ac = ws.carg[row * nch + c];
-    b_all |= ws.cbad[row * nch + c];
-    if (mc > m_all || (mc == m_all && ac < a_all)) {
-      m_all = mc;
-      a_all = ac;
-    }
+    better(m_all, a_all, S.cmax[row * nch + c], S.carg[row * nch + c]);
+    b_all |= S.cbad[row * nch + c];
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float om = __shfl_xor(m_all, o);
-    const int oa = __shfl_xor(a_all, o);
-    if (om > m_all || (om == m_all && oa < a_all)) {
-      m_all = om;
-      a_all = oa;
-    }
-  }
+  for (int o = 32; o > 0; o >>= 1) better(m_all, a_all, __shfl_xor(m_all, o), __shfl_xor(a_all, o));
   b_all = wave_or_i(b_all);
   double z = 0.0;
-  if (!greedy && m_all > -INFINITY) {
-    // chunk order is fixed: lane c holds chunk c (plus c + 64, ...), then a fixed butterfly
+  if (!S.greedy && m_all > -INFINITY) {
     for (int c = lane; c < nch; c += 64) {
-      const float mc = ws.cmax[row * nch + c];
-      const double sc = ws.csum[row * nch + c];
-      if (mc > -INFINITY) z += sc * exp(((double)mc - (double)m_all) * inv_t);
+      const float mc = S.cmax[row * nch + c];
+      if (mc > -INFINITY) z += S.csum[row * nch + c] * exp(((double)mc - (double)m_all) * S.inv_t);
     }
     z = wave_sum_d(z);
   }
   if (lane == 0) {
-    ws.count[row] = 0;  // leave the workspace ready for the next call
     const bool bad_row = b_all || !(m_all > -INFINITY);
-    row_max[row] = bad_row ? NAN : m_all;
-    if (row_sumexp) row_sumexp[row] = bad_row ? NAN : (float)z;
-    if (row_argmax) row_argmax[row] = bad_row ? -1 : a_all;
+    S.row_max[row] = bad_row ? NAN : m_all;
+    if (S.row_sumexp) S.row_sumexp[row] = bad_row ? NAN : (float)z;
+    if (S.row_argmax) S.row_argmax[row] = bad_row ? -1 : a_all;
     if (bad_row) report(status, SPEC_ERR_BAD_INPUT);
   }
 }
@@ -219,44 +206,92 @@ __global__ __launch_bounds__(256) void softmax_probs_kernel(const float* __restr
   probs[row * (int64_t)vocab + x] = isnan(m) ? NAN : exp_scaled(l - m, es) * inv_z;
 }
 
+inline SmSet make_set(const float* logits, int64_t rows, float t, float* mx, float* se, int32_t* am) {
+  SmSet s{};
+  s.logits = logits;
+  s.rows = rows;
+  s.greedy = t == 0.0f;
+  s.inv_t = s.greedy ? 0.0 : 1.0 / (double)t;
+  s.es = make_exp_scale(s.inv_t);
+  s.row_max = mx;
+  s.row_sumexp = se;
+  s.row_argmax = am;
+  return s;
+}
+
+inline int launch_stats(const SmSet& A, const SmSet& B, int32_t vocab, int32_t* status, hipStream_t st) {
+  const int nch = sm_chunks(vocab);
+  const int64_t blocks = (A.rows + B.rows) * nch;
+  if (blocks > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+  bool vec = vocab % 4 == 0 && (((uintptr_t)A.logits & 15) == 0);
+  if (B.rows) vec = vec && (((uintptr_t)B.logits & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL(softmax_stats_kernel<true>, dim3((unsigned)blocks), dim3(kSmThreads), 0, st, A, B, vocab, nch,
+                       status);
+  else
+    hipLaunchKernelGGL(softmax_stats_kernel<false>, dim3((unsigned)blocks), dim3(kSmThreads), 0, st, A, B, vocab,
+                       nch, status);
+  SPEC_LAUNCH_CHECK();
+  const int64_t rows = A.rows + B.rows;
+  hipLaunchKernelGGL(softmax_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, A, B, nch, status);
+  SPEC_LAUNCH_CHECK();
+  return SPEC_OK;
+}
+
 }  // namespace spectree
+
+extern "C" int32_t spec_tree_softmax_chunk(void) { return spectree::kChunk; }
 
 extern "C" size_t spec_tree_softmax_workspace_size(int64_t rows, int32_t vocab) {
   if (rows < 1 || vocab < 1) return 0;
-  return spectree::sm_layout(rows, vocab, nullptr, nullptr);
+  return spectree::sm_set_bytes(rows, vocab);
 }
 
 extern "C" int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float temperature,
                                  float* row_max, float* row_sumexp, int32_t* row_argmax, float* probs,
-                                 void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
+                                 float* chunk_max, double* chunk_sum, void* workspace, size_t workspace_bytes,
+                                 int32_t* status, void* stream) {
   using namespace spectree;
   if (!logits || !row_max || rows < 1 || vocab < 1) return SPEC_ERR_INVALID_ARG;
   if (!(temperature >= 0.0f) || isinf(temperature)) return SPEC_ERR_INVALID_ARG;
   const bool greedy = temperature == 0.0f;
   if (!greedy && !row_sumexp) return SPEC_ERR_INVALID_ARG;
-  if ((int64_t)sm_chunks(vocab) * rows > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
-  const size_t need = sm_layout(rows, vocab, nullptr, nullptr);
-  if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
-  SmWorkspace ws;
-  sm_layout(rows, vocab, (char*)workspace, &ws);
-  const int nch = sm_chunks(vocab);
-  const double inv_t = greedy ? 0.0 : 1.0 / (double)temperature;
-  const ExpScale es = make_exp_scale(inv_t);
-  const bool vec = (vocab % 4 == 0) && (((uintptr_t)logits & 15) == 0);
-  dim3 grid((unsigned)(nch * rows));
-  if (vec)
-    hipLaunchKernelGGL(softmax_stats_kernel<true>, grid, dim3(kSmThreads), 0, (hipStream_t)stream, logits, vocab, nch,
-                       inv_t, es, greedy ? 1 : 0, ws, row_max, row_sumexp, row_argmax, status);
-  else
-    hipLaunchKernelGGL(softmax_stats_kernel<false>, grid, dim3(kSmThreads), 0, (hipStream_t)stream, logits, vocab,
-                       nch, inv_t, es, greedy ? 1 : 0, ws, row_max, row_sumexp, row_argmax, status);
-  SPEC_LAUNCH_CHECK();
+  if (!workspace || workspace_bytes < sm_set_bytes(rows, vocab)) return SPEC_ERR_WORKSPACE;
+  SmSet A = make_set(logits, rows, temperature, row_max, row_sumexp, row_argmax);
+  sm_set_carve((char*)workspace, rows, vocab, &A, chunk_max, chunk_sum);
+  SmSet B{};
+  const int rc = launch_stats(A, B, vocab, status, (hipStream_t)stream);
+  if (rc != SPEC_OK) return rc;
   if (probs && !greedy) {
     if (rows > 65535) return SPEC_ERR_UNSUPPORTED;
     dim3 g2((unsigned)((vocab + 255) / 256), (unsigned)rows);
-    hipLaunchKernelGGL(softmax_probs_kernel, g2, dim3(256), 0, (hipStream_t)stream, logits, vocab, es, row_max,
+    hipLaunchKernelGGL(softmax_probs_kernel, g2, dim3(256), 0, (hipStream_t)stream, logits, vocab, A.es, row_max,
                        row_sumexp, probs);
     SPEC_LAUNCH_CHECK();
   }
   return SPEC_OK;
+}
+
+extern "C" size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vocab) {
+  if (rows < 1 || vocab < 1) return 0;
+  return 2 * spectree::sm_set_bytes(rows, vocab);
+}
+
+extern "C" int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
+                                      float draft_temperature, int64_t rows, int32_t vocab, float* tgt_max,
+                                      float* tgt_sumexp, int32_t* tgt_argmax, float* tgt_chunk_max,
+                                      double* tgt_chunk_sum, float* dft_max, float* dft_sumexp, void* workspace,
+                                      size_t workspace_bytes, int32_t* status, void* stream) {
+  using namespace spectree;
+  if (!tgt_logits || !dft_logits || !tgt_max || !tgt_sumexp || !dft_max || !dft_sumexp) return SPEC_ERR_INVALID_ARG;
+  if (rows < 1 || vocab < 1) return SPEC_ERR_INVALID_ARG;
+  if (!(temperature > 0.0f) || isinf(temperature) || !(draft_temperature > 0.0f) || isinf(draft_temperature))
+    return SPEC_ERR_INVALID_ARG;
+  const size_t one = sm_set_bytes(rows, vocab);
+  if (!workspace || workspace_bytes < 2 * one) return SPEC_ERR_WORKSPACE;
+  SmSet A = make_set(tgt_logits, rows, temperature, tgt_max, tgt_sumexp, tgt_argmax);
+  SmSet B = make_set(dft_logits, rows, draft_temperature, dft_max, dft_sumexp, nullptr);
+  sm_set_carve((char*)workspace, rows, vocab, &A, tgt_chunk_max, tgt_chunk_sum);
+  sm_set_carve((char*)workspace + one, rows, vocab, &B, nullptr, nullptr);
+  return launch_stats(A, B, vocab, status, (hipStream_t)stream);
 }

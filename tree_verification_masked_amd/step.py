@@ -4,9 +4,9 @@
 once, outputs, workspaces, the status word) so that ``run()`` allocates nothing
 and only issues the library calls, in order, on one stream:
 
-    spec_tree_mask_build -> spec_tree_attention -> spec_tree_softmax (target)
-    -> spec_tree_softmax (draft, skipped at T = 0) -> spec_tree_reject_sample
-    -> spec_accept_path
+    spec_tree_mask_build -> spec_tree_attention -> spec_tree_softmax_pair (target
+    and draft rows in one launch; spec_tree_softmax on the target rows at T = 0)
+    -> spec_tree_reject_sample -> spec_accept_path
 """
 from __future__ import annotations
 
@@ -59,9 +59,10 @@ class VerifyStep:
         R = Bn * n_max
         self.tmax, self.tsum, self.targ = torch.zeros(R, **f32), torch.zeros(R, **f32), torch.zeros(R, **i32)
         self.dmax, self.dsum = torch.zeros(R, **f32), torch.zeros(R, **f32)
-        sm_ws = B.spec_tree_softmax_workspace_size(R, V)
-        self.sm_ws_t = torch.zeros(sm_ws, dtype=torch.uint8, device=cuda)
-        self.sm_ws_d = torch.zeros(sm_ws, dtype=torch.uint8, device=cuda)
+        nch = -(-V // B.spec_tree_softmax_chunk())
+        self.tcmax = torch.zeros((R, nch), **f32)
+        self.tcsum = torch.zeros((R, nch), dtype=torch.float64, device=cuda)
+        self.sm_ws = torch.zeros(B.spec_tree_softmax_pair_workspace_size(R, V), dtype=torch.uint8, device=cuda)
         rj = B.spec_tree_reject_sample_workspace_size(Bn, n_max, V)
         self.rj_ws = torch.zeros(max(rj, 256), dtype=torch.uint8, device=cuda)
         self.accepted_child = torch.zeros((Bn, n_max), **i32)
@@ -85,11 +86,14 @@ class VerifyStep:
 
     def softmax(self, stream=None, tgt=None, dft=None):
         d = self.d
-        B.spec_tree_softmax(d["tgt_logits"] if tgt is None else tgt, self.T, self.tmax, self.tsum, self.targ,
-                            self.sm_ws_t, status=self.status, stream=stream)
+        tgt = d["tgt_logits"] if tgt is None else tgt
         if self.T > 0:
-            B.spec_tree_softmax(d["dft_logits"] if dft is None else dft, self.Td, self.dmax, self.dsum, None,
-                                self.sm_ws_d, status=self.status, stream=stream)
+            B.spec_tree_softmax_pair(tgt, self.T, d["dft_logits"] if dft is None else dft, self.Td, self.tmax,
+                                     self.tsum, self.targ, self.tcmax, self.tcsum, self.dmax, self.dsum, self.sm_ws,
+                                     status=self.status, stream=stream)
+        else:
+            B.spec_tree_softmax(tgt, 0.0, self.tmax, self.tsum, self.targ, self.sm_ws, status=self.status,
+                                stream=stream)
 
     def reject(self, stream=None, tgt=None, dft=None):
         d = self.d
@@ -99,7 +103,8 @@ class VerifyStep:
                                   None if greedy else self.dmax, None if greedy else self.dsum, self.Td,
                                   d["tokens"], d["parent"], d["n_nodes"], None if greedy else d["u_accept"],
                                   None if greedy else d["u_sample"], self.accepted_child, self.term_token,
-                                  self.rj_ws, self.status, stream)
+                                  self.rj_ws, self.status, stream, tgt_chunk_max=None if greedy else self.tcmax,
+                                  tgt_chunk_sum=None if greedy else self.tcsum)
 
     def path(self, stream=None):
         d = self.d
