@@ -19,26 +19,34 @@
 //
 // Every node is evaluated in parallel (the uniforms are indexed by node and child,
 // so a node's outcome does not depend on how the walk reached it); the walk from
-// the root then only follows the per-node results.  Large vocabularies (two or
-// more chunks) add two launches before that, so that no workgroup ever waits for
-// another:
-//   R1  every internal node whose first child is rejected, one workgroup per
-//       4096-token chunk: histogram of rho over 128 buckets per octave on [1, 16)
-//       (two more just below 1, one for rho >= 16 or q == 0).  The bucket comes
+// the root then only follows the per-node results.  Launches (T > 0):
+//   P   one wavefront per request: validity, children, the tested tokens' p and q
+//       at their parents (fp64), the first-child test of every node, and the list
+//       of nodes whose first child is rejected ("active": only they need W(c)).
+//   R1  (two or more vocabulary chunks) every (active node, 4096-token chunk):
+//       histogram of rho over 128 buckets per octave on [1, 16), two more just
+//       below 1 and one for rho >= 16 or q == 0, with exact fixed-point sums of p
+//       and q per bucket, merged per node with integer atomics.  The bucket comes
 //       from an fp32 log-domain estimate whose error is far below the 1% of a
-//       bucket assumed everywhere; the bucket sums of p and q are exact.
-//   R2  the same nodes and chunks: from the merged histogram, rigorous intervals
-//       I_l holding c_{l+1} for every level l; then exact sums of p and q over
-//       tokens with rho above each interval, the few tokens inside an interval in
-//       a per-node list, and per-chunk sums for the terminal draw.  Only tokens in
-//       buckets that straddle an interval end get an exact fp64 ratio.
+//       bucket assumed everywhere.
+//   R2  the same items: from the merged histogram, rigorous intervals
+//       I_l = [a_l, b_l] holding c_{l+1} for every level l (every workgroup of a
+//       node derives the same ones); then exact sums of p and q over tokens with
+//       rho above each interval, the few tokens inside an interval in a per-node
+//       list, and per-chunk sums for the terminal draw.  Only tokens in buckets
+//       that straddle an interval end get an exact fp64 ratio.
 //   R3  one workgroup per node: sibling tests with exact W(c_j) from R2's sums and
 //       list, terminal draws located by exact chunk sums and one chunk scan; the
 //       last workgroup of a request walks from the root and writes the outputs.
-// All sums of p and q are kept in 2^-62 fixed point, so they are exact, independent
-// of summation order and bitwise reproducible.  Small vocabularies (one chunk) and
-// any case outside the fast path's guarantees (list or queue overflow, threshold
-// beyond the histogram range, zero-mass steps) take direct vocabulary passes in R3.
+//       Each node clears the chain state it consumed, so the next call finds the
+//       workspace ready without any cross-workgroup wait.
+// Masses are summed as exact integers: the fp32 unnormalised mass exp((l - m)/T)
+// in [0, 1] is truncated to a multiple of 2^-42 (bit arithmetic, no rounding), so
+// the sums are exact, independent of summation order and bitwise reproducible;
+// the normalisation 1/Z is applied once to each sum.  Small vocabularies (one
+// chunk) and any case outside the fast path's guarantees (list or queue overflow,
+// threshold beyond the histogram range, zero-mass steps) take direct vocabulary
+// passes in R3.
 #include "common.hpp"
 
 namespace spectree {
@@ -47,20 +55,21 @@ constexpr int kHB = 512;            // ratio buckets over [1, 16): 128 per octav
 constexpr int kHLow = 2;            // buckets just below rho = 1
 constexpr int kHTop = kHB + kHLow;  // rho >= 16 or q == 0
 constexpr int kHN = kHTop + 1;
-constexpr double kHMargin = 0.01;   // bound on the estimate's error, in buckets
+constexpr float kHMargin = 0.01f;   // bound on the estimate's error, in buckets
 constexpr int kMaxKids = 63;        // chain levels per node
 constexpr int kListCap = 4096;      // exact in-interval tokens kept per node
 constexpr int kWgList = 256;        // in-interval tokens one R2 workgroup can stage
 constexpr int kQueue = 1024;        // edge tokens one R2 workgroup can stage
 constexpr int kLdsList = 512;       // list entries R3 keeps in LDS
 constexpr int kMaxEdge = 24;        // edge buckets per level before the direct path
-constexpr double kFx = 4611686018427387904.0;  // 2^62
+constexpr double kFx = 4398046511104.0;  // 2^42
 constexpr double kFxInv = 1.0 / kFx;
 constexpr int kRjThreads = 256;
 constexpr int kFlagFallback = 1;
 
-struct ListEntry {
-  double p, q, rho;
+struct ListEntry {  // a token inside some interval
+  long long fp, fq; // fixed-point unnormalised masses
+  double rho;
   int32_t tok, pad;
 };
 struct QEntry {
@@ -70,18 +79,41 @@ struct QEntry {
 struct NodeRes {
   int32_t acc, term, err, pad;
 };
+struct NodeInfo {     // written by P for every node slot
+  uint64_t kids;      // bit c: node c is a child
+  int32_t active;     // first child rejected: the chain is needed
+  int32_t verdict;    // the request's tree / token verdict (0 = fine)
+  float K;            // log2(Z_d / Z_t), the bucket estimate's row constant
+  int32_t pad;
+  double izt, izd;    // 1 / Z_t, 1 / Z_d
+};
+struct KidInfo {      // tested token of a child: p(x), q(x) at its parent's row
+  double px, qx;
+};
+struct ChainRec {     // R2 -> R3
+  double a[kMaxKids], b[kMaxKids];
+  int32_t flags, pad;
+};
+// Per-bucket table of R2: certain ratio range lb <= rho < ub of the bucket's tokens
+// and the suffix sums of the merged histogram from this bucket up.
+struct BucketRec {
+  double lb, ub;
+  long long SP, SQ;
+};
 
-struct NodeWs {         // per-node slots, nd = b * n_max + n
-  NodeRes* res;         // [nd]                     R3 -> its request's last workgroup
-  uint32_t* req_count;  // [batch]                  self-resetting
-  long long* hist;      // [nd][kHN][2]             R1 -> R2 (cleared by R2)
-  long long* lvl;       // [nd][kMaxKids][2]        R2 -> R3 (cleared by R1)
-  double* ivl;          // [nd][kMaxKids][2]        R2 -> R3
-  long long* cdraw;     // [nd][nch][2]             R2 -> R3
-  ListEntry* list;      // [nd][kListCap]           R2 -> R3
-  uint32_t* list_n;     // [nd]                     (cleared by R1)
-  uint32_t* r2_count;   // [nd]                     self-resetting
-  int32_t* flags;       // [nd]                     (cleared by R1)
+struct NodeWs {            // nd = b * n_max + n
+  NodeRes* res;            // [nd]          R3 -> its request's last workgroup
+  uint32_t* req_count;     // [batch]       self-resetting
+  NodeInfo* info;          // [nd]          P -> R1, R2, R3
+  KidInfo* kid;            // [nd]          P -> R3
+  uint32_t* act_count;     // [1]           P -> R1, R2 (cleared by R3)
+  int32_t* act_list;       // [nd]          P -> R1, R2
+  long long* hist;         // [nd][kHN][2]  R1 -> R2 (cleared by R3)
+  ChainRec* rec;           // [nd]          R2 -> R3 (flags cleared by R3)
+  long long* lvl;          // [nd][kMaxKids][2]  R2 -> R3 (cleared by R3)
+  long long* cdraw;        // [nd][nch][2]  R2 -> R3
+  ListEntry* list;         // [nd][kListCap]     R2 -> R3
+  uint32_t* list_n;        // [nd]          R2 -> R3 (cleared by R3)
 };
 
 struct RejArgs {
@@ -92,7 +124,6 @@ struct RejArgs {
   const float *dft_logits, *dft_max, *dft_sumexp;
   double inv_t, inv_td;
   ExpScale est, esd;
-  int greedy;
   const int32_t *tokens, *parent, *n_nodes;
   const float *u_accept, *u_sample;
   int32_t batch, n_max, vocab, nch;
@@ -140,7 +171,15 @@ __device__ inline void load_run(const float* row, int r0, int t1, bool vec, floa
   }
 }
 
-__device__ inline long long to_fx(double v) { return __double2ll_rz(v * kFx); }
+// floor(pp * 2^42) of an unnormalised mass pp in [0, 1], by bit arithmetic (exact).
+__device__ inline long long fx42(float pp) {
+  const uint32_t bits = __float_as_uint(pp);
+  const int e = (int)(bits >> 23);  // pp >= 0
+  if (e == 0 || e > 127) return 0;  // zero and subnormals are below 2^-42
+  const uint64_t m = (uint64_t)((bits & 0x7fffffu) | 0x800000u);
+  const int sh = e - 108;  // pp * 2^42 = m * 2^(e - 150 + 42)
+  return (long long)(sh >= 0 ? (m << sh) : (sh > -24 ? (m >> -sh) : 0ull));
+}
 
 struct RowView {
   const float* lt;
@@ -148,18 +187,6 @@ struct RowView {
   float mt, md;
   double izt, izd;
 };
-
-// Row view of node row `row`; false if either row's statistics are invalid.
-__device__ inline bool row_view(const RejArgs& a, int64_t row, RowView& r) {
-  r.lt = a.tgt_logits + row * (int64_t)a.vocab;
-  r.ld = a.dft_logits + row * (int64_t)a.vocab;
-  r.mt = a.tgt_max[row];
-  r.md = a.dft_max[row];
-  if (isnan(r.mt) || isnan(r.md)) return false;
-  r.izt = 1.0 / (double)a.tgt_sumexp[row];
-  r.izd = 1.0 / (double)a.dft_sumexp[row];
-  return true;
-}
 // Exponent of the fp32 exp of the softmax kernel: exp_scaled(l - m) = 2^e.
 __device__ inline float exp2_arg(float l, float m, ExpScale s) {
   const float d = fmaxf(l - m, -3.402823466e38f);
@@ -172,30 +199,11 @@ __device__ inline double p_el(const RejArgs& a, const RowView& r, float l) {
 __device__ inline double q_el(const RejArgs& a, const RowView& r, float l) {
   return (double)exp_scaled(l - r.md, a.esd) * r.izd;
 }
-// Tested tokens: fp64 exp.
-__device__ inline double p_tok(const RejArgs& a, const RowView& r, int x) {
-  return exp(((double)r.lt[x] - (double)r.mt) * a.inv_t) * r.izt;
-}
-__device__ inline double q_tok(const RejArgs& a, const RowView& r, int x) {
-  return exp(((double)r.ld[x] - (double)r.md) * a.inv_td) * r.izd;
-}
 // Acceptance ratio r(x)/q(x) with r = max(0, p - c q) / W.
 __device__ inline double accept_ratio(double px, double qx, double c, double W) {
   const double num = fmax(0.0, px - c * qx);
   if (qx > 0.0) return num / (W * qx);
   return num > 0.0 ? INFINITY : 0.0;
-}
-
-// Node n of a request with nb nodes: number of children, first child (-1 if none).
-__device__ inline int count_kids(const int* s_par, int n, int nb, int& first) {
-  int k = 0;
-  first = -1;
-  for (int c = n + 1; c < nb; ++c)
-    if (s_par[c] == n) {
-      if (first < 0) first = c;
-      ++k;
-    }
-  return k;
 }
 
 // ---------------------------------------------------------------------------
@@ -218,19 +226,20 @@ __device__ inline int est_bucket(float ep, float eq, float pp, float qq, float K
   if (x < (float)-kHLow) return -1;
   return (int)x + kHLow;
 }
-__device__ inline float row_k(const RejArgs& a, int64_t row) {
-  return (float)(log2((double)a.dft_sumexp[row]) - log2((double)a.tgt_sumexp[row]));
-}
-// Certain ratio range of each bucket: lb[h] <= rho < ub[h].
-__device__ inline void fill_edges(double* lb, double* ub) {
-  for (int h = threadIdx.x; h < kHN; h += blockDim.x) {
-    const double beta = (double)(h - kHLow);
-    if (h == kHTop) {
-      lb[h] = exp2(((double)kHB - kHMargin) / 128.0);
-      ub[h] = INFINITY;
+// Certain ratio range of each bucket: lb <= rho < ub (fp32 exp2 is within 2e-7
+// relative, well inside the margin).  Entry kHN is a sentinel above every bucket.
+__device__ inline void fill_edges(BucketRec* T) {
+  for (int h = threadIdx.x; h <= kHN; h += blockDim.x) {
+    const float beta = (float)(h - kHLow);
+    if (h == kHN) {
+      T[h].lb = INFINITY;
+      T[h].ub = INFINITY;
+    } else if (h == kHTop) {
+      T[h].lb = (double)exp2f(((float)kHB - kHMargin) / 128.0f);
+      T[h].ub = INFINITY;
     } else {
-      lb[h] = exp2((beta - kHMargin) / 128.0);
-      ub[h] = exp2((beta + 1.0 + kHMargin) / 128.0);
+      T[h].lb = (double)exp2f((beta - kHMargin) / 128.0f);
+      T[h].ub = (double)exp2f((beta + 1.0f + kHMargin) / 128.0f);
     }
   }
 }
@@ -239,55 +248,72 @@ __device__ inline int bucket_guess(double c) {
   return min(max(i, 0), kHTop);
 }
 // First bucket all of whose tokens have rho > c (kHN if none).
-__device__ inline int first_above(double c, const double* lb) {
+__device__ inline int first_above(double c, const BucketRec* T) {
   int i = bucket_guess(c);
-  while (i > 0 && lb[i - 1] > c) --i;
-  while (i <= kHTop && !(lb[i] > c)) ++i;
+  while (i > 0 && T[i - 1].lb > c) --i;
+  while (i < kHN && !(T[i].lb > c)) ++i;
   return i;
 }
 // First bucket that may hold a token with rho > c.
-__device__ inline int first_maybe(double c, const double* ub) {
+__device__ inline int first_maybe(double c, const BucketRec* T) {
   int i = bucket_guess(c);
-  while (i > 0 && ub[i - 1] > c) --i;
-  while (i <= kHTop && !(ub[i] > c)) ++i;
+  while (i > 0 && T[i - 1].ub > c) --i;
+  while (i < kHN && !(T[i].ub > c)) ++i;
   return i;
 }
-
-// Shared prelude of R1 and R2.  A workgroup serves one chunk of one node.
-struct NodeJob {
-  int b, n, nd, chunk, nb, k, first;
-  int64_t row;
-  RowView rv;
-  float K;
-};
-// The tree of the node's request into LDS; false if the node has no children.
-__device__ bool node_tree(const RejArgs& a, int* s_par, int* s_tok, NodeJob& j) {
-  j.nd = blockIdx.x / a.nch;
-  j.chunk = blockIdx.x % a.nch;
-  j.b = j.nd / a.n_max;
-  j.n = j.nd % a.n_max;
-  j.row = j.nd;
-  const int64_t base = (int64_t)j.b * a.n_max;
-  if (threadIdx.x < 64) {
-    const bool in = (int)threadIdx.x < a.n_max;
-    s_par[threadIdx.x] = in ? a.parent[base + threadIdx.x] : -2;
-    s_tok[threadIdx.x] = in ? a.tokens[base + threadIdx.x] : 0;
+// Bounds of W(c) from the merged histogram (fixed point of the unnormalised masses;
+// p = P * izt * 2^-42): the buckets from ia = first_above(c) count in full, the one
+// or two buckets [im, ia) straddling c contribute between max(0, P - cQ) (jointly)
+// and (ub - c) Q each.  The six table entries around the fp32 guess of c's bucket
+// are read at once; a guess that misses falls back to the scans above.
+__device__ double w_bound(double c, const BucketRec* T, double izt, double izd, bool upper) {
+  const int g = bucket_guess(c);
+  const int base = min(max(g - 2, 0), kHN + 1 - 6);
+  BucketRec r[6];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) r[j] = T[base + j];
+  int ia = -1, im = -1;
+#pragma unroll
+  for (int j = 5; j >= 0; --j) {
+    if (r[j].lb > c) ia = j;
+    if (r[j].ub > c) im = j;
   }
-  j.nb = a.n_nodes[j.b];
-  __syncthreads();
-  if (j.nb < 1 || j.nb > a.n_max || j.n >= j.nb) return false;
-  j.k = count_kids(s_par, j.n, j.nb, j.first);
-  return j.k > 0;
-}
-// Whether the node's first child is rejected: only then is its chain needed.  The
-// test is the one R3 makes (residual p, c = 0, W = 1).
-__device__ bool first_rejected(const RejArgs& a, const int* s_tok, NodeJob& j) {
-  const int x = __builtin_amdgcn_readfirstlane(s_tok[j.first]);
-  if (x < 0 || x >= a.vocab) return false;
-  if (!row_view(a, j.row, j.rv)) return false;
-  j.K = row_k(a, j.row);
-  const double ratio = accept_ratio(p_tok(a, j.rv, x), q_tok(a, j.rv, x), 0.0, 1.0);
-  return !((double)a.u_accept[(int64_t)j.b * a.n_max + j.first] < ratio);
+  const bool ok = ia >= 0 && im >= 0 && (base == 0 || !(r[0].ub > c));
+  if (!ok) {  // rare: scan the table
+    const int A = first_above(c, T), M = first_maybe(c, T);
+    const double full = ((double)T[A].SP * izt - c * (double)T[A].SQ * izd) * kFxInv;
+    if (!upper) return full + fmax(0.0, ((double)(T[M].SP - T[A].SP) * izt - c * (double)(T[M].SQ - T[A].SQ) * izd) * kFxInv);
+    double extra = 0.0;
+    for (int h = M; h < A; ++h) {
+      const double P = (double)(T[h].SP - T[h + 1].SP) * izt * kFxInv, Q = (double)(T[h].SQ - T[h + 1].SQ) * izd * kFxInv;
+      extra += Q > 0.0 ? (isinf(T[h].ub) ? INFINITY : fmax(0.0, (T[h].ub - c) * Q)) : P;
+    }
+    return full + extra;
+  }
+  long long SPa = 0, SQa = 0, SPm = 0, SQm = 0;
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    if (j == ia) {
+      SPa = r[j].SP;
+      SQa = r[j].SQ;
+    }
+    if (j == im) {
+      SPm = r[j].SP;
+      SQm = r[j].SQ;
+    }
+  }
+  const double full = ((double)SPa * izt - c * (double)SQa * izd) * kFxInv;
+  if (!upper) return full + fmax(0.0, ((double)(SPm - SPa) * izt - c * (double)(SQm - SQa) * izd) * kFxInv);
+  double extra = 0.0;
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    if (j >= im && j < ia) {
+      const double P = (double)(r[j].SP - r[j + 1].SP) * izt * kFxInv;
+      const double Q = (double)(r[j].SQ - r[j + 1].SQ) * izd * kFxInv;
+      extra += Q > 0.0 ? (isinf(r[j].ub) ? INFINITY : fmax(0.0, (r[j].ub - c) * Q)) : P;
+    }
+  }
+  return full + extra;
 }
 
 __device__ inline long long wave_sum_ll(long long v) {
@@ -315,275 +341,360 @@ __device__ inline double block_sum_d(double v, double* s_red) {
   for (int i = 0; i < nw; ++i) t += s_red[i];
   return t;
 }
+// Exclusive prefix sum over the block in thread order (fixed combination order).
+__device__ inline double block_excl_scan_d(double v, double* s_w, double* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const double inc = wave_incl_scan_d(v, lane);
+  __syncthreads();
+  if (lane == 63) s_w[wid] = inc;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < wid) before += s_w[i];
+    all += s_w[i];
+  }
+  *total = all;
+  return before + inc - v;
+}
+
+// ---------------------------------------------------------------------------
+// P: per-request plan
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void plan_kernel(RejArgs a, NodeWs w, int chunked) {
+  const int lane = threadIdx.x, b = blockIdx.x;
+  const int64_t base = (int64_t)b * a.n_max;
+  const bool in = lane < a.n_max;
+  const int nb = a.n_nodes[b];
+  const int par = in ? a.parent[base + lane] : -2;
+  const int tok = in ? a.tokens[base + lane] : 0;
+  const float ua = in ? a.u_accept[base + lane] : 0.0f;
+  const float mt = in ? a.tgt_max[base + lane] : 0.0f, md = in ? a.dft_max[base + lane] : 0.0f;
+  const float zt = in ? a.tgt_sumexp[base + lane] : 1.0f, zd = in ? a.dft_sumexp[base + lane] : 1.0f;
+  const bool n_ok = nb >= 1 && nb <= a.n_max;
+  const bool live = n_ok && lane < nb;
+  const bool bad_link = live && (lane == 0 ? par != -1 : (par < 0 || par >= lane));
+  const bool bad_tok = live && lane > 0 && (tok < 0 || tok >= a.vocab);
+  const unsigned long long m_link = __ballot(bad_link), m_tok = __ballot(bad_tok);
+  const int verdict = (!n_ok || m_link) ? SPEC_ERR_BAD_TREE : (m_tok ? SPEC_ERR_BAD_INPUT : 0);
+  const bool tree_ok = verdict == 0;
+  uint64_t kids = 0;
+  for (int n = 0; n < nb && tree_ok; ++n) {  // uniform
+    const unsigned long long m = __ballot(live && lane > 0 && par == n);
+    if (lane == n) kids = m;
+  }
+  const bool row_ok = !isnan(mt) && !isnan(md);
+  const double izt = 1.0 / (double)zt, izd = 1.0 / (double)zd;
+  // the tested token of child `lane`, at its parent's row
+  const bool child = tree_ok && live && lane > 0;
+  const int pl = child ? par : 0;
+  const float pmt = __shfl(mt, pl), pmd = __shfl(md, pl);
+  const double pizt = __shfl(izt, pl), pizd = __shfl(izd, pl);
+  double px = 0.0, qx = 0.0;
+  if (child) {
+    const int64_t prow = base + par;
+    const float lt = a.tgt_logits[prow * a.vocab + tok], ld = a.dft_logits[prow * a.vocab + tok];
+    px = exp(((double)lt - (double)pmt) * a.inv_t) * pizt;
+    qx = exp(((double)ld - (double)pmd) * a.inv_td) * pizd;
+  }
+  // first-child test of node `lane`
+  const int fc = kids ? __ffsll((unsigned long long)kids) - 1 : 0;
+  const double fpx = __shfl(px, fc), fqx = __shfl(qx, fc);
+  const float fua = __shfl(ua, fc);
+  const bool active = tree_ok && live && kids && row_ok && !((double)fua < accept_ratio(fpx, fqx, 0.0, 1.0));
+  if (in) {
+    NodeInfo inf;
+    inf.kids = kids;
+    inf.active = active;
+    inf.verdict = verdict;
+    inf.K = (float)(log2((double)zd) - log2((double)zt));
+    inf.pad = 0;
+    inf.izt = izt;
+    inf.izd = izd;
+    w.info[base + lane] = inf;
+    w.kid[base + lane] = KidInfo{px, qx};
+  }
+  if (chunked) {
+    const unsigned long long m = __ballot(active);
+    int at = 0;
+    if (lane == 0 && m) at = (int)atomicAdd(w.act_count, (uint32_t)__popcll(m));
+    at = __shfl(at, 0);
+    if (active) w.act_list[at + __popcll(m & ((1ull << lane) - 1ull))] = (int)(base + lane);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // R1: ratio histogram
 // ---------------------------------------------------------------------------
+// Items are (active node, chunk) pairs, item = slot * nch + chunk, visited
+// grid-stride.  The first item's node id is read together with the item count.
 __global__ __launch_bounds__(256) void chain_hist_kernel(RejArgs a, NodeWs w) {
-  __shared__ int s_par[64], s_tok[64];
   __shared__ unsigned long long s_P[4][kHN], s_Q[4][kHN];  // one copy per wavefront
-  NodeJob j;
-  if (!node_tree(a, s_par, s_tok, j)) return;
   const int tid = threadIdx.x, wv = tid >> 6;
-  float xl[kPer], xd[kPer];  // issued before the first-child test, which needs other rows
-  load_chunk(a.tgt_logits + j.row * a.vocab, j.chunk * kChunk, a.vocab, a.vec, xl);
-  load_chunk(a.dft_logits + j.row * a.vocab, j.chunk * kChunk, a.vocab, a.vec, xd);
-  if (!first_rejected(a, s_tok, j)) return;
-  if (j.chunk == 0) {  // R2's accumulators for this node start from zero
-    for (int i = tid; i < 2 * kMaxKids; i += blockDim.x) w.lvl[(int64_t)j.nd * 2 * kMaxKids + i] = 0;
-    if (tid == 0) {
-      w.list_n[j.nd] = 0;
-      w.flags[j.nd] = 0;
-    }
-  }
-  for (int i = tid; i < kHN; i += blockDim.x)
-    for (int c = 0; c < 4; ++c) s_P[c][i] = s_Q[c][i] = 0;
-  __syncthreads();
+  const int nodes = a.batch * a.n_max;
+  const int items = (int)(*w.act_count) * a.nch;
+  const int first_nd = w.act_list[min((int)blockIdx.x / a.nch, nodes - 1)];
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int nd = it == (int)blockIdx.x ? first_nd : w.act_list[it / a.nch];
+    const int chunk = it % a.nch;
+    const NodeInfo inf = w.info[nd];
+    const float mt = a.tgt_max[nd], md = a.dft_max[nd];
+    float xl[kPer], xd[kPer];
+    load_chunk(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
+    load_chunk(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
+    for (int i = tid; i < kHN; i += blockDim.x)
+      for (int c = 0; c < 4; ++c) s_P[c][i] = s_Q[c][i] = 0;
+    __syncthreads();
 #pragma unroll
-  for (int s2 = 0; s2 < kPer; ++s2) {
-    const float ep = exp2_arg(xl[s2], j.rv.mt, a.est), eq = exp2_arg(xd[s2], j.rv.md, a.esd);
-    const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
-    const int h = est_bucket(ep, eq, pp, qq, j.K);
-    if (h < 0) continue;
-    atomicAdd(&s_P[wv][h], (unsigned long long)to_fx((double)pp * j.rv.izt));
-    atomicAdd(&s_Q[wv][h], (unsigned long long)to_fx((double)qq * j.rv.izd));
-  }
-  __syncthreads();
-  unsigned long long* hg = (unsigned long long*)w.hist + (int64_t)j.nd * 2 * kHN;
-  for (int i = tid; i < kHN; i += blockDim.x) {
-    const unsigned long long P = s_P[0][i] + s_P[1][i] + s_P[2][i] + s_P[3][i];
-    const unsigned long long Q = s_Q[0][i] + s_Q[1][i] + s_Q[2][i] + s_Q[3][i];
-    if (P) atomicAdd(&hg[2 * i], P);
-    if (Q) atomicAdd(&hg[2 * i + 1], Q);
+    for (int s2 = 0; s2 < kPer; ++s2) {
+      const float ep = exp2_arg(xl[s2], mt, a.est), eq = exp2_arg(xd[s2], md, a.esd);
+      const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
+      const int h = est_bucket(ep, eq, pp, qq, inf.K);
+      if (h < 0) continue;
+      atomicAdd(&s_P[wv][h], (unsigned long long)fx42(pp));
+      atomicAdd(&s_Q[wv][h], (unsigned long long)fx42(qq));
+    }
+    __syncthreads();
+    unsigned long long* hg = (unsigned long long*)w.hist + (int64_t)nd * 2 * kHN;
+    for (int i = tid; i < kHN; i += blockDim.x) {
+      const unsigned long long P = s_P[0][i] + s_P[1][i] + s_P[2][i] + s_P[3][i];
+      const unsigned long long Q = s_Q[0][i] + s_Q[1][i] + s_Q[2][i] + s_Q[3][i];
+      if (P) atomicAdd(&hg[2 * i], P);
+      if (Q) atomicAdd(&hg[2 * i + 1], Q);
+    }
+    __syncthreads();  // LDS is reused by the next item
   }
 }
 
 // ---------------------------------------------------------------------------
-// R2: chain intervals and exact sums
+// R2: intervals, exact sums above each interval, in-interval list, draw sums
 // ---------------------------------------------------------------------------
-// Bounds of W(c) from the histogram's suffix sums S (fixed point, scaled back):
-// buckets from first_above(c) count in full; the one or two buckets straddling c
-// contribute between max(0, P - cQ) (jointly) and (ub - c) Q each.
-__device__ void w_bounds(double c, const double* lb, const double* ub, const long long* S, double& lo,
-                         double& hi) {
-  const int ia = first_above(c, lb), im = first_maybe(c, ub);
-  const double full = ia < kHN ? ((double)S[2 * ia] - c * (double)S[2 * ia + 1]) * kFxInv : 0.0;
-  double up = 0.0, uq = 0.0, extra = 0.0;
-  for (int i = im; i < ia && i < kHN; ++i) {
-    const double P = (double)(S[2 * i] - S[2 * i + 2]) * kFxInv, Q = (double)(S[2 * i + 1] - S[2 * i + 3]) * kFxInv;
-    up += P;
-    uq += Q;
-    if (Q > 0.0) extra += isinf(ub[i]) ? INFINITY : fmax(0.0, (ub[i] - c) * Q);
-    else extra += P;  // q == 0 tokens count in full
-  }
-  lo = full + fmax(0.0, up - c * uq);
-  hi = full + extra;
-}
-
-// Pushes v onto the LDS queue for the lanes with e set (one LDS atomic per wave).
-__device__ inline void queue_push(bool e, const QEntry& v, QEntry* q, int* qn) {
-  const unsigned long long m = __ballot(e);
-  if (m == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)m) - 1;
-  int base = 0;
-  if (lane == leader) base = atomicAdd(qn, __popcll(m));
-  base = __shfl(base, leader);
-  const int off = __popcll(m & ((1ull << lane) - 1ull));
-  if (e && base + off < kQueue) q[base + off] = v;
-}
-
 // Levels: l = 0 .. k-1 is the threshold after l + 1 rejections, c_{l+1} in
-// I_l = [a_l, b_l] (I_0 = [1, 1]).  With H_l the first bucket certainly above b_l
-// and G_l the first bucket that may hold rho > a_l:
+// I_l = [a_l, b_l] (I_0 = [1, 1]); g(c) = c + W(c) is nondecreasing, so
+// I_{l+1} = [a_l + lower W(a_l), b_l + upper W(b_l)], padded for rounding.  With
+// H_l the first bucket certainly above b_l and G_l the first bucket that may hold
+// rho > a_l:
 //   P_above(l) = sum_{rho > b_l} p = S[H_l] + (tokens of buckets [G_l, H_l) with rho > b_l),
 // and the tokens of [G_l, H_l) with a_l < rho <= b_l are kept in the node's list.
 __global__ __launch_bounds__(256) void chain_exact_kernel(RejArgs a, NodeWs w) {
-  __shared__ int s_par[64], s_tok[64];
-  __shared__ double s_lb[kHN], s_ub[kHN];
-  __shared__ long long s_S[2 * (kHN + 1)];  // suffix sums of the merged histogram
+  __shared__ BucketRec s_T[kHN + 1];
   __shared__ long long s_wt[2][4];
   __shared__ double s_a[kMaxKids], s_b[kMaxKids];
   __shared__ int s_G[kMaxKids], s_H[kMaxKids];
-  __shared__ unsigned char s_edge[kHN];
+  __shared__ unsigned long long s_mask[kHN];  // levels whose edge range holds bucket h
   __shared__ unsigned long long s_EP[kMaxKids], s_EQ[kMaxKids];
   __shared__ QEntry s_q[kQueue];
   __shared__ ListEntry s_list[kWgList];
   __shared__ long long s_ll[4];
-  __shared__ int s_qn, s_nlist, s_base, s_clear, s_bad, s_htop;
-  NodeJob j;
-  if (!node_tree(a, s_par, s_tok, j)) return;
+  __shared__ int s_qn, s_nlist, s_base, s_bad;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  float xl[kPer], xd[kPer];
-  load_chunk(a.tgt_logits + j.row * a.vocab, j.chunk * kChunk, a.vocab, a.vec, xl);
-  load_chunk(a.dft_logits + j.row * a.vocab, j.chunk * kChunk, a.vocab, a.vec, xd);
-  if (!first_rejected(a, s_tok, j)) return;
-  const long long* hg = w.hist + (int64_t)j.nd * 2 * kHN;
-  // suffix sums S[h] = sum_{h' >= h} hist[h'] (S[kHN] = 0): thread t owns buckets 3t .. 3t+2
-  long long v0[3], v1[3];
+  const int nodes = a.batch * a.n_max;
+  const int items = (int)(*w.act_count) * a.nch;
+  const int first_nd = w.act_list[min((int)blockIdx.x / a.nch, nodes - 1)];
+  fill_edges(s_T);  // ratio ranges are the same for every node
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int nd = it == (int)blockIdx.x ? first_nd : w.act_list[it / a.nch];
+    const int chunk = it % a.nch;
+    const NodeInfo inf = w.info[nd];
+    const int k = __popcll(inf.kids);
+    const float mt = a.tgt_max[nd], md = a.dft_max[nd];
+    float xl[kPer], xd[kPer];
+    load_chunk(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
+    load_chunk(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
+    // merged histogram -> suffix sums (thread t owns buckets 3t .. 3t+2)
+    const long long* hg = w.hist + (int64_t)nd * 2 * kHN;
+    long long v0[3], v1[3];
 #pragma unroll
-  for (int e = 0; e < 3; ++e) {
-    const int h = 3 * tid + e;
-    v0[e] = h < kHN ? hg[2 * h] : 0;
-    v1[e] = h < kHN ? hg[2 * h + 1] : 0;
-  }
-  fill_edges(s_lb, s_ub);
-  for (int i = tid; i < kHN; i += blockDim.x) s_edge[i] = 0;
-  for (int i = tid; i < kMaxKids; i += blockDim.x) s_EP[i] = s_EQ[i] = 0;
-  if (tid == 0) {
-    s_qn = 0;
-    s_nlist = 0;
-  }
-  {
-    const long long t0 = v0[0] + v0[1] + v0[2], t1 = v1[0] + v1[1] + v1[2];
-    long long i0 = t0, i1 = t1;  // inclusive suffix within the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long u0 = __shfl_down(i0, o), u1 = __shfl_down(i1, o);
-      if (lane + o < 64) {
-        i0 += u0;
-        i1 += u1;
-      }
+    for (int e = 0; e < 3; ++e) {
+      const int h = 3 * tid + e;
+      v0[e] = h < kHN ? hg[2 * h] : 0;
+      v1[e] = h < kHN ? hg[2 * h + 1] : 0;
     }
-    if (lane == 0) {
-      s_wt[0][wv] = i0;
-      s_wt[1][wv] = i1;
+    for (int l = tid; l < k; l += blockDim.x) s_EP[l] = s_EQ[l] = 0;
+    if (tid == 0) {
+      s_qn = 0;
+      s_nlist = 0;
+      s_bad = 0;
+    }
+    {
+      const long long t0 = v0[0] + v0[1] + v0[2], t1 = v1[0] + v1[1] + v1[2];
+      long long i0 = t0, i1 = t1;  // inclusive suffix within the wave
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const long long u0 = __shfl_down(i0, o), u1 = __shfl_down(i1, o);
+        if (lane + o < 64) {
+          i0 += u0;
+          i1 += u1;
+        }
+      }
+      if (lane == 0) {
+        s_wt[0][wv] = i0;
+        s_wt[1][wv] = i1;
+      }
+      __syncthreads();
+      long long e0 = i0 - t0, e1 = i1 - t1;
+      for (int x = wv + 1; x < 4; ++x) {
+        e0 += s_wt[0][x];
+        e1 += s_wt[1][x];
+      }
+      for (int e = 2; e >= 0; --e) {
+        e0 += v0[e];
+        e1 += v1[e];
+        const int h = 3 * tid + e;
+        if (h <= kHN) {
+          s_T[h].SP = e0;
+          s_T[h].SQ = e1;
+        }
+      }
     }
     __syncthreads();
-    long long e0 = i0 - t0, e1 = i1 - t1;  // exclusive suffix
-    for (int x = wv + 1; x < 4; ++x) {
-      e0 += s_wt[0][x];
-      e1 += s_wt[1][x];
-    }
-    for (int e = 2; e >= 0; --e) {
-      e0 += v0[e];
-      e1 += v1[e];
-      const int h = 3 * tid + e;
-      if (h <= kHN) {
-        s_S[2 * h] = e0;
-        s_S[2 * h + 1] = e1;
+    // interval chains: lower ends on wave 0, upper ends on wave 1
+    if (tid == 0) {
+      double c = 1.0;
+      s_a[0] = 1.0;
+      for (int l = 1; l < k; ++l) {
+        const double na = c + w_bound(c, s_T, inf.izt, inf.izd, false);
+        c = na - 1e-10 * na;
+        s_a[l] = c;
+      }
+    } else if (tid == 64) {
+      double c = 1.0;
+      s_b[0] = 1.0;
+      for (int l = 1; l < k; ++l) {
+        const double nb = c + w_bound(c, s_T, inf.izt, inf.izd, true);
+        c = nb + 1e-10 * nb;
+        s_b[l] = c;
+        if (!(c < 15.5)) {  // beyond the histogram: direct path
+          s_bad = 1;
+          for (int m = l + 1; m < k; ++m) s_b[m] = c;
+          break;
+        }
       }
     }
-  }
-  __syncthreads();
-  // every workgroup of this node has read the histogram: the last one clears it
-  if (tid == 0) s_clear = pub_arrive(&w.r2_count[j.nd]) == (uint32_t)(a.nch - 1);
-  __syncthreads();
-  if (s_clear) {
-    long long* hw = w.hist + (int64_t)j.nd * 2 * kHN;
-    for (int i = tid; i < 2 * kHN; i += blockDim.x) hw[i] = 0;
-    if (tid == 0) w.r2_count[j.nd] = 0;
-  }
-  const int k = j.k;
-  if (tid == 0) {  // intervals and their bucket ranges
-    int bad = 0;
-    s_a[0] = s_b[0] = 1.0;
-    for (int l = 1; l < k; ++l) {
-      double lo1, hi1, lo2, hi2;
-      w_bounds(s_a[l - 1], s_lb, s_ub, s_S, lo1, hi1);
-      w_bounds(s_b[l - 1], s_lb, s_ub, s_S, lo2, hi2);
-      const double na = s_a[l - 1] + lo1, nb = s_b[l - 1] + hi2;
-      const double pad = 1e-7 * (nb - na) + 1e-12 * nb;
-      s_a[l] = na - pad;
-      s_b[l] = nb + pad;
-      if (!(s_b[l] < 16.0)) {
-        bad = 1;
-        break;
-      }
-    }
-    for (int l = 0; l < k && !bad; ++l) {
-      s_G[l] = first_maybe(s_a[l], s_ub);
-      s_H[l] = first_above(s_b[l], s_lb);
-      if (s_H[l] > kHTop || s_H[l] - s_G[l] > kMaxEdge) bad = 1;  // outside the histogram: direct path
-    }
-    if (!bad) {
-      for (int l = 0; l < k; ++l)
-        for (int i = s_G[l]; i < s_H[l]; ++i) s_edge[i] = 1;
-      s_htop = s_H[k - 1];
-    }
-    s_bad = bad;
-  }
-  __syncthreads();
-  if (s_bad) {
-    if (tid == 0) atomicOr(&w.flags[j.nd], kFlagFallback);
-    return;
-  }
-  if (j.chunk == 0) {  // the certain parts above each interval, and the intervals
-    unsigned long long* lv = (unsigned long long*)w.lvl + (int64_t)j.nd * 2 * kMaxKids;
+    __syncthreads();
     for (int l = tid; l < k; l += blockDim.x) {
-      const int i = s_H[l];
-      if (s_S[2 * i]) atomicAdd(&lv[2 * l], (unsigned long long)s_S[2 * i]);
-      if (s_S[2 * i + 1]) atomicAdd(&lv[2 * l + 1], (unsigned long long)s_S[2 * i + 1]);
-      w.ivl[((int64_t)j.nd * kMaxKids + l) * 2] = s_a[l];
-      w.ivl[((int64_t)j.nd * kMaxKids + l) * 2 + 1] = s_b[l];
+      const int G = first_maybe(s_a[l], s_T), H = s_bad ? kHN : first_above(s_b[l], s_T);
+      s_G[l] = G;
+      s_H[l] = H;
+      if (H > kHTop || H - G > kMaxEdge) s_bad = 1;
     }
-  }
-  const int htop = s_htop;
-  const double btop = s_b[k - 1];
-  long long cp = 0, cq = 0;  // this chunk's tokens with rho > b_{k-1} (the terminal draw)
-#pragma unroll
-  for (int s2 = 0; s2 < kPer; ++s2) {
-    const float ep = exp2_arg(xl[s2], j.rv.mt, a.est), eq = exp2_arg(xd[s2], j.rv.md, a.esd);
-    const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
-    const int h = est_bucket(ep, eq, pp, qq, j.K);
-    if (h >= htop) {
-      cp += to_fx((double)pp * j.rv.izt);
-      cq += to_fx((double)qq * j.rv.izd);
+    __syncthreads();
+    if (s_bad) {
+      if (chunk == 0 && tid == 0) atomicOr(&w.rec[nd].flags, kFlagFallback);
+      __syncthreads();
+      continue;
     }
-    const bool edge = h >= 0 && h < htop && s_edge[h];
-    queue_push(edge, QEntry{chunk_tok(j.chunk * kChunk, s2), h, pp, qq}, s_q, &s_qn);
-  }
-  __syncthreads();
-  const int qn = s_qn;
-  for (int i = tid; i < min(qn, kQueue); i += blockDim.x) {
-    const QEntry e = s_q[i];
-    const double p = (double)e.pp * j.rv.izt, q = (double)e.qq * j.rv.izd;
-    const double rho = q > 0.0 ? p / q : INFINITY;
-    const long long fp = to_fx(p), fq = to_fx(q);
-    if (rho > btop) {
-      cp += fp;
-      cq += fq;
+    for (int h = tid; h < kHN; h += blockDim.x) {
+      unsigned long long m = 0;
+      for (int l = 0; l < k; ++l)
+        if (h >= s_G[l] && h < s_H[l]) m |= 1ull << l;
+      s_mask[h] = m;
     }
-    bool in_list = false;
-    for (int l = 0; l < k; ++l) {
-      if (e.h < s_G[l] || e.h >= s_H[l]) continue;
-      if (rho > s_b[l]) {
-        if (fp) atomicAdd(&s_EP[l], (unsigned long long)fp);
-        if (fq) atomicAdd(&s_EQ[l], (unsigned long long)fq);
-      } else if (rho > s_a[l]) {
-        in_list = true;
+    if (chunk == 0) {  // the certain part above each interval, and the intervals
+      unsigned long long* lv = (unsigned long long*)w.lvl + (int64_t)nd * 2 * kMaxKids;
+      for (int l = tid; l < k; l += blockDim.x) {
+        const int H = s_H[l];
+        if (s_T[H].SP) atomicAdd(&lv[2 * l], (unsigned long long)s_T[H].SP);
+        if (s_T[H].SQ) atomicAdd(&lv[2 * l + 1], (unsigned long long)s_T[H].SQ);
+        w.rec[nd].a[l] = s_a[l];
+        w.rec[nd].b[l] = s_b[l];
       }
     }
-    if (in_list) {
-      const int x = atomicAdd(&s_nlist, 1);
-      if (x < kWgList) s_list[x] = ListEntry{p, q, rho, e.tok, 0};
+    __syncthreads();
+    const int htop = s_H[k - 1];
+    long long cp = 0, cq = 0;  // this chunk's tokens with rho > b_{k-1} (the terminal draw)
+    int hh[kPer];
+    float pq[kPer], qq2[kPer];
+#pragma unroll
+    for (int s2 = 0; s2 < kPer; ++s2) {
+      const float ep = exp2_arg(xl[s2], mt, a.est), eq = exp2_arg(xd[s2], md, a.esd);
+      const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
+      const int h = est_bucket(ep, eq, pp, qq, inf.K);
+      if (h >= htop) {
+        cp += fx42(pp);
+        cq += fx42(qq);
+      }
+      hh[s2] = h;
+      pq[s2] = pp;
+      qq2[s2] = qq;
     }
-  }
-  cp = block_sum_ll(cp, s_ll);
-  cq = block_sum_ll(cq, s_ll);
-  if (tid == 0) {
-    long long* cd = w.cdraw + ((int64_t)j.nd * a.nch + j.chunk) * 2;
-    cd[0] = cp;
-    cd[1] = cq;
-    const int n_in = s_nlist;
-    if (qn > kQueue || n_in > kWgList) {
-      atomicOr(&w.flags[j.nd], kFlagFallback);
-      s_base = -1;
-    } else {
-      s_base = n_in ? (int)atomicAdd(&w.list_n[j.nd], (uint32_t)n_in) : 0;
-      if (s_base + n_in > kListCap) atomicOr(&w.flags[j.nd], kFlagFallback);
+    unsigned edge = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kPer; ++s2) {
+      const int h = hh[s2];
+      if (h >= 0 && h < htop && s_mask[h]) edge |= 1u << s2;
     }
+    // queue slots: one LDS atomic per wavefront
+    const int ne = __popc(edge);
+    int pre = ne;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(pre, o);
+      if (lane >= o) pre += t;
+    }
+    int qbase = 0;
+    if (lane == 63 && pre) qbase = atomicAdd(&s_qn, pre);
+    qbase = __shfl(qbase, 63) + pre - ne;
+#pragma unroll
+    for (int s2 = 0; s2 < kPer; ++s2) {
+      if (edge & (1u << s2)) {
+        if (qbase < kQueue) s_q[qbase] = QEntry{chunk_tok(chunk * kChunk, s2), hh[s2], pq[s2], qq2[s2]};
+        ++qbase;
+      }
+    }
+    __syncthreads();
+    const int qn = s_qn;
+    const double btop = s_b[k - 1];
+    for (int i = tid; i < min(qn, kQueue); i += blockDim.x) {
+      const QEntry e = s_q[i];
+      const double p = (double)e.pp * inf.izt, q = (double)e.qq * inf.izd;
+      const double rho = q > 0.0 ? p / q : INFINITY;
+      const long long fp = fx42(e.pp), fq = fx42(e.qq);
+      if (rho > btop) {
+        cp += fp;
+        cq += fq;
+      }
+      bool in_list = false;
+      for (unsigned long long m = s_mask[e.h]; m; m &= m - 1) {
+        const int l = __ffsll(m) - 1;
+        if (rho > s_b[l]) {
+          if (fp) atomicAdd(&s_EP[l], (unsigned long long)fp);
+          if (fq) atomicAdd(&s_EQ[l], (unsigned long long)fq);
+        } else if (rho > s_a[l]) {
+          in_list = true;
+        }
+      }
+      if (in_list) {
+        const int x = atomicAdd(&s_nlist, 1);
+        if (x < kWgList) s_list[x] = ListEntry{fp, fq, rho, e.tok, 0};
+      }
+    }
+    cp = block_sum_ll(cp, s_ll);
+    cq = block_sum_ll(cq, s_ll);
+    if (tid == 0) {
+      long long* cd = w.cdraw + ((int64_t)nd * a.nch + chunk) * 2;
+      cd[0] = cp;
+      cd[1] = cq;
+      const int n_in = s_nlist;
+      if (qn > kQueue || n_in > kWgList) {
+        atomicOr(&w.rec[nd].flags, kFlagFallback);
+        s_base = -1;
+      } else {
+        s_base = n_in ? (int)atomicAdd(&w.list_n[nd], (uint32_t)n_in) : 0;
+        if (s_base + n_in > kListCap) atomicOr(&w.rec[nd].flags, kFlagFallback);
+      }
+    }
+    unsigned long long* lv = (unsigned long long*)w.lvl + (int64_t)nd * 2 * kMaxKids;
+    for (int l = tid; l < k; l += blockDim.x) {
+      if (s_EP[l]) atomicAdd(&lv[2 * l], s_EP[l]);
+      if (s_EQ[l]) atomicAdd(&lv[2 * l + 1], s_EQ[l]);
+    }
+    __syncthreads();
+    const int n_in = min(s_nlist, kWgList);
+    if (s_base >= 0)
+      for (int i = tid; i < n_in; i += blockDim.x)
+        if (s_base + i < kListCap) w.list[(int64_t)nd * kListCap + s_base + i] = s_list[i];
+    __syncthreads();  // LDS is reused by the next item
   }
-  unsigned long long* lv = (unsigned long long*)w.lvl + (int64_t)j.nd * 2 * kMaxKids;
-  for (int l = tid; l < k; l += blockDim.x) {
-    if (s_EP[l]) atomicAdd(&lv[2 * l], s_EP[l]);
-    if (s_EQ[l]) atomicAdd(&lv[2 * l + 1], s_EQ[l]);
-  }
-  __syncthreads();
-  const int n_in = min(s_nlist, kWgList);
-  if (s_base >= 0)
-    for (int i = tid; i < n_in; i += blockDim.x)
-      if (s_base + i < kListCap) w.list[(int64_t)j.nd * kListCap + s_base + i] = s_list[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -608,26 +719,15 @@ __device__ double direct_W(const RejArgs& a, const RowView& r, double c, double*
 // combined by an exclusive scan in thread order.  Returns -1 if rounding leaves no
 // crossing in the range.  elem(t) gives the unnormalised mass of token t.
 template <typename Elem>
-__device__ int scan_range(int t0, int t1, double pre, double target, Elem elem, double* s_scan, int* s_pick) {
+__device__ int scan_range(int t0, int t1, double pre, double target, Elem elem, double* s_w, int* s_pick) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int per = (t1 - t0 + nt - 1) / nt;
   const int r0 = t0 + tid * per, r1 = min(t1, r0 + per);
   double own = 0.0;
   for (int t = r0; t < r1; ++t) own += elem(t);
-  __syncthreads();
-  s_scan[tid] = own;
   if (tid == 0) *s_pick = 0x7fffffff;
-  __syncthreads();
-  if (tid == 0) {  // exclusive prefix in thread order
-    double run = 0.0;
-    for (int i = 0; i < nt; ++i) {
-      const double v = s_scan[i];
-      s_scan[i] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  const double before = pre + s_scan[tid];
+  double total;
+  const double before = pre + block_excl_scan_d(own, s_w, &total);
   if (r0 < r1 && before + own > target && !(before > target)) {
     double run = 0.0;
     int pick = r1 - 1;
@@ -670,7 +770,7 @@ __device__ int last_positive(int t0, int t1, Elem elem, int* s_pick) {
 // max(0, p - c q) for a residual.  Returns the smallest token whose running sum
 // added to `pre` exceeds `target`, or -1 if rounding leaves no crossing.
 __device__ int chunk_scan(const RejArgs& a, const RowView& rv, int t0, int t1, bool resid, float mc, double scale,
-                          double c, double pre, double target, double* s_scan, int* s_pick) {
+                          double c, double pre, double target, double* s_w, int* s_pick) {
   const int tid = threadIdx.x;
   const int r0 = t0 + tid * kPer;
   float xl[kPer], xd[kPer];
@@ -683,20 +783,9 @@ __device__ int chunk_scan(const RejArgs& a, const RowView& rv, int t0, int t1, b
   double own = 0.0;
 #pragma unroll
   for (int s2 = 0; s2 < kPer; ++s2) own += mass(s2);
-  __syncthreads();
-  s_scan[tid] = own;
   if (tid == 0) *s_pick = 0x7fffffff;
-  __syncthreads();
-  if (tid == 0) {  // exclusive prefix in thread order
-    double run = 0.0;
-    for (int i = 0; i < (int)blockDim.x; ++i) {
-      const double v = s_scan[i];
-      s_scan[i] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  const double before = pre + s_scan[tid];
+  double total;
+  const double before = pre + block_excl_scan_d(own, s_w, &total);
   if (r0 < t1 && before + own > target && !(before > target)) {
     double run = 0.0;
     int pick = min(t1, r0 + kPer) - 1;
@@ -717,7 +806,7 @@ __device__ int chunk_scan(const RejArgs& a, const RowView& rv, int t0, int t1, b
 }
 
 // Direct inverse-CDF draw over the whole vocabulary, in kChunk pieces.
-__device__ int direct_draw(const RejArgs& a, const RowView& r, double c, double u, double* s_red, double* s_scan,
+__device__ int direct_draw(const RejArgs& a, const RowView& r, double c, double u, double* s_red, double* s_w,
                            int* s_pick) {
   const int nch = (a.vocab + kChunk - 1) / kChunk;
   auto el = [&](int t) { return resid_el(a, r, t, c); };
@@ -738,7 +827,7 @@ __device__ int direct_draw(const RejArgs& a, const RowView& r, double c, double 
     for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) acc += el(t);
     const double sc = block_sum_d(acc, s_red);
     if (pre + sc > target || ch == nch - 1) {
-      int k = scan_range(t0, t1, pre, target, el, s_scan, s_pick);
+      int k = scan_range(t0, t1, pre, target, el, s_w, s_pick);
       if (k < 0) k = last_positive(0, a.vocab, el, s_pick);
       return k;
     }
@@ -747,202 +836,256 @@ __device__ int direct_draw(const RejArgs& a, const RowView& r, double c, double 
   return -1;
 }
 
-// Chunk holding the target u * sum(s_chunk) in the exact per-chunk masses s_chunk;
-// *pre is the mass of the chunks before it.
-__device__ inline int pick_chunk(const double* s_chunk, int nch, double u, double* pre, double* target) {
-  double S = 0.0;
-  for (int ch = 0; ch < nch; ++ch) S += s_chunk[ch];
-  *target = u * S;
-  double run = 0.0;
-  int ch = 0;
-  for (; ch < nch - 1; ++ch) {
-    if (run + s_chunk[ch] > *target) break;
-    run += s_chunk[ch];
-  }
-  *pre = run;
+// Chunk holding the target u * sum(s_chunk[0 .. nch)) (nch <= blockDim.x); *pre is
+// the mass of the chunks before it.
+__device__ inline int pick_chunk(const double* s_chunk, int nch, double u, double* s_w, int* s_pick, double* pre,
+                                 double* target) {
+  const int tid = threadIdx.x;
+  const double v = tid < nch ? s_chunk[tid] : 0.0;
+  if (tid == 0) *s_pick = nch - 1;
+  double S;
+  const double before = block_excl_scan_d(v, s_w, &S);
+  const double tg = u * S;
+  if (tid < nch - 1 && before + v > tg) atomicMin(s_pick, tid);
+  __syncthreads();
+  const int ch = *s_pick;
+  __syncthreads();
+  *target = tg;
+  // the prefix of the chosen chunk, as its owner computed it
+  if (tid == ch) s_w[4] = before;
+  __syncthreads();
+  *pre = s_w[4];
+  __syncthreads();
   return ch;
 }
 
 // One workgroup per node slot.  Node results go to the workspace; the request's
 // last workgroup walks from the root and writes accepted_child / term_token.
+struct SibState {
+  uint64_t rest;  // children not yet tested
+  double c, W;
+  int acc, lvl, zero_last, pending;  // pending: a rejection whose W needs a direct pass
+};
 __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, int chunked) {
-  __shared__ int s_par[64], s_tok[64];
-  __shared__ float s_ua[64], s_xl[64], s_xd[64];
+  __shared__ float s_ua[64];
+  __shared__ double s_px[64], s_qx[64];
   __shared__ long long s_lv[2 * kMaxKids];
-  __shared__ double s_iv[2 * kMaxKids];
+  __shared__ double s_ia[kMaxKids], s_ib[kMaxKids];
   __shared__ ListEntry s_list[kLdsList];
   __shared__ double s_red[kRjThreads / 64];
-  __shared__ long long s_ll[kRjThreads / 64];
-  __shared__ double s_scan[kRjThreads];
+  __shared__ double s_w[8];
   __shared__ double s_chunk[256];
+  __shared__ float s_cmx[256];
   __shared__ unsigned long long s_cP[256], s_cQ[256];
-  __shared__ int s_pick, s_bad, s_flag, s_nlist, s_last;
+  __shared__ int s_pick, s_flags, s_nlist, s_last;
+  __shared__ SibState s_st;
   __shared__ NodeRes s_res[64];
   __shared__ int s_oacc[64], s_oterm[64];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int nd = blockIdx.x;
   const int b = nd / a.n_max, n = nd % a.n_max;
   const int64_t base = (int64_t)b * a.n_max, row = nd;
+  if (blockIdx.x == 0 && tid == 0 && chunked) *w.act_count = 0;  // R1 and R2 are done with it
+  // ---- everything this node may need, in one round of loads ----
+  const NodeInfo inf = w.info[nd];
+  const int nb = a.n_nodes[b];
   if (tid < 64) {
     const bool in = tid < a.n_max;
-    s_par[tid] = in ? a.parent[base + tid] : -2;
-    s_tok[tid] = in ? a.tokens[base + tid] : 0;
     s_ua[tid] = in ? a.u_accept[base + tid] : 0.0f;
+    const KidInfo ki = in ? w.kid[base + tid] : KidInfo{0.0, 0.0};
+    s_px[tid] = ki.px;
+    s_qx[tid] = ki.qx;
   }
-  if (tid == 0) s_bad = 0;
-  const int nb = a.n_nodes[b];
-  const bool n_ok = nb >= 1 && nb <= a.n_max;
   RowView rv;
   rv.lt = a.tgt_logits + row * (int64_t)a.vocab;
   rv.ld = a.dft_logits + row * (int64_t)a.vocab;
   rv.mt = a.tgt_max[row];
   rv.md = a.dft_max[row];
-  const float zt = a.tgt_sumexp[row], zd = a.dft_sumexp[row];
+  rv.izt = inf.izt;
+  rv.izd = inf.izd;
   const float us = a.u_sample[row];
-  __syncthreads();
-  // the request's tree: parents precede children, tokens in range
-  if (n_ok && tid < nb) {
-    const int p = s_par[tid];
-    if (tid == 0 ? p != -1 : (p < 0 || p >= tid)) atomicOr(&s_bad, 1);
-    else if (tid > 0 && (s_tok[tid] < 0 || s_tok[tid] >= a.vocab)) atomicOr(&s_bad, 2);
+  const int k = __popcll(inf.kids);
+  const bool node_ok = inf.verdict == 0 && n < nb;
+  const bool chain = chunked && node_ok && inf.active;
+  if (chain) {
+    const ChainRec* R = w.rec + nd;
+    for (int l = tid; l < k; l += blockDim.x) {
+      s_ia[l] = R->a[l];
+      s_ib[l] = R->b[l];
+    }
+    for (int i = tid; i < 2 * k; i += blockDim.x) s_lv[i] = w.lvl[(int64_t)nd * 2 * kMaxKids + i];
+    const long long* cd = w.cdraw + (int64_t)nd * a.nch * 2;
+    for (int ch = tid; ch < a.nch; ch += blockDim.x) {
+      s_cP[ch] = (unsigned long long)cd[2 * ch];
+      s_cQ[ch] = (unsigned long long)cd[2 * ch + 1];
+    }
+    if (tid == 0) {
+      s_flags = R->flags;
+      s_nlist = (int)min(w.list_n[nd], (uint32_t)kListCap);
+    }
+  }
+  const bool leaf_chunks = chunked && node_ok && k == 0 && a.tgt_chunk_max != nullptr;
+  if (leaf_chunks && tid < a.nch) {
+    const float cm = a.tgt_chunk_max[row * a.nch + tid];
+    s_cmx[tid] = cm;
+    s_chunk[tid] = a.tgt_chunk_sum[row * a.nch + tid] * exp(((double)cm - (double)rv.mt) * a.inv_t);
   }
   __syncthreads();
   NodeRes res{SPEC_NODE_NOT_EVALUATED, SPEC_NODE_NOT_EVALUATED, 0, 0};
-  if (n_ok && s_bad == 0 && n < nb) {
+  if (node_ok) {
     if (isnan(rv.mt) || isnan(rv.md)) {
       res.err = 1;
     } else {
-      rv.izt = 1.0 / (double)zt;
-      rv.izd = 1.0 / (double)zd;
-      int first;
-      const int k = count_kids(s_par, n, nb, first);
-      if (tid > n && tid < nb && s_par[tid] == n) {  // the children's tokens in this row
-        s_xl[tid] = rv.lt[s_tok[tid]];
-        s_xd[tid] = rv.ld[s_tok[tid]];
-      }
-      if (k > 0 && chunked) {
-        for (int i = tid; i < 2 * k; i += blockDim.x) {
-          s_lv[i] = w.lvl[(int64_t)nd * 2 * kMaxKids + i];
-          s_iv[i] = w.ivl[(int64_t)nd * kMaxKids * 2 + i];
-        }
-        if (tid == 0) {
-          s_flag = w.flags[nd];
-          s_nlist = (int)min(w.list_n[nd], (uint32_t)kListCap);
-        }
-      }
-      __syncthreads();
       int acc = SPEC_NODE_NONE, term = -1;
       if (k == 0) {
         // ---- leaf: the bonus is drawn from p ----
         const double u = (double)us;
-        if (chunked && a.tgt_chunk_max) {
-          const float* cmx = a.tgt_chunk_max + row * a.nch;
-          const double* csm = a.tgt_chunk_sum + row * a.nch;
-          if (tid < a.nch) s_chunk[tid] = csm[tid] * exp(((double)cmx[tid] - (double)rv.mt) * a.inv_t);
-          __syncthreads();
+        if (leaf_chunks) {
           double pre, target;
-          const int ch = pick_chunk(s_chunk, a.nch, u, &pre, &target);
-          const float mc = cmx[ch];
+          const int ch = pick_chunk(s_chunk, a.nch, u, s_w, &s_pick, &pre, &target);
+          const float mc = s_cmx[ch];
           const double scale = exp(((double)mc - (double)rv.mt) * a.inv_t);
           const int t0 = ch * kChunk, t1 = min(a.vocab, t0 + kChunk);
-          term = chunk_scan(a, rv, t0, t1, false, mc, scale, 0.0, pre, target, s_scan, &s_pick);
+          term = chunk_scan(a, rv, t0, t1, false, mc, scale, 0.0, pre, target, s_w, &s_pick);
           if (term < 0) {
             auto el = [&](int t) { return (double)exp_scaled(rv.lt[t] - mc, a.est) * scale; };
             term = last_positive(t0, t1, el, &s_pick);
           }
         } else {
-          term = direct_draw(a, rv, 0.0, u, s_red, s_scan, &s_pick);
+          term = direct_draw(a, rv, 0.0, u, s_red, s_w, &s_pick);
         }
       } else {
         // ---- children in ascending index, tested against the running residual ----
-        const bool fast = chunked && !(s_flag & kFlagFallback);
+        const bool fast = chain && !(s_flags & kFlagFallback);
         const ListEntry* L = w.list + (int64_t)nd * kListCap;
         const int nlist = fast ? s_nlist : 0;
         const bool in_lds = nlist <= kLdsList;
+        const ListEntry* LL = in_lds ? s_list : L;
         if (in_lds)
           for (int i = tid; i < nlist; i += blockDim.x) s_list[i] = L[i];
-        const ListEntry* LL = in_lds ? s_list : L;
+        if (tid == 0) s_st = SibState{inf.kids, 0.0, 1.0, SPEC_NODE_NONE, 0, 0, 0};
         __syncthreads();
-        int lvl = 0;  // rejections so far
-        double c = 0.0, W = 1.0;
-        bool fell_back = !fast, zero_last = false;
-        for (int ci = first; ci < nb; ++ci) {
-          if (s_par[ci] != n) continue;
-          const double px = exp(((double)s_xl[ci] - (double)rv.mt) * a.inv_t) * rv.izt;
-          const double qx = exp(((double)s_xd[ci] - (double)rv.md) * a.inv_td) * rv.izd;
-          if ((double)s_ua[ci] < accept_ratio(px, qx, c, W)) {
-            acc = ci;
-            break;
-          }
-          ++lvl;  // cn = c + W is the threshold after this rejection
-          const double cn = c + W;
-          double Wn = 0.0;
-          if (!fell_back) {
-            const double ia = s_iv[2 * (lvl - 1)], ib = s_iv[2 * (lvl - 1) + 1];
+        // wavefront 0 follows the exact path as long as its guarantees hold
+        if (fast && tid < 64) {
+          uint64_t m = inf.kids;
+          double c = 0.0, W = 1.0;
+          int acc0 = SPEC_NODE_NONE, lvl = 0, zl = 0, pend = 0;
+          while (m) {
+            const int ci = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            if ((double)s_ua[ci] < accept_ratio(s_px[ci], s_qx[ci], c, W)) {
+              acc0 = ci;
+              break;
+            }
+            ++lvl;  // cn = c + W is the threshold after this rejection
+            const double cn = c + W;
+            const double ia = s_ia[lvl - 1], ib = s_ib[lvl - 1];
             if (!(cn >= ia && cn <= ib)) {
-              fell_back = true;
-            } else {
-              long long lp = 0, lq = 0;  // listed tokens inside the interval and above cn
-              for (int i = tid; i < nlist; i += blockDim.x) {
-                const ListEntry e = LL[i];
-                if (e.rho > cn && e.rho <= ib) {
-                  lp += to_fx(e.p);
-                  lq += to_fx(e.q);
-                }
+              pend = 1;
+              break;
+            }
+            long long lp = 0, lq = 0;  // listed tokens inside the interval and above cn
+            for (int i = lane; i < nlist; i += 64) {
+              const ListEntry e = LL[i];
+              if (e.rho > cn && e.rho <= ib) {
+                lp += e.fp;
+                lq += e.fq;
               }
-              lp = block_sum_ll(lp, s_ll);
-              lq = block_sum_ll(lq, s_ll);
-              Wn = ((double)(s_lv[2 * (lvl - 1)] + lp) - cn * (double)(s_lv[2 * (lvl - 1) + 1] + lq)) * kFxInv;
+            }
+            lp = wave_sum_ll(lp);
+            lq = wave_sum_ll(lq);
+            const double Wn =
+                ((double)(s_lv[2 * (lvl - 1)] + lp) * rv.izt - cn * (double)(s_lv[2 * (lvl - 1) + 1] + lq) * rv.izd) *
+                kFxInv;
+            if (Wn > 0.0) {
+              c = cn;
+              W = Wn;
+              zl = 0;
+            } else {
+              zl = 1;  // the residual keeps its previous threshold
             }
           }
-          if (fell_back) Wn = direct_W(a, rv, cn, s_red);
-          if (Wn > 0.0) {
-            c = cn;
-            W = Wn;
-            zero_last = false;
-          } else {
-            zero_last = true;  // the residual keeps its previous threshold
+          if (lane == 0) s_st = SibState{m, c, W, acc0, lvl, zl, pend};
+        }
+        __syncthreads();
+        const SibState st = s_st;
+        __syncthreads();
+        acc = st.acc;
+        double c = st.c, W = st.W;
+        bool zero_last = st.zero_last;
+        const bool fell_back = !fast || st.pending;
+        if (acc < 0 && fell_back) {  // finish with direct vocabulary passes
+          if (st.pending) {
+            const double cn = c + W;
+            const double Wn = direct_W(a, rv, cn, s_red);
+            if (Wn > 0.0) {
+              c = cn;
+              W = Wn;
+              zero_last = false;
+            } else {
+              zero_last = true;
+            }
+          }
+          for (uint64_t m = st.rest; m; m &= m - 1) {
+            const int ci = __ffsll((unsigned long long)m) - 1;
+            if ((double)s_ua[ci] < accept_ratio(s_px[ci], s_qx[ci], c, W)) {
+              acc = ci;
+              break;
+            }
+            const double cn = c + W;
+            const double Wn = direct_W(a, rv, cn, s_red);
+            if (Wn > 0.0) {
+              c = cn;
+              W = Wn;
+              zero_last = false;
+            } else {
+              zero_last = true;
+            }
           }
         }
         if (acc < 0) {
           // ---- all children rejected: the bonus is drawn from the residual ----
           const double u = (double)us;
           if (!fell_back && !zero_last) {
-            const double ib = s_iv[2 * (k - 1) + 1];
-            const long long* cd = w.cdraw + (int64_t)nd * a.nch * 2;
-            for (int ch = tid; ch < a.nch; ch += blockDim.x) {
-              s_cP[ch] = (unsigned long long)cd[2 * ch];
-              s_cQ[ch] = (unsigned long long)cd[2 * ch + 1];
-            }
-            __syncthreads();
+            const double ib = s_ib[k - 1];
             for (int i = tid; i < nlist; i += blockDim.x) {
               const ListEntry e = LL[i];
               if (e.rho > c && e.rho <= ib) {
                 const int ch = e.tok / kChunk;
-                atomicAdd(&s_cP[ch], (unsigned long long)to_fx(e.p));
-                atomicAdd(&s_cQ[ch], (unsigned long long)to_fx(e.q));
+                atomicAdd(&s_cP[ch], (unsigned long long)e.fp);
+                atomicAdd(&s_cQ[ch], (unsigned long long)e.fq);
               }
             }
             __syncthreads();
             if (tid < a.nch)
-              s_chunk[tid] = ((double)(long long)s_cP[tid] - c * (double)(long long)s_cQ[tid]) * kFxInv;
+              s_chunk[tid] = ((double)(long long)s_cP[tid] * rv.izt - c * (double)(long long)s_cQ[tid] * rv.izd) * kFxInv;
             __syncthreads();
             double pre, target;
-            const int ch = pick_chunk(s_chunk, a.nch, u, &pre, &target);
+            const int ch = pick_chunk(s_chunk, a.nch, u, s_w, &s_pick, &pre, &target);
             const int t0 = ch * kChunk, t1 = min(a.vocab, t0 + kChunk);
-            term = chunk_scan(a, rv, t0, t1, true, 0.0f, 1.0, c, pre, target, s_scan, &s_pick);
+            term = chunk_scan(a, rv, t0, t1, true, 0.0f, 1.0, c, pre, target, s_w, &s_pick);
             if (term < 0) {
               const double cc = c;
               auto el = [&](int t) { return resid_el(a, rv, t, cc); };
               term = last_positive(t0, t1, el, &s_pick);
             }
           } else {
-            term = direct_draw(a, rv, c, u, s_red, s_scan, &s_pick);
+            term = direct_draw(a, rv, c, u, s_red, s_w, &s_pick);
           }
         }
       }
       res.acc = acc;
       res.term = acc >= 0 ? SPEC_NODE_NOT_EVALUATED : term;
+    }
+  }
+  if (chain) {  // the chain state of this node is consumed: clear it for the next call
+    __syncthreads();
+    long long* hw = w.hist + (int64_t)nd * 2 * kHN;
+    for (int i = tid; i < 2 * kHN; i += blockDim.x) hw[i] = 0;
+    for (int i = tid; i < 2 * kMaxKids; i += blockDim.x) w.lvl[(int64_t)nd * 2 * kMaxKids + i] = 0;
+    if (tid == 0) {
+      w.list_n[nd] = 0;
+      w.rec[nd].flags = 0;
     }
   }
   // ---- publish; the request's last workgroup walks ----
@@ -967,7 +1110,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
   __syncthreads();
   if (tid == 0) {
     pub_store(&w.req_count[b], 0u);
-    int verdict = !n_ok || (s_bad & 1) ? SPEC_ERR_BAD_TREE : (s_bad ? SPEC_ERR_BAD_INPUT : 0);
+    int verdict = inf.verdict;
     int cur = 0;
     for (int step = 0; verdict == 0 && step < nb; ++step) {
       const NodeRes r = s_res[cur];
@@ -1058,8 +1201,8 @@ __global__ __launch_bounds__(64) void greedy_walk_kernel(RejArgs a) {
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout: node results and request counters always; the chain arrays
-// when the vocabulary spans two or more chunks.
+// Workspace layout: node results, plan and request counters always; the chain
+// arrays when the vocabulary spans two or more chunks.
 inline size_t node_ws_layout(int64_t batch, int64_t nodes, int nch, char* base, NodeWs* w) {
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -1070,15 +1213,17 @@ inline size_t node_ws_layout(int64_t batch, int64_t nodes, int nch, char* base, 
   NodeWs t{};
   t.res = (NodeRes*)take((size_t)nodes * sizeof(NodeRes));
   t.req_count = (uint32_t*)take((size_t)batch * 4);
+  t.info = (NodeInfo*)take((size_t)nodes * sizeof(NodeInfo));
+  t.kid = (KidInfo*)take((size_t)nodes * sizeof(KidInfo));
   if (nch >= 2) {
+    t.act_count = (uint32_t*)take(4);
+    t.act_list = (int32_t*)take((size_t)nodes * 4);
     t.hist = (long long*)take((size_t)nodes * kHN * 16);
+    t.rec = (ChainRec*)take((size_t)nodes * sizeof(ChainRec));
     t.lvl = (long long*)take((size_t)nodes * kMaxKids * 16);
-    t.ivl = (double*)take((size_t)nodes * kMaxKids * 16);
     t.cdraw = (long long*)take((size_t)nodes * nch * 16);
     t.list = (ListEntry*)take((size_t)nodes * kListCap * sizeof(ListEntry));
     t.list_n = (uint32_t*)take((size_t)nodes * 4);
-    t.r2_count = (uint32_t*)take((size_t)nodes * 4);
-    t.flags = (int32_t*)take((size_t)nodes * 4);
   }
   if (w) *w = t;
   return off;
@@ -1126,7 +1271,6 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt
   a.dft_logits = dft_logits;
   a.dft_max = dft_max;
   a.dft_sumexp = dft_sumexp;
-  a.greedy = greedy ? 1 : 0;
   a.inv_t = greedy ? 0.0 : 1.0 / (double)temperature;
   a.inv_td = greedy ? 0.0 : 1.0 / (double)draft_temperature;
   a.est = make_exp_scale(a.inv_t);
@@ -1152,12 +1296,15 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt
   }
   const int64_t nodes = (int64_t)batch * n_max;
   if (!workspace || workspace_bytes < node_ws_layout(batch, nodes, nch, nullptr, nullptr)) return SPEC_ERR_WORKSPACE;
+  if (nodes > 0x7fffffffLL || nodes * nch > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
   NodeWs w{};
   node_ws_layout(batch, nodes, nch, (char*)workspace, &w);
-  if (nodes > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)batch), dim3(64), 0, st, a, w, chunked ? 1 : 0);
+  SPEC_LAUNCH_CHECK();
   if (chunked) {
-    const int64_t grid = nodes * nch;
-    if (grid > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+    // grid-stride over (active node, chunk) items; the item count is known on the device only
+    const int64_t upper = nodes * nch;
+    const int64_t grid = std::min<int64_t>(upper, std::max<int64_t>(256, upper / 4));
     hipLaunchKernelGGL(chain_hist_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, w);
     SPEC_LAUNCH_CHECK();
     hipLaunchKernelGGL(chain_exact_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, w);
