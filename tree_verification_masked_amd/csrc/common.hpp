@@ -19,39 +19,131 @@ __device__ inline void report(int32_t* status, int32_t code) {
   if (status) atomicCAS(status, 0, code);
 }
 
-// ---- wave64 reductions (fixed butterfly order, so results are deterministic) ----
+// ---- wave64 cross-lane steps through DPP ----
+// Reductions use row-local permutes (quad swaps, half-row and row mirrors) and the
+// two row broadcasts; the total ends in lane 63 and is read back as a scalar, so
+// every lane sees it.  Scans use row shifts plus the row broadcasts.  Everything
+// stays in the vector ALU (no LDS permute) and the order of operations is fixed,
+// so results are deterministic.  Callers keep all 64 lanes active.
+constexpr int kDppQuad1032 = 0xb1, kDppQuad2301 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+
+// DPP move of v; lanes of rows outside kRowMask (or with no source lane) get `old`.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, kCtrl, kRowMask, 0xf, false);
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<kCtrl, kRowMask>(__float_as_int(old), __float_as_int(v)));
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline long long dpp_ll(long long old, long long v) {
+  const int lo = dpp_i<kCtrl, kRowMask>((int)(uint32_t)old, (int)(uint32_t)v);
+  const int hi = dpp_i<kCtrl, kRowMask>((int)(uint32_t)((unsigned long long)old >> 32),
+                                        (int)(uint32_t)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline double dpp_d(double old, double v) {
+  return __longlong_as_double(dpp_ll<kCtrl, kRowMask>(__double_as_longlong(old), __double_as_longlong(v)));
+}
+__device__ inline int lane63_i(int v) { return __builtin_amdgcn_readlane(v, 63); }
+__device__ inline float lane63_f(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+__device__ inline long long lane63_ll(long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((unsigned long long)v >> 32), 63);
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+__device__ inline double lane63_d(double v) { return __longlong_as_double(lane63_ll(__double_as_longlong(v))); }
+
 __device__ inline float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f<kDppQuad1032>(v, v));
+  v = fmaxf(v, dpp_f<kDppQuad2301>(v, v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppBcast15, 0xa>(v, v));
+  v = fmaxf(v, dpp_f<kDppBcast31, 0xc>(v, v));
+  return lane63_f(v);
 }
 __device__ inline float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f<kDppQuad1032>(0.0f, v);
+  v += dpp_f<kDppQuad2301>(0.0f, v);
+  v += dpp_f<kDppHalfMirror>(0.0f, v);
+  v += dpp_f<kDppMirror>(0.0f, v);
+  v += dpp_f<kDppBcast15, 0xa>(0.0f, v);
+  v += dpp_f<kDppBcast31, 0xc>(0.0f, v);
+  return lane63_f(v);
 }
 __device__ inline double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_d<kDppQuad1032>(0.0, v);
+  v += dpp_d<kDppQuad2301>(0.0, v);
+  v += dpp_d<kDppHalfMirror>(0.0, v);
+  v += dpp_d<kDppMirror>(0.0, v);
+  v += dpp_d<kDppBcast15, 0xa>(0.0, v);
+  v += dpp_d<kDppBcast31, 0xc>(0.0, v);
+  return lane63_d(v);
+}
+__device__ inline long long wave_sum_ll(long long v) {
+  v += dpp_ll<kDppQuad1032>(0, v);
+  v += dpp_ll<kDppQuad2301>(0, v);
+  v += dpp_ll<kDppHalfMirror>(0, v);
+  v += dpp_ll<kDppMirror>(0, v);
+  v += dpp_ll<kDppBcast15, 0xa>(0, v);
+  v += dpp_ll<kDppBcast31, 0xc>(0, v);
+  return lane63_ll(v);
+}
+__device__ inline int wave_max_i(int v) {
+  v = max(v, dpp_i<kDppQuad1032>(v, v));
+  v = max(v, dpp_i<kDppQuad2301>(v, v));
+  v = max(v, dpp_i<kDppHalfMirror>(v, v));
+  v = max(v, dpp_i<kDppMirror>(v, v));
+  v = max(v, dpp_i<kDppBcast15, 0xa>(v, v));
+  v = max(v, dpp_i<kDppBcast31, 0xc>(v, v));
+  return lane63_i(v);
 }
 __device__ inline int wave_or_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o);
+  v |= dpp_i<kDppQuad1032>(0, v);
+  v |= dpp_i<kDppQuad2301>(0, v);
+  v |= dpp_i<kDppHalfMirror>(0, v);
+  v |= dpp_i<kDppMirror>(0, v);
+  v |= dpp_i<kDppBcast15, 0xa>(0, v);
+  v |= dpp_i<kDppBcast31, 0xc>(0, v);
+  return lane63_i(v);
+}
+// Inclusive prefix sums across the wave in lane order (lanes without a source in a
+// shift add 0).
+__device__ inline int wave_incl_scan_i(int v) {
+  v += dpp_i<kDppShr1>(0, v);
+  v += dpp_i<kDppShr2>(0, v);
+  v += dpp_i<kDppShr4>(0, v);
+  v += dpp_i<kDppShr8>(0, v);
+  v += dpp_i<kDppBcast15, 0xa>(0, v);
+  v += dpp_i<kDppBcast31, 0xc>(0, v);
+  return v;
+}
+__device__ inline long long wave_incl_scan_ll(long long v) {
+  v += dpp_ll<kDppShr1>(0, v);
+  v += dpp_ll<kDppShr2>(0, v);
+  v += dpp_ll<kDppShr4>(0, v);
+  v += dpp_ll<kDppShr8>(0, v);
+  v += dpp_ll<kDppBcast15, 0xa>(0, v);
+  v += dpp_ll<kDppBcast31, 0xc>(0, v);
+  return v;
+}
+__device__ inline double wave_incl_scan_d(double v, int /*lane*/) {
+  v += dpp_d<kDppShr1>(0.0, v);
+  v += dpp_d<kDppShr2>(0.0, v);
+  v += dpp_d<kDppShr4>(0.0, v);
+  v += dpp_d<kDppShr8>(0.0, v);
+  v += dpp_d<kDppBcast15, 0xa>(0.0, v);
+  v += dpp_d<kDppBcast31, 0xc>(0.0, v);
   return v;
 }
 __device__ inline uint64_t shfl_u64(uint64_t v, int src) {
   uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
   return ((uint64_t)hi << 32) | lo;
-}
-// Inclusive prefix sum across the wave (Hillis-Steele, fixed order).
-__device__ inline double wave_incl_scan_d(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
 }
 
 // exp(d / T) for d <= 0 written as 2^(d * log2(e) / T); the scale is carried as an

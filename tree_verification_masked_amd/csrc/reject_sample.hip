@@ -154,6 +154,22 @@ __device__ inline void load_chunk(const float* row, int c0, int vocab, bool vec,
     }
   }
 }
+// R1 / R2 use 1024-thread workgroups: thread t holds tokens c0 + 4t .. c0 + 4t + 3.
+constexpr int kCThreads = 1024;
+constexpr int kCPer = kChunk / kCThreads;
+__device__ inline void load_chunk4(const float* row, int c0, int vocab, bool vec, float* x) {
+  const int t = c0 + 4 * (int)threadIdx.x;
+  if (vec && t + 4 <= vocab) {
+    const float4 f = *reinterpret_cast<const float4*>(row + t);
+    x[0] = f.x;
+    x[1] = f.y;
+    x[2] = f.z;
+    x[3] = f.w;
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) x[s2] = t + s2 < vocab ? row[t + s2] : -INFINITY;
+  }
+}
 // Contiguous layout (R3 scans): thread owns tokens r0 .. r0 + kPer - 1.
 __device__ inline void load_run(const float* row, int r0, int t1, bool vec, float* x) {
   if (vec && r0 + kPer <= t1) {
@@ -171,14 +187,16 @@ __device__ inline void load_run(const float* row, int r0, int t1, bool vec, floa
   }
 }
 
-// floor(pp * 2^42) of an unnormalised mass pp in [0, 1], by bit arithmetic (exact).
+// floor(pp * 2^42) of an unnormalised mass pp in [0, 1], by bit arithmetic (exact;
+// zero and subnormals, all below 2^-42, give 0).  Branch-free.
 __device__ inline long long fx42(float pp) {
   const uint32_t bits = __float_as_uint(pp);
   const int e = (int)(bits >> 23);  // pp >= 0
-  if (e == 0 || e > 127) return 0;  // zero and subnormals are below 2^-42
   const uint64_t m = (uint64_t)((bits & 0x7fffffu) | 0x800000u);
-  const int sh = e - 108;  // pp * 2^42 = m * 2^(e - 150 + 42)
-  return (long long)(sh >= 0 ? (m << sh) : (sh > -24 ? (m >> -sh) : 0ull));
+  const int sh = e - 108;  // pp * 2^42 = m * 2^(e - 150 + 42), sh <= 19
+  const uint64_t up = m << max(sh, 0), down = m >> min(-sh, 63);
+  const uint64_t v = sh >= 0 ? up : down;
+  return (e == 0 || e > 127) ? 0 : (long long)v;
 }
 
 struct RowView {
@@ -219,12 +237,10 @@ __device__ inline double accept_ratio(double px, double qx, double c, double W) 
 // R1 and R2 evaluate the same expression on the same inputs, with explicit
 // rounding, so they always agree on h.
 __device__ inline int est_bucket(float ep, float eq, float pp, float qq, float K) {
-  if (!(pp > 0.0f)) return -1;
-  if (!(qq > 0.0f)) return kHTop;
-  const float x = floorf(__fmul_rn(__fadd_rn(__fsub_rn(ep, eq), K), 128.0f));
-  if (x >= (float)kHB) return kHTop;
-  if (x < (float)-kHLow) return -1;
-  return (int)x + kHLow;
+  float x = floorf(__fmul_rn(__fadd_rn(__fsub_rn(ep, eq), K), 128.0f));
+  x = fminf(fmaxf(x, (float)(-kHLow - 1)), (float)kHB);  // NaN (both masses 0) becomes -3
+  const int h = (int)x + kHLow;                           // -1 .. kHTop
+  return pp > 0.0f ? (qq > 0.0f ? h : kHTop) : -1;
 }
 // Certain ratio range of each bucket: lb <= rho < ub (fp32 exp2 is within 2e-7
 // relative, well inside the margin).  Entry kHN is a sentinel above every bucket.
@@ -316,11 +332,6 @@ __device__ double w_bound(double c, const BucketRec* T, double izt, double izd, 
   return full + extra;
 }
 
-__device__ inline long long wave_sum_ll(long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 __device__ inline long long block_sum_ll(long long v, long long* s_ll) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
   v = wave_sum_ll(v);
@@ -427,9 +438,9 @@ __global__ __launch_bounds__(64) void plan_kernel(RejArgs a, NodeWs w, int chunk
 // ---------------------------------------------------------------------------
 // Items are (active node, chunk) pairs, item = slot * nch + chunk, visited
 // grid-stride.  The first item's node id is read together with the item count.
-__global__ __launch_bounds__(256) void chain_hist_kernel(RejArgs a, NodeWs w) {
-  __shared__ unsigned long long s_P[4][kHN], s_Q[4][kHN];  // one copy per wavefront
-  const int tid = threadIdx.x, wv = tid >> 6;
+__global__ __launch_bounds__(kCThreads) void chain_hist_kernel(RejArgs a, NodeWs w) {
+  __shared__ unsigned long long s_P[4][kHN], s_Q[4][kHN];  // copy (wave % 4): few lanes ever meet
+  const int tid = threadIdx.x, cp = (tid >> 6) & 3;
   const int nodes = a.batch * a.n_max;
   const int items = (int)(*w.act_count) * a.nch;
   const int first_nd = w.act_list[min((int)blockIdx.x / a.nch, nodes - 1)];
@@ -438,20 +449,23 @@ __global__ __launch_bounds__(256) void chain_hist_kernel(RejArgs a, NodeWs w) {
     const int chunk = it % a.nch;
     const NodeInfo inf = w.info[nd];
     const float mt = a.tgt_max[nd], md = a.dft_max[nd];
-    float xl[kPer], xd[kPer];
-    load_chunk(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
-    load_chunk(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
-    for (int i = tid; i < kHN; i += blockDim.x)
-      for (int c = 0; c < 4; ++c) s_P[c][i] = s_Q[c][i] = 0;
+    float xl[kCPer], xd[kCPer];
+    load_chunk4(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
+    load_chunk4(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
+    for (int i = tid; i < 4 * kHN; i += blockDim.x) {
+      (&s_P[0][0])[i] = 0;
+      (&s_Q[0][0])[i] = 0;
+    }
     __syncthreads();
 #pragma unroll
-    for (int s2 = 0; s2 < kPer; ++s2) {
+    for (int s2 = 0; s2 < kCPer; ++s2) {
       const float ep = exp2_arg(xl[s2], mt, a.est), eq = exp2_arg(xd[s2], md, a.esd);
       const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
       const int h = est_bucket(ep, eq, pp, qq, inf.K);
-      if (h < 0) continue;
-      atomicAdd(&s_P[wv][h], (unsigned long long)fx42(pp));
-      atomicAdd(&s_Q[wv][h], (unsigned long long)fx42(qq));
+      if (h >= 0) {
+        atomicAdd(&s_P[cp][h], (unsigned long long)fx42(pp));
+        atomicAdd(&s_Q[cp][h], (unsigned long long)fx42(qq));
+      }
     }
     __syncthreads();
     unsigned long long* hg = (unsigned long long*)w.hist + (int64_t)nd * 2 * kHN;
@@ -475,18 +489,18 @@ __global__ __launch_bounds__(256) void chain_hist_kernel(RejArgs a, NodeWs w) {
 // rho > a_l:
 //   P_above(l) = sum_{rho > b_l} p = S[H_l] + (tokens of buckets [G_l, H_l) with rho > b_l),
 // and the tokens of [G_l, H_l) with a_l < rho <= b_l are kept in the node's list.
-__global__ __launch_bounds__(256) void chain_exact_kernel(RejArgs a, NodeWs w) {
+__global__ __launch_bounds__(kCThreads) void chain_exact_kernel(RejArgs a, NodeWs w) {
   __shared__ BucketRec s_T[kHN + 1];
-  __shared__ long long s_wt[2][4];
+  __shared__ long long s_wt[2][kCThreads / 64];
   __shared__ double s_a[kMaxKids], s_b[kMaxKids];
   __shared__ int s_G[kMaxKids], s_H[kMaxKids];
   __shared__ unsigned long long s_mask[kHN];  // levels whose edge range holds bucket h
   __shared__ unsigned long long s_EP[kMaxKids], s_EQ[kMaxKids];
   __shared__ QEntry s_q[kQueue];
   __shared__ ListEntry s_list[kWgList];
-  __shared__ long long s_ll[4];
+  __shared__ long long s_ll[kCThreads / 64];
   __shared__ int s_qn, s_nlist, s_base, s_bad;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
   const int nodes = a.batch * a.n_max;
   const int items = (int)(*w.act_count) * a.nch;
   const int first_nd = w.act_list[min((int)blockIdx.x / a.nch, nodes - 1)];
@@ -497,53 +511,36 @@ __global__ __launch_bounds__(256) void chain_exact_kernel(RejArgs a, NodeWs w) {
     const NodeInfo inf = w.info[nd];
     const int k = __popcll(inf.kids);
     const float mt = a.tgt_max[nd], md = a.dft_max[nd];
-    float xl[kPer], xd[kPer];
-    load_chunk(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
-    load_chunk(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
-    // merged histogram -> suffix sums (thread t owns buckets 3t .. 3t+2)
+    float xl[kCPer], xd[kCPer];
+    load_chunk4(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
+    load_chunk4(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
+    // merged histogram -> suffix sums S[h] = sum_{h' >= h} hist[h'], S[kHN] = 0
     const long long* hg = w.hist + (int64_t)nd * 2 * kHN;
-    long long v0[3], v1[3];
-#pragma unroll
-    for (int e = 0; e < 3; ++e) {
-      const int h = 3 * tid + e;
-      v0[e] = h < kHN ? hg[2 * h] : 0;
-      v1[e] = h < kHN ? hg[2 * h + 1] : 0;
-    }
+    const long long v0 = tid < kHN ? hg[2 * tid] : 0, v1 = tid < kHN ? hg[2 * tid + 1] : 0;
     for (int l = tid; l < k; l += blockDim.x) s_EP[l] = s_EQ[l] = 0;
+    for (int h = tid; h < kHN; h += blockDim.x) s_mask[h] = 0;
     if (tid == 0) {
       s_qn = 0;
       s_nlist = 0;
       s_bad = 0;
     }
     {
-      const long long t0 = v0[0] + v0[1] + v0[2], t1 = v1[0] + v1[1] + v1[2];
-      long long i0 = t0, i1 = t1;  // inclusive suffix within the wave
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const long long u0 = __shfl_down(i0, o), u1 = __shfl_down(i1, o);
-        if (lane + o < 64) {
-          i0 += u0;
-          i1 += u1;
-        }
-      }
+      // suffix within the wave = wave total - inclusive prefix + own value
+      const long long p0 = wave_incl_scan_ll(v0), p1 = wave_incl_scan_ll(v1);
+      const long long w0 = lane63_ll(p0), w1 = lane63_ll(p1);
+      long long i0 = w0 - p0 + v0, i1 = w1 - p1 + v1;
       if (lane == 0) {
-        s_wt[0][wv] = i0;
-        s_wt[1][wv] = i1;
+        s_wt[0][wv] = w0;
+        s_wt[1][wv] = w1;
       }
       __syncthreads();
-      long long e0 = i0 - t0, e1 = i1 - t1;
-      for (int x = wv + 1; x < 4; ++x) {
-        e0 += s_wt[0][x];
-        e1 += s_wt[1][x];
+      for (int x = wv + 1; x < nw; ++x) {
+        i0 += s_wt[0][x];
+        i1 += s_wt[1][x];
       }
-      for (int e = 2; e >= 0; --e) {
-        e0 += v0[e];
-        e1 += v1[e];
-        const int h = 3 * tid + e;
-        if (h <= kHN) {
-          s_T[h].SP = e0;
-          s_T[h].SQ = e1;
-        }
+      if (tid <= kHN) {
+        s_T[tid].SP = i0;
+        s_T[tid].SQ = i1;
       }
     }
     __syncthreads();
@@ -583,11 +580,9 @@ __global__ __launch_bounds__(256) void chain_exact_kernel(RejArgs a, NodeWs w) {
       __syncthreads();
       continue;
     }
-    for (int h = tid; h < kHN; h += blockDim.x) {
-      unsigned long long m = 0;
-      for (int l = 0; l < k; ++l)
-        if (h >= s_G[l] && h < s_H[l]) m |= 1ull << l;
-      s_mask[h] = m;
+    for (int x = tid; x < k * kMaxEdge; x += blockDim.x) {  // mark the edge ranges
+      const int l = x / kMaxEdge, h = s_G[l] + x % kMaxEdge;
+      if (h < s_H[l]) atomicOr(&s_mask[h], 1ull << l);
     }
     if (chunk == 0) {  // the certain part above each interval, and the intervals
       unsigned long long* lv = (unsigned long long*)w.lvl + (int64_t)nd * 2 * kMaxKids;
@@ -602,42 +597,37 @@ __global__ __launch_bounds__(256) void chain_exact_kernel(RejArgs a, NodeWs w) {
     __syncthreads();
     const int htop = s_H[k - 1];
     long long cp = 0, cq = 0;  // this chunk's tokens with rho > b_{k-1} (the terminal draw)
-    int hh[kPer];
-    float pq[kPer], qq2[kPer];
+    int hh[kCPer];
+    float pq[kCPer], qq2[kCPer];
+    unsigned edge = 0;
 #pragma unroll
-    for (int s2 = 0; s2 < kPer; ++s2) {
+    for (int s2 = 0; s2 < kCPer; ++s2) {
       const float ep = exp2_arg(xl[s2], mt, a.est), eq = exp2_arg(xd[s2], md, a.esd);
       const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
       const int h = est_bucket(ep, eq, pp, qq, inf.K);
-      if (h >= htop) {
-        cp += fx42(pp);
-        cq += fx42(qq);
-      }
+      const bool above = h >= htop;
+      cp += above ? fx42(pp) : 0;
+      cq += above ? fx42(qq) : 0;
       hh[s2] = h;
       pq[s2] = pp;
       qq2[s2] = qq;
     }
-    unsigned edge = 0;
 #pragma unroll
-    for (int s2 = 0; s2 < kPer; ++s2) {
+    for (int s2 = 0; s2 < kCPer; ++s2) {
       const int h = hh[s2];
       if (h >= 0 && h < htop && s_mask[h]) edge |= 1u << s2;
     }
     // queue slots: one LDS atomic per wavefront
     const int ne = __popc(edge);
-    int pre = ne;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(pre, o);
-      if (lane >= o) pre += t;
-    }
+    const int pre = wave_incl_scan_i(ne);
     int qbase = 0;
     if (lane == 63 && pre) qbase = atomicAdd(&s_qn, pre);
-    qbase = __shfl(qbase, 63) + pre - ne;
+    qbase = lane63_i(qbase) + pre - ne;
+    const int c0 = chunk * kChunk + 4 * tid;
 #pragma unroll
-    for (int s2 = 0; s2 < kPer; ++s2) {
+    for (int s2 = 0; s2 < kCPer; ++s2) {
       if (edge & (1u << s2)) {
-        if (qbase < kQueue) s_q[qbase] = QEntry{chunk_tok(chunk * kChunk, s2), hh[s2], pq[s2], qq2[s2]};
+        if (qbase < kQueue) s_q[qbase] = QEntry{c0 + s2, hh[s2], pq[s2], qq2[s2]};
         ++qbase;
       }
     }
@@ -752,8 +742,7 @@ __device__ int last_positive(int t0, int t1, Elem elem, int* s_pick) {
   int best = -1;
   for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x)
     if (elem(t) > 0.0) best = t;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
+  best = wave_max_i(best);
   __syncthreads();
   if (threadIdx.x == 0) *s_pick = -1;
   __syncthreads();
@@ -967,6 +956,21 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
         __syncthreads();
         // wavefront 0 follows the exact path as long as its guarantees hold
         if (fast && tid < 64) {
+          // this lane's list entries stay in registers across the levels
+          double er[kLdsList / 64];
+          long long efp[kLdsList / 64], efq[kLdsList / 64];
+#pragma unroll
+          for (int j = 0; j < kLdsList / 64; ++j) {
+            const int i = lane + 64 * j;
+            er[j] = -1.0;  // never above a threshold
+            efp[j] = efq[j] = 0;
+            if (in_lds && i < nlist) {
+              const ListEntry e = s_list[i];
+              er[j] = e.rho;
+              efp[j] = e.fp;
+              efq[j] = e.fq;
+            }
+          }
           uint64_t m = inf.kids;
           double c = 0.0, W = 1.0;
           int acc0 = SPEC_NODE_NONE, lvl = 0, zl = 0, pend = 0;
@@ -985,11 +989,20 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
               break;
             }
             long long lp = 0, lq = 0;  // listed tokens inside the interval and above cn
-            for (int i = lane; i < nlist; i += 64) {
-              const ListEntry e = LL[i];
-              if (e.rho > cn && e.rho <= ib) {
-                lp += e.fp;
-                lq += e.fq;
+            if (in_lds) {
+#pragma unroll
+              for (int j = 0; j < kLdsList / 64; ++j) {
+                const bool inside = er[j] > cn && er[j] <= ib;
+                lp += inside ? efp[j] : 0;
+                lq += inside ? efq[j] : 0;
+              }
+            } else {
+              for (int i = lane; i < nlist; i += 64) {
+                const ListEntry e = LL[i];
+                if (e.rho > cn && e.rho <= ib) {
+                  lp += e.fp;
+                  lq += e.fq;
+                }
               }
             }
             lp = wave_sum_ll(lp);
@@ -1305,9 +1318,9 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt
     // grid-stride over (active node, chunk) items; the item count is known on the device only
     const int64_t upper = nodes * nch;
     const int64_t grid = std::min<int64_t>(upper, std::max<int64_t>(256, upper / 4));
-    hipLaunchKernelGGL(chain_hist_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, w);
+    hipLaunchKernelGGL(chain_hist_kernel, dim3((unsigned)grid), dim3(kCThreads), 0, st, a, w);
     SPEC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(chain_exact_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, w);
+    hipLaunchKernelGGL(chain_exact_kernel, dim3((unsigned)grid), dim3(kCThreads), 0, st, a, w);
     SPEC_LAUNCH_CHECK();
   }
   hipLaunchKernelGGL(node_kernel, dim3((unsigned)nodes), dim3(kRjThreads), 0, st, a, w, chunked ? 1 : 0);

@@ -64,6 +64,23 @@ __device__ inline void better(float& m, int& a, float om, int oa) {
     a = oa;
   }
 }
+// Wave-wide (max, lowest index) in DPP steps; every lane gets the result.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline void better_dpp(float& m, int& a) {
+  const float m2 = dpp_f<kCtrl, kRowMask>(m, m);
+  const int a2 = dpp_i<kCtrl, kRowMask>(a, a);
+  better(m, a, m2, a2);
+}
+__device__ inline void wave_best(float& m, int& a) {
+  better_dpp<kDppQuad1032>(m, a);
+  better_dpp<kDppQuad2301>(m, a);
+  better_dpp<kDppHalfMirror>(m, a);
+  better_dpp<kDppMirror>(m, a);
+  better_dpp<kDppBcast15, 0xa>(m, a);
+  better_dpp<kDppBcast31, 0xc>(m, a);
+  m = lane63_f(m);
+  a = lane63_i(a);
+}
 
 template <bool kVec>
 __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSet B, int32_t vocab, int nch,
@@ -119,8 +136,7 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSe
   __shared__ int s_a[kSmThreads / 64];
   __shared__ int s_b[kSmThreads / 64];
   __shared__ double s_s[kSmThreads / 64];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) better(m, am, __shfl_xor(m, o), __shfl_xor(am, o));
+  wave_best(m, am);
   bad = wave_or_i(bad);
   if (lane == 0) {
     s_m[wid] = m;
@@ -172,8 +188,7 @@ __global__ __launch_bounds__(256) void softmax_merge_kernel(SmSet A, SmSet B, in
     better(m_all, a_all, S.cmax[row * nch + c], S.carg[row * nch + c]);
     b_all |= S.cbad[row * nch + c];
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) better(m_all, a_all, __shfl_xor(m_all, o), __shfl_xor(a_all, o));
+  wave_best(m_all, a_all);
   b_all = wave_or_i(b_all);
   double z = 0.0;
   if (!S.greedy && m_all > -INFINITY) {
