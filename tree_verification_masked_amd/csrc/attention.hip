@@ -35,6 +35,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTile = 64;           // keys per tile
 constexpr int kMfmaRowsPerWg = 128; // 4 waves x 32 rows
 constexpr int kShflRowsPerWg = 16;  // 4 waves x 4 rows
+constexpr int kMaxSplitPages = 1024;  // page ids of one split kept in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -82,17 +83,91 @@ __device__ inline bool key_visible(int t, int len, int ctx, uint64_t anc_row) {
 // ---------------------------------------------------------------------------
 // MFMA path
 // ---------------------------------------------------------------------------
+// K and V tiles (64 keys) go from HBM straight into LDS with 16-byte
+// global_load_lds, kStages tiles in flight, no register staging.  A key row of D
+// bf16 is CH = D/8 chunks of 16 bytes; chunk c of key k sits at slot c ^ (k % CH),
+// so the 32 keys an MFMA operand read touches fall on distinct banks.  K is read
+// as the A operand of S^T = K Q^T (16 bytes per lane).  V is read with the gfx950
+// LDS transpose load: within each 16-lane group, lane i returns element i % 4 of
+// the 8-byte rows addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12; addressing
+// key kb + r/4, dims d0 + 4 (r % 4) from lane r hands every lane four consecutive
+// keys of one dimension, which is the V^T operand of O^T = V^T P^T.
+constexpr int kStages = 3;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+__device__ inline float xor32_f(float v) {  // the value of lane l ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ inline void vm_wait() {
+  static_assert(n < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+__device__ inline void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Eight transpose reads and the wait for them in one inline-asm block.  Written
+// through the compiler's own LDS reads, the wait insertion would treat them as
+// possibly aliasing the LDS tiles still being filled and wait for every
+// outstanding load; inside one block the results exist only after the wait.
+__device__ inline uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+// Eight 16-byte reads (the K operands of one 32-key block) and their wait, likewise.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ inline void ds_read_b128_x8(v4i (&r)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %9\n"
+      "ds_read_b128 %2, %10\n"
+      "ds_read_b128 %3, %11\n"
+      "ds_read_b128 %4, %12\n"
+      "ds_read_b128 %5, %13\n"
+      "ds_read_b128 %6, %14\n"
+      "ds_read_b128 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
+}
+__device__ inline void ds_read_tr16_x8(v4s (&r)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %9\n"
+      "ds_read_b64_tr_b16 %2, %10\n"
+      "ds_read_b64_tr_b16 %3, %11\n"
+      "ds_read_b64_tr_b16 %4, %12\n"
+      "ds_read_b64_tr_b16 %5, %13\n"
+      "ds_read_b64_tr_b16 %6, %14\n"
+      "ds_read_b64_tr_b16 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int KS = D + 8;      // LDS row stride (bf16) of the K tile
-  constexpr int VS = kTile + 8;  // LDS row stride (bf16) of the transposed V tile
-  constexpr int PIECES = kTile * D / 8;  // 16-byte pieces per tile
-  constexpr int PER_THREAD = PIECES / 256;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[kTile * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 sVt[D * VS];
+  constexpr int ROWB = D * 2;           // bytes per key row
+  constexpr int CH = D / 8;             // 16-byte chunks per key row
+  constexpr int TILE_B = kTile * ROWB;  // bytes per K (or V) tile
+  constexpr int KPB = 1024 / ROWB;      // keys per 1 KB wave load
+  constexpr int LOADS = TILE_B / 1024 / 4;  // wave loads per tile per operand
+  __shared__ __attribute__((aligned(1024))) char sKV[kStages][2][TILE_B];
+  __shared__ int s_page[kMaxSplitPages];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int blk = blockIdx.x;
+  // XCD-aware order: consecutive logical workgroups (the splits and query blocks
+  // of one KV head) land on the same XCD and share its L2.
+  const int W = a.batch * a.hkv * a.qblocks * a.S;
+  const int per_xcd = (W + 7) / 8;
+  const int L = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (L >= W) return;
+  int blk = L;
   const int s = blk % a.S;
   blk /= a.S;
   const int qb = blk % a.qblocks;
@@ -102,135 +177,213 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   const int hpg = a.hq / a.hkv;
   const int G = a.n_max * hpg;
 
+  const int k_begin = s * a.split_len;
+  const __bf16* kbase = (const __bf16*)a.k;
+  const __bf16* vbase = (const __bf16*)a.v;
+  // tile it -> stage it % kStages; wave w issues LOADS 1 KB loads of K and of V.
+  // Keys at or past `kend` read key kend - 1 instead (valid memory; masked later).
+  auto issue_tile = [&](int it, int kend, auto key_off) {
+    const int t0 = k_begin + it * kTile;
+    char* dk = sKV[it % kStages][0];
+    char* dv = sKV[it % kStages][1];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int kbi = wid * LOADS + i;
+      const int key = kbi * KPB + lane / CH, slot = lane % CH;
+      const int c = slot ^ (key & (CH - 1));
+      const int t = min(t0 + key, kend - 1);
+      const int64_t off = key_off(t) + c * 8;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (__attribute__((address_space(3))) void*)(dk + kbi * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (__attribute__((address_space(3))) void*)(dv + kbi * 1024), 16, 0, 0);
+    }
+  };
+  auto flat_off = [&](int t) -> int64_t { return (((int64_t)b * a.kv_capacity + t) * a.hkv + g) * D; };
+  // contiguous KV: the first tiles go out before the request's lengths are known
+  int n_spec = 0;
+  if (!a.block_table) {
+    const int cap_end = min(k_begin + a.split_len, a.kv_capacity);
+    const int cap_tiles = cap_end > k_begin ? (cap_end - k_begin + kTile - 1) / kTile : 0;
+    n_spec = min(cap_tiles, kStages - 1);
+    for (int it = 0; it < n_spec; ++it) issue_tile(it, cap_end, flat_off);
+  }
   const int len = request_len(a, b);
   const int n = a.n_nodes[b];
   const int ctx = a.ctx_len[b];
-  // this lane's query row
   const int r = qb * kMfmaRowsPerWg + wid * 32 + (lane & 31);
   const int node = r / hpg;
   const int h = g * hpg + r % hpg;
   const bool row_live = len >= 0 && r < G && node < n;
-  const uint64_t anc_row = row_live ? a.anc[(int64_t)b * a.n_max + node] : 0ull;
-
-  const int k_begin = s * a.split_len;
   const int k_end = min(k_begin + a.split_len, len < 0 ? 0 : len);
+  const int n_tiles = k_end > k_begin ? (k_end - k_begin + kTile - 1) / kTile : 0;
 
+  // page ids of this split (paged KV), one lookup per key afterwards
+  int bad_page = 0;
+  if (a.block_table && n_tiles > 0) {
+    const int p0 = k_begin / a.page_size, p1 = (k_end - 1) / a.page_size;
+    for (int i = tid; i <= p1 - p0; i += 256) {
+      int pg = a.block_table[(int64_t)b * a.kv_capacity + p0 + i];
+      if (pg < 0 || pg >= a.n_pages) {
+        bad_page = 1;
+        pg = 0;  // a valid page: the request's output is unspecified, status says why
+      }
+      s_page[i] = pg;
+    }
+    __syncthreads();
+  }
+  const int page0 = a.block_table ? k_begin / a.page_size : 0;
+  auto key_off = [&](int t) -> int64_t {  // element offset of key t (< k_end) of head g
+    if (!a.block_table) return (((int64_t)b * a.kv_capacity + t) * a.hkv + g) * D;
+    const int pg = s_page[t / a.page_size - page0];
+    return (((int64_t)pg * a.page_size + t % a.page_size) * a.hkv + g) * D;
+  };
+  auto issue = [&](int it) {
+    if (a.block_table) issue_tile(it, k_end, key_off);
+    else issue_tile(it, k_end, flat_off);
+  };
+  if (a.block_table)
+    for (int it = 0; it < kStages - 1 && it < n_tiles; ++it) issue(it);
+  const uint64_t anc_row = row_live ? a.anc[(int64_t)b * a.n_max + node] : 0ull;
   // Q fragments: lane holds row r, dims kk*16 + 8*(lane/32) .. +8
   bf16x8 qf[D / 16];
   {
     const __bf16* qrow = (const __bf16*)a.q + (((int64_t)b * a.n_max + node) * a.hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      if (row_live && anc_row)
+      if (row_live)
         qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + 8 * (lane >> 5));
       else
         qf[kk] = bf16x8{};
     }
   }
+  // anc_row and Q are in registers before the loop (with the first tiles, which the
+  // first iteration needs anyway), so no wait inside the loop is for them
+  vm_wait<0>();
   f32x16 acc_o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc_o[db] = f32x16{};
+  // Running max and sum of the row.  The max used for the exponentials is raised
+  // only when a score exceeds it by more than 2^8 (log2 domain 8): until then the
+  // terms stay below 256 and the accumulators need no rescaling.
   float m_run = -INFINITY, l_run = 0.0f;
-
-  const __bf16* kbase = (const __bf16*)a.k;
-  const __bf16* vbase = (const __bf16*)a.v;
-  uint4 kreg[PER_THREAD], vreg[PER_THREAD];
-  int bad_page = 0;
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int j = 0; j < PER_THREAD; ++j) {
-      const int p = tid + j * 256;
-      const int key = p / (D / 8), dc = p % (D / 8);
-      const int t = t0 + key;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (t < k_end) {
-        const int64_t off = kv_off(a, b, t, g);
-        if (off >= 0) {
-          kv = *reinterpret_cast<const uint4*>(kbase + off + dc * 8);
-          vv = *reinterpret_cast<const uint4*>(vbase + off + dc * 8);
-        } else {
-          bad_page = 1;
-        }
-      }
-      kreg[j] = kv;
-      vreg[j] = vv;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int j = 0; j < PER_THREAD; ++j) {
-      const int p = tid + j * 256;
-      const int key = p / (D / 8), dc = p % (D / 8);
-      *reinterpret_cast<uint4*>(&sK[key * KS + dc * 8]) = kreg[j];
-      const __bf16* vv = reinterpret_cast<const __bf16*>(&vreg[j]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sVt[(dc * 8 + e) * VS + key] = vv[e];
-    }
-  };
-
-  const int n_tiles = k_end > k_begin ? (k_end - k_begin + kTile - 1) / kTile : 0;
-  if (n_tiles > 0) load_tile(k_begin);
   for (int it = 0; it < n_tiles; ++it) {
+    // this wave's loads of tile `it` are done once at most (tiles issued after it) x
+    // 2 LOADS operations remain in flight
+    const int ahead = min(n_tiles - 1 - it, kStages - 2);
+    if (ahead >= 1 && it > 0) vm_wait<2 * LOADS>();
+    else vm_wait<0>();  // (the first tile also waits for the Q loads issued after it)
+    lds_barrier();  // every wave's part of tile `it` is in LDS; tile it-1 is consumed
+    if (it + kStages - 1 < n_tiles) issue(it + kStages - 1);
+    const char* sk = sKV[it % kStages][0];
+    const char* sv = sKV[it % kStages][1];
     const int t0 = k_begin + it * kTile;
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (it + 1 < n_tiles) load_tile(t0 + kTile);  // overlaps the math below
 
-    // ---- S^T = K Q^T for two 32-key blocks ----
-    f32x16 acc_s[2];
+    // ---- S^T = K Q^T for two 32-key blocks: all 2 * D/16 operand reads first (in
+    // batches of 8), then MFMAs alternating between the two independent blocks ----
+    f32x16 acc_s[2] = {f32x16{}, f32x16{}};
+    v4i kr[D / 64][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      acc_s[kb] = f32x16{};
+    for (int bi = 0; bi < D / 64; ++bi) {
+      uint32_t ad[8];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&sK[(kb * 32 + (lane & 31)) * KS + kk * 16 + 8 * (lane >> 5)]);
-        acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s[kb], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        const int x = 8 * bi + j, kb = x & 1, kk = x >> 1;
+        const int key = kb * 32 + (lane & 31);
+        const int c = 2 * kk + (lane >> 5);
+        ad[j] = lds_addr(sk + key * ROWB + ((c ^ (key & (CH - 1))) * 16));
       }
+      ds_read_b128_x8(kr[bi], ad);
+    }
+#pragma unroll
+    for (int x = 0; x < 2 * (D / 16); ++x) {
+      const int kb = x & 1, kk = x >> 1;
+      bf16x8 kf;
+      __builtin_memcpy(&kf, &kr[x >> 3][x & 7], sizeof(kf));
+      acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s[kb], 0, 0, 0);
     }
     // ---- mask, scale, online softmax (lane owns row lane%32; lane^32 holds the other keys) ----
     float tmax = -INFINITY;
+    if (t0 + kTile <= min(ctx, k_end)) {  // every key of the tile is a prompt key
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int t = t0 + key;
-        const bool vis = row_live && t < k_end && key_visible(t, len, ctx, anc_row);
-        const float sc = vis ? acc_s[kb][e] * a.scale_log2 : -INFINITY;
-        acc_s[kb][e] = sc;
-        tmax = fmaxf(tmax, sc);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        for (int e = 0; e < 16; ++e) {
+          acc_s[kb][e] *= a.scale_log2;
+          tmax = fmaxf(tmax, acc_s[kb][e]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int t = t0 + kb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int j = t - ctx;  // tree slot
+          const bool vis = t < k_end && (j < 0 || ((anc_row >> (j & 63)) & 1ull));
+          const float sc = vis ? acc_s[kb][e] * a.scale_log2 : -INFINITY;
+          acc_s[kb][e] = sc;
+          tmax = fmaxf(tmax, sc);
+        }
+    }
+    tmax = fmaxf(tmax, xor32_f(tmax));
+    if (!row_live) tmax = -INFINITY;
+    if (__any(tmax > m_run + 8.0f)) {  // raise the reference max (rare after the first tile)
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = (m_new == -INFINITY || m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc_o[db] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.0f;
     bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = (m_new == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(acc_s[kb][e] - m_new);
+        const float p = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(acc_s[kb][e] - m_run);
         psum += p;
         pf[kb * 2 + (e >> 3)][e & 7] = (__bf16)p;
       }
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    psum += xor32_f(psum);
+    l_run += psum;
+    // ---- O^T += V^T P^T; k-step ks covers keys 16 ks .. 16 ks + 15 in the order
+    // sigma(k) = 8 ((k >> 2) & 1) + 4 (k >> 3) + (k & 3) that the S^T accumulator gives ----
+    const int g4 = lane >> 4, rr = lane & 15;
+    // operands of k-step ks for every d-block: D/32 blocks x (lo, hi) reads, in
+    // batches of 8 (one batch covers 4 d-blocks)
+    auto read_v = [&](int ks, int bq, v4s (&va)[8]) {
+      const int key0 = 16 * ks + 4 * (g4 >> 1) + (rr >> 2);
+      const int key1 = key0 + 8;
+      uint32_t ad[8];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc_o[db] *= alpha;
-    // ---- O^T += V^T P^T; k-step ks covers keys 16*ks .. 16*ks+15 in the permuted order ----
+      for (int q = 0; q < 4; ++q) {
+        const int db = 4 * bq + q;
+        const int d = (db % (D / 32)) * 32 + 16 * (g4 & 1) + 4 * (rr & 3);
+        const int c = d >> 3, half = (d >> 2) & 1;
+        ad[2 * q] = lds_addr(sv + key0 * ROWB + ((c ^ (key0 & (CH - 1))) * 16) + half * 8);
+        ad[2 * q + 1] = lds_addr(sv + key1 * ROWB + ((c ^ (key1 & (CH - 1))) * 16) + half * 8);
+      }
+      ds_read_tr16_x8(va, ad);
+    };
+    constexpr int NB = (D / 32 + 3) / 4;  // batches per k-step (1 for D <= 128)
+    constexpr int NDB = D / 32;
+    v4s va[2][NB][8];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const __bf16* vrow = &sVt[(db * 32 + (lane & 31)) * VS + 4 * (lane >> 5)];
+    for (int bq = 0; bq < NB; ++bq) read_v(0, bq, va[0][bq]);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + ks * 16);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + ks * 16 + 8);
-        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const v4s lohi[2] = {va[ks & 1][db / 4][2 * (db % 4)], va[ks & 1][db / 4][2 * (db % 4) + 1]};
+        bf16x8 vf;
+        __builtin_memcpy(&vf, lohi, sizeof(vf));
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc_o[db], 0, 0, 0);
       }
+      // the next k-step's operands are read while these MFMAs run
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < 4)
+#pragma unroll
+        for (int bq = 0; bq < NB; ++bq) read_v(ks + 1, bq, va[(ks + 1) & 1][bq]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (bad_page) report(a.status, SPEC_ERR_BAD_INPUT);
@@ -383,22 +536,37 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* __rest
   float res[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) res[v] = 0.0f;
-  if (live) {
-    const int64_t stride = (int64_t)a.batch * a.n_max * a.hq;
+  if (live) {  // wave-uniform
+    const int64_t stride = rows;
+    // split maxima and sums: lane s holds split s (and s + 64, ...)
     float m = -INFINITY;
-    for (int s = 0; s < a.S; ++s) m = fmaxf(m, a.mpart[s * stride + rowid]);
-    if (m > -INFINITY) {
-      float L = 0.0f;
+    for (int s = lane; s < a.S; s += 64) m = fmaxf(m, a.mpart[s * stride + rowid]);
+    m = wave_max_f(m);
+    float L = 0.0f;
+    for (int s = lane; s < a.S; s += 64) {
+      const float ms = a.mpart[s * stride + rowid];
+      if (ms > -INFINITY) L += a.lpart[s * stride + rowid] * __builtin_amdgcn_exp2f(ms - m);
+    }
+    L = wave_sum_f(L);
+    if (m > -INFINITY && L > 0.0f) {
       float acc[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
-      for (int s = 0; s < a.S; ++s) {
-        const float ms = a.mpart[s * stride + rowid];
-        if (ms == -INFINITY) continue;
-        const float w = __builtin_amdgcn_exp2f(ms - m);
-        L = fmaf(a.lpart[s * stride + rowid], w, L);
+      for (int s0 = 0; s0 < a.S; s0 += 8) {  // eight splits' rows in flight at once
+        float wts[8], vals[8][NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) acc[v] = fmaf(a.opart[(s * stride + rowid) * D + lane + 64 * v], w, acc[v]);
+        for (int j = 0; j < 8; ++j) {
+          const int s = s0 + j;
+          const bool in = s < a.S;
+          const float ms = in ? a.mpart[s * stride + rowid] : -INFINITY;
+          wts[j] = ms > -INFINITY ? __builtin_amdgcn_exp2f(ms - m) : 0.0f;
+#pragma unroll
+          for (int v = 0; v < NV; ++v) vals[j][v] = in ? a.opart[(s * stride + rowid) * D + lane + 64 * v] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int v = 0; v < NV; ++v) acc[v] = fmaf(vals[j][v], wts[j], acc[v]);
       }
       const float inv = 1.0f / L;
 #pragma unroll
@@ -422,10 +590,12 @@ inline AttnPlan make_plan(int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
   p.qblocks = (G + rows_per_wg - 1) / rows_per_wg;
   const int tiles = max(1, (max_kv_len + kTile - 1) / kTile);
   const int64_t base = (int64_t)batch * hkv * p.qblocks;
-  const int64_t target = 512;  // two workgroups per CU
+  const int64_t target = p.mfma ? 256 : 512;  // MFMA: about one workgroup per CU
   int S = (int)std::min<int64_t>((target + base - 1) / base, tiles);
   S = std::max(S, 1);
-  const int tiles_per_split = (tiles + S - 1) / S;
+  int tiles_per_split = (tiles + S - 1) / S;
+  // a split's page ids must fit the LDS table (16-token pages or larger)
+  tiles_per_split = std::min(tiles_per_split, (kMaxSplitPages - 1) * 16 / kTile);
   p.S = (tiles + tiles_per_split - 1) / tiles_per_split;
   p.split_len = tiles_per_split * kTile;
   return p;
@@ -462,8 +632,11 @@ extern "C" int spec_tree_attention(const void* q, const void* k, const void* v, 
   if (head_dim != 64 && head_dim != 128) return SPEC_ERR_UNSUPPORTED;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
   const AttnPlan p = make_plan(batch, n_max, hq, hkv, max_kv_len, dtype);
+  // the MFMA path keeps a split's page ids in LDS, sized for pages of 16 tokens or more
+  if (p.mfma && block_table && page_size < 16) return SPEC_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < attn_ws_bytes(p, batch, n_max, hq, head_dim)) return SPEC_ERR_WORKSPACE;
-  const int64_t grid = (int64_t)batch * hkv * p.qblocks * p.S;
+  int64_t grid = (int64_t)batch * hkv * p.qblocks * p.S;
+  if (p.mfma) grid = (grid + 7) / 8 * 8;  // whole rounds over the 8 XCDs
   if (grid > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
   AttnArgs a;
   a.q = q;
