@@ -23,6 +23,7 @@
 //    the tile against one row, the row softmax uses wave reductions, and P V is
 //    accumulated with one lane per head dimension.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -93,6 +94,13 @@ __device__ inline bool key_visible(int t, int len, int ctx, uint64_t anc_row) {
 // key kb + r/4, dims d0 + 4 (r % 4) from lane r hands every lane four consecutive
 // keys of one dimension, which is the V^T operand of O^T = V^T P^T.
 constexpr int kStages = 3;
+// LDS slot of 16-byte chunk c of key k is c ^ kv_swz(k): a bijection of the low key
+// bits, so 16 consecutive keys (K operand reads) hit 16 different slots, and the
+// 4 consecutive keys x 2 chunks of one transpose-read group hit 8 different slots.
+template <int CH>
+__device__ inline int kv_swz(int key) {
+  return ((((key & 3) << 1) | ((key >> 2) & 1) | (key & 8))) & (CH - 1);
+}
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -119,35 +127,39 @@ __device__ inline void lds_barrier() {
 __device__ inline uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
-// Eight 16-byte reads (the K operands of one 32-key block) and their wait, likewise.
+// Eight 16-byte reads and their wait, likewise: read 2j at ad[j], read 2j+1 at
+// ad[j] + OFF1 (the same K chunk of the second 32-key block).
 typedef int v4i __attribute__((ext_vector_type(4)));
-__device__ inline void ds_read_b128_x8(v4i (&r)[8], const uint32_t (&ad)[8]) {
+template <int OFF1>
+__device__ inline void ds_read_b128_x8(v4i (&r)[8], const uint32_t (&ad)[4]) {
   asm volatile(
       "ds_read_b128 %0, %8\n"
-      "ds_read_b128 %1, %9\n"
-      "ds_read_b128 %2, %10\n"
-      "ds_read_b128 %3, %11\n"
-      "ds_read_b128 %4, %12\n"
-      "ds_read_b128 %5, %13\n"
-      "ds_read_b128 %6, %14\n"
-      "ds_read_b128 %7, %15\n"
+      "ds_read_b128 %1, %8 offset:%12\n"
+      "ds_read_b128 %2, %9\n"
+      "ds_read_b128 %3, %9 offset:%12\n"
+      "ds_read_b128 %4, %10\n"
+      "ds_read_b128 %5, %10 offset:%12\n"
+      "ds_read_b128 %6, %11\n"
+      "ds_read_b128 %7, %11 offset:%12\n"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "n"(OFF1));
 }
+// Eight transpose reads at ad[j] + OFF and their wait.
+template <int OFF>
 __device__ inline void ds_read_tr16_x8(v4s (&r)[8], const uint32_t (&ad)[8]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n"
-      "ds_read_b64_tr_b16 %1, %9\n"
-      "ds_read_b64_tr_b16 %2, %10\n"
-      "ds_read_b64_tr_b16 %3, %11\n"
-      "ds_read_b64_tr_b16 %4, %12\n"
-      "ds_read_b64_tr_b16 %5, %13\n"
-      "ds_read_b64_tr_b16 %6, %14\n"
-      "ds_read_b64_tr_b16 %7, %15\n"
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]), "n"(OFF));
 }
 
 template <int D>
@@ -160,7 +172,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char sKV[kStages][2][TILE_B];
   __shared__ int s_page[kMaxSplitPages];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: consecutive logical workgroups (the splits and query blocks
   // of one KV head) land on the same XCD and share its L2.
   const int W = a.batch * a.hkv * a.qblocks * a.S;
@@ -190,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
     for (int i = 0; i < LOADS; ++i) {
       const int kbi = wid * LOADS + i;
       const int key = kbi * KPB + lane / CH, slot = lane % CH;
-      const int c = slot ^ (key & (CH - 1));
+      const int c = slot ^ kv_swz<CH>(key);
       const int t = min(t0 + key, kend - 1);
       const int64_t off = key_off(t) + c * 8;
       __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (__attribute__((address_space(3))) void*)(dk + kbi * 1024), 16, 0, 0);
@@ -206,12 +218,24 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
     n_spec = min(cap_tiles, kStages - 1);
     for (int it = 0; it < n_spec; ++it) issue_tile(it, cap_end, flat_off);
   }
+  // Q and the ancestor row go out before the request's lengths are known: the row's
+  // node index is clamped into [0, n_max) so the addresses are valid for every row,
+  // and rows that turn out dead drop what they loaded
+  const int r = qb * kMfmaRowsPerWg + wid * 32 + (lane & 31);
+  const int node = r / hpg;
+  const int node_c = min(node, a.n_max - 1);
+  const int h = g * hpg + r % hpg;
+  const uint64_t anc_raw = a.anc[(int64_t)b * a.n_max + node_c];
+  // Q fragments: lane holds row r, dims kk*16 + 8*(lane/32) .. +8
+  bf16x8 qf[D / 16];
+  {
+    const __bf16* qrow = (const __bf16*)a.q + (((int64_t)b * a.n_max + node_c) * a.hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + 8 * (lane >> 5));
+  }
   const int len = request_len(a, b);
   const int n = a.n_nodes[b];
   const int ctx = a.ctx_len[b];
-  const int r = qb * kMfmaRowsPerWg + wid * 32 + (lane & 31);
-  const int node = r / hpg;
-  const int h = g * hpg + r % hpg;
   const bool row_live = len >= 0 && r < G && node < n;
   const int k_end = min(k_begin + a.split_len, len < 0 ? 0 : len);
   const int n_tiles = k_end > k_begin ? (k_end - k_begin + kTile - 1) / kTile : 0;
@@ -236,36 +260,73 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
     const int pg = s_page[t / a.page_size - page0];
     return (((int64_t)pg * a.page_size + t % a.page_size) * a.hkv + g) * D;
   };
+  // Contiguous KV, a tile wholly below k_end: a uniform tile base plus per-lane 32-bit
+  // offsets that are the same for every tile.
+  uint32_t loff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int key = (wid * LOADS + i) * KPB + lane / CH, slot = lane % CH;
+    loff[i] = (uint32_t)(((int64_t)key * a.hkv * D + (slot ^ kv_swz<CH>(key)) * 8) * 2);
+  }
   auto issue = [&](int it) {
-    if (a.block_table) issue_tile(it, k_end, key_off);
-    else issue_tile(it, k_end, flat_off);
+    const int t0 = k_begin + it * kTile;
+    if (a.block_table) {
+      issue_tile(it, k_end, key_off);
+    } else if (t0 + kTile <= k_end) {
+      const int64_t tb = ((((int64_t)b * a.kv_capacity + t0) * a.hkv + g) * D) * 2;
+      const char* kt = (const char*)kbase + tb;
+      const char* vt = (const char*)vbase + tb;
+      char* dk = sKV[it % kStages][0];
+      char* dv = sKV[it % kStages][1];
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int kbi = wid * LOADS + i;
+        __builtin_amdgcn_global_load_lds((const void*)(kt + loff[i]), (__attribute__((address_space(3))) void*)(dk + kbi * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + loff[i]), (__attribute__((address_space(3))) void*)(dv + kbi * 1024), 16, 0, 0);
+      }
+    } else {
+      issue_tile(it, k_end, flat_off);
+    }
   };
   if (a.block_table)
     for (int it = 0; it < kStages - 1 && it < n_tiles; ++it) issue(it);
-  const uint64_t anc_row = row_live ? a.anc[(int64_t)b * a.n_max + node] : 0ull;
-  // Q fragments: lane holds row r, dims kk*16 + 8*(lane/32) .. +8
-  bf16x8 qf[D / 16];
-  {
-    const __bf16* qrow = (const __bf16*)a.q + (((int64_t)b * a.n_max + node) * a.hq + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      if (row_live)
-        qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + 8 * (lane >> 5));
-      else
-        qf[kk] = bf16x8{};
-    }
-  }
   // anc_row and Q are in registers before the loop (with the first tiles, which the
   // first iteration needs anyway), so no wait inside the loop is for them
   vm_wait<0>();
+  const uint64_t anc_row = row_live ? anc_raw : 0ull;
+  if (!row_live)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = bf16x8{};
   f32x16 acc_o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc_o[db] = f32x16{};
-  // Running max and sum of the row.  The max used for the exponentials is raised
-  // only when a score exceeds it by more than 2^8 (log2 domain 8): until then the
-  // terms stay below 256 and the accumulators need no rescaling.
+  // Running max and sum of the row (log2 domain, scaled scores).  The max used for
+  // the exponentials is raised only when a score exceeds it by more than 8 (a factor
+  // 2^8): until then the terms stay below 256 and the accumulators need no rescaling.
   float m_run = -INFINITY, l_run = 0.0f;
-  for (int it = 0; it < n_tiles; ++it) {
+  const float sl2 = a.scale_log2;
+  // per-lane LDS byte offsets of the operand reads within a tile, fixed for the loop
+  const int g4 = lane >> 4, rr = lane & 15;
+  uint32_t koff[D / 16];  // K operand of key block 0, step kk (block 1: + 32 rows)
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const int key = lane & 31, c = 2 * kk + (lane >> 5);
+    koff[kk] = key * ROWB + ((c ^ kv_swz<CH>(key)) * 16);
+  }
+  uint32_t voff[D / 32][2];  // V^T operand of d-block db, keys +0 / +8 (k-step ks: + 16 ks rows)
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+      const int key = 4 * (g4 >> 1) + (rr >> 2) + 8 * hl;
+      const int d = db * 32 + 16 * (g4 & 1) + 4 * (rr & 3);
+      voff[db][hl] = key * ROWB + (((d >> 3) ^ kv_swz<CH>(key)) * 16) + ((d >> 2) & 1) * 8;
+    }
+  // One 64-key tile.  kMasked: some key of the tile is a tree key or lies past the
+  // request's end, so scores go through the visibility test; the other tiles (all
+  // prompt keys, the bulk of the work) skip it.
+  auto tile = [&](int it, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     // this wave's loads of tile `it` are done once at most (tiles issued after it) x
     // 2 LOADS operations remain in flight
     const int ahead = min(n_tiles - 1 - it, kStages - 2);
@@ -279,19 +340,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 
     // ---- S^T = K Q^T for two 32-key blocks: all 2 * D/16 operand reads first (in
     // batches of 8), then MFMAs alternating between the two independent blocks ----
+    const uint32_t kbase_lds = lds_addr(sk), vbase_lds = lds_addr(sv);
     f32x16 acc_s[2] = {f32x16{}, f32x16{}};
     v4i kr[D / 64][8];
 #pragma unroll
     for (int bi = 0; bi < D / 64; ++bi) {
-      uint32_t ad[8];
+      uint32_t ad[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int x = 8 * bi + j, kb = x & 1, kk = x >> 1;
-        const int key = kb * 32 + (lane & 31);
-        const int c = 2 * kk + (lane >> 5);
-        ad[j] = lds_addr(sk + key * ROWB + ((c ^ (key & (CH - 1))) * 16));
-      }
-      ds_read_b128_x8(kr[bi], ad);
+      for (int j = 0; j < 4; ++j) ad[j] = kbase_lds + koff[4 * bi + j];
+      ds_read_b128_x8<32 * ROWB>(kr[bi], ad);
     }
 #pragma unroll
     for (int x = 0; x < 2 * (D / 16); ++x) {
@@ -300,16 +357,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       __builtin_memcpy(&kf, &kr[x >> 3][x & 7], sizeof(kf));
       acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s[kb], 0, 0, 0);
     }
-    // ---- mask, scale, online softmax (lane owns row lane%32; lane^32 holds the other keys) ----
+    // ---- mask, online softmax (lane owns row lane%32; lane^32 holds the other keys);
+    // raw scores, the scale is applied inside the exponent ----
     float tmax = -INFINITY;
-    if (t0 + kTile <= min(ctx, k_end)) {  // every key of the tile is a prompt key
+    if constexpr (!kMasked) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          acc_s[kb][e] *= a.scale_log2;
-          tmax = fmaxf(tmax, acc_s[kb][e]);
-        }
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, acc_s[kb][e]);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -318,12 +373,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
           const int t = t0 + kb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           const int j = t - ctx;  // tree slot
           const bool vis = t < k_end && (j < 0 || ((anc_row >> (j & 63)) & 1ull));
-          const float sc = vis ? acc_s[kb][e] * a.scale_log2 : -INFINITY;
+          const float sc = vis ? acc_s[kb][e] : -INFINITY;
           acc_s[kb][e] = sc;
           tmax = fmaxf(tmax, sc);
         }
     }
-    tmax = fmaxf(tmax, xor32_f(tmax));
+    tmax = fmaxf(tmax, xor32_f(tmax)) * sl2;
     if (!row_live) tmax = -INFINITY;
     if (__any(tmax > m_run + 8.0f)) {  // raise the reference max (rare after the first tile)
       const float m_new = fmaxf(m_run, tmax);
@@ -333,59 +388,66 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       for (int db = 0; db < D / 32; ++db) acc_o[db] *= alpha;
       m_run = m_new;
     }
+    const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;
     float psum = 0.0f;
     bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(acc_s[kb][e] - m_run);
+        const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[kb][e], sl2, neg_m));
         psum += p;
         pf[kb * 2 + (e >> 3)][e & 7] = (__bf16)p;
       }
     psum += xor32_f(psum);
-    l_run += psum;
+    l_run += m_run == -INFINITY ? 0.0f : psum;
     // ---- O^T += V^T P^T; k-step ks covers keys 16 ks .. 16 ks + 15 in the order
     // sigma(k) = 8 ((k >> 2) & 1) + 4 (k >> 3) + (k & 3) that the S^T accumulator gives ----
-    const int g4 = lane >> 4, rr = lane & 15;
     // operands of k-step ks for every d-block: D/32 blocks x (lo, hi) reads, in
     // batches of 8 (one batch covers 4 d-blocks)
-    auto read_v = [&](int ks, int bq, v4s (&va)[8]) {
-      const int key0 = 16 * ks + 4 * (g4 >> 1) + (rr >> 2);
-      const int key1 = key0 + 8;
-      uint32_t ad[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int db = 4 * bq + q;
-        const int d = (db % (D / 32)) * 32 + 16 * (g4 & 1) + 4 * (rr & 3);
-        const int c = d >> 3, half = (d >> 2) & 1;
-        ad[2 * q] = lds_addr(sv + key0 * ROWB + ((c ^ (key0 & (CH - 1))) * 16) + half * 8);
-        ad[2 * q + 1] = lds_addr(sv + key1 * ROWB + ((c ^ (key1 & (CH - 1))) * 16) + half * 8);
-      }
-      ds_read_tr16_x8(va, ad);
-    };
+    // one batch: the lo/hi reads of d-blocks 4 bq .. 4 bq + 3 at k-step KS
     constexpr int NB = (D / 32 + 3) / 4;  // batches per k-step (1 for D <= 128)
     constexpr int NDB = D / 32;
+    uint32_t vad[NB][8];
+#pragma unroll
+    for (int bq = 0; bq < NB; ++bq)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int db = (4 * bq + q) % NDB;
+        vad[bq][2 * q] = vbase_lds + voff[db][0];
+        vad[bq][2 * q + 1] = vbase_lds + voff[db][1];
+      }
     v4s va[2][NB][8];
+    auto read_v = [&](auto ks_tag, v4s (&dst)[NB][8]) {
+      constexpr int KS = decltype(ks_tag)::value;
 #pragma unroll
-    for (int bq = 0; bq < NB; ++bq) read_v(0, bq, va[0][bq]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int bq = 0; bq < NB; ++bq) ds_read_tr16_x8<16 * KS * ROWB>(dst[bq], vad[bq]);
+    };
+    auto pv_step = [&](auto ks_tag) {
+      constexpr int KS = decltype(ks_tag)::value;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const v4s lohi[2] = {va[ks & 1][db / 4][2 * (db % 4)], va[ks & 1][db / 4][2 * (db % 4) + 1]};
+        const v4s lohi[2] = {va[KS & 1][db / 4][2 * (db % 4)], va[KS & 1][db / 4][2 * (db % 4) + 1]};
         bf16x8 vf;
         __builtin_memcpy(&vf, lohi, sizeof(vf));
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc_o[db], 0, 0, 0);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[KS], acc_o[db], 0, 0, 0);
       }
       // the next k-step's operands are read while these MFMAs run
       __builtin_amdgcn_sched_barrier(0);
-      if (ks + 1 < 4)
-#pragma unroll
-        for (int bq = 0; bq < NB; ++bq) read_v(ks + 1, bq, va[(ks + 1) & 1][bq]);
+      if constexpr (KS + 1 < 4) read_v(std::integral_constant<int, KS + 1>{}, va[(KS + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+    };
+    read_v(std::integral_constant<int, 0>{}, va[0]);
+    pv_step(std::integral_constant<int, 0>{});
+    pv_step(std::integral_constant<int, 1>{});
+    pv_step(std::integral_constant<int, 2>{});
+    pv_step(std::integral_constant<int, 3>{});
+  };
+  // tiles below min(ctx, k_end) hold prompt keys only
+  const int n_plain = min(n_tiles, max(0, (min(ctx, k_end) - k_begin) / kTile));
+  int it = 0;
+  for (; it < n_plain; ++it) tile(it, std::false_type{});
+  for (; it < n_tiles; ++it) tile(it, std::true_type{});
   if (bad_page) report(a.status, SPEC_ERR_BAD_INPUT);
   // ---- write this split's partials for the lane's row ----
   if (r < G && node < a.n_max) {
