@@ -61,6 +61,7 @@ constexpr int kListCap = 4096;      // exact in-interval tokens kept per node
 constexpr int kWgList = 256;        // in-interval tokens one R2 workgroup can stage
 constexpr int kQueue = 1024;        // edge tokens one R2 workgroup can stage
 constexpr int kLdsList = 512;       // list entries R3 keeps in LDS
+constexpr int kShortList = 32;      // lists R3 walks with a single lane
 constexpr int kMaxEdge = 24;        // edge buckets per level before the direct path
 constexpr double kFx = 4398046511104.0;  // 2^42
 constexpr double kFxInv = 1.0 / kFx;
@@ -511,12 +512,13 @@ __global__ __launch_bounds__(kCThreads) void chain_exact_kernel(RejArgs a, NodeW
     const NodeInfo inf = w.info[nd];
     const int k = __popcll(inf.kids);
     const float mt = a.tgt_max[nd], md = a.dft_max[nd];
+    // merged histogram -> suffix sums S[h] = sum_{h' >= h} hist[h'], S[kHN] = 0; it is
+    // loaded before the chunk's logits, which are only needed after the intervals
+    const long long* hg = w.hist + (int64_t)nd * 2 * kHN;
+    const long long v0 = tid < kHN ? hg[2 * tid] : 0, v1 = tid < kHN ? hg[2 * tid + 1] : 0;
     float xl[kCPer], xd[kCPer];
     load_chunk4(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
     load_chunk4(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
-    // merged histogram -> suffix sums S[h] = sum_{h' >= h} hist[h'], S[kHN] = 0
-    const long long* hg = w.hist + (int64_t)nd * 2 * kHN;
-    const long long v0 = tid < kHN ? hg[2 * tid] : 0, v1 = tid < kHN ? hg[2 * tid + 1] : 0;
     for (int l = tid; l < k; l += blockDim.x) s_EP[l] = s_EQ[l] = 0;
     for (int h = tid; h < kHN; h += blockDim.x) s_mask[h] = 0;
     if (tid == 0) {
@@ -954,8 +956,48 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
           for (int i = tid; i < nlist; i += blockDim.x) s_list[i] = L[i];
         if (tid == 0) s_st = SibState{inf.kids, 0.0, 1.0, SPEC_NODE_NONE, 0, 0, 0};
         __syncthreads();
-        // wavefront 0 follows the exact path as long as its guarantees hold
-        if (fast && tid < 64) {
+        // A short list (the usual case): one lane follows the exact path alone, with
+        // no wave reductions between the sequential levels.  The sums are exact
+        // integers, so the result is the same as the wavefront version below.
+        if (fast && nlist <= kShortList && tid == 0) {
+          uint64_t m = inf.kids;
+          double c = 0.0, W = 1.0;
+          int acc0 = SPEC_NODE_NONE, lvl = 0, zl = 0, pend = 0;
+          while (m) {
+            const int ci = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            if ((double)s_ua[ci] < accept_ratio(s_px[ci], s_qx[ci], c, W)) {
+              acc0 = ci;
+              break;
+            }
+            ++lvl;
+            const double cn = c + W;
+            const double ia = s_ia[lvl - 1], ib = s_ib[lvl - 1];
+            if (!(cn >= ia && cn <= ib)) {
+              pend = 1;
+              break;
+            }
+            long long lp = s_lv[2 * (lvl - 1)], lq = s_lv[2 * (lvl - 1) + 1];
+            for (int i = 0; i < nlist; ++i) {
+              const double rho = s_list[i].rho;
+              if (rho > cn && rho <= ib) {
+                lp += s_list[i].fp;
+                lq += s_list[i].fq;
+              }
+            }
+            const double Wn = ((double)lp * rv.izt - cn * (double)lq * rv.izd) * kFxInv;
+            if (Wn > 0.0) {
+              c = cn;
+              W = Wn;
+              zl = 0;
+            } else {
+              zl = 1;  // the residual keeps its previous threshold
+            }
+          }
+          s_st = SibState{m, c, W, acc0, lvl, zl, pend};
+        }
+        // otherwise wavefront 0 follows it, the list spread over its lanes
+        if (fast && nlist > kShortList && tid < 64) {
           // this lane's list entries stay in registers across the levels
           double er[kLdsList / 64];
           long long efp[kLdsList / 64], efq[kLdsList / 64];
