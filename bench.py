@@ -2,7 +2,8 @@
 
 A step is the whole hot path over one input set, issued on one HIP stream:
     spec_tree_mask_build, spec_tree_attention (one layer's KV), spec_tree_softmax
-    (target rows, and draft rows at T > 0), spec_tree_reject_sample, spec_accept_path.
+    (target rows, and draft rows at T > 0), spec_tree_reject_sample (whose final walk
+    also writes the accepted path, the result of spec_accept_path).
 Workload (default): the Llama-3-8B-shaped step -- one request, a 60-node EAGLE-2
 tree (top-k 10, depth 6), 4096 cached tokens, 32 query / 8 KV heads, head_dim 128,
 bf16 KV, fp32 logits over a 128256-token vocabulary, T = 1.  Synthetic, seeded.
@@ -94,9 +95,8 @@ def main():
             step.softmax(None, r["tgt_logits"], r.get("dft_logits"))
             ev[3].record(stream)
             ev[4].record(stream)
-            step.reject(None, r["tgt_logits"], r.get("dft_logits"))
+            step.reject(None, r["tgt_logits"], r.get("dft_logits"))  # writes the accepted path too
             ev[5].record(stream)
-            step.path()
             ev[6].record(stream)
 
     # warm-up, then the clean timed region
@@ -117,7 +117,7 @@ def main():
     torch.cuda.synchronize()
     stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(6)] for e in evs]) * 1e3  # us
     st_mean = stage.mean(axis=0)
-    names = ["mask_build", "attention", "softmax_pair", "-", "reject_sample", "accept_path"]
+    names = ["mask_build", "attention", "softmax_pair", "-", "reject_sample", "-"]
 
     attn_b, logit_b, samp_b = algorithmic_bytes(inp)
     step_b = attn_b + samp_b

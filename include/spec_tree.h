@@ -184,14 +184,17 @@ int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const flo
  * SPEC_NODE_NOT_EVALUATED.  A request with a bad tree, a token outside
  * [0, vocab) or an invalid logit row gets accepted_child[b,0] =
  * SPEC_NODE_BAD_REQUEST and a device error code.
+ * path_nodes, out_tokens [batch, n_max] and accept_len [batch] (int32, all three
+ * or none, NULL to skip): the accepted path, exactly as spec_accept_path would
+ * derive it from accepted_child and term_token, written by the same walk.
  * T > 0 needs the workspace of spec_tree_reject_sample_workspace_size
  * (zero-filled once; every call leaves it ready for the next).  Each node is
  * evaluated in parallel and the last workgroup of a request walks the results;
  * vocabularies of more than one chunk add a ratio-histogram launch and an
  * exact-sum launch first, so no workgroup waits on another.  At T == 0 the
  * workspace may be NULL.
- * Host errors: T < 0 or NaN, T > 0 with T_d <= 0, null required pointers, sizes,
- * workspace.
+ * Host errors: T < 0 or NaN, T > 0 with T_d <= 0, null required pointers, only
+ * some of the path outputs, sizes, workspace.
  */
 size_t spec_tree_reject_sample_workspace_size(int32_t batch, int32_t n_max, int32_t vocab);
 int spec_tree_reject_sample(const float* tgt_logits, const float* tgt_max, const float* tgt_sumexp,
@@ -200,8 +203,9 @@ int spec_tree_reject_sample(const float* tgt_logits, const float* tgt_max, const
                             const float* dft_max, const float* dft_sumexp, float draft_temperature,
                             const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
                             const float* u_accept, const float* u_sample, int32_t batch, int32_t n_max, int32_t vocab,
-                            int32_t* accepted_child, int32_t* term_token, void* workspace, size_t workspace_bytes,
-                            int32_t* status, void* stream);
+                            int32_t* accepted_child, int32_t* term_token, int32_t* path_nodes, int32_t* out_tokens,
+                            int32_t* accept_len, void* workspace, size_t workspace_bytes, int32_t* status,
+                            void* stream);
 
 /*
  * Accepted path plus bonus token (tree notes, parts C and G; gingerlabs page, "A

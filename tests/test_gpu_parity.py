@@ -187,9 +187,13 @@ def _sampling_gpu(inp):
     d = to_device(dict(inp, q=None))
     st = VerifyStep(d, with_attention=False)
     st.softmax()
-    st.reject()
-    st.path()
-    return st.results()
+    st.reject()  # its walk writes the accepted path too
+    fused = st.results()
+    st.path()  # spec_accept_path from accepted_child and term_token
+    got = st.results()
+    for k in ("path_nodes", "out_tokens", "accept_len"):
+        assert np.array_equal(fused[k], got[k]), k
+    return got
 
 
 def _compare_sampling(got, ref, n_nodes):
@@ -468,3 +472,9 @@ def test_full_step(cfg, T):
     ref = _oracle_sampling(inp)
     ties = _compare_sampling(got, ref, inp["n_nodes"])
     print("accept_len", got["accept_len"].tolist(), "near ties", ties)
+    # the path the sampler's walk wrote equals what spec_accept_path derives
+    fused = {k: got[k].copy() for k in ("path_nodes", "out_tokens", "accept_len")}
+    st.path()
+    sep = st.results()
+    for k in fused:
+        assert np.array_equal(fused[k], sep[k]), k

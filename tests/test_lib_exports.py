@@ -90,8 +90,9 @@ def test_host_errors_attention(lib):
 
 def test_host_errors_reject(lib):
     f = lib.spec_tree_reject_sample
-    #       tl mx se am cmx csm T    dl mx se Td   tok par nn ua us B  nmax V    acc term ws   wsb st   s
-    args = [P, P, P, P, None, None, 1.0, P, P, P, 1.0, P, P, P, P, P, 1, 8, 100, P, P, None, 0, None, None]
+    #       tl mx se am cmx csm T    dl mx se Td   tok par nn ua us B  nmax V    acc term pn ot al ws wsb st s
+    args = [P, P, P, P, None, None, 1.0, P, P, P, 1.0, P, P, P, P, P, 1, 8, 100, P, P, None, None, None, None, 0,
+            None, None]
     a = list(args)
     a[6] = -0.5
     assert f(*a) == -1
@@ -110,6 +111,11 @@ def test_host_errors_reject(lib):
     a = list(args)
     a[4] = P  # chunk partials come as a pair
     assert f(*a) == -1
+    a = list(args)
+    a[21] = P  # the path outputs come together
+    assert f(*a) == -1
+    a[22], a[23] = P, P
+    assert f(*a) == -5  # all three given: accepted, then the missing workspace
     assert f(*args) == -5  # T > 0 needs the workspace (per-node results)
     a = list(args)
     a[18] = 100000

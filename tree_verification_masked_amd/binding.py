@@ -47,7 +47,7 @@ _SIGNATURES = {
                                _VP],
     "spec_tree_reject_sample_workspace_size": [_I32, _I32, _I32],
     "spec_tree_reject_sample": [_VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _I32,
-                                _I32, _I32, _VP, _VP, _VP, _SZ, _VP, _VP],
+                                _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_version": [],
 }
@@ -236,7 +236,7 @@ def spec_tree_softmax_pair(tgt_logits, temperature, dft_logits, draft_temperatur
 def spec_tree_reject_sample(tgt_logits, tgt_max, tgt_sumexp, tgt_argmax, temperature, dft_logits, dft_max,
                             dft_sumexp, draft_temperature, tokens, parent, n_nodes, u_accept, u_sample,
                             accepted_child, term_token, workspace=None, status=None, stream=None,
-                            tgt_chunk_max=None, tgt_chunk_sum=None):
+                            tgt_chunk_max=None, tgt_chunk_sum=None, path_nodes=None, out_tokens=None, accept_len=None):
     B, n_max, V = tgt_logits.shape
     _check(tgt_logits, torch.float32, (B, n_max, V), "tgt_logits")
     _check(dft_logits, torch.float32, (B, n_max, V), "dft_logits")
@@ -249,12 +249,15 @@ def spec_tree_reject_sample(tgt_logits, tgt_max, tgt_sumexp, tgt_argmax, tempera
     _check(tgt_chunk_max, torch.float32, None, "tgt_chunk_max")
     _check(tgt_chunk_sum, torch.float64, None, "tgt_chunk_sum")
     _check(status, torch.int32, (1,), "status")
+    _check(path_nodes, torch.int32, (B, n_max), "path_nodes")
+    _check(out_tokens, torch.int32, (B, n_max), "out_tokens")
+    _check(accept_len, torch.int32, (B,), "accept_len")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("spec_tree_reject_sample", _ptr(tgt_logits), _ptr(tgt_max), _ptr(tgt_sumexp), _ptr(tgt_argmax),
           _ptr(tgt_chunk_max), _ptr(tgt_chunk_sum), float(temperature), _ptr(dft_logits), _ptr(dft_max),
           _ptr(dft_sumexp), float(draft_temperature), _ptr(tokens), _ptr(parent), _ptr(n_nodes), _ptr(u_accept),
-          _ptr(u_sample), B, n_max, V, _ptr(accepted_child), _ptr(term_token), _ptr(workspace), ws_bytes,
-          _ptr(status), _stream(stream))
+          _ptr(u_sample), B, n_max, V, _ptr(accepted_child), _ptr(term_token), _ptr(path_nodes), _ptr(out_tokens),
+          _ptr(accept_len), _ptr(workspace), ws_bytes, _ptr(status), _stream(stream))
 
 
 def spec_accept_path(accepted_child, term_token, tokens, n_nodes, path_nodes, out_tokens, accept_len, status=None,

@@ -4,6 +4,7 @@
 // the committed path runs from the root to the first rejection or a leaf and is
 // unique; part G, step 6: the emitted tokens are the accepted ones followed by the
 // bonus token.  One lane per request follows accepted_child (at most 63 steps).
+// The rejection sampler can emit the same path from its own walk.
 #include "common.hpp"
 
 namespace spectree {
@@ -18,46 +19,10 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const int32_t* __restr
   const int b = (int)(blockIdx.x * blockDim.x + threadIdx.x);
   if (b >= batch) return;
   const int64_t base = (int64_t)b * n_max;
-  const int32_t* acc = accepted_child + base;
-  const int32_t* term = term_token + base;
-  int32_t* pn = path_nodes + base;
-  int32_t* ot = out_tokens + base;
-  for (int i = 0; i < n_max; ++i) {
-    pn[i] = -1;
-    ot[i] = -1;
-  }
-  const int n = n_nodes[b];
-  if (n < 1 || n > n_max || acc[0] == SPEC_NODE_BAD_REQUEST) {
-    accept_len[b] = -1;
-    return;
-  }
-  int cur = 0, len = 0;
-  bool ok = true;
-  pn[0] = 0;
-  for (int step = 0; step < n_max; ++step) {
-    const int nxt = acc[cur];
-    if (nxt < 0) break;
-    if (nxt <= cur || nxt >= n || len + 1 >= n_max) {
-      ok = false;
-      break;
-    }
-    cur = nxt;
-    ++len;
-    pn[len] = cur;
-    ot[len - 1] = tokens[base + cur];
-  }
-  if (ok && (acc[cur] != SPEC_NODE_NONE || term[cur] < 0)) ok = false;
-  if (!ok) {
-    for (int i = 0; i < n_max; ++i) {
-      pn[i] = -1;
-      ot[i] = -1;
-    }
-    accept_len[b] = -1;
-    report(status, SPEC_ERR_BAD_INPUT);
-    return;
-  }
-  ot[len] = term[cur];
-  accept_len[b] = len;
+  bool bad;
+  accept_len[b] = accept_walk(accepted_child + base, term_token + base, tokens + base, n_nodes[b], n_max,
+                              path_nodes + base, out_tokens + base, &bad);
+  if (bad) report(status, SPEC_ERR_BAD_INPUT);
 }
 
 }  // namespace spectree

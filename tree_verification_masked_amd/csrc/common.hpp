@@ -192,6 +192,43 @@ __device__ inline uint32_t pub_arrive(uint32_t* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Accepted path of one request from its per-node results, by one thread (tree
+// notes, parts C and G: the path runs from the root to the first node without an
+// accepted child and is unique; the emitted tokens are the accepted ones followed
+// by that node's terminal token).  acc, term, tok: n_max entries of the request
+// (LDS or global).  pn, ot receive n_max entries: -1 padding, then the path.
+// Returns the number of accepted nodes; -1 for a request marked invalid (or with
+// n outside [1, n_max]), and -1 with *bad set when the results are inconsistent.
+__device__ inline int accept_walk(const int32_t* acc, const int32_t* term, const int32_t* tok, int n, int n_max,
+                                  int32_t* pn, int32_t* ot, bool* bad) {
+  *bad = false;
+  for (int i = 0; i < n_max; ++i) pn[i] = ot[i] = -1;
+  if (n < 1 || n > n_max || acc[0] == SPEC_NODE_BAD_REQUEST) return -1;
+  int cur = 0, len = 0;
+  bool ok = true;
+  pn[0] = 0;
+  for (int step = 0; step < n_max; ++step) {
+    const int nxt = acc[cur];
+    if (nxt < 0) break;
+    if (nxt <= cur || nxt >= n || len + 1 >= n_max) {
+      ok = false;
+      break;
+    }
+    cur = nxt;
+    ++len;
+    pn[len] = cur;
+    ot[len - 1] = tok[cur];
+  }
+  if (ok && (acc[cur] != SPEC_NODE_NONE || term[cur] < 0)) ok = false;
+  if (!ok) {
+    for (int i = 0; i < n_max; ++i) pn[i] = ot[i] = -1;
+    *bad = true;
+    return -1;
+  }
+  ot[len] = term[cur];
+  return len;
+}
+
 }  // namespace spectree
 
 // ---- host side ----

@@ -130,7 +130,27 @@ struct RejArgs {
   int32_t batch, n_max, vocab, nch;
   int32_t vec;  // rows start 16-byte aligned (vocab % 4 == 0, aligned bases)
   int32_t *accepted_child, *term_token, *status;
+  int32_t *path_nodes, *out_tokens, *accept_len;  // optional: the accepted path too
 };
+
+// The request's accepted path from the walk's results in LDS (the rules of
+// spec_accept_path), when the caller asked for it.  Called by the whole workgroup.
+__device__ inline void emit_path(const RejArgs& a, int b, const int* s_oacc, const int* s_oterm, const int* s_tok,
+                                 int nb, int* s_pn, int* s_ot, int* s_len) {
+  if (!a.path_nodes) return;
+  if (threadIdx.x == 0) {
+    bool bad;
+    *s_len = accept_walk(s_oacc, s_oterm, s_tok, nb, a.n_max, s_pn, s_ot, &bad);
+    if (bad) report(a.status, SPEC_ERR_BAD_INPUT);
+  }
+  __syncthreads();
+  const int64_t base = (int64_t)b * a.n_max;
+  for (int i = threadIdx.x; i < a.n_max; i += blockDim.x) {
+    a.path_nodes[base + i] = s_pn[i];
+    a.out_tokens[base + i] = s_ot[i];
+  }
+  if (threadIdx.x == 0) a.accept_len[b] = *s_len;
+}
 
 // A thread's 16 tokens of a chunk held in registers.  Chunk layout (R1, R2): token
 // of slot s is c0 + ((s / 4) * 256 + tid) * 4 + s % 4, so each 16-byte load of a
@@ -373,7 +393,9 @@ __device__ inline double block_excl_scan_d(double v, double* s_w, double* total)
 // P: per-request plan
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void plan_kernel(RejArgs a, NodeWs w, int chunked) {
+  __shared__ unsigned long long s_kids[64];
   const int lane = threadIdx.x, b = blockIdx.x;
+  s_kids[lane] = 0;
   const int64_t base = (int64_t)b * a.n_max;
   const bool in = lane < a.n_max;
   const int nb = a.n_nodes[b];
@@ -389,11 +411,10 @@ __global__ __launch_bounds__(64) void plan_kernel(RejArgs a, NodeWs w, int chunk
   const unsigned long long m_link = __ballot(bad_link), m_tok = __ballot(bad_tok);
   const int verdict = (!n_ok || m_link) ? SPEC_ERR_BAD_TREE : (m_tok ? SPEC_ERR_BAD_INPUT : 0);
   const bool tree_ok = verdict == 0;
-  uint64_t kids = 0;
-  for (int n = 0; n < nb && tree_ok; ++n) {  // uniform
-    const unsigned long long m = __ballot(live && lane > 0 && par == n);
-    if (lane == n) kids = m;
-  }
+  // children: every live non-root node sets its bit in its parent's mask
+  if (tree_ok && live && lane > 0) atomicOr(&s_kids[par], 1ull << lane);
+  __syncthreads();
+  const uint64_t kids = tree_ok && live ? s_kids[lane] : 0ull;
   const bool row_ok = !isnan(mt) && !isnan(md);
   const double izt = 1.0 / (double)zt, izd = 1.0 / (double)zd;
   // the tested token of child `lane`, at its parent's row
@@ -428,8 +449,12 @@ __global__ __launch_bounds__(64) void plan_kernel(RejArgs a, NodeWs w, int chunk
   if (chunked) {
     const unsigned long long m = __ballot(active);
     int at = 0;
-    if (lane == 0 && m) at = (int)atomicAdd(w.act_count, (uint32_t)__popcll(m));
-    at = __shfl(at, 0);
+    if (gridDim.x == 1) {  // one request: its nodes are the whole list
+      if (lane == 0) *w.act_count = (uint32_t)__popcll(m);
+    } else {
+      if (lane == 0 && m) at = (int)atomicAdd(w.act_count, (uint32_t)__popcll(m));
+      at = __shfl(at, 0);
+    }
     if (active) w.act_list[at + __popcll(m & ((1ull << lane) - 1ull))] = (int)(base + lane);
   }
 }
@@ -871,7 +896,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
   __shared__ int s_pick, s_flags, s_nlist, s_last;
   __shared__ SibState s_st;
   __shared__ NodeRes s_res[64];
-  __shared__ int s_oacc[64], s_oterm[64];
+  __shared__ int s_oacc[64], s_oterm[64], s_tok[64], s_pn[64], s_ot[64], s_len;
   const int tid = threadIdx.x, lane = tid & 63;
   const int nd = blockIdx.x;
   const int b = nd / a.n_max, n = nd % a.n_max;
@@ -1157,6 +1182,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
     s_res[tid].acc = pub_load(&w.res[base + tid].acc);
     s_res[tid].term = pub_load(&w.res[base + tid].term);
     s_res[tid].err = pub_load(&w.res[base + tid].err);
+    s_tok[tid] = a.path_nodes ? a.tokens[base + tid] : 0;
   }
   if (tid < 64) {
     s_oacc[tid] = SPEC_NODE_NOT_EVALUATED;
@@ -1193,13 +1219,14 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
     a.accepted_child[base + tid] = s_oacc[tid];
     a.term_token[base + tid] = s_oterm[tid];
   }
+  emit_path(a, b, s_oacc, s_oterm, s_tok, nb, s_pn, s_ot, &s_len);
 }
 
 // T == 0: one wavefront per request follows the target argmax.
 __global__ __launch_bounds__(64) void greedy_walk_kernel(RejArgs a) {
-  __shared__ int s_par[64], s_tok[64], s_arg[64], s_oacc[64], s_oterm[64];
+  __shared__ int s_par[64], s_tok[64], s_arg[64], s_oacc[64], s_oterm[64], s_pn[64], s_ot[64];
   __shared__ float s_max[64];
-  __shared__ int s_bad;
+  __shared__ int s_bad, s_len;
   const int tid = threadIdx.x, b = blockIdx.x;
   const int64_t base = (int64_t)b * a.n_max;
   const int nb = a.n_nodes[b];
@@ -1252,6 +1279,7 @@ __global__ __launch_bounds__(64) void greedy_walk_kernel(RejArgs a) {
     a.accepted_child[base + tid] = s_oacc[tid];
     a.term_token[base + tid] = s_oterm[tid];
   }
+  emit_path(a, b, s_oacc, s_oterm, s_tok, nb, s_pn, s_ot, &s_len);
 }
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1299,7 +1327,8 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt
                                        const float* dft_max, const float* dft_sumexp, float draft_temperature,
                                        const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
                                        const float* u_accept, const float* u_sample, int32_t batch, int32_t n_max,
-                                       int32_t vocab, int32_t* accepted_child, int32_t* term_token, void* workspace,
+                                       int32_t vocab, int32_t* accepted_child, int32_t* term_token,
+                                       int32_t* path_nodes, int32_t* out_tokens, int32_t* accept_len, void* workspace,
                                        size_t workspace_bytes, int32_t* status, void* stream) {
   using namespace spectree;
   if (!(temperature >= 0.0f) || isinf(temperature)) return SPEC_ERR_INVALID_ARG;
@@ -1307,6 +1336,8 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt
   if (!tgt_logits || !tgt_max || !tokens || !parent || !n_nodes || !accepted_child || !term_token)
     return SPEC_ERR_INVALID_ARG;
   if (greedy && !tgt_argmax) return SPEC_ERR_INVALID_ARG;
+  if ((path_nodes == nullptr) != (out_tokens == nullptr) || (path_nodes == nullptr) != (accept_len == nullptr))
+    return SPEC_ERR_INVALID_ARG;  // the path outputs come together
   if (!greedy) {
     if (!tgt_sumexp || !dft_logits || !dft_max || !dft_sumexp || !u_accept || !u_sample) return SPEC_ERR_INVALID_ARG;
     if (!(draft_temperature > 0.0f) || isinf(draft_temperature)) return SPEC_ERR_INVALID_ARG;
@@ -1342,6 +1373,9 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt
   a.vec = (vocab % 4 == 0) && (((uintptr_t)tgt_logits & 15) == 0) && (greedy || (((uintptr_t)dft_logits & 15) == 0));
   a.accepted_child = accepted_child;
   a.term_token = term_token;
+  a.path_nodes = path_nodes;
+  a.out_tokens = out_tokens;
+  a.accept_len = accept_len;
   a.status = status;
   hipStream_t st = (hipStream_t)stream;
   if (greedy) {

@@ -95,7 +95,9 @@ class VerifyStep:
             B.spec_tree_softmax(tgt, 0.0, self.tmax, self.tsum, self.targ, self.sm_ws, status=self.status,
                                 stream=stream)
 
-    def reject(self, stream=None, tgt=None, dft=None):
+    def reject(self, stream=None, tgt=None, dft=None, with_path=True):
+        """Rejection sampling; with_path: the same walk also writes the accepted path
+        (path_nodes, out_tokens, accept_len), the result spec_accept_path gives."""
         d = self.d
         greedy = self.T == 0
         B.spec_tree_reject_sample(d["tgt_logits"] if tgt is None else tgt, self.tmax, self.tsum, self.targ, self.T,
@@ -104,7 +106,10 @@ class VerifyStep:
                                   d["tokens"], d["parent"], d["n_nodes"], None if greedy else d["u_accept"],
                                   None if greedy else d["u_sample"], self.accepted_child, self.term_token,
                                   self.rj_ws, self.status, stream, tgt_chunk_max=None if greedy else self.tcmax,
-                                  tgt_chunk_sum=None if greedy else self.tcsum)
+                                  tgt_chunk_sum=None if greedy else self.tcsum,
+                                  path_nodes=self.path_nodes if with_path else None,
+                                  out_tokens=self.out_tokens if with_path else None,
+                                  accept_len=self.accept_len if with_path else None)
 
     def path(self, stream=None):
         d = self.d
@@ -119,8 +124,7 @@ class VerifyStep:
         if self.with_attention:
             self.attention(stream, r.get("q"), r.get("k"), r.get("v"))
         self.softmax(stream, r.get("tgt_logits"), r.get("dft_logits"))
-        self.reject(stream, r.get("tgt_logits"), r.get("dft_logits"))
-        self.path(stream)
+        self.reject(stream, r.get("tgt_logits"), r.get("dft_logits"))  # and the accepted path
 
     def results(self) -> dict:
         torch.cuda.synchronize()
