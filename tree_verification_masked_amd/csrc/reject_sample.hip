@@ -191,6 +191,28 @@ __device__ inline void load_chunk4(const float* row, int c0, int vocab, bool vec
     for (int s2 = 0; s2 < 4; ++s2) x[s2] = t + s2 < vocab ? row[t + s2] : -INFINITY;
   }
 }
+// R2 uses 512-thread workgroups (two per CU, so every item of a call is resident
+// at once): thread t holds tokens c0 + 2048 j + 4t .. + 3 for j = 0, 1.
+constexpr int kXThreads = 512;
+constexpr int kXPer = kChunk / kXThreads;
+static_assert(kXThreads == kHB && kXPer == 8, "R2 layout: one histogram bucket per thread below kHB");
+__device__ inline int xtok(int c0, int s2) { return c0 + 2048 * (s2 >> 2) + 4 * (int)threadIdx.x + (s2 & 3); }
+__device__ inline void load_chunk8(const float* row, int c0, int vocab, bool vec, float* x) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = c0 + 2048 * j + 4 * (int)threadIdx.x;
+    if (vec && t + 4 <= vocab) {
+      const float4 f = *reinterpret_cast<const float4*>(row + t);
+      x[4 * j + 0] = f.x;
+      x[4 * j + 1] = f.y;
+      x[4 * j + 2] = f.z;
+      x[4 * j + 3] = f.w;
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) x[4 * j + s2] = t + s2 < vocab ? row[t + s2] : -INFINITY;
+    }
+  }
+}
 // Contiguous layout (R3 scans): thread owns tokens r0 .. r0 + kPer - 1.
 __device__ inline void load_run(const float* row, int r0, int t1, bool vec, float* x) {
   if (vec && r0 + kPer <= t1) {
@@ -515,16 +537,16 @@ __global__ __launch_bounds__(kCThreads) void chain_hist_kernel(RejArgs a, NodeWs
 // rho > a_l:
 //   P_above(l) = sum_{rho > b_l} p = S[H_l] + (tokens of buckets [G_l, H_l) with rho > b_l),
 // and the tokens of [G_l, H_l) with a_l < rho <= b_l are kept in the node's list.
-__global__ __launch_bounds__(kCThreads) void chain_exact_kernel(RejArgs a, NodeWs w) {
+__global__ __launch_bounds__(kXThreads) void chain_exact_kernel(RejArgs a, NodeWs w) {
   __shared__ BucketRec s_T[kHN + 1];
-  __shared__ long long s_wt[2][kCThreads / 64];
+  __shared__ long long s_wt[2][kXThreads / 64];
   __shared__ double s_a[kMaxKids], s_b[kMaxKids];
   __shared__ int s_G[kMaxKids], s_H[kMaxKids];
   __shared__ unsigned long long s_mask[kHN];  // levels whose edge range holds bucket h
   __shared__ unsigned long long s_EP[kMaxKids], s_EQ[kMaxKids];
   __shared__ QEntry s_q[kQueue];
   __shared__ ListEntry s_list[kWgList];
-  __shared__ long long s_ll[kCThreads / 64];
+  __shared__ long long s_ll[kXThreads / 64];
   __shared__ int s_qn, s_nlist, s_base, s_bad;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
   const int nodes = a.batch * a.n_max;
@@ -539,11 +561,18 @@ __global__ __launch_bounds__(kCThreads) void chain_exact_kernel(RejArgs a, NodeW
     const float mt = a.tgt_max[nd], md = a.dft_max[nd];
     // merged histogram -> suffix sums S[h] = sum_{h' >= h} hist[h'], S[kHN] = 0; it is
     // loaded before the chunk's logits, which are only needed after the intervals
+    // (thread t holds bucket t < kHB; the kHN - kHB top buckets are added to every suffix)
     const long long* hg = w.hist + (int64_t)nd * 2 * kHN;
-    const long long v0 = tid < kHN ? hg[2 * tid] : 0, v1 = tid < kHN ? hg[2 * tid + 1] : 0;
-    float xl[kCPer], xd[kCPer];
-    load_chunk4(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
-    load_chunk4(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
+    const long long v0 = hg[2 * tid], v1 = hg[2 * tid + 1];
+    long long tp[kHN - kHB], tq[kHN - kHB];
+#pragma unroll
+    for (int j = 0; j < kHN - kHB; ++j) {
+      tp[j] = hg[2 * (kHB + j)];
+      tq[j] = hg[2 * (kHB + j) + 1];
+    }
+    float xl[kXPer], xd[kXPer];
+    load_chunk8(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
+    load_chunk8(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
     for (int l = tid; l < k; l += blockDim.x) s_EP[l] = s_EQ[l] = 0;
     for (int h = tid; h < kHN; h += blockDim.x) s_mask[h] = 0;
     if (tid == 0) {
@@ -565,9 +594,21 @@ __global__ __launch_bounds__(kCThreads) void chain_exact_kernel(RejArgs a, NodeW
         i0 += s_wt[0][x];
         i1 += s_wt[1][x];
       }
-      if (tid <= kHN) {
-        s_T[tid].SP = i0;
-        s_T[tid].SQ = i1;
+      long long top0 = 0, top1 = 0;  // suffix sums of the top buckets
+#pragma unroll
+      for (int j = kHN - kHB - 1; j >= 0; --j) {
+        top0 += tp[j];
+        top1 += tq[j];
+        if (tid == j) {
+          s_T[kHB + j].SP = top0;
+          s_T[kHB + j].SQ = top1;
+        }
+      }
+      s_T[tid].SP = i0 + top0;
+      s_T[tid].SQ = i1 + top1;
+      if (tid == 0) {
+        s_T[kHN].SP = 0;
+        s_T[kHN].SQ = 0;
       }
     }
     __syncthreads();
@@ -624,11 +665,11 @@ __global__ __launch_bounds__(kCThreads) void chain_exact_kernel(RejArgs a, NodeW
     __syncthreads();
     const int htop = s_H[k - 1];
     long long cp = 0, cq = 0;  // this chunk's tokens with rho > b_{k-1} (the terminal draw)
-    int hh[kCPer];
-    float pq[kCPer], qq2[kCPer];
+    int hh[kXPer];
+    float pq[kXPer], qq2[kXPer];
     unsigned edge = 0;
 #pragma unroll
-    for (int s2 = 0; s2 < kCPer; ++s2) {
+    for (int s2 = 0; s2 < kXPer; ++s2) {
       const float ep = exp2_arg(xl[s2], mt, a.est), eq = exp2_arg(xd[s2], md, a.esd);
       const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
       const int h = est_bucket(ep, eq, pp, qq, inf.K);
@@ -640,7 +681,7 @@ __global__ __launch_bounds__(kCThreads) void chain_exact_kernel(RejArgs a, NodeW
       qq2[s2] = qq;
     }
 #pragma unroll
-    for (int s2 = 0; s2 < kCPer; ++s2) {
+    for (int s2 = 0; s2 < kXPer; ++s2) {
       const int h = hh[s2];
       if (h >= 0 && h < htop && s_mask[h]) edge |= 1u << s2;
     }
@@ -650,11 +691,10 @@ __global__ __launch_bounds__(kCThreads) void chain_exact_kernel(RejArgs a, NodeW
     int qbase = 0;
     if (lane == 63 && pre) qbase = atomicAdd(&s_qn, pre);
     qbase = lane63_i(qbase) + pre - ne;
-    const int c0 = chunk * kChunk + 4 * tid;
 #pragma unroll
-    for (int s2 = 0; s2 < kCPer; ++s2) {
+    for (int s2 = 0; s2 < kXPer; ++s2) {
       if (edge & (1u << s2)) {
-        if (qbase < kQueue) s_q[qbase] = QEntry{c0 + s2, hh[s2], pq[s2], qq2[s2]};
+        if (qbase < kQueue) s_q[qbase] = QEntry{xtok(chunk * kChunk, s2), hh[s2], pq[s2], qq2[s2]};
         ++qbase;
       }
     }
@@ -1396,7 +1436,7 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt
     const int64_t grid = std::min<int64_t>(upper, std::max<int64_t>(256, upper / 4));
     hipLaunchKernelGGL(chain_hist_kernel, dim3((unsigned)grid), dim3(kCThreads), 0, st, a, w);
     SPEC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(chain_exact_kernel, dim3((unsigned)grid), dim3(kCThreads), 0, st, a, w);
+    hipLaunchKernelGGL(chain_exact_kernel, dim3((unsigned)grid), dim3(kXThreads), 0, st, a, w);
     SPEC_LAUNCH_CHECK();
   }
   hipLaunchKernelGGL(node_kernel, dim3((unsigned)nodes), dim3(kRjThreads), 0, st, a, w, chunked ? 1 : 0);
