@@ -420,6 +420,9 @@ def _custom_attention_case(rng, B_, n_max, hq, hkv, d, ctxs, n_nodes, bf16, page
     ("paged ragged bf16", 3, 12, 16, 4, 128, [1, 47, 1000], [12, 5, 9], True, True),
     ("paged fp32 d64", 2, 5, 4, 4, 64, [31, 100], [5, 4], False, True),
     ("empty prompt", 2, 10, 8, 8, 64, [0, 0], [10, 1], True, False),
+    # one KV head, long context: more key splits than a wavefront has lanes
+    ("many splits fp32 shuffle", 1, 4, 1, 1, 64, [12800], [4], False, False),
+    ("many splits bf16 mfma", 1, 4, 4, 1, 128, [12000], [3], True, False),
 ])
 def test_attention_edge_cases(name, B_, n_max, hq, hkv, d, ctxs, nn, bf16, paged):
     say("attention edge", name)

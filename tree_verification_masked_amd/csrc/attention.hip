@@ -11,7 +11,8 @@
 // 64-key tiles; a workgroup owns (request, KV head, query block, split) and keeps an
 // online softmax per query row.  The rows of one KV head are its n_max * hq/hkv
 // (node, query head) pairs, so K/V tiles are loaded once per workgroup and reused by
-// every row (GQA).  Partials (max, sum, unnormalised output) go to the workspace and
+// every row (GQA).  Partials (max, sum, output divided by the sum, stored in the
+// element type of the inputs) go to the workspace and
 // a combine kernel merges the splits with a log-sum-exp rescale.
 //
 //  * MFMA path (bf16, >= 16 rows per KV head): four waves of 32 rows each.  Scores
@@ -51,9 +52,10 @@ struct AttnArgs {
   int32_t batch, n_max, hq, hkv, head_dim, max_kv_len;
   float scale_log2;  // scale * log2(e): scores live in the log2 domain
   int32_t S, split_len, qblocks;
-  float* opart;  // [S, B, n_max, hq, D]
-  float* mpart;  // [S, B, n_max, hq]
-  float* lpart;  // [S, B, n_max, hq]
+  float* mpart;    // [S, B, n_max, hq]     split max (log2 domain)
+  float* lpart;    // [S, B, n_max, hq]     split sum of exponentials
+  void* opart;     // [S, B, n_max, hq, D]  split output divided by its sum (0 if the sum is 0),
+                   // in the element type of Q/K/V (bf16 or fp32)
   int32_t* status;
 };
 
@@ -449,22 +451,45 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   for (; it < n_plain; ++it) tile(it, std::false_type{});
   for (; it < n_tiles; ++it) tile(it, std::true_type{});
   if (bad_page) report(a.status, SPEC_ERR_BAD_INPUT);
-  // ---- write this split's partials for the lane's row ----
-  if (r < G && node < a.n_max) {
-    const int64_t prow = (((int64_t)s * a.batch + b) * a.n_max + node) * a.hq + h;
-    if (lane < 32) {
-      a.mpart[prow] = m_run;
-      a.lpart[prow] = l_run;
-    }
-    float* orow = a.opart + prow * D;
+  // ---- write this split's partials: the wave's 32 rows go through LDS (the tiles
+  // are consumed) so that the normalised outputs leave as whole rows ----
+  const bool row_out = r < G && node < a.n_max;
+  const int64_t prow = (((int64_t)s * a.batch + b) * a.n_max + node) * a.hq + h;
+  if (row_out && lane < 32) {
+    a.mpart[prow] = m_run;
+    a.lpart[prow] = l_run;
+  }
+  lds_barrier();  // every wave is done with the K/V stages
+  constexpr int OROW = D * 2 + 16;  // bytes per staged row (padded)
+  char* so = &sKV[0][0][0] + wid * 32 * OROW;
+  {
+    const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int d = db * 32 + 8 * e4 + 4 * (lane >> 5);
-        *reinterpret_cast<float4*>(orow + d) =
-            make_float4(acc_o[db][4 * e4 + 0], acc_o[db][4 * e4 + 1], acc_o[db][4 * e4 + 2], acc_o[db][4 * e4 + 3]);
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(acc_o[db][4 * e4 + i] * inv_l);
+        *reinterpret_cast<bf16x4*>(so + (lane & 31) * OROW + d * 2) = o4;
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  // 16-byte pieces: lane covers piece (lane % CPR) of rows lane / CPR + rpi * j
+  constexpr int CPR = D * 2 / 16;  // pieces per row
+  constexpr int RPI = 64 / CPR;    // rows per wave instruction
+#pragma unroll
+  for (int j = 0; j < 32 / RPI; ++j) {
+    const int rl = j * RPI + lane / CPR;  // row within the wave
+    const int rg = qb * kMfmaRowsPerWg + wid * 32 + rl;
+    const int nd2 = rg / hpg;
+    if (rg < G && nd2 < a.n_max) {
+      const int64_t prow2 = (((int64_t)s * a.batch + b) * a.n_max + nd2) * a.hq + g * hpg + rg % hpg;
+      const int4 v = *reinterpret_cast<const int4*>(so + rl * OROW + (lane % CPR) * 16);
+      *reinterpret_cast<int4*>((char*)a.opart + prow2 * D * 2 + (lane % CPR) * 16) = v;
+    }
   }
 }
 
@@ -573,70 +598,107 @@ __global__ __launch_bounds__(256) void attn_shfl_kernel(AttnArgs a) {
       a.mpart[prow] = m_run[j];
       a.lpart[prow] = l_run[j];
     }
+    const float inv_l = l_run[j] > 0.0f ? 1.0f / l_run[j] : 0.0f;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) a.opart[prow * D + lane + 64 * v] = o[j][v];
+    for (int v = 0; v < NV; ++v) ((T*)a.opart)[prow * D + lane + 64 * v] = (T)(o[j][v] * inv_l);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Split combine: one wave per output row (b, node, head)
 // ---------------------------------------------------------------------------
+// NV consecutive elements as one load.
+template <typename T, int NV>
+__device__ inline void load_elems(const T* p, float (&x)[NV]) {
+  if constexpr (sizeof(T) == 2 && NV == 2) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    x[0] = __uint_as_float(u << 16);
+    x[1] = __uint_as_float(u & 0xffff0000u);
+  } else if constexpr (sizeof(T) == 4 && NV == 2) {
+    const float2 f = *reinterpret_cast<const float2*>(p);
+    x[0] = f.x;
+    x[1] = f.y;
+  } else {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) x[v] = (float)p[v];
+  }
+}
+
 template <int D, typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* __restrict__ out) {
   constexpr int NV = D / 64;
+  constexpr int kBatch = 16;  // splits whose partial outputs are loaded at once
   const int lane = threadIdx.x & 63;
   const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t rows = (int64_t)a.batch * a.n_max * a.hq;
   if (rowid >= rows) return;
-  const int h = (int)(rowid % a.hq);
   const int node = (int)((rowid / a.hq) % a.n_max);
   const int b = (int)(rowid / ((int64_t)a.hq * a.n_max));
+  const int64_t stride = rows;
+  // Every load is issued before any result is used: the request's lengths, the
+  // split maxima and sums (lane s holds split s) and the first kBatch partial
+  // outputs (every row of every split is written by the attention launch, so these
+  // addresses are valid whether or not the row turns out live).
   const int len = request_len(a, b);
   const uint64_t anc_row = a.anc[(int64_t)b * a.n_max + node];
-  const bool live = len >= 0 && node < a.n_nodes[b] && ((anc_row >> node) & 1ull);
-  if (len < 0 && node == 0 && h == 0 && lane == 0) report(a.status, SPEC_ERR_BAD_INPUT);
+  const int nb = a.n_nodes[b];
+  const int sl = min(lane, a.S - 1);
+  const float m_l = a.mpart[sl * stride + rowid], l_l = a.lpart[sl * stride + rowid];
+  float vals[kBatch][NV];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    load_elems<T, NV>((const T*)a.opart + (min(j, a.S - 1) * stride + rowid) * D + NV * lane, vals[j]);
+  const bool live = len >= 0 && node < nb && ((anc_row >> node) & 1ull);
+  if (len < 0 && node == 0 && rowid % a.hq == 0 && lane == 0) report(a.status, SPEC_ERR_BAD_INPUT);
   float res[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) res[v] = 0.0f;
-  if (live) {  // wave-uniform
-    const int64_t stride = rows;
-    // split maxima and sums: lane s holds split s (and s + 64, ...)
-    float m = -INFINITY;
-    for (int s = lane; s < a.S; s += 64) m = fmaxf(m, a.mpart[s * stride + rowid]);
-    m = wave_max_f(m);
-    float L = 0.0f;
-    for (int s = lane; s < a.S; s += 64) {
-      const float ms = a.mpart[s * stride + rowid];
-      if (ms > -INFINITY) L += a.lpart[s * stride + rowid] * __builtin_amdgcn_exp2f(ms - m);
-    }
-    L = wave_sum_f(L);
-    if (m > -INFINITY && L > 0.0f) {
-      float acc[NV];
+  // split weights w_s = l_s 2^(m_s - m) (an empty split has m_s = -inf, l_s = 0);
+  // lane s keeps w_s for s < 64, later splits (very long contexts) are reloaded
+  float mx = lane < a.S ? m_l : -INFINITY;
+  for (int s2 = lane + 64; s2 < a.S; s2 += 64) mx = fmaxf(mx, a.mpart[s2 * stride + rowid]);
+  const float m = wave_max_f(mx);
+  auto weight = [&](float ms, float ls) { return m > -INFINITY ? ls * __builtin_amdgcn_exp2f(ms - m) : 0.0f; };
+  const float w_l = lane < a.S ? weight(m_l, l_l) : 0.0f;
+  float lsum = w_l;
+  for (int s2 = lane + 64; s2 < a.S; s2 += 64) lsum += weight(a.mpart[s2 * stride + rowid], a.lpart[s2 * stride + rowid]);
+  const float L = wave_sum_f(lsum);
+  auto w_of = [&](int s2) -> float {  // uniform s2
+    if (s2 < 64) return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w_l), s2));
+    return weight(a.mpart[s2 * stride + rowid], a.lpart[s2 * stride + rowid]);
+  };
+  if (live && L > 0.0f) {  // wave-uniform
+    float acc[NV];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
-      for (int s0 = 0; s0 < a.S; s0 += 8) {  // eight splits' rows in flight at once
-        float wts[8], vals[8][NV];
+    for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int s = s0 + j;
-          const bool in = s < a.S;
-          const float ms = in ? a.mpart[s * stride + rowid] : -INFINITY;
-          wts[j] = ms > -INFINITY ? __builtin_amdgcn_exp2f(ms - m) : 0.0f;
+    for (int j = 0; j < kBatch; ++j) {
+      if (j < a.S) {
+        const float w = w_of(j);
 #pragma unroll
-          for (int v = 0; v < NV; ++v) vals[j][v] = in ? a.opart[(s * stride + rowid) * D + lane + 64 * v] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int v = 0; v < NV; ++v) acc[v] = fmaf(vals[j][v], wts[j], acc[v]);
+        for (int v = 0; v < NV; ++v) acc[v] = fmaf(vals[j][v], w, acc[v]);
       }
-      const float inv = 1.0f / L;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) res[v] = acc[v] * inv;
     }
+    for (int s0 = kBatch; s0 < a.S; s0 += kBatch) {  // more splits than one batch
+      float more[kBatch][NV];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        load_elems<T, NV>((const T*)a.opart + (min(s0 + j, a.S - 1) * stride + rowid) * D + NV * lane, more[j]);
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (s0 + j < a.S) {
+          const float w = w_of(s0 + j);
+#pragma unroll
+          for (int v = 0; v < NV; ++v) acc[v] = fmaf(more[j][v], w, acc[v]);
+        }
+      }
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) res[v] = acc[v] * inv;
   }
 #pragma unroll
-  for (int v = 0; v < NV; ++v) out[rowid * D + lane + 64 * v] = (T)res[v];
+  for (int v = 0; v < NV; ++v) out[rowid * D + NV * lane + v] = (T)res[v];
 }
 
 struct AttnPlan {
@@ -665,7 +727,7 @@ inline AttnPlan make_plan(int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
 
 inline size_t attn_ws_bytes(const AttnPlan& p, int32_t batch, int32_t n_max, int32_t hq, int32_t D) {
   const size_t rows = (size_t)p.S * batch * n_max * hq;
-  return rows * D * sizeof(float) + 2 * rows * sizeof(float);
+  return 2 * rows * sizeof(float) + rows * D * sizeof(float);  // fp32 partials for fp32 inputs
 }
 
 }  // namespace spectree
@@ -722,9 +784,9 @@ extern "C" int spec_tree_attention(const void* q, const void* k, const void* v, 
   a.split_len = p.split_len;
   a.qblocks = p.qblocks;
   const size_t rows = (size_t)p.S * batch * n_max * hq;
-  a.opart = (float*)workspace;
-  a.mpart = a.opart + rows * head_dim;
+  a.mpart = (float*)workspace;
   a.lpart = a.mpart + rows;
+  a.opart = (void*)(a.lpart + rows);
   a.status = status;
   hipStream_t st = (hipStream_t)stream;
   const dim3 g1((unsigned)grid), blk(256);
