@@ -4,7 +4,8 @@
 // the tree is flattened breadth-first and every node may attend only to itself and
 // its ancestors.  One wavefront handles one tree: lane i owns node i, validity is a
 // wave vote, the ancestor sets come from pointer jumping over the parent links
-// (six doubling steps cover depth 63), and each child mask is one ballot.
+// (six doubling steps cover depth 63), and every node sets its bit in its parent's
+// child mask with one LDS atomic.
 #include "common.hpp"
 
 namespace spectree {
@@ -14,9 +15,11 @@ __global__ __launch_bounds__(256) void mask_build_kernel(const int32_t* __restri
                                                          int32_t n_max, uint64_t* __restrict__ anc_mask,
                                                          uint64_t* __restrict__ child_mask, int32_t* __restrict__ depth,
                                                          int32_t* status) {
-  const int lane = threadIdx.x & 63;
+  __shared__ unsigned long long s_kids[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int b = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
-  if (b >= batch) return;  // whole wavefront leaves together
+  if (b >= batch) return;  // whole wavefront leaves together (no workgroup barrier below)
+  s_kids[wv][lane] = 0;
   const int64_t base = (int64_t)b * n_max;
   const int n = n_nodes[b];
   const bool n_ok = n >= 1 && n <= n_max;
@@ -47,11 +50,10 @@ __global__ __launch_bounds__(256) void mask_build_kernel(const int32_t* __restri
       jp = jp_src;
     }
   }
-  uint64_t kids = 0;
-  for (int q = 0; q < n; ++q) {
-    const uint64_t m = __ballot(node && p == q);
-    if (lane == q) kids = m;
-  }
+  // the wavefront's own LDS row: in-order LDS operations of one wavefront need no barrier
+  if (node && lane > 0) atomicOr(&s_kids[wv][p], 1ull << lane);
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t kids = s_kids[wv][lane];
   if (in_row) {
     anc_mask[base + lane] = node ? a : 0ull;
     child_mask[base + lane] = node ? kids : 0ull;
