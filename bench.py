@@ -12,8 +12,9 @@ Timing: W warm-up steps, then K steps bracketed by synchronize + HIP events.  Ea
 step reads one of R input replicas in turn (distinct device buffers, 8 x ~80 MB)
 so the working set is far larger than the 256 MB last-level cache and the numbers
 are HBM numbers.  A second timed pass records events around every stage to report
-per-kernel durations; the dominant kernel (the vocabulary softmax) gives the
-roofline entry.  The CPU oracle is timed on the host on full steps of the same
+per-call durations; the call holding the longest kernel (tree attention) gives the
+roofline entry, the logit softmax a second one.  Measured HBM traffic per call comes
+from the committed counter summary under profiles/ while the kernel sources match.  The CPU oracle is timed on the host on full steps of the same
 workload.  Prints one JSON line.
 """
 from __future__ import annotations
@@ -31,6 +32,41 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tree-verify steps/sec + attn/sampling HBM GB/s (8B-shape, 60-node tree, 4k ctx)"
 HBM_PEAK_GBS = 8000.0
+COPY_ELEMS = 1 << 27  # fp32: 512 MiB read and 512 MiB written per copy
+# HBM bytes per call measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by the
+# same counters on a plain copy); valid only while the sources listed there are unchanged
+COUNTERS_MD = os.path.join(ROOT, "profiles", "attention_softmax_llama8b_60node_ctx4096_hbm_counters.md")
+
+
+def measured_traffic():
+    """{call: bytes} from the counter summary, for calls whose kernel sources still
+    hash to the values recorded with the counters."""
+    import hashlib
+    import re
+
+    if not os.path.exists(COUNTERS_MD):
+        return {}
+    text = open(COUNTERS_MD).read()
+    shas = dict(re.findall(r"^- sha256 (\S+): ([0-9a-f]{64})", text, flags=re.M))
+    calls = re.findall(r"^- traffic_bytes (\S+): (\d+) \(sources: ([^)]*)\)", text, flags=re.M)
+    out = {}
+    for call, nbytes, srcs in calls:
+        ok = True
+        for src in srcs.split(","):
+            src = src.strip()
+            path = os.path.join(ROOT, src)
+            if src not in shas or not os.path.exists(path) or \
+                    hashlib.sha256(open(path, "rb").read()).hexdigest() != shas[src]:
+                ok = False
+        out[call] = int(nbytes) if ok else None
+    return out
+
+
+def roofline_entry(kernel, nbytes, us, traffic):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "bytes_per_launch": int(nbytes),
+            "avg_launch_us": round(float(us), 3)}
 
 
 def parse():
@@ -44,6 +80,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run four plain 512 MiB device-to-device copies (the reference kernel whose "
+                         "FETCH_SIZE / WRITE_SIZE counters scale the traffic of the step's kernels)")
     return ap.parse_args()
 
 
@@ -59,8 +98,23 @@ def algorithmic_bytes(inp):
     return attn, logits, sampling
 
 
+def copy_calibration():
+    import torch
+
+    a = torch.ones(COPY_ELEMS, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4,
+                                           "launches": 4}}))
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -120,6 +174,7 @@ def main():
     names = ["mask_build", "attention", "softmax_pair", "-", "reject_sample", "-"]
 
     attn_b, logit_b, samp_b = algorithmic_bytes(inp)
+    traffic = measured_traffic()
     step_b = attn_b + samp_b
     sm_us = st_mean[2]
     samp_us = st_mean[2] + st_mean[4] + st_mean[5]
@@ -147,16 +202,13 @@ def main():
         "attn_gbs": round(attn_b / (st_mean[1] * 1e-6) / 1e9, 1),
         "sampling_gbs": round(samp_b / (samp_us * 1e-6) / 1e9, 1),
         "stage_us": {n: round(float(v), 2) for n, v in zip(names, st_mean) if n != "-"},
-        "roofline": {
-            "kernel": "softmax_stats_kernel (one launch = target and draft logit rows)",
-            "bound": "hbm",
-            "achieved": round(samp_b / (sm_us * 1e-6) / 1e9, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(samp_b / (sm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "bytes_per_launch": samp_b,
-            "avg_launch_us": round(float(sm_us), 3),
+        # the longest kernel of the step is the attention kernel; events bracket its call
+        # (the attention kernel and the split combine), so the entry covers both
+        "roofline": roofline_entry("spec_tree_attention call: attn_mfma_kernel<128> + attn_combine_kernel",
+                                   attn_b, st_mean[1], traffic.get("spec_tree_attention")),
+        "stage_roofline": {
+            "softmax_pair": roofline_entry("spec_tree_softmax_pair call: softmax_stats_kernel + softmax_merge_kernel",
+                                           samp_b, sm_us, traffic.get("spec_tree_softmax_pair")),
         },
     }
 
