@@ -106,11 +106,18 @@ int spec_tree_mask_build(const int32_t* parent, const int32_t* n_nodes, int32_t 
  * dtype SPEC_BF16 (fp32 accumulate) or SPEC_F32.  head_dim 64 or 128.
  * Query rows per KV head G = n_max * hq / hkv: bf16 with G >= 16 runs on MFMA
  * tiles, otherwise on a shuffle dot-product kernel.
- * Device errors: ctx_len[b] + n_nodes[b] beyond the cache, a page id outside
- * [0, n_pages), a bad tree -> SPEC_ERR_BAD_INPUT / SPEC_ERR_BAD_TREE; the
- * affected request's rows are written as zeros.
- * Host errors: null pointers, hq % hkv != 0, head_dim not 64/128, n_max outside
- * [1, 64], page_size < 1 with a block table, workspace too small.
+ * max_kv_len bounds ctx_len[b] + n_nodes[b] over the batch; it sizes the key
+ * splits (and the workspace), so a tight bound gives the best split.
+ * Device errors: ctx_len[b] + n_nodes[b] beyond max_kv_len or the cache ->
+ * SPEC_ERR_BAD_INPUT and the request's rows are written as zeros; a page id
+ * outside [0, n_pages) -> SPEC_ERR_BAD_INPUT and the request's outputs are
+ * unspecified (page 0 is read in its place, so no memory outside the pool is
+ * touched).  A node whose ancestor mask lacks its own bit (the all-zero masks
+ * spec_tree_mask_build writes for a bad tree) gets a zero row.
+ * Host errors: null pointers, hq % hkv != 0, n_max outside [1, 64], page_size < 1
+ * with a block table, scale not finite and positive, workspace too small;
+ * SPEC_ERR_UNSUPPORTED for head_dim not 64/128, another dtype, or a block table
+ * with pages of fewer than 16 tokens on the MFMA path (bf16, G >= 16).
  */
 size_t spec_tree_attention_workspace_size(int32_t batch, int32_t n_max, int32_t hq, int32_t hkv, int32_t head_dim,
                                           int32_t max_kv_len);
