@@ -1021,34 +1021,54 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
           for (int i = tid; i < nlist; i += blockDim.x) s_list[i] = L[i];
         if (tid == 0) s_st = SibState{inf.kids, 0.0, 1.0, SPEC_NODE_NONE, 0, 0, 0};
         __syncthreads();
-        // A short list (the usual case): one lane follows the exact path alone, with
-        // no wave reductions between the sequential levels.  The sums are exact
-        // integers, so the result is the same as the wavefront version below.
-        if (fast && nlist <= kShortList && tid == 0) {
-          uint64_t m = inf.kids;
+        // A short list (the usual case): wavefront 0 follows the exact path with the
+        // level data in registers, lane l holding level l (its child's test inputs,
+        // interval and exact sums above it) and lane i list entry i; each level
+        // fetches what it needs with readlane, and the listed tokens inside the
+        // interval come from one ballot.  The sums are exact integers, so the
+        // result equals the wavefront version below.
+        if (fast && nlist <= kShortList && tid < 64) {
+          const int kk = min(k, 64);
+          uint64_t rest_l = inf.kids;  // children left after the child of level `lane`
+          for (int i = 0; i < lane && rest_l; ++i) rest_l &= rest_l - 1;
+          const int ci_l = rest_l ? __ffsll((unsigned long long)rest_l) - 1 : 0;
+          rest_l = rest_l ? rest_l & (rest_l - 1) : 0;
+          const bool lv_in = lane < kk;
+          const float u_l = lv_in ? s_ua[ci_l] : 0.0f;
+          const double px_l = lv_in ? s_px[ci_l] : 0.0, qx_l = lv_in ? s_qx[ci_l] : 0.0;
+          const double ia_l = lv_in ? s_ia[lane] : 0.0, ib_l = lv_in ? s_ib[lane] : 0.0;
+          const long long lp_l = lv_in ? s_lv[2 * lane] : 0, lq_l = lv_in ? s_lv[2 * lane + 1] : 0;
+          const bool e_in = lane < nlist;
+          const double er_l = e_in ? s_list[lane].rho : -1.0;
+          const long long ep_l = e_in ? s_list[lane].fp : 0, eq_l = e_in ? s_list[lane].fq : 0;
+          auto rl_i = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };
+          auto rl_ll = [&](long long v, int l) {
+            return (long long)(((unsigned long long)(uint32_t)rl_i((int)(v >> 32), l) << 32) |
+                               (uint32_t)rl_i((int)(uint32_t)v, l));
+          };
+          auto rl_d = [&](double v, int l) { return __longlong_as_double(rl_ll(__double_as_longlong(v), l)); };
           double c = 0.0, W = 1.0;
           int acc0 = SPEC_NODE_NONE, lvl = 0, zl = 0, pend = 0;
-          while (m) {
-            const int ci = __ffsll((unsigned long long)m) - 1;
-            m &= m - 1;
-            if ((double)s_ua[ci] < accept_ratio(s_px[ci], s_qx[ci], c, W)) {
-              acc0 = ci;
+          uint64_t m = 0;
+          for (int l = 0; l < kk; ++l) {
+            m = (uint64_t)rl_ll((long long)rest_l, l);
+            const float u = __int_as_float(rl_i(__float_as_int(u_l), l));
+            if ((double)u < accept_ratio(rl_d(px_l, l), rl_d(qx_l, l), c, W)) {
+              acc0 = rl_i(ci_l, l);
               break;
             }
-            ++lvl;
+            ++lvl;  // cn = c + W is the threshold after this rejection
             const double cn = c + W;
-            const double ia = s_ia[lvl - 1], ib = s_ib[lvl - 1];
+            const double ia = rl_d(ia_l, l), ib = rl_d(ib_l, l);
             if (!(cn >= ia && cn <= ib)) {
               pend = 1;
               break;
             }
-            long long lp = s_lv[2 * (lvl - 1)], lq = s_lv[2 * (lvl - 1) + 1];
-            for (int i = 0; i < nlist; ++i) {
-              const double rho = s_list[i].rho;
-              if (rho > cn && rho <= ib) {
-                lp += s_list[i].fp;
-                lq += s_list[i].fq;
-              }
+            long long lp = rl_ll(lp_l, l), lq = rl_ll(lq_l, l);
+            for (uint64_t bits = __ballot(e_in && er_l > cn && er_l <= ib); bits; bits &= bits - 1) {
+              const int j = __ffsll((unsigned long long)bits) - 1;
+              lp += rl_ll(ep_l, j);
+              lq += rl_ll(eq_l, j);
             }
             const double Wn = ((double)lp * rv.izt - cn * (double)lq * rv.izd) * kFxInv;
             if (Wn > 0.0) {
@@ -1059,7 +1079,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
               zl = 1;  // the residual keeps its previous threshold
             }
           }
-          s_st = SibState{m, c, W, acc0, lvl, zl, pend};
+          if (lane == 0) s_st = SibState{m, c, W, acc0, lvl, zl, pend};
         }
         // otherwise wavefront 0 follows it, the list spread over its lanes
         if (fast && nlist > kShortList && tid < 64) {
