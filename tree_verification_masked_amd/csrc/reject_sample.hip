@@ -375,6 +375,38 @@ __device__ double w_bound(double c, const BucketRec* T, double izt, double izd, 
   return full + extra;
 }
 
+// The same bounds as w_bound, evaluated by a whole wavefront for a uniform c: lane j
+// holds entry base + j of a 64-entry window around the guess, so the two bucket
+// boundaries come from ballots and the sums from readlane; the terms are combined
+// in the same order as in w_bound, so the result is identical.
+__device__ double w_bound_wave(double c, const BucketRec* T, double izt, double izd, bool upper) {
+  const int lane = threadIdx.x & 63;
+  const int base = min(max(bucket_guess(c) - 16, 0), kHN + 1 - 64);
+  const BucketRec r = T[base + lane];
+  const uint64_t ma = __ballot(r.lb > c), mm = __ballot(r.ub > c);
+  auto rl_ll = [](long long v, int l) {
+    return (long long)(((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l));
+  };
+  auto rl_d = [&](double v, int l) { return __longlong_as_double(rl_ll(__double_as_longlong(v), l)); };
+  if (!(ma && mm && (base == 0 || !(mm & 1ull)))) return w_bound(c, T, izt, izd, upper);  // rare
+  const int ia = __ffsll((unsigned long long)ma) - 1, im = __ffsll((unsigned long long)mm) - 1;
+  const long long SPa = rl_ll(r.SP, ia), SQa = rl_ll(r.SQ, ia);
+  const double full = ((double)SPa * izt - c * (double)SQa * izd) * kFxInv;
+  if (!upper) {
+    const long long SPm = rl_ll(r.SP, im), SQm = rl_ll(r.SQ, im);
+    return full + fmax(0.0, ((double)(SPm - SPa) * izt - c * (double)(SQm - SQa) * izd) * kFxInv);
+  }
+  double extra = 0.0;
+  for (int h = im; h < ia; ++h) {
+    const double P = (double)(rl_ll(r.SP, h) - rl_ll(r.SP, h + 1)) * izt * kFxInv;
+    const double Q = (double)(rl_ll(r.SQ, h) - rl_ll(r.SQ, h + 1)) * izd * kFxInv;
+    const double ub = rl_d(r.ub, h);
+    extra += Q > 0.0 ? (isinf(ub) ? INFINITY : fmax(0.0, (ub - c) * Q)) : P;
+  }
+  return full + extra;
+}
+
 __device__ inline long long block_sum_ll(long long v, long long* s_ll) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
   v = wave_sum_ll(v);
@@ -612,25 +644,28 @@ __global__ __launch_bounds__(kXThreads) void chain_exact_kernel(RejArgs a, NodeW
       }
     }
     __syncthreads();
-    // interval chains: lower ends on wave 0, upper ends on wave 1
-    if (tid == 0) {
+    // interval chains: lower ends on wavefront 0, upper ends on wavefront 1, each
+    // level's bound evaluated by the whole wavefront
+    if (wv == 0) {
       double c = 1.0;
-      s_a[0] = 1.0;
+      if (lane == 0) s_a[0] = 1.0;
       for (int l = 1; l < k; ++l) {
-        const double na = c + w_bound(c, s_T, inf.izt, inf.izd, false);
+        const double na = c + w_bound_wave(c, s_T, inf.izt, inf.izd, false);
         c = na - 1e-10 * na;
-        s_a[l] = c;
+        if (lane == 0) s_a[l] = c;
       }
-    } else if (tid == 64) {
+    } else if (wv == 1) {
       double c = 1.0;
-      s_b[0] = 1.0;
+      if (lane == 0) s_b[0] = 1.0;
       for (int l = 1; l < k; ++l) {
-        const double nb = c + w_bound(c, s_T, inf.izt, inf.izd, true);
+        const double nb = c + w_bound_wave(c, s_T, inf.izt, inf.izd, true);
         c = nb + 1e-10 * nb;
-        s_b[l] = c;
+        if (lane == 0) s_b[l] = c;
         if (!(c < 15.5)) {  // beyond the histogram: direct path
-          s_bad = 1;
-          for (int m = l + 1; m < k; ++m) s_b[m] = c;
+          if (lane == 0) {
+            s_bad = 1;
+            for (int m = l + 1; m < k; ++m) s_b[m] = c;
+          }
           break;
         }
       }
