@@ -181,10 +181,19 @@ __global__ __launch_bounds__(256) void softmax_merge_kernel(SmSet A, SmSet B, in
   const bool second = row >= A.rows;
   const SmSet& S = second ? B : A;
   if (second) row -= A.rows;
+  // the first 64 chunks' partials are loaded in one round (lane c holds chunk c)
+  const int c0 = min(lane, nch - 1);
+  const float mc0 = S.cmax[row * nch + c0];
+  const int ac0 = S.carg[row * nch + c0], bc0 = S.cbad[row * nch + c0];
+  const double sc0 = S.greedy ? 0.0 : S.csum[row * nch + c0];
   float m_all = -INFINITY;
   int a_all = 0x7fffffff;
   int b_all = 0;
-  for (int c = lane; c < nch; c += 64) {
+  if (lane < nch) {
+    better(m_all, a_all, mc0, ac0);
+    b_all = bc0;
+  }
+  for (int c = lane + 64; c < nch; c += 64) {
     better(m_all, a_all, S.cmax[row * nch + c], S.carg[row * nch + c]);
     b_all |= S.cbad[row * nch + c];
   }
@@ -192,7 +201,8 @@ __global__ __launch_bounds__(256) void softmax_merge_kernel(SmSet A, SmSet B, in
   b_all = wave_or_i(b_all);
   double z = 0.0;
   if (!S.greedy && m_all > -INFINITY) {
-    for (int c = lane; c < nch; c += 64) {
+    if (lane < nch && mc0 > -INFINITY) z = sc0 * exp(((double)mc0 - (double)m_all) * S.inv_t);
+    for (int c = lane + 64; c < nch; c += 64) {
       const float mc = S.cmax[row * nch + c];
       if (mc > -INFINITY) z += S.csum[row * nch + c] * exp(((double)mc - (double)m_all) * S.inv_t);
     }
