@@ -35,7 +35,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 64;           // keys per tile
-constexpr int kMfmaRowsPerWg = 128; // 4 waves x 32 rows
+constexpr int kMfmaRowsPerWg = 128; // 4 row blocks of 32 (each done by two waves, one per key half)
 constexpr int kShflRowsPerWg = 16;  // 4 waves x 4 rows
 constexpr int kMaxSplitPages = 1024;  // page ids of one split kept in LDS
 constexpr float kLog2e = 1.4426950408889634f;
@@ -147,6 +147,32 @@ __device__ inline void ds_read_b128_x8(v4i (&r)[8], const uint32_t (&ad)[4]) {
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
       : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "n"(OFF1));
 }
+// Four 16-byte reads and their wait.
+__device__ inline void ds_read_b128_x4(v4i (&r)[4], const uint32_t (&ad)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %5\n"
+      "ds_read_b128 %2, %6\n"
+      "ds_read_b128 %3, %7\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]));
+}
+// Eight independent 16-byte reads and their wait.
+__device__ inline void ds_read_b128_x8(v4i (&r)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %9\n"
+      "ds_read_b128 %2, %10\n"
+      "ds_read_b128 %3, %11\n"
+      "ds_read_b128 %4, %12\n"
+      "ds_read_b128 %5, %13\n"
+      "ds_read_b128 %6, %14\n"
+      "ds_read_b128 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
+}
 // Eight transpose reads at ad[j] + OFF and their wait.
 template <int OFF>
 __device__ inline void ds_read_tr16_x8(v4s (&r)[8], const uint32_t (&ad)[8]) {
@@ -164,17 +190,22 @@ __device__ inline void ds_read_tr16_x8(v4s (&r)[8], const uint32_t (&ad)[8]) {
       : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]), "n"(OFF));
 }
 
+// Eight waves: wave w owns query rows 32 (w % 4) .. + 31 of the block and key half
+// w / 4 (keys 32 (w / 4) .. + 31) of every tile, so each SIMD runs two waves whose
+// MFMA and VALU work interleave; the two halves of a row merge in LDS at the end.
 template <int D>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   constexpr int ROWB = D * 2;           // bytes per key row
   constexpr int CH = D / 8;             // 16-byte chunks per key row
   constexpr int TILE_B = kTile * ROWB;  // bytes per K (or V) tile
   constexpr int KPB = 1024 / ROWB;      // keys per 1 KB wave load
-  constexpr int LOADS = TILE_B / 1024 / 4;  // wave loads per tile per operand
+  constexpr int LOADS = TILE_B / 1024 / 8;  // wave loads per tile per operand
+  static_assert(LOADS >= 1 && LOADS * 8 * 1024 == TILE_B, "tile split over the eight waves");
   __shared__ __attribute__((aligned(1024))) char sKV[kStages][2][TILE_B];
   __shared__ int s_page[kMaxSplitPages];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wid & 3, kh = wid >> 2;  // row block, key half
   // XCD-aware order: consecutive logical workgroups (the splits and query blocks
   // of one KV head) land on the same XCD and share its L2.
   const int W = a.batch * a.hkv * a.qblocks * a.S;
@@ -223,7 +254,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   // Q and the ancestor row go out before the request's lengths are known: the row's
   // node index is clamped into [0, n_max) so the addresses are valid for every row,
   // and rows that turn out dead drop what they loaded
-  const int r = qb * kMfmaRowsPerWg + wid * 32 + (lane & 31);
+  const int r = qb * kMfmaRowsPerWg + wr * 32 + (lane & 31);
   const int node = r / hpg;
   const int node_c = min(node, a.n_max - 1);
   const int h = g * hpg + r % hpg;
@@ -246,7 +277,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   int bad_page = 0;
   if (a.block_table && n_tiles > 0) {
     const int p0 = k_begin / a.page_size, p1 = (k_end - 1) / a.page_size;
-    for (int i = tid; i <= p1 - p0; i += 256) {
+    for (int i = tid; i <= p1 - p0; i += 512) {
       int pg = a.block_table[(int64_t)b * a.kv_capacity + p0 + i];
       if (pg < 0 || pg >= a.n_pages) {
         bad_page = 1;
@@ -340,45 +371,41 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
     const char* sv = sKV[it % kStages][1];
     const int t0 = k_begin + it * kTile;
 
-    // ---- S^T = K Q^T for two 32-key blocks: all 2 * D/16 operand reads first (in
-    // batches of 8), then MFMAs alternating between the two independent blocks ----
-    const uint32_t kbase_lds = lds_addr(sk), vbase_lds = lds_addr(sv);
-    f32x16 acc_s[2] = {f32x16{}, f32x16{}};
-    v4i kr[D / 64][8];
+    // ---- S^T = K Q^T for this wave's 32 keys: the D/16 operand reads first, then
+    // the MFMAs ----
+    const uint32_t kbase_lds = lds_addr(sk) + kh * 32 * ROWB, vbase_lds = lds_addr(sv) + kh * 32 * ROWB;
+    f32x16 acc_s = f32x16{};
+    static_assert(D == 64 || D == 128, "head_dim");
+    v4i kr[D / 16];
+    {
+      uint32_t ad[D / 16];
 #pragma unroll
-    for (int bi = 0; bi < D / 64; ++bi) {
-      uint32_t ad[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ad[j] = kbase_lds + koff[4 * bi + j];
-      ds_read_b128_x8<32 * ROWB>(kr[bi], ad);
+      for (int j = 0; j < D / 16; ++j) ad[j] = kbase_lds + koff[j];
+      if constexpr (D == 128) ds_read_b128_x8(kr, ad);
+      else ds_read_b128_x4(kr, ad);
     }
 #pragma unroll
-    for (int x = 0; x < 2 * (D / 16); ++x) {
-      const int kb = x & 1, kk = x >> 1;
+    for (int kk = 0; kk < D / 16; ++kk) {
       bf16x8 kf;
-      __builtin_memcpy(&kf, &kr[x >> 3][x & 7], sizeof(kf));
-      acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s[kb], 0, 0, 0);
+      __builtin_memcpy(&kf, &kr[kk], sizeof(kf));
+      acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s, 0, 0, 0);
     }
-    // ---- mask, online softmax (lane owns row lane%32; lane^32 holds the other keys);
-    // raw scores, the scale is applied inside the exponent ----
+    // ---- mask, online softmax (lane owns row lane%32; lane^32 holds the other keys
+    // of the half); raw scores, the scale is applied inside the exponent ----
     float tmax = -INFINITY;
     if constexpr (!kMasked) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, acc_s[kb][e]);
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, acc_s[e]);
     } else {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int t = t0 + kb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          const int j = t - ctx;  // tree slot
-          const bool vis = t < k_end && (j < 0 || ((anc_row >> (j & 63)) & 1ull));
-          const float sc = vis ? acc_s[kb][e] : -INFINITY;
-          acc_s[kb][e] = sc;
-          tmax = fmaxf(tmax, sc);
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int t = t0 + kh * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int j = t - ctx;  // tree slot
+        const bool vis = t < k_end && (j < 0 || ((anc_row >> (j & 63)) & 1ull));
+        const float sc = vis ? acc_s[e] : -INFINITY;
+        acc_s[e] = sc;
+        tmax = fmaxf(tmax, sc);
+      }
     }
     tmax = fmaxf(tmax, xor32_f(tmax)) * sl2;
     if (!row_live) tmax = -INFINITY;
@@ -392,22 +419,20 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
     }
     const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;
     float psum = 0.0f;
-    bf16x8 pf[4];
+    bf16x8 pf[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[kb][e], sl2, neg_m));
-        psum += p;
-        pf[kb * 2 + (e >> 3)][e & 7] = (__bf16)p;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[e], sl2, neg_m));
+      psum += p;
+      pf[e >> 3][e & 7] = (__bf16)p;
+    }
     psum += xor32_f(psum);
     l_run += m_run == -INFINITY ? 0.0f : psum;
-    // ---- O^T += V^T P^T; k-step ks covers keys 16 ks .. 16 ks + 15 in the order
-    // sigma(k) = 8 ((k >> 2) & 1) + 4 (k >> 3) + (k & 3) that the S^T accumulator gives ----
-    // operands of k-step ks for every d-block: D/32 blocks x (lo, hi) reads, in
+    // ---- O^T += V^T P^T over the half's two k-steps; k-step ks covers keys
+    // 16 ks .. 16 ks + 15 of the half in the order sigma(k) = 8 ((k >> 2) & 1) +
+    // 4 (k >> 3) + (k & 3) that the S^T accumulator gives ----
+    // operands of a k-step for every d-block: D/32 blocks x (lo, hi) reads, in
     // batches of 8 (one batch covers 4 d-blocks)
-    // one batch: the lo/hi reads of d-blocks 4 bq .. 4 bq + 3 at k-step KS
     constexpr int NB = (D / 32 + 3) / 4;  // batches per k-step (1 for D <= 128)
     constexpr int NDB = D / 32;
     uint32_t vad[NB][8];
@@ -429,21 +454,16 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       constexpr int KS = decltype(ks_tag)::value;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const v4s lohi[2] = {va[KS & 1][db / 4][2 * (db % 4)], va[KS & 1][db / 4][2 * (db % 4) + 1]};
+        const v4s lohi[2] = {va[KS][db / 4][2 * (db % 4)], va[KS][db / 4][2 * (db % 4) + 1]};
         bf16x8 vf;
         __builtin_memcpy(&vf, lohi, sizeof(vf));
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[KS], acc_o[db], 0, 0, 0);
       }
-      // the next k-step's operands are read while these MFMAs run
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (KS + 1 < 4) read_v(std::integral_constant<int, KS + 1>{}, va[(KS + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
     };
     read_v(std::integral_constant<int, 0>{}, va[0]);
+    read_v(std::integral_constant<int, 1>{}, va[1]);
     pv_step(std::integral_constant<int, 0>{});
     pv_step(std::integral_constant<int, 1>{});
-    pv_step(std::integral_constant<int, 2>{});
-    pv_step(std::integral_constant<int, 3>{});
   };
   // tiles below min(ctx, k_end) hold prompt keys only
   const int n_plain = min(n_tiles, max(0, (min(ctx, k_end) - k_begin) / kTile));
@@ -451,17 +471,40 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   for (; it < n_plain; ++it) tile(it, std::false_type{});
   for (; it < n_tiles; ++it) tile(it, std::true_type{});
   if (bad_page) report(a.status, SPEC_ERR_BAD_INPUT);
-  // ---- write this split's partials: the wave's 32 rows go through LDS (the tiles
-  // are consumed) so that the normalised outputs leave as whole rows ----
+  // ---- merge the two key halves of each row: the key-half-1 wave hands its
+  // (m, l, O) to its partner through LDS (the tiles are consumed) ----
+  constexpr int NACC = D / 32 * 16;  // accumulator values per lane
+  float* mw = reinterpret_cast<float*>(&sKV[0][0][0]) + wr * (NACC + 2) * 64;  // [NACC + 2][64]
+  lds_barrier();  // every wave is done with the K/V stages
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) mw[i * 64 + lane] = acc_o[i / 16][i % 16];
+    mw[NACC * 64 + lane] = m_run;
+    mw[(NACC + 1) * 64 + lane] = l_run;
+  }
+  lds_barrier();
+  if (kh == 0) {
+    const float mb = mw[NACC * 64 + lane], lb = mw[(NACC + 1) * 64 + lane];
+    const float m = fmaxf(m_run, mb);
+    const float wa = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+    const float wb = mb == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - m);
+    l_run = l_run * wa + lb * wb;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc_o[i / 16][i % 16] = acc_o[i / 16][i % 16] * wa + mw[i * 64 + lane] * wb;
+    m_run = m;
+  }
+  lds_barrier();  // the merge area is free again
+  if (kh == 1) return;
+  // ---- write this split's partials: the wave's 32 rows go through LDS so that
+  // the normalised outputs leave as whole rows ----
   const bool row_out = r < G && node < a.n_max;
   const int64_t prow = (((int64_t)s * a.batch + b) * a.n_max + node) * a.hq + h;
   if (row_out && lane < 32) {
     a.mpart[prow] = m_run;
     a.lpart[prow] = l_run;
   }
-  lds_barrier();  // every wave is done with the K/V stages
   constexpr int OROW = D * 2 + 16;  // bytes per staged row (padded)
-  char* so = &sKV[0][0][0] + wid * 32 * OROW;
+  char* so = &sKV[0][0][0] + wr * 32 * OROW;
   {
     const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
 #pragma unroll
@@ -483,7 +526,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < 32 / RPI; ++j) {
     const int rl = j * RPI + lane / CPR;  // row within the wave
-    const int rg = qb * kMfmaRowsPerWg + wid * 32 + rl;
+    const int rg = qb * kMfmaRowsPerWg + wr * 32 + rl;
     const int nd2 = rg / hpg;
     if (rg < G && nd2 < a.n_max) {
       const int64_t prow2 = (((int64_t)s * a.batch + b) * a.n_max + nd2) * a.hq + g * hpg + rg % hpg;
@@ -791,10 +834,11 @@ extern "C" int spec_tree_attention(const void* q, const void* k, const void* v, 
   hipStream_t st = (hipStream_t)stream;
   const dim3 g1((unsigned)grid), blk(256);
   if (p.mfma) {
+    const dim3 bm(512);  // eight waves: four row blocks x two key halves
     if (head_dim == 128)
-      hipLaunchKernelGGL(attn_mfma_kernel<128>, g1, blk, 0, st, a);
+      hipLaunchKernelGGL(attn_mfma_kernel<128>, g1, bm, 0, st, a);
     else
-      hipLaunchKernelGGL(attn_mfma_kernel<64>, g1, blk, 0, st, a);
+      hipLaunchKernelGGL(attn_mfma_kernel<64>, g1, bm, 0, st, a);
   } else if (dtype == SPEC_BF16) {
     if (head_dim == 128)
       hipLaunchKernelGGL((attn_shfl_kernel<128, __bf16>), g1, blk, 0, st, a);
