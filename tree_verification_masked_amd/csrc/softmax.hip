@@ -20,6 +20,7 @@
 namespace spectree {
 
 constexpr int kSmThreads = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSmPerThread = kChunk / kSmThreads;  // 32 fp32 elements held per thread
 
 inline int sm_chunks(int32_t vocab) { return (vocab + kChunk - 1) / kChunk; }
@@ -103,7 +104,9 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSe
   if (kVec && c0 + kChunk <= vocab) {
 #pragma unroll
     for (int k = 0; k < kSmPerThread / 4; ++k) {
-      const float4 f = *reinterpret_cast<const float4*>(src + c0 + (k * kSmThreads + tid) * 4);
+      // streaming, read-once data: non-temporal loads
+      const f32x4 f4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + c0 + (k * kSmThreads + tid) * 4));
+      const float4 f = make_float4(f4[0], f4[1], f4[2], f4[3]);
       x[4 * k + 0] = f.x;
       x[4 * k + 1] = f.y;
       x[4 * k + 2] = f.z;
