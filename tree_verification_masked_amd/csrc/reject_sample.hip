@@ -977,8 +977,43 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
   const int b = nd / a.n_max, n = nd % a.n_max;
   const int64_t base = (int64_t)b * a.n_max, row = nd;
   if (blockIdx.x == 0 && tid == 0 && chunked) *w.act_count = 0;  // R1 and R2 are done with it
-  // ---- everything this node may need, in one round of loads ----
+  // ---- everything this node may need, in one round of loads: its plan record,
+  // and (chunked vocabularies) the chain state R2 left for it, which is valid
+  // memory for every node slot and kept only if the node turns out to need it ----
   const NodeInfo inf = w.info[nd];
+  static_assert(kMaxKids <= kRjThreads && 2 * kMaxKids <= kRjThreads && kLdsList % kRjThreads == 0, "R3 preload");
+  double sp_a = 0.0, sp_b = 0.0;
+  long long sp_lv = 0, sp_cp = 0, sp_cq = 0;
+  int sp_flags = 0;
+  uint32_t sp_n = 0;
+  constexpr int kSpE = kLdsList / kRjThreads;  // list entries per thread
+  long long sp_fp[kSpE] = {}, sp_fq[kSpE] = {};
+  double sp_rho[kSpE] = {};
+  int sp_tok[kSpE] = {};
+  if (chunked) {
+    const ChainRec* R = w.rec + nd;
+    if (tid < kMaxKids) {
+      sp_a = R->a[tid];
+      sp_b = R->b[tid];
+    }
+    if (tid < 2 * kMaxKids) sp_lv = w.lvl[(int64_t)nd * 2 * kMaxKids + tid];
+    if (tid < a.nch) {
+      const long long* cd = w.cdraw + (int64_t)nd * a.nch * 2;
+      sp_cp = cd[2 * tid];
+      sp_cq = cd[2 * tid + 1];
+    }
+    sp_flags = R->flags;
+    sp_n = w.list_n[nd];
+    const ListEntry* L0 = w.list + (int64_t)nd * kListCap;
+#pragma unroll
+    for (int j = 0; j < kSpE; ++j) {
+      const ListEntry* e = L0 + tid + kRjThreads * j;
+      sp_fp[j] = e->fp;
+      sp_fq[j] = e->fq;
+      sp_rho[j] = e->rho;
+      sp_tok[j] = e->tok;
+    }
+  }
   const int nb = a.n_nodes[b];
   if (tid < 64) {
     const bool in = tid < a.n_max;
@@ -998,21 +1033,24 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
   const int k = __popcll(inf.kids);
   const bool node_ok = inf.verdict == 0 && n < nb;
   const bool chain = chunked && node_ok && inf.active;
-  if (chain) {
-    const ChainRec* R = w.rec + nd;
-    for (int l = tid; l < k; l += blockDim.x) {
-      s_ia[l] = R->a[l];
-      s_ib[l] = R->b[l];
+  if (chain) {  // (loaded above in the first round; kept only for chain nodes)
+    const int nl = (int)min(sp_n, (uint32_t)kListCap);
+    if (tid < k) {
+      s_ia[tid] = sp_a;
+      s_ib[tid] = sp_b;
     }
-    for (int i = tid; i < 2 * k; i += blockDim.x) s_lv[i] = w.lvl[(int64_t)nd * 2 * kMaxKids + i];
-    const long long* cd = w.cdraw + (int64_t)nd * a.nch * 2;
-    for (int ch = tid; ch < a.nch; ch += blockDim.x) {
-      s_cP[ch] = (unsigned long long)cd[2 * ch];
-      s_cQ[ch] = (unsigned long long)cd[2 * ch + 1];
+    if (tid < 2 * k) s_lv[tid] = sp_lv;
+    if (tid < a.nch) {
+      s_cP[tid] = (unsigned long long)sp_cp;
+      s_cQ[tid] = (unsigned long long)sp_cq;
     }
+#pragma unroll
+    for (int j = 0; j < kSpE; ++j)
+      if (nl <= kLdsList && tid + kRjThreads * j < nl)
+        s_list[tid + kRjThreads * j] = ListEntry{sp_fp[j], sp_fq[j], sp_rho[j], sp_tok[j], 0};
     if (tid == 0) {
-      s_flags = R->flags;
-      s_nlist = (int)min(w.list_n[nd], (uint32_t)kListCap);
+      s_flags = sp_flags;
+      s_nlist = nl;
     }
   }
   const bool leaf_chunks = chunked && node_ok && k == 0 && a.tgt_chunk_max != nullptr;
@@ -1050,10 +1088,8 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
         const bool fast = chain && !(s_flags & kFlagFallback);
         const ListEntry* L = w.list + (int64_t)nd * kListCap;
         const int nlist = fast ? s_nlist : 0;
-        const bool in_lds = nlist <= kLdsList;
+        const bool in_lds = nlist <= kLdsList;  // then s_list holds it (filled with the preload)
         const ListEntry* LL = in_lds ? s_list : L;
-        if (in_lds)
-          for (int i = tid; i < nlist; i += blockDim.x) s_list[i] = L[i];
         if (tid == 0) s_st = SibState{inf.kids, 0.0, 1.0, SPEC_NODE_NONE, 0, 0, 0};
         __syncthreads();
         // A short list (the usual case): wavefront 0 follows the exact path with the
