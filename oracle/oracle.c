@@ -30,6 +30,8 @@
  *   oracle_reject_sample    pinned (worked example, chi-square, alpha^d, greedy vs
  *                           target-only decode, special cases)
  *   oracle_accept_path      pinned (worked example)
+ *   oracle_kv_commit        pinned (hand-checked moves on a small cache, both
+ *                           layouts; untouched positions; page release)
  */
 #include <math.h>
 #include <omp.h>
@@ -629,6 +631,78 @@ int oracle_accept_path(const int32_t* accepted_child, const int32_t* term_token,
     accept_len[b] = len;
   }
   return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O6. KV commit and rollback after the path.                                   */
+/* [FAL] "EAGLE-4 verification trees and harness": after verification the       */
+/* accepted continuation is kept and the rejected KV-cache entries are freed.    */
+/* [ZS] part D.2: every tree node writes its own K/V, and rejected nodes must    */
+/* not stay in the cache (rollback; paged caches free whole pages).              */
+/* Reading: node j's K/V sits at logical position ctx + j; the root (node 0) is  */
+/* committed where it is, and path node i (i = 1..L) moves from ctx + path[i] to */
+/* ctx + i, so the committed length becomes ctx + 1 + L.  All sources are read   */
+/* before any destination is written.  With a page table, the pages whose slots  */
+/* hold only positions in [new_len, ctx + n) are released: their table entries   */
+/* become -1 and their ids are listed in freed[b][0..] (-1 padded, 64 entries).  */
+/* A request with accept_len < 0, an invalid path or a position outside the      */
+/* cache is left untouched with new_len = -1 (ORC_EDATA is returned if any).     */
+/* elem = bytes per element (2 for bf16, 4 for fp32); k, v in the layouts of O2. */
+/* ------------------------------------------------------------------------- */
+int oracle_kv_commit(void* k, void* v, int32_t elem, int32_t* block_table, int32_t page_size, int32_t kv_capacity,
+                     int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes, const int32_t* path_nodes,
+                     const int32_t* accept_len, int32_t batch, int32_t n_max, int32_t hkv, int32_t d,
+                     int32_t* new_len, int32_t* freed) {
+  if (!k || !v || !ctx_len || !n_nodes || !path_nodes || !accept_len || !new_len || !freed) return ORC_EARG;
+  if (elem != 2 && elem != 4) return ORC_EARG;
+  const size_t row = (size_t)d * (size_t)elem; /* bytes of one (position, head) vector */
+  unsigned char* tmp = (unsigned char*)malloc((size_t)2 * n_max * hkv * row);
+  if (!tmp) return ORC_ENOMEM;
+  int rc = ORC_OK;
+  for (int32_t b = 0; b < batch; ++b) {
+    int32_t* fr = freed + (int64_t)b * 64;
+    for (int j = 0; j < 64; ++j) fr[j] = -1;
+    new_len[b] = -1;
+    const int32_t L = accept_len[b], n = n_nodes[b], ctx = ctx_len[b];
+    const int32_t* path = path_nodes + (int64_t)b * n_max;
+    if (L < 0) continue;
+    int ok = n >= 1 && n <= n_max && ctx >= 0 && L < n && path[0] == 0;
+    for (int32_t i = 1; ok && i <= L; ++i) ok = path[i] > path[i - 1] && path[i] < n;
+    /* every position the commit touches must exist */
+    for (int32_t t = ctx; ok && t < ctx + n; ++t)
+      for (int32_t g = 0; ok && g < hkv; ++g)
+        ok = kv_offset(b, t, g, block_table, page_size, kv_capacity, n_pages, hkv, d) >= 0;
+    if (!ok) {
+      rc = ORC_EDATA;
+      continue;
+    }
+    /* read every source first ... */
+    for (int32_t i = 1; i <= L; ++i)
+      for (int32_t g = 0; g < hkv; ++g) {
+        const int64_t off = kv_offset(b, ctx + path[i], g, block_table, page_size, kv_capacity, n_pages, hkv, d);
+        memcpy(tmp + ((size_t)(2 * i) * hkv + g) * row, (unsigned char*)k + off * elem, row);
+        memcpy(tmp + ((size_t)(2 * i + 1) * hkv + g) * row, (unsigned char*)v + off * elem, row);
+      }
+    /* ... then write every destination */
+    for (int32_t i = 1; i <= L; ++i)
+      for (int32_t g = 0; g < hkv; ++g) {
+        const int64_t off = kv_offset(b, ctx + i, g, block_table, page_size, kv_capacity, n_pages, hkv, d);
+        memcpy((unsigned char*)k + off * elem, tmp + ((size_t)(2 * i) * hkv + g) * row, row);
+        memcpy((unsigned char*)v + off * elem, tmp + ((size_t)(2 * i + 1) * hkv + g) * row, row);
+      }
+    new_len[b] = ctx + 1 + L;
+    if (block_table) { /* release the pages left holding only freed positions */
+      int32_t* tab = block_table + (int64_t)b * kv_capacity;
+      const int32_t first = (new_len[b] + page_size - 1) / page_size, end = (ctx + n + page_size - 1) / page_size;
+      int j = 0;
+      for (int32_t slot = first; slot < end; ++slot) {
+        fr[j++] = tab[slot];
+        tab[slot] = -1;
+      }
+    }
+  }
+  free(tmp);
+  return rc;
 }
 
 /* Thread plumbing for timing runs (no arithmetic). */
