@@ -8,6 +8,7 @@
  *   spec_tree_softmax         per-node vocabulary softmax statistics (target, draft)
  *   spec_tree_reject_sample   lossless tree rejection sampling (or greedy at T = 0)
  *   spec_accept_path          longest accepted root-to-leaf path plus the bonus token
+ *   spec_tree_kv_commit       keep the accepted path's K/V, free the rejected tree slots
  *
  * Sources.  "EAGLE 演化史 (1 → 2 → 3) 与 DFlash 的回答" (zhangshuibai.github.io paper
  * notes), section "Tree Verification 详解": part B (BFS flattening and the
@@ -227,6 +228,36 @@ int spec_tree_reject_sample(const float* tgt_logits, const float* tgt_max, const
 int spec_accept_path(const int32_t* accepted_child, const int32_t* term_token, const int32_t* tokens,
                      const int32_t* n_nodes, int32_t batch, int32_t n_max, int32_t* path_nodes, int32_t* out_tokens,
                      int32_t* accept_len, int32_t* status, void* stream);
+
+/*
+ * KV commit and rollback after the path (fal.ai page, "EAGLE-4 verification trees
+ * and harness": keep the accepted continuation, free the rejected KV entries; tree
+ * notes, part D.2: rejected nodes must not stay in the cache).  Node j's K/V sits
+ * at logical position ctx_len[b] + j; for path_nodes / accept_len as
+ * spec_accept_path writes them, path node i (i = 1..L, L = accept_len[b]) is
+ * moved from position ctx + path_nodes[b,i] to ctx + i for every KV head, K and V;
+ * the root stays at ctx.  Sources are read before destinations are written, so
+ * overlapping moves are exact.
+ *   k, v          the cache of spec_tree_attention (contiguous or paged), in place
+ *   block_table   paged: pages whose slots hold only positions in
+ *                 [new_len, ctx + n_nodes) are released: their entries become -1
+ *   new_len [batch]      ctx + 1 + L, the committed length; -1 for a request that
+ *                        was refused (accept_len < 0) or is invalid (path not an
+ *                        increasing walk from the root inside the tree, a tree
+ *                        position outside the cache, a bad page id), which is left
+ *                        untouched (SPEC_ERR_BAD_INPUT in status for the invalid ones)
+ *   freed_pages [batch, 64]  released page ids in slot order, -1 padded (nullable)
+ * One workgroup per request; the moved bytes are L * hkv * head_dim * elem * 2,
+ * read and written once.
+ * Host errors: null required pointers, batch < 1, n_max outside [1, 64], hkv < 1,
+ * a block table with page_size < 1 or n_pages < 1; SPEC_ERR_UNSUPPORTED for another
+ * dtype, head_dim not 64/128, or hkv * head_dim * element size above 32 KiB.
+ */
+int spec_tree_kv_commit(void* k, void* v, int32_t dtype, int32_t* block_table, int32_t page_size,
+                        int32_t kv_capacity, int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes,
+                        const int32_t* path_nodes, const int32_t* accept_len, int32_t batch, int32_t n_max,
+                        int32_t hkv, int32_t head_dim, int32_t* new_len, int32_t* freed_pages, int32_t* status,
+                        void* stream);
 
 /* Library version string (static storage). */
 const char* spec_tree_version(void);

@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding and header disagree"
@@ -123,3 +123,28 @@ def test_host_errors_reject(lib):
     assert 0 < binding.spec_tree_reject_sample_workspace_size(1, 60, 4096) < 16384
     assert binding.spec_tree_reject_sample_workspace_size(1, 65, 4096) == 0
     assert binding.spec_tree_reject_sample_workspace_size(1, 60, 128256) > 60 * 4096 * 32
+
+
+def test_host_errors_kv_commit(lib):
+    f = lib.spec_tree_kv_commit
+    #       k  v  dt bt    ps cap np ctx nn path al B  nmax hkv D    nl fr    st    s
+    args = [P, P, 1, None, 0, 100, 0, P, P, P, P, 1, 8, 8, 128, P, None, None, None]
+    for i, bad in ((0, None), (7, None), (15, None)):
+        a = list(args)
+        a[i] = bad
+        assert f(*a) == -1
+    a = list(args)
+    a[12] = 65  # n_max
+    assert f(*a) == -1
+    a = list(args)
+    a[3], a[4] = P, 0  # block table without a page size
+    assert f(*a) == -1
+    a = list(args)
+    a[14] = 96  # head_dim
+    assert f(*a) == -2
+    a = list(args)
+    a[2] = 5  # dtype
+    assert f(*a) == -2
+    a = list(args)
+    a[2], a[13] = 0, 65  # 65 heads x 128 fp32 above the 32 KiB staged per row
+    assert f(*a) == -2

@@ -49,6 +49,8 @@ _SIGNATURES = {
     "spec_tree_reject_sample": [_VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _I32,
                                 _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
+    "spec_tree_kv_commit": [_VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
+                            _VP, _VP, _VP, _VP],
     "spec_tree_version": [],
 }
 _RESTYPES = {
@@ -271,3 +273,29 @@ def spec_accept_path(accepted_child, term_token, tokens, n_nodes, path_nodes, ou
     _check(status, torch.int32, (1,), "status")
     _call("spec_accept_path", _ptr(accepted_child), _ptr(term_token), _ptr(tokens), _ptr(n_nodes), B, n_max,
           _ptr(path_nodes), _ptr(out_tokens), _ptr(accept_len), _ptr(status), _stream(stream))
+
+
+def spec_tree_kv_commit(k, v, ctx_len, n_nodes, path_nodes, accept_len, new_len, freed_pages=None, *,
+                        block_table=None, page_size=0, n_pages=0, status=None, stream=None):
+    """In place on k, v (and block_table when paged)."""
+    if k.dtype == torch.bfloat16:
+        dtype = SPEC_BF16
+    elif k.dtype == torch.float32:
+        dtype = SPEC_F32
+    else:
+        raise TypeError(f"k: unsupported dtype {k.dtype}")
+    _check(v, k.dtype, tuple(k.shape), "v")
+    B, n_max = path_nodes.shape
+    hkv, D = k.shape[-2], k.shape[-1]
+    for t, nm in ((path_nodes, "path_nodes"),):
+        _check(t, torch.int32, (B, n_max), nm)
+    for t, nm in ((ctx_len, "ctx_len"), (n_nodes, "n_nodes"), (accept_len, "accept_len"), (new_len, "new_len")):
+        _check(t, torch.int32, (B,), nm)
+    _check(freed_pages, torch.int32, (B, 64), "freed_pages")
+    _check(status, torch.int32, (1,), "status")
+    cap = k.shape[1] if block_table is None else block_table.shape[1]
+    if block_table is not None:
+        _check(block_table, torch.int32, (B, cap), "block_table")
+    _call("spec_tree_kv_commit", _ptr(k), _ptr(v), dtype, _ptr(block_table), int(page_size), int(cap), int(n_pages),
+          _ptr(ctx_len), _ptr(n_nodes), _ptr(path_nodes), _ptr(accept_len), B, n_max, hkv, D, _ptr(new_len),
+          _ptr(freed_pages), _ptr(status), _stream(stream))
