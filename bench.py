@@ -8,14 +8,20 @@ Workload (default): the Llama-3-8B-shaped step -- one request, a 60-node EAGLE-2
 tree (top-k 10, depth 6), 4096 cached tokens, 32 query / 8 KV heads, head_dim 128,
 bf16 KV, fp32 logits over a 128256-token vocabulary, T = 1.  Synthetic, seeded.
 
-Timing: W warm-up steps, then K steps bracketed by synchronize + HIP events.  Each
+Timing: W warm-up steps, then K steps bracketed by synchronize + HIP events, queued
+behind a short spin kernel so that the events time the GPU, not Python's launch rate.  Each
 step reads one of R input replicas in turn (distinct device buffers, 8 x ~80 MB)
 so the working set is far larger than the 256 MB last-level cache and the numbers
 are HBM numbers.  A second timed pass records events around every stage to report
 per-call durations; the call holding the longest kernel (tree attention) gives the
 roofline entry, the logit softmax a second one.  Measured HBM traffic per call comes
 from the committed counter summary under profiles/ while the kernel sources match.  The CPU oracle is timed on the host on full steps of the same
-workload.  Prints one JSON line.
+workload.  After the timed regions the KV commit that follows a step (one layer, the
+deepest path of the tree) is timed on a scratch copy of the cache and reported under
+"next_rows".  Prints one JSON line.
+
+``--cost-table PREFIX`` instead sweeps the step over (batch, context, nodes) and writes
+the verify-latency table (PREFIX.json, PREFIX.md) that cost_table.CostTable reads.
 """
 from __future__ import annotations
 
@@ -80,6 +86,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cost-table", metavar="PREFIX", default=None,
+                    help="sweep (batch, context, nodes) and write PREFIX.json and PREFIX.md: the verify-latency "
+                         "table a cost-aware tree harness calibrates on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run four plain 512 MiB device-to-device copies (the reference kernel whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the traffic of the step's kernels)")
@@ -110,10 +119,222 @@ def copy_calibration():
                                            "launches": 4}}))
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def prefill(ms=20.0):
+    """Hold the GPU on a short spin kernel while the host queues the timed work behind
+    it, so that the timed region measures the GPU and not the Python launch rate."""
+    global _SLEEP_CYCLES_PER_MS
+    import torch
+
+    if _SLEEP_CYCLES_PER_MS is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1e6 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * ms))
+
+
+def run_steps(step, replicas, stream, n, first=0, events=None):
+    """n steps, rotating over the input replicas; with events, 7 events per step
+    bracket the stages (mask, attention, softmax, -, reject + path, -)."""
+    for i in range(n):
+        r = replicas[(first + i) % len(replicas)]
+        if events is None:
+            step.run(replica=r)
+            continue
+        ev = events[i]
+        ev[0].record(stream)
+        step.mask()
+        ev[1].record(stream)
+        if step.with_attention:
+            step.attention(None, r["q"], r["k"], r["v"])
+        ev[2].record(stream)
+        step.softmax(None, r["tgt_logits"], r.get("dft_logits"))
+        ev[3].record(stream)
+        ev[4].record(stream)
+        step.reject(None, r["tgt_logits"], r.get("dft_logits"))  # writes the accepted path too
+        ev[5].record(stream)
+        ev[6].record(stream)
+
+
+def time_steps(step, replicas, stream, steps, warmup):
+    """(ms per step over a clean timed region, mean us per stage from an instrumented pass)."""
+    import torch
+
+    run_steps(step, replicas, stream, warmup)
+    torch.cuda.synchronize()
+    prefill()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    run_steps(step, replicas, stream, steps, first=warmup)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / steps
+    assert int(step.status.item()) == 0, f"device status {int(step.status.item())}"
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    prefill()
+    run_steps(step, replicas, stream, steps, first=0, events=evs)
+    torch.cuda.synchronize()
+    stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(6)] for e in evs]) * 1e3  # us
+    return ms_per_step, stage.mean(axis=0)
+
+
+def deepest_paths(parent, n_nodes):
+    """Per request, the root-to-leaf path to the first deepest node (a full accept)."""
+    B, n_max = parent.shape
+    path = np.zeros((B, n_max), np.int32)
+    L = np.zeros(B, np.int32)
+    for b in range(B):
+        depth = np.zeros(n_max, np.int64)
+        for i in range(1, int(n_nodes[b])):
+            depth[i] = depth[parent[b, i]] + 1
+        j, chain = int(np.argmax(depth[: int(n_nodes[b])])), []
+        while j > 0:
+            chain.append(j)
+            j = int(parent[b, j])
+        chain = [0] + chain[::-1]
+        path[b, : len(chain)] = chain
+        L[b] = len(chain) - 1
+    return path, L
+
+
+def time_kv_commit(step, dev, k_src, v_src, stream, iters=200):
+    """The commit after the step (one layer's K and V) along each tree's deepest path
+    (every draft token accepted, the most rows a commit moves), timed on a scratch copy
+    of the cache with back-to-back calls.  Repeating a commit is valid on a contiguous
+    cache (it copies the same rows again); a paged one has its pages released by the
+    first call, so it is not timed here."""
+    import torch
+
+    from tree_verification_masked_amd import binding as Bd
+
+    if dev.get("block_table") is not None or not step.with_attention:
+        return None
+    k, v = k_src.clone(), v_src.clone()
+    Bn = dev["B"]
+    new_len = torch.zeros(Bn, dtype=torch.int32, device=k.device)
+    status = torch.zeros(1, dtype=torch.int32, device=k.device)
+    path_h, L = deepest_paths(dev["parent"].cpu().numpy(), dev["n_nodes"].cpu().numpy())
+    path, acc = torch.from_numpy(path_h).to(k.device), torch.from_numpy(L).to(k.device)
+
+    def call():
+        Bd.spec_tree_kv_commit(k, v, dev["ctx_len"], dev["n_nodes"], path, acc, new_len, status=status)
+
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize()
+    prefill()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(iters):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / iters
+    L = L.astype(np.int64)
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+    assert np.array_equal(new_len.cpu().numpy(), dev["ctx_len"].cpu().numpy() + 1 + L)
+    el = k.element_size()
+    moved = int(L.sum()) * dev["hkv"] * dev["d"] * el * 2 * 2  # K and V rows, read once and written once
+    return {"call": "spec_tree_kv_commit (one layer, contiguous KV)", "us": round(us, 2),
+            "accept_len": [int(x) for x in L], "bytes_moved": moved,
+            "gbs": round(moved / (us * 1e-6) / 1e9, 2), "iters": iters,
+            "note": "deepest path of each tree; back-to-back calls queued behind a spin kernel, on a scratch "
+                    "copy after the timed region"}
+
+
+COST_GRID = {"batch": (1, 2, 4, 8), "ctx": (1024, 4096, 16384), "n_nodes": (16, 32, 64)}
+
+
+def cost_table(args):
+    """Verify latency of the whole step (and its attention and sampling calls) over
+    (batch, context, nodes): random breadth-first trees (branching 1..4, depth <= 8),
+    Llama-3-8B head geometry, bf16 KV, vocabulary 128256.  One input at the largest
+    point; every point takes the first B requests, the first N nodes of each tree and
+    context C, each in enough replicas to exceed the last-level cache."""
+    import torch
+
+    from tree_verification_masked_amd import synth
+    from tree_verification_masked_amd.step import VerifyStep, to_device
+
+    torch.cuda.set_device(0)
+    cuda = torch.device("cuda")
+    bm, cm, nm = max(COST_GRID["batch"]), max(COST_GRID["ctx"]), max(COST_GRID["n_nodes"])
+    inp = synth.make_config(6, seed=args.seed, T=args.temperature, with_kv=False, grid=(bm, cm, nm))
+    par = inp["parent"]
+    assert np.all(par[:, 0] == -1) and np.all(par[:, 1:] < np.arange(1, nm)[None, :])  # prefixes are trees
+    base = to_device(inp)
+    g = torch.Generator(device=cuda)
+    g.manual_seed(args.seed)
+    hq, hkv, d = inp["hq"], inp["hkv"], inp["d"]
+    qf = torch.randn((bm, nm, hq, d), generator=g, device=cuda, dtype=torch.bfloat16)
+    kf = torch.randn((bm, cm + nm, hkv, d), generator=g, device=cuda, dtype=torch.bfloat16)
+    vf = torch.randn((bm, cm + nm, hkv, d), generator=g, device=cuda, dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    V = inp["V"]
+    rows = []
+    for Bn in COST_GRID["batch"]:
+        for ctx in COST_GRID["ctx"]:
+            for N in COST_GRID["n_nodes"]:
+                pt = dict(base)
+                for key in ("parent", "tokens", "tgt_logits", "dft_logits", "u_accept", "u_sample"):
+                    pt[key] = base[key][:Bn, :N].contiguous()
+                pt.update(B=Bn, n_max=N, kv_capacity=ctx + N, max_kv_len=ctx + N,
+                          n_nodes=torch.full((Bn,), N, dtype=torch.int32, device=cuda),
+                          ctx_len=torch.full((Bn,), ctx, dtype=torch.int32, device=cuda))
+                kv_b = 2 * Bn * (ctx + N) * hkv * d * 2
+                lg_b = Bn * N * V * 4 * (2 if inp["T"] > 0 else 1)
+                reps = int(min(32, max(2, -(-(1 << 30) // (kv_b + lg_b)))))
+                replicas = []
+                for _ in range(reps):
+                    replicas.append({"q": qf[:Bn, :N].clone(), "k": kf[:Bn, : ctx + N].clone(),
+                                     "v": vf[:Bn, : ctx + N].clone(), "tgt_logits": pt["tgt_logits"].clone(),
+                                     "dft_logits": pt["dft_logits"].clone()})
+                pt.update(q=replicas[0]["q"], k=replicas[0]["k"], v=replicas[0]["v"])
+                step = VerifyStep(pt)
+                ms, st = time_steps(step, replicas, stream, args.steps, args.warmup)
+                rows.append({"batch": Bn, "ctx": ctx, "n_nodes": N, "step_us": round(ms * 1e3, 2),
+                             "attention_us": round(float(st[1]), 2),
+                             "sampling_us": round(float(st[2] + st[4]), 2),
+                             "mask_us": round(float(st[0]), 2), "replicas": reps,
+                             "mean_accept_len": round(float(step.accept_len.float().mean().item()), 3)})
+                print(json.dumps({"cost_point": rows[-1]}), flush=True)
+                del replicas, step, pt
+                torch.cuda.empty_cache()
+    meta = {"what": "verify latency of one tree-verification step (one layer's attention + full-vocabulary "
+                    "sampling) on one MI355X, HIP events, inputs resident in HBM",
+            "workload": synth.CONFIGS[6], "T": inp["T"], "hq": hq, "hkv": hkv, "head_dim": d, "vocab": V,
+            "steps": args.steps, "warmup": args.warmup, "seed": args.seed, "grid": COST_GRID,
+            "command": " ".join(["python", "bench.py"] + sys.argv[1:])}
+    with open(args.cost_table + ".json", "w") as f:
+        json.dump({"meta": meta, "rows": rows}, f, indent=1)
+    with open(args.cost_table + ".md", "w") as f:
+        f.write("# Verify-latency cost table (one MI355X)\n\n")
+        f.write(f"{meta['what']}.  Workload: {meta['workload']}; T = {meta['T']}.  "
+                f"{args.steps} timed steps per point after {args.warmup} warm-up steps.\n\n")
+        f.write(f"Command: `{meta['command']}`\n\n")
+        f.write("| batch | ctx | nodes | step us | attention us | sampling us | mask us | mean accept len |\n")
+        f.write("|---:|---:|---:|---:|---:|---:|---:|---:|\n")
+        for r in rows:
+            f.write(f"| {r['batch']} | {r['ctx']} | {r['n_nodes']} | {r['step_us']} | {r['attention_us']} | "
+                    f"{r['sampling_us']} | {r['mask_us']} | {r['mean_accept_len']} |\n")
+    print(json.dumps({"cost_table": args.cost_table, "points": len(rows)}))
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gpus == 1 and args.cost_table:
+        cost_table(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -133,44 +354,9 @@ def main():
     replicas = [{k: dev[k].clone() for k in big} for _ in range(args.replicas)]
     stream = torch.cuda.current_stream()
 
-    def run_steps(n, first=0, events=None):
-        for i in range(n):
-            r = replicas[(first + i) % len(replicas)]
-            if events is None:
-                step.run(replica=r)
-                continue
-            ev = events[i]
-            ev[0].record(stream)
-            step.mask()
-            ev[1].record(stream)
-            if step.with_attention:
-                step.attention(None, r["q"], r["k"], r["v"])
-            ev[2].record(stream)
-            step.softmax(None, r["tgt_logits"], r.get("dft_logits"))
-            ev[3].record(stream)
-            ev[4].record(stream)
-            step.reject(None, r["tgt_logits"], r.get("dft_logits"))  # writes the accepted path too
-            ev[5].record(stream)
-            ev[6].record(stream)
-
-    # warm-up, then the clean timed region
-    run_steps(args.warmup)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    run_steps(args.steps, first=args.warmup)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    assert int(step.status.item()) == 0, f"device status {int(step.status.item())}"
-
-    # instrumented region: events around every stage of every step
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    run_steps(args.steps, first=0, events=evs)
-    torch.cuda.synchronize()
-    stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(6)] for e in evs]) * 1e3  # us
-    st_mean = stage.mean(axis=0)
+    # warm-up, the clean timed region, then an instrumented pass with events around
+    # every stage of every step
+    ms_per_step, st_mean = time_steps(step, replicas, stream, args.steps, args.warmup)
     names = ["mask_build", "attention", "softmax_pair", "-", "reject_sample", "-"]
 
     attn_b, logit_b, samp_b = algorithmic_bytes(inp)
@@ -211,6 +397,9 @@ def main():
                                            samp_b, sm_us, traffic.get("spec_tree_softmax_pair")),
         },
     }
+    kvc = time_kv_commit(step, dev, replicas[0]["k"], replicas[0]["v"], stream) if "k" in dev else None
+    if kvc is not None:
+        res["next_rows"] = {"kv_commit": kvc}
 
     if not args.no_cpu_baseline:
         import oracle

@@ -234,6 +234,7 @@ CONFIGS = {
     3: "chain-16 (DFlash block): ctx 8192, 32/8 heads, d 128, bf16, vocab 151936, T=0.7",
     4: "batch 8 x 32-node random trees, ctx U[512,8192], paged KV (16-token pages), 32/8 heads, bf16, vocab 128256",
     5: "long-context shard: 1 x 64-node EAGLE-2 tree (k=8, depth 8), ctx 32768, 64/8 heads, bf16, vocab 152064, t(3)x2 logits",
+    6: "cost-table grid: B x N-node random trees, one ctx for all requests, contiguous KV, 32/8 heads, d 128, bf16, vocab 128256",
 }
 
 
@@ -247,10 +248,13 @@ def _activations(rng, B, n_max, hq, hkv, d, s_cap, bf16):
 
 
 def make_config(cfg: int, seed: int = 0, T: float | None = None, with_kv: bool = True,
-                ctx_override: int | None = None, vocab_override: int | None = None):
-    """Build one input set for workload ``cfg`` (1..5).  Returns a dict of numpy arrays
+                ctx_override: int | None = None, vocab_override: int | None = None, grid=None):
+    """Build one input set for workload ``cfg`` (1..6).  Returns a dict of numpy arrays
     and scalars.  ``ctx_override`` / ``vocab_override`` shrink a workload for fast tests
-    while keeping its tree generator and head geometry."""
+    while keeping its tree generator and head geometry.  Workload 6 takes
+    ``grid = (B, ctx, N)``: workload 4's trees, tokens and logits with N nodes per tree,
+    every request at context ``ctx`` and contiguous KV (see ``grid_point`` for cutting
+    smaller points out of one such input)."""
     rng = rng_for(seed, cfg, 1)
     inp: dict = {"cfg": cfg, "seed": seed, "page_size": 0, "n_pages": 0, "block_table": None}
     if cfg == 1:
@@ -293,14 +297,18 @@ def make_config(cfg: int, seed: int = 0, T: float | None = None, with_kv: bool =
         trees = [(parent, tokens, list(range(n)))]
         bf16, B = True, 1
         ctxs = [ctx]
-    elif cfg == 4:
+    elif cfg in (4, 6):
         V, hq, hkv, d, n, B = 128256, 32, 8, 128, 32, 8
         V = vocab_override or V
         T_ = 1.0 if T is None else T
         Td = T_ if T_ > 0 else 1.0
-        hi = ctx_override or 8192
-        lo = min(512, hi)
-        ctxs = [int(c) for c in rng.integers(lo, hi + 1, size=B)]
+        if cfg == 4:
+            hi = ctx_override or 8192
+            lo = min(512, hi)
+            ctxs = [int(c) for c in rng.integers(lo, hi + 1, size=B)]
+        else:
+            B, c_all, n = (int(x) for x in grid)
+            ctxs = [c_all] * B
         trees = []
         for b in range(B):
             src = RowSource(seed * 7919 + 4000 + b, V, "normal", sigma_t=3.0, sigma_d=1.0)
@@ -339,7 +347,7 @@ def make_config(cfg: int, seed: int = 0, T: float | None = None, with_kv: bool =
                     ctx_len=np.array(ctxs, np.int32)))
     if with_kv:
         arng = rng_for(seed, cfg, 5)
-        if cfg == 4:
+        if cfg == 4:  # workload 6 keeps the contiguous layout
             page = 16
             pages_per = [math.ceil((ctxs[b] + n_nodes[b]) / page) for b in range(B)]
             n_pages = sum(pages_per) + 8  # a few spare pages that no request owns
@@ -363,6 +371,27 @@ def make_config(cfg: int, seed: int = 0, T: float | None = None, with_kv: bool =
     else:
         inp.update(q=None, k=None, v=None)
     return inp
+
+
+def grid_point(inp: dict, B: int, ctx: int, N: int) -> dict:
+    """A smaller point of the cost-table grid cut out of a workload-6 input: the first
+    B requests, the first N nodes of each tree and context ``ctx`` for every request.
+    The trees are built breadth-first, so every parent precedes its children and a
+    prefix of the node order is again a tree.  K/V keep their capacity; the tree's own
+    entries move with the context (slots ctx .. ctx + N - 1), whose contents are as
+    random as the prompt's."""
+    assert inp["cfg"] == 6 and inp["block_table"] is None
+    assert B <= inp["B"] and N <= inp["n_max"] and ctx + N <= inp["kv_capacity"]
+    par = inp["parent"][:B, :N]
+    assert np.all(par[:, 1:] < np.arange(1, N)[None, :]) and np.all(par[:, 0] == -1)
+    out = dict(inp)
+    for key in ("parent", "tokens", "tgt_logits", "dft_logits", "u_accept", "u_sample"):
+        out[key] = np.ascontiguousarray(inp[key][:B, :N])
+    if inp.get("q") is not None:
+        out["q"] = np.ascontiguousarray(inp["q"][:B, :N])
+        out["k"], out["v"] = inp["k"][:B], inp["v"][:B]
+    out.update(B=B, n_max=N, n_nodes=np.full(B, N, np.int32), ctx_len=np.full(B, ctx, np.int32))
+    return out
 
 
 # --------------------------------------------------------------------------
