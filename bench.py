@@ -204,8 +204,9 @@ def deepest_paths(parent, n_nodes):
     return path, L
 
 
-def time_kv_commit(step, dev, k_src, v_src, stream, iters=200):
-    """The commit after the step (one layer's K and V) along each tree's deepest path
+def time_kv_commit(step, dev, k_src, v_src, stream, iters=200, layers=1):
+    """The commit after the step (``layers`` layers' K and V, in one call: one layer, or
+    a whole model's cache stacked on a leading axis) along each tree's deepest path
     (every draft token accepted, the most rows a commit moves), timed on a scratch copy
     of the cache with back-to-back calls.  Repeating a commit is valid on a contiguous
     cache (it copies the same rows again); a paged one has its pages released by the
@@ -216,7 +217,11 @@ def time_kv_commit(step, dev, k_src, v_src, stream, iters=200):
 
     if dev.get("block_table") is not None or not step.with_attention:
         return None
-    k, v = k_src.clone(), v_src.clone()
+    if layers == 1:
+        k, v = k_src.clone(), v_src.clone()
+    else:
+        k = k_src.unsqueeze(0).repeat(layers, *([1] * k_src.dim()))
+        v = v_src.unsqueeze(0).repeat(layers, *([1] * v_src.dim()))
     Bn = dev["B"]
     new_len = torch.zeros(Bn, dtype=torch.int32, device=k.device)
     status = torch.zeros(1, dtype=torch.int32, device=k.device)
@@ -242,8 +247,10 @@ def time_kv_commit(step, dev, k_src, v_src, stream, iters=200):
     assert int(status.item()) == 0, f"device status {int(status.item())}"
     assert np.array_equal(new_len.cpu().numpy(), dev["ctx_len"].cpu().numpy() + 1 + L)
     el = k.element_size()
-    moved = int(L.sum()) * dev["hkv"] * dev["d"] * el * 2 * 2  # K and V rows, read once and written once
-    return {"call": "spec_tree_kv_commit (one layer, contiguous KV)", "us": round(us, 2),
+    moved = layers * int(L.sum()) * dev["hkv"] * dev["d"] * el * 2 * 2  # K and V rows, read once, written once
+    del k, v
+    return {"call": f"spec_tree_kv_commit ({layers} layer{'s' if layers > 1 else ''}, contiguous KV)",
+            "layers": layers, "us": round(us, 2),
             "accept_len": [int(x) for x in L], "bytes_moved": moved,
             "gbs": round(moved / (us * 1e-6) / 1e9, 2), "iters": iters,
             "note": "deepest path of each tree; back-to-back calls queued behind a spin kernel, on a scratch "
@@ -397,9 +404,12 @@ def main():
                                            samp_b, sm_us, traffic.get("spec_tree_softmax_pair")),
         },
     }
-    kvc = time_kv_commit(step, dev, replicas[0]["k"], replicas[0]["v"], stream) if "k" in dev else None
-    if kvc is not None:
-        res["next_rows"] = {"kv_commit": kvc}
+    if "k" in dev and dev.get("block_table") is None:
+        res["next_rows"] = {
+            "kv_commit": time_kv_commit(step, dev, replicas[0]["k"], replicas[0]["v"], stream),
+            # every layer of a 32-layer model (the Llama-3-8B depth) in one call
+            "kv_commit_32_layers": time_kv_commit(step, dev, replicas[0]["k"], replicas[0]["v"], stream, layers=32),
+        }
 
     if not args.no_cpu_baseline:
         import oracle

@@ -239,6 +239,12 @@ int spec_accept_path(const int32_t* accepted_child, const int32_t* term_token, c
  * the root stays at ctx.  Sources are read before destinations are written, so
  * overlapping moves are exact.
  *   k, v          the cache of spec_tree_attention (contiguous or paged), in place
+ *   n_layers      how many layers' caches to commit (>= 1): layer l's K and V start
+ *                 at k + l * layer_stride and v + l * layer_stride elements; every
+ *                 layer holds the tree at the same positions and shares block_table
+ *   layer_stride  elements between consecutive layers (ignored for one layer; at
+ *                 least one layer's size, batch * kv_capacity * hkv * head_dim or
+ *                 n_pages * page_size * hkv * head_dim, so the layers never overlap)
  *   block_table   paged: pages whose slots hold only positions in
  *                 [new_len, ctx + n_nodes) are released: their entries become -1
  *   new_len [batch]      ctx + 1 + L, the committed length; -1 for a request that
@@ -247,13 +253,16 @@ int spec_accept_path(const int32_t* accepted_child, const int32_t* term_token, c
  *                        position outside the cache, a bad page id), which is left
  *                        untouched (SPEC_ERR_BAD_INPUT in status for the invalid ones)
  *   freed_pages [batch, 64]  released page ids in slot order, -1 padded (nullable)
- * One workgroup per request; the moved bytes are L * hkv * head_dim * elem * 2,
- * read and written once.
+ * One workgroup per (request, layer), plus a per-request release kernel when
+ * n_layers > 1; the moved bytes are n_layers * L * hkv * head_dim * elem * 2, read
+ * and written once.
  * Host errors: null required pointers, batch < 1, n_max outside [1, 64], hkv < 1,
- * a block table with page_size < 1 or n_pages < 1; SPEC_ERR_UNSUPPORTED for another
+ * n_layers outside [1, 65535], a layer_stride below one layer's size, a block table
+ * with page_size < 1 or n_pages < 1; SPEC_ERR_UNSUPPORTED for another
  * dtype, head_dim not 64/128, or hkv * head_dim * element size above 32 KiB.
  */
-int spec_tree_kv_commit(void* k, void* v, int32_t dtype, int32_t* block_table, int32_t page_size,
+int spec_tree_kv_commit(void* k, void* v, int32_t dtype, int32_t n_layers, int64_t layer_stride,
+                        int32_t* block_table, int32_t page_size,
                         int32_t kv_capacity, int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes,
                         const int32_t* path_nodes, const int32_t* accept_len, int32_t batch, int32_t n_max,
                         int32_t hkv, int32_t head_dim, int32_t* new_len, int32_t* freed_pages, int32_t* status,

@@ -182,7 +182,9 @@ def accept_path(accepted_child, term_token, tokens, n_nodes):
 
 def kv_commit(k, v, ctx_len, n_nodes, path_nodes, accept_len, block_table=None, page_size=0, n_pages=0):
     """Returns (k, v, new_len, freed, block_table) after the commit; the inputs are not
-    modified.  k, v: numpy arrays (float32, or uint16 bf16 bit patterns)."""
+    modified.  k, v: numpy arrays (float32, or uint16 bf16 bit patterns), one layer's
+    cache ([B, cap, hkv, d] or a paged pool [P, page, hkv, d]) or every layer's stacked
+    on a leading axis."""
     k = np.array(k, copy=True, order="C")
     v = np.array(v, copy=True, order="C")
     assert k.dtype == v.dtype and k.dtype in (np.float32, np.uint16)
@@ -193,11 +195,14 @@ def kv_commit(k, v, ctx_len, n_nodes, path_nodes, accept_len, block_table=None, 
     accept_len = _c(accept_len, np.int32)
     B, n_max = path_nodes.shape
     hkv, d = k.shape[-2], k.shape[-1]
+    assert k.ndim in (4, 5) and k.shape == v.shape
+    n_layers, stride = (k.shape[0], k[0].size) if k.ndim == 5 else (1, 0)
     bt = None if block_table is None else np.array(block_table, np.int32, copy=True, order="C")
-    cap = k.shape[1] if bt is None else bt.shape[1]
+    cap = k.shape[-3] if bt is None else bt.shape[1]
     new_len = np.zeros(B, np.int32)
     freed = np.zeros((B, 64), np.int32)
-    rc = lib().oracle_kv_commit(_p(k), _p(v), ctypes.c_int32(elem), _p(bt), ctypes.c_int32(page_size),
+    rc = lib().oracle_kv_commit(_p(k), _p(v), ctypes.c_int32(elem), ctypes.c_int32(n_layers), ctypes.c_int64(stride),
+                                _p(bt), ctypes.c_int32(page_size),
                                 ctypes.c_int32(cap), ctypes.c_int32(n_pages), _p(ctx_len), _p(n_nodes),
                                 _p(path_nodes), _p(accept_len), ctypes.c_int32(B), ctypes.c_int32(n_max),
                                 ctypes.c_int32(hkv), ctypes.c_int32(d), _p(new_len), _p(freed))

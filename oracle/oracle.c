@@ -648,13 +648,18 @@ int oracle_accept_path(const int32_t* accepted_child, const int32_t* term_token,
 /* A request with accept_len < 0, an invalid path or a position outside the      */
 /* cache is left untouched with new_len = -1 (ORC_EDATA is returned if any).     */
 /* elem = bytes per element (2 for bf16, 4 for fp32); k, v in the layouts of O2. */
+/* Reading for a model with several layers: every layer's cache holds the tree    */
+/* at the same positions, so layer l (at k, v + l * layer_stride elements) takes  */
+/* the same moves; the page table is shared and released once.                   */
 /* ------------------------------------------------------------------------- */
-int oracle_kv_commit(void* k, void* v, int32_t elem, int32_t* block_table, int32_t page_size, int32_t kv_capacity,
+int oracle_kv_commit(void* k, void* v, int32_t elem, int32_t n_layers, int64_t layer_stride, int32_t* block_table,
+                     int32_t page_size, int32_t kv_capacity,
                      int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes, const int32_t* path_nodes,
                      const int32_t* accept_len, int32_t batch, int32_t n_max, int32_t hkv, int32_t d,
                      int32_t* new_len, int32_t* freed) {
   if (!k || !v || !ctx_len || !n_nodes || !path_nodes || !accept_len || !new_len || !freed) return ORC_EARG;
   if (elem != 2 && elem != 4) return ORC_EARG;
+  if (n_layers < 1 || (n_layers > 1 && layer_stride < 1)) return ORC_EARG;
   const size_t row = (size_t)d * (size_t)elem; /* bytes of one (position, head) vector */
   unsigned char* tmp = (unsigned char*)malloc((size_t)2 * n_max * hkv * row);
   if (!tmp) return ORC_ENOMEM;
@@ -676,20 +681,24 @@ int oracle_kv_commit(void* k, void* v, int32_t elem, int32_t* block_table, int32
       rc = ORC_EDATA;
       continue;
     }
-    /* read every source first ... */
-    for (int32_t i = 1; i <= L; ++i)
-      for (int32_t g = 0; g < hkv; ++g) {
-        const int64_t off = kv_offset(b, ctx + path[i], g, block_table, page_size, kv_capacity, n_pages, hkv, d);
-        memcpy(tmp + ((size_t)(2 * i) * hkv + g) * row, (unsigned char*)k + off * elem, row);
-        memcpy(tmp + ((size_t)(2 * i + 1) * hkv + g) * row, (unsigned char*)v + off * elem, row);
-      }
-    /* ... then write every destination */
-    for (int32_t i = 1; i <= L; ++i)
-      for (int32_t g = 0; g < hkv; ++g) {
-        const int64_t off = kv_offset(b, ctx + i, g, block_table, page_size, kv_capacity, n_pages, hkv, d);
-        memcpy((unsigned char*)k + off * elem, tmp + ((size_t)(2 * i) * hkv + g) * row, row);
-        memcpy((unsigned char*)v + off * elem, tmp + ((size_t)(2 * i + 1) * hkv + g) * row, row);
-      }
+    for (int32_t l = 0; l < n_layers; ++l) {
+      unsigned char* lk = (unsigned char*)k + (size_t)l * (size_t)layer_stride * elem;
+      unsigned char* lv = (unsigned char*)v + (size_t)l * (size_t)layer_stride * elem;
+      /* read every source first ... */
+      for (int32_t i = 1; i <= L; ++i)
+        for (int32_t g = 0; g < hkv; ++g) {
+          const int64_t off = kv_offset(b, ctx + path[i], g, block_table, page_size, kv_capacity, n_pages, hkv, d);
+          memcpy(tmp + ((size_t)(2 * i) * hkv + g) * row, lk + off * elem, row);
+          memcpy(tmp + ((size_t)(2 * i + 1) * hkv + g) * row, lv + off * elem, row);
+        }
+      /* ... then write every destination */
+      for (int32_t i = 1; i <= L; ++i)
+        for (int32_t g = 0; g < hkv; ++g) {
+          const int64_t off = kv_offset(b, ctx + i, g, block_table, page_size, kv_capacity, n_pages, hkv, d);
+          memcpy(lk + off * elem, tmp + ((size_t)(2 * i) * hkv + g) * row, row);
+          memcpy(lv + off * elem, tmp + ((size_t)(2 * i + 1) * hkv + g) * row, row);
+        }
+    }
     new_len[b] = ctx + 1 + L;
     if (block_table) { /* release the pages left holding only freed positions */
       int32_t* tab = block_table + (int64_t)b * kv_capacity;

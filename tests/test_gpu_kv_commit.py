@@ -72,11 +72,11 @@ def _paths(rng, n_nodes, n_max, kinds):
     return path, al
 
 
-@pytest.mark.parametrize("bf16,paged,d,hkv,page", [
-    (True, False, 128, 8, 0), (False, False, 64, 4, 0), (True, True, 128, 8, 16), (False, True, 64, 2, 1),
-    (True, True, 64, 4, 7)])
-def test_kv_commit_parity(bf16, paged, d, hkv, page):
-    say("kv_commit", bf16, paged, d, hkv, page)
+@pytest.mark.parametrize("bf16,paged,d,hkv,page,layers", [
+    (True, False, 128, 8, 0, 1), (False, False, 64, 4, 0, 1), (True, True, 128, 8, 16, 1), (False, True, 64, 2, 1, 1),
+    (True, True, 64, 4, 7, 1), (True, False, 128, 8, 0, 5), (False, True, 64, 2, 3, 3)])
+def test_kv_commit_parity(bf16, paged, d, hkv, page, layers):
+    say("kv_commit", bf16, paged, d, hkv, page, layers)
     rng = np.random.default_rng(d + hkv + page)
     Bn, n_max = 7, 40
     n_nodes = rng.integers(1, n_max + 1, size=Bn).astype(np.int32)
@@ -99,6 +99,8 @@ def test_kv_commit_parity(bf16, paged, d, hkv, page):
     else:
         bt, n_pages, cap = None, 0, int(ctx.max()) + n_max + 5
         shape = (Bn, cap, hkv, d)
+    if layers > 1:  # every layer's cache, stacked on a leading axis
+        shape = (layers,) + shape
     k = rng.standard_normal(shape, dtype=np.float32)
     v = rng.standard_normal(shape, dtype=np.float32)
     if bf16:

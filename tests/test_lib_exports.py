@@ -127,24 +127,30 @@ def test_host_errors_reject(lib):
 
 def test_host_errors_kv_commit(lib):
     f = lib.spec_tree_kv_commit
-    #       k  v  dt bt    ps cap np ctx nn path al B  nmax hkv D    nl fr    st    s
-    args = [P, P, 1, None, 0, 100, 0, P, P, P, P, 1, 8, 8, 128, P, None, None, None]
-    for i, bad in ((0, None), (7, None), (15, None)):
+    #       k  v  dt nly lstr  bt    ps cap np ctx nn path al B  nmax hkv D    nl fr    st    s
+    args = [P, P, 1, 1,  0,    None, 0, 100, 0, P, P, P, P, 1, 8, 8, 128, P, None, None, None]
+    for i, bad in ((0, None), (9, None), (17, None)):
         a = list(args)
         a[i] = bad
         assert f(*a) == -1
     a = list(args)
-    a[12] = 65  # n_max
+    a[14] = 65  # n_max
     assert f(*a) == -1
     a = list(args)
-    a[3], a[4] = P, 0  # block table without a page size
+    a[5], a[6] = P, 0  # block table without a page size
     assert f(*a) == -1
     a = list(args)
-    a[14] = 96  # head_dim
+    a[3] = 0  # no layers
+    assert f(*a) == -1
+    a = list(args)
+    a[3], a[4] = 2, 100 * 8 * 128 - 1  # layers that would overlap (one layer is 100 x 8 x 128 elements)
+    assert f(*a) == -1
+    a = list(args)
+    a[16] = 96  # head_dim
     assert f(*a) == -2
     a = list(args)
     a[2] = 5  # dtype
     assert f(*a) == -2
     a = list(args)
-    a[2], a[13] = 0, 65  # 65 heads x 128 fp32 above the 32 KiB staged per row
+    a[2], a[15] = 0, 65  # 65 heads x 128 fp32 above the 32 KiB staged per row
     assert f(*a) == -2

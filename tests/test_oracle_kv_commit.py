@@ -77,3 +77,35 @@ def test_paged_moves_and_page_release():
     # new_len 5 -> slots 0..2 stay; slot 3 (positions 6, 7) is released
     assert nt.tolist() == [[4, 0, 5, -1]]
     assert freed[0, 0] == 2 and (freed[0, 1:] == -1).all()
+
+
+def test_every_layer_takes_the_same_moves():
+    # three layers stacked on a leading axis, each with distinct values (layer l adds 1e5 l)
+    k1, _ = _cache(1, 10, 2, 3)
+    k = np.stack([k1 + 1e5 * l for l in range(3)]).astype(np.float32)
+    v = -k
+    nk, nv, new_len, _, _ = oracle.kv_commit(k, v, [3], [5], [[0, 2, 4, -1, -1]], [2])
+    assert new_len.tolist() == [6]
+    exp = k.copy()
+    for l in range(3):
+        exp[l, 0, 4] = k[l, 0, 5]
+        exp[l, 0, 5] = k[l, 0, 7]
+    assert np.array_equal(nk, exp) and np.array_equal(nv, -exp)
+
+
+def test_layers_share_one_page_release():
+    page, hkv, d = 2, 1, 2
+    pool, _ = _cache(1, 6 * page, hkv, d)
+    pool = pool.reshape(6, page, hkv, d)
+    k = np.stack([pool, pool + 1e5]).astype(np.float32)  # two layers
+    table = np.array([[4, 0, 5, 2]], np.int32)
+    nk, nv, new_len, freed, nt = oracle.kv_commit(k, -k, [3], [5], [[0, 3, -1, -1, -1]], [1],
+                                                  block_table=table, page_size=page, n_pages=6)
+    assert new_len.tolist() == [5]
+    for l in range(2):  # position 4 <- node 3 (position 6) in both layers, under the original table
+        assert np.array_equal(nk[l, table[0, 2], 0], k[l, table[0, 3], 0])
+    changed = np.zeros(k.shape[:3], bool)
+    changed[:, table[0, 2], 0] = True
+    assert np.array_equal(nk[~changed], k[~changed]) and np.array_equal(nv, -nk)
+    assert nt.tolist() == [[4, 0, 5, -1]]  # slot 3 released once, not once per layer
+    assert freed[0, 0] == 2 and (freed[0, 1:] == -1).all()

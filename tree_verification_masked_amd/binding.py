@@ -49,8 +49,8 @@ _SIGNATURES = {
     "spec_tree_reject_sample": [_VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _I32,
                                 _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
-    "spec_tree_kv_commit": [_VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
-                            _VP, _VP, _VP, _VP],
+    "spec_tree_kv_commit": [_VP, _VP, _I32, _I32, _I64, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
+                            _I32, _VP, _VP, _VP, _VP],
     "spec_tree_version": [],
 }
 _RESTYPES = {
@@ -277,7 +277,9 @@ def spec_accept_path(accepted_child, term_token, tokens, n_nodes, path_nodes, ou
 
 def spec_tree_kv_commit(k, v, ctx_len, n_nodes, path_nodes, accept_len, new_len, freed_pages=None, *,
                         block_table=None, page_size=0, n_pages=0, status=None, stream=None):
-    """In place on k, v (and block_table when paged)."""
+    """In place on k, v (and block_table when paged).  k, v: one layer's cache
+    ([B, cap, hkv, D] or the paged pool [P, page, hkv, D]), or every layer's, stacked
+    on a leading layer axis ([layers, ...]); the layers share the page table."""
     if k.dtype == torch.bfloat16:
         dtype = SPEC_BF16
     elif k.dtype == torch.float32:
@@ -287,15 +289,23 @@ def spec_tree_kv_commit(k, v, ctx_len, n_nodes, path_nodes, accept_len, new_len,
     _check(v, k.dtype, tuple(k.shape), "v")
     B, n_max = path_nodes.shape
     hkv, D = k.shape[-2], k.shape[-1]
+    if k.dim() == 5:
+        n_layers, layer_stride = k.shape[0], k[0].numel()
+        per_layer = k.shape[1:]
+    elif k.dim() == 4:
+        n_layers, layer_stride, per_layer = 1, 0, k.shape
+    else:
+        raise ValueError("k/v must be [..., hkv, D] with 4 dims, or 5 with a leading layer axis")
     for t, nm in ((path_nodes, "path_nodes"),):
         _check(t, torch.int32, (B, n_max), nm)
     for t, nm in ((ctx_len, "ctx_len"), (n_nodes, "n_nodes"), (accept_len, "accept_len"), (new_len, "new_len")):
         _check(t, torch.int32, (B,), nm)
     _check(freed_pages, torch.int32, (B, 64), "freed_pages")
     _check(status, torch.int32, (1,), "status")
-    cap = k.shape[1] if block_table is None else block_table.shape[1]
+    cap = per_layer[1] if block_table is None else block_table.shape[1]
     if block_table is not None:
         _check(block_table, torch.int32, (B, cap), "block_table")
-    _call("spec_tree_kv_commit", _ptr(k), _ptr(v), dtype, _ptr(block_table), int(page_size), int(cap), int(n_pages),
+    _call("spec_tree_kv_commit", _ptr(k), _ptr(v), dtype, int(n_layers), int(layer_stride), _ptr(block_table),
+          int(page_size), int(cap), int(n_pages),
           _ptr(ctx_len), _ptr(n_nodes), _ptr(path_nodes), _ptr(accept_len), B, n_max, hkv, D, _ptr(new_len),
           _ptr(freed_pages), _ptr(status), _stream(stream))

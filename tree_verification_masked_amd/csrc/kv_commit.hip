@@ -11,8 +11,11 @@
 // becomes ctx + 1 + L.  Since path[i] >= i, the destination of row i is never the
 // source of a later row, so rows can be moved in increasing order in chunks; within
 // a chunk every source is staged in LDS before any destination is written.  One
-// workgroup per request moves all its KV heads (the accepted rows are few), then
-// releases the pages that now hold only freed positions.
+// workgroup per (request, layer) moves all the layer's KV heads (the accepted rows
+// are few); every layer's cache holds the tree at the same positions and shares the
+// page table.  Pages that now hold only freed positions are released once per
+// request, after every layer has read its sources: by the same workgroup when there
+// is one layer, else by a second, per-request kernel on the same stream.
 #include "common.hpp"
 
 namespace spectree {
@@ -23,7 +26,8 @@ constexpr int kMaxFreed = 64;
 
 struct CommitArgs {
   char *k, *v;
-  int32_t elem;  // bytes per element
+  int64_t layer_bytes;  // distance between consecutive layers' caches
+  int32_t elem;         // bytes per element
   int32_t* block_table;
   int32_t page_size, kv_capacity, n_pages;
   const int32_t *ctx_len, *n_nodes, *path_nodes, *accept_len;
@@ -44,39 +48,70 @@ __device__ inline int64_t commit_off(const CommitArgs& a, int b, int t, int g) {
   return row * a.head_dim * a.elem;
 }
 
+// Whether request b's commit is valid: the path must be a walk from the root inside
+// the tree, and every position of the tree must exist in the cache.
+__device__ inline bool commit_valid(const CommitArgs& a, int b) {
+  const int L = a.accept_len[b], n = a.n_nodes[b], ctx = a.ctx_len[b];
+  const int32_t* path = a.path_nodes + (int64_t)b * a.n_max;
+  bool ok = L >= 0 && n >= 1 && n <= a.n_max && L < n && ctx >= 0 && path[0] == 0;
+  for (int i = 1; ok && i <= L; ++i) ok = path[i] > path[i - 1] && path[i] < n;
+  if (ok) {
+    const int64_t end = (int64_t)ctx + n;
+    if (!a.block_table) {
+      ok = end <= a.kv_capacity;
+    } else {
+      ok = end <= (int64_t)a.kv_capacity * a.page_size;
+      for (int s = ctx / a.page_size; ok && s < (int)((end + a.page_size - 1) / a.page_size); ++s) {
+        const int pg = a.block_table[(int64_t)b * a.kv_capacity + s];
+        ok = pg >= 0 && pg < a.n_pages;
+      }
+    }
+  }
+  return ok;
+}
+
+// The per-request end of a commit (one thread): new length, error report, page
+// release.  Runs only after every layer of the request has read its sources.
+__device__ inline void commit_finish(const CommitArgs& a, int b, bool ok) {
+  const int L = a.accept_len[b], n = a.n_nodes[b], ctx = a.ctx_len[b];
+  if (!ok) {
+    a.new_len[b] = -1;
+    if (L >= 0) report(a.status, SPEC_ERR_BAD_INPUT);  // (accept_len < 0: a request already refused)
+    return;
+  }
+  const int nl = ctx + 1 + L;
+  a.new_len[b] = nl;
+  if (a.block_table) {  // release the pages left holding only freed positions
+    int32_t* tab = a.block_table + (int64_t)b * a.kv_capacity;
+    const int first = (nl + a.page_size - 1) / a.page_size, end = (ctx + n + a.page_size - 1) / a.page_size;
+    int j = 0;
+    for (int s = first; s < end; ++s) {
+      if (a.freed) a.freed[(int64_t)b * kMaxFreed + j] = tab[s];
+      ++j;
+      tab[s] = -1;
+    }
+  }
+}
+
+// grid (batch, layers).  FINISH: one layer, so the same workgroup ends the request.
+template <bool FINISH>
 __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitArgs a) {
   __shared__ __attribute__((aligned(16))) int4 s_buf[kCommitLds / 16];
   __shared__ int s_ok;
   const int tid = threadIdx.x, b = blockIdx.x;
-  const int L = a.accept_len[b], n = a.n_nodes[b], ctx = a.ctx_len[b];
+  const int L = a.accept_len[b], ctx = a.ctx_len[b];
   const int32_t* path = a.path_nodes + (int64_t)b * a.n_max;
-  if (a.freed)
+  if (FINISH && a.freed)
     for (int j = tid; j < kMaxFreed; j += kCommitThreads) a.freed[(int64_t)b * kMaxFreed + j] = -1;
   if (tid == 0) {
-    // the path must be a walk from the root inside the tree, and every position
-    // of the tree must exist in the cache
-    int ok = L >= 0 && n >= 1 && n <= a.n_max && L < n && ctx >= 0 && path[0] == 0;
-    for (int i = 1; ok && i <= L; ++i) ok = path[i] > path[i - 1] && path[i] < n;
-    if (ok) {
-      const int64_t end = (int64_t)ctx + n;
-      if (!a.block_table) {
-        ok = end <= a.kv_capacity;
-      } else {
-        ok = end <= (int64_t)a.kv_capacity * a.page_size;
-        for (int s = ctx / a.page_size; ok && s < (int)((end + a.page_size - 1) / a.page_size); ++s) {
-          const int pg = a.block_table[(int64_t)b * a.kv_capacity + s];
-          ok = pg >= 0 && pg < a.n_pages;
-        }
-      }
-    }
+    const bool ok = commit_valid(a, b);
     s_ok = ok;
-    if (!ok) {
-      a.new_len[b] = -1;
-      if (L >= 0) report(a.status, SPEC_ERR_BAD_INPUT);  // (accept_len < 0: a request already refused)
-    }
+    if (FINISH && !ok) commit_finish(a, b, false);
   }
   __syncthreads();
   if (!s_ok) return;
+  char* const lk = a.k + (int64_t)blockIdx.y * a.layer_bytes;
+  char* const lv = a.v + (int64_t)blockIdx.y * a.layer_bytes;
   const int pv = a.head_dim * a.elem / 16;       // 16-byte pieces per (position, head) vector
   const int per_row = a.hkv * 2 * pv;            // pieces per accepted row (K and V, every head)
   const int rows_per_chunk = kCommitLds / 16 / per_row;
@@ -86,37 +121,34 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitArgs a)
     for (int x = tid; x < total; x += kCommitThreads) {  // gather the chunk's sources
       const int r = x / per_row, y = x % per_row;
       const int g = y / (2 * pv), kv = (y / pv) & 1, p = y % pv;
-      const char* base = kv ? a.v : a.k;
+      const char* base = kv ? lv : lk;
       s_buf[x] = *reinterpret_cast<const int4*>(base + commit_off(a, b, ctx + path[i0 + r], g) + p * 16);
     }
     __syncthreads();
     for (int x = tid; x < total; x += kCommitThreads) {  // then write its destinations
       const int r = x / per_row, y = x % per_row;
       const int g = y / (2 * pv), kv = (y / pv) & 1, p = y % pv;
-      char* base = kv ? a.v : a.k;
+      char* base = kv ? lv : lk;
       *reinterpret_cast<int4*>(base + commit_off(a, b, ctx + i0 + r, g) + p * 16) = s_buf[x];
     }
     __syncthreads();  // the buffer is reused and the next chunk's sources are read after these writes
   }
-  if (tid == 0) {
-    const int nl = ctx + 1 + L;
-    a.new_len[b] = nl;
-    if (a.block_table) {  // release the pages left holding only freed positions
-      int32_t* tab = a.block_table + (int64_t)b * a.kv_capacity;
-      const int first = (nl + a.page_size - 1) / a.page_size, end = (ctx + n + a.page_size - 1) / a.page_size;
-      int j = 0;
-      for (int s = first; s < end; ++s) {
-        if (a.freed) a.freed[(int64_t)b * kMaxFreed + j] = tab[s];
-        ++j;
-        tab[s] = -1;
-      }
-    }
-  }
+  if (FINISH && tid == 0) commit_finish(a, b, true);
+}
+
+// After the moves of every layer: one workgroup per request.
+__global__ __launch_bounds__(64) void kv_commit_finish_kernel(CommitArgs a) {
+  const int b = blockIdx.x;
+  if (a.freed)
+    for (int j = threadIdx.x; j < kMaxFreed; j += 64) a.freed[(int64_t)b * kMaxFreed + j] = -1;
+  __syncthreads();
+  if (threadIdx.x == 0) commit_finish(a, b, commit_valid(a, b));
 }
 
 }  // namespace spectree
 
-extern "C" int spec_tree_kv_commit(void* k, void* v, int32_t dtype, int32_t* block_table, int32_t page_size,
+extern "C" int spec_tree_kv_commit(void* k, void* v, int32_t dtype, int32_t n_layers, int64_t layer_stride,
+                                   int32_t* block_table, int32_t page_size,
                                    int32_t kv_capacity, int32_t n_pages, const int32_t* ctx_len,
                                    const int32_t* n_nodes, const int32_t* path_nodes, const int32_t* accept_len,
                                    int32_t batch, int32_t n_max, int32_t hkv, int32_t head_dim, int32_t* new_len,
@@ -124,14 +156,21 @@ extern "C" int spec_tree_kv_commit(void* k, void* v, int32_t dtype, int32_t* blo
   using namespace spectree;
   if (!k || !v || !ctx_len || !n_nodes || !path_nodes || !accept_len || !new_len) return SPEC_ERR_INVALID_ARG;
   if (batch < 1 || n_max < 1 || n_max > 64 || hkv < 1 || kv_capacity < 1) return SPEC_ERR_INVALID_ARG;
+  if (n_layers < 1 || n_layers > 65535) return SPEC_ERR_INVALID_ARG;
   if (block_table && (page_size < 1 || n_pages < 1)) return SPEC_ERR_INVALID_ARG;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return SPEC_ERR_UNSUPPORTED;
   const int elem = dtype == SPEC_F32 ? 4 : 2;
   if ((int64_t)hkv * head_dim * elem * 2 > kCommitLds) return SPEC_ERR_UNSUPPORTED;  // one row must fit the stage
+  if (n_layers > 1) {  // the layers' caches must not overlap
+    const int64_t layer_elems = block_table ? (int64_t)n_pages * page_size * hkv * head_dim
+                                            : (int64_t)batch * kv_capacity * hkv * head_dim;
+    if (layer_stride < layer_elems) return SPEC_ERR_INVALID_ARG;
+  }
   CommitArgs a;
   a.k = (char*)k;
   a.v = (char*)v;
+  a.layer_bytes = n_layers > 1 ? layer_stride * elem : 0;
   a.elem = elem;
   a.block_table = block_table;
   a.page_size = page_size;
@@ -148,7 +187,16 @@ extern "C" int spec_tree_kv_commit(void* k, void* v, int32_t dtype, int32_t* blo
   a.new_len = new_len;
   a.freed = freed_pages;
   a.status = status;
-  hipLaunchKernelGGL(kv_commit_kernel, dim3((unsigned)batch), dim3(kCommitThreads), 0, (hipStream_t)stream, a);
+  if (n_layers == 1) {
+    hipLaunchKernelGGL(kv_commit_kernel<true>, dim3((unsigned)batch), dim3(kCommitThreads), 0, (hipStream_t)stream,
+                       a);
+    SPEC_LAUNCH_CHECK();
+    return SPEC_OK;
+  }
+  hipLaunchKernelGGL(kv_commit_kernel<false>, dim3((unsigned)batch, (unsigned)n_layers), dim3(kCommitThreads), 0,
+                     (hipStream_t)stream, a);
+  SPEC_LAUNCH_CHECK();
+  hipLaunchKernelGGL(kv_commit_finish_kernel, dim3((unsigned)batch), dim3(64), 0, (hipStream_t)stream, a);
   SPEC_LAUNCH_CHECK();
   return SPEC_OK;
 }
