@@ -6,7 +6,9 @@ the library and its Python binding never do.  The arithmetic lives in ``oracle.c
 (plain C, double precision, scalar loops); this module only marshals numpy arrays
 into it with ctypes.  It shares no code with the GPU path.
 
-Functions and the passages they follow are documented in ``oracle.c``.
+Functions and the passages they follow are documented in ``oracle.c``.  The
+draft-tree construction (EAGLE-2 expand, rerank and flatten) is the numpy module
+``oracle.tree_build``.
 """
 from __future__ import annotations
 
