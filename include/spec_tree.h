@@ -9,6 +9,9 @@
  *   spec_tree_reject_sample   lossless tree rejection sampling (or greedy at T = 0)
  *   spec_accept_path          longest accepted root-to-leaf path plus the bonus token
  *   spec_tree_kv_commit       keep the accepted path's K/V, free the rejected tree slots
+ *   spec_tree_build_init      start EAGLE-2 draft trees at their roots
+ *   spec_tree_expand          one EAGLE-2 expand round from the frontier's draft rows
+ *   spec_tree_rerank          keep the top-N nodes by path value, flattened breadth-first
  *
  * Sources.  "EAGLE 演化史 (1 → 2 → 3) 与 DFlash 的回答" (zhangshuibai.github.io paper
  * notes), section "Tree Verification 详解": part B (BFS flattening and the
@@ -267,6 +270,82 @@ int spec_tree_kv_commit(void* k, void* v, int32_t dtype, int32_t n_layers, int64
                         const int32_t* path_nodes, const int32_t* accept_len, int32_t batch, int32_t n_max,
                         int32_t hkv, int32_t head_dim, int32_t* new_len, int32_t* freed_pages, int32_t* status,
                         void* stream);
+
+/*
+ * Draft-tree construction, EAGLE-2 style (tree notes, part E.2: a node's value is
+ * the product of the draft confidences on its root path; expand rounds grow the
+ * frontier nodes of largest value by their top-k draft tokens; the rerank keeps the
+ * N nodes of largest value, a connected subtree since value never grows along a
+ * path; EAGLE family page, "EAGLE-2: context-aware dynamic trees": the kept nodes
+ * are flattened with a tree mask for verification).  The output of
+ * spec_tree_rerank is the parent[] / tokens / n_nodes input of the verify step.
+ *
+ * State of the trees under construction, caller-owned device arrays ([batch, cap]
+ * unless stated), indexed by node id (root = 0; children get consecutive ids as
+ * they are created: expanded nodes in frontier order, each node's children in top-k
+ * order):
+ *   cand_parent int32    parent id (-1 for the root)
+ *   cand_token int32     token
+ *   cand_path uint64     breadth-first key: depth in bits 63..60, then for
+ *                        d = 1..depth the node's ancestor at depth d's rank among
+ *                        its siblings (top-k order) in bits (63 - 4d)..(60 - 4d)
+ *   cand_value double    product of the confidences on the root path (root 1)
+ *   cand_conf double     the node's own confidence (draft probability of its token)
+ *   cand_count [batch]   nodes so far
+ *   frontier [batch, max_frontier], frontier_count [batch]
+ *                        the nodes the next expand round grows, in the order
+ *                        its draft rows must be given (value desc, ties to the
+ *                        lower id); frontier_count 0 = nothing to grow
+ * Limits: cap <= 1024, max_frontier <= 16, top_k <= 16, depth <= 15.
+ */
+int spec_tree_build_init(const int32_t* root_token, int32_t batch, int32_t cap, int32_t max_frontier,
+                         int32_t* cand_parent, int32_t* cand_token, uint64_t* cand_path, double* cand_value,
+                         double* cand_conf, int32_t* cand_count, int32_t* frontier, int32_t* frontier_count,
+                         void* stream);
+
+/*
+ * One expand round.  draft_logits [batch, max_frontier, vocab] fp32: row j of
+ * request b is the drafter's logits at node frontier[b][j] (rows j >=
+ * frontier_count[b] are not read).  Each such node gets as children its top_k
+ * tokens by logit (ties to the lower token id), with confidence
+ * c = softmax(row / T_d)[token] (fp32 exponentials summed in fp64; c itself in
+ * fp64) and value = value(node) * c.  The new frontier is the select_k new children
+ * of largest value (ties to the lower id).  One read of every row.
+ * Device errors (SPEC_ERR_BAD_INPUT in status; the request's frontier_count becomes
+ * 0 and nothing is appended): a row with NaN or +inf or only -inf, a frontier entry
+ * that is not an existing node or sits at depth 15, frontier_count above
+ * max_frontier, or more than cap nodes.
+ * Host errors: null pointers; batch < 1; max_frontier outside [1, 16]; top_k
+ * outside [1, 16]; select_k outside [1, max_frontier]; cap outside [1, 1024];
+ * vocab < top_k; T_d not finite and positive; SPEC_ERR_UNSUPPORTED for vocab above
+ * 262144; SPEC_ERR_WORKSPACE for a workspace smaller than
+ * spec_tree_expand_workspace_size(batch, max_frontier, vocab) (0 = bad sizes).
+ */
+size_t spec_tree_expand_workspace_size(int32_t batch, int32_t max_frontier, int32_t vocab);
+int spec_tree_expand(const float* draft_logits, int32_t vocab, float T_d, int32_t batch, int32_t max_frontier,
+                     int32_t top_k, int32_t select_k, int32_t cap, int32_t* cand_parent, int32_t* cand_token,
+                     uint64_t* cand_path, double* cand_value, double* cand_conf, int32_t* cand_count,
+                     int32_t* frontier, int32_t* frontier_count, void* workspace, size_t workspace_bytes,
+                     int32_t* status, void* stream);
+
+/*
+ * Rerank and flatten.  Keeps the root and the n_final - 1 other nodes of largest
+ * value (ties to the shallower node, then the lower id), in breadth-first order:
+ * by depth, then the parent's flattened index, then sibling (top-k) order.
+ *   parent, tokens, cand_id [batch, n_final]  flattened tree (parent[0] = -1;
+ *                        parent[i] < i), its tokens, and each flattened node's id in
+ *                        the state; entries i >= n_nodes[b] are -1
+ *   n_nodes [batch]      min(n_final, cand_count[b])
+ * Device errors: cand_count outside [1, cap] -> n_nodes 0 and SPEC_ERR_BAD_INPUT;
+ * a kept node whose parent is not kept (a state that is not a tree) -> n_nodes 0
+ * and SPEC_ERR_BAD_TREE.
+ * Host errors: null pointers; batch < 1; cap outside [1, 1024]; n_final outside
+ * [1, 64].
+ */
+int spec_tree_rerank(const int32_t* cand_parent, const int32_t* cand_token, const uint64_t* cand_path,
+                     const double* cand_value, const int32_t* cand_count, int32_t batch, int32_t cap,
+                     int32_t n_final, int32_t* parent, int32_t* tokens, int32_t* n_nodes, int32_t* cand_id,
+                     int32_t* status, void* stream);
 
 /* Library version string (static storage). */
 const char* spec_tree_version(void);

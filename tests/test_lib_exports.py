@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding and header disagree"
@@ -154,3 +154,29 @@ def test_host_errors_kv_commit(lib):
     a = list(args)
     a[2], a[15] = 0, 65  # 65 heads x 128 fp32 above the 32 KiB staged per row
     assert f(*a) == -2
+
+
+def test_host_errors_tree_build(lib):
+    f = lib.spec_tree_build_init
+    assert f(P, 1, 1025, 4, P, P, P, P, P, P, P, P, None) == -1  # cap above 1024
+    assert f(P, 1, 64, 17, P, P, P, P, P, P, P, P, None) == -1   # frontier above 16
+    assert f(None, 1, 64, 4, P, P, P, P, P, P, P, P, None) == -1
+    g = lib.spec_tree_expand
+    #       lg V     T    B  R  k  sk cap par tok path val conf cnt fr fc ws wsb      st    s
+    args = [P, 1000, 1.0, 1, 4, 4, 4, 64, P, P, P, P, P, P, P, P, P, 1 << 30, None, None]
+    for i, bad in ((2, 0.0), (2, float("inf")), (5, 17), (5, 0), (6, 5), (1, 3), (7, 2000), (4, 17)):
+        a = list(args)
+        a[i] = bad
+        assert g(*a) == -1, (i, bad)
+    a = list(args)
+    a[1] = 64 * 4096 + 1  # vocabulary above 64 chunks
+    assert g(*a) == -2
+    a = list(args)
+    a[17] = 16
+    assert g(*a) == -5
+    assert binding.spec_tree_expand_workspace_size(1, 4, 1000) > 4 * 16 * 8
+    assert binding.spec_tree_expand_workspace_size(1, 17, 1000) == 0
+    h = lib.spec_tree_rerank
+    assert h(P, P, P, P, P, 1, 64, 65, P, P, P, P, None, None) == -1  # n_final above 64
+    assert h(P, P, P, P, P, 1, 0, 8, P, P, P, P, None, None) == -1
+    assert h(P, P, None, P, P, 1, 64, 8, P, P, P, P, None, None) == -1

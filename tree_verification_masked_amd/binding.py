@@ -51,6 +51,11 @@ _SIGNATURES = {
     "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_kv_commit": [_VP, _VP, _I32, _I32, _I64, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
                             _I32, _VP, _VP, _VP, _VP],
+    "spec_tree_build_init": [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "spec_tree_expand_workspace_size": [_I32, _I32, _I32],
+    "spec_tree_expand": [_VP, _I32, _F32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                         _SZ, _VP, _VP],
+    "spec_tree_rerank": [_VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_version": [],
 }
 _RESTYPES = {
@@ -59,6 +64,7 @@ _RESTYPES = {
     "spec_tree_softmax_workspace_size": _SZ,
     "spec_tree_softmax_pair_workspace_size": _SZ,
     "spec_tree_reject_sample_workspace_size": _SZ,
+    "spec_tree_expand_workspace_size": _SZ,
     "spec_tree_version": ctypes.c_char_p,
 }
 
@@ -309,3 +315,66 @@ def spec_tree_kv_commit(k, v, ctx_len, n_nodes, path_nodes, accept_len, new_len,
           int(page_size), int(cap), int(n_pages),
           _ptr(ctx_len), _ptr(n_nodes), _ptr(path_nodes), _ptr(accept_len), B, n_max, hkv, D, _ptr(new_len),
           _ptr(freed_pages), _ptr(status), _stream(stream))
+
+
+# ---------------------------------------------------------------- draft-tree construction
+# The state of the trees under construction: int32 parent / token, int64 path keys
+# (the uint64 bit patterns), float64 values and confidences, all [B, cap]; int32
+# count [B]; int32 frontier [B, max_frontier] and frontier_count [B].
+
+def spec_tree_expand_workspace_size(batch, max_frontier, vocab) -> int:
+    return int(lib().spec_tree_expand_workspace_size(batch, max_frontier, vocab))
+
+
+def _check_state(cand_parent, cand_token, cand_path, cand_value, cand_conf, cand_count, frontier, frontier_count):
+    B, cap = cand_parent.shape
+    R = frontier.shape[1]
+    _check(cand_parent, torch.int32, (B, cap), "cand_parent")
+    _check(cand_token, torch.int32, (B, cap), "cand_token")
+    _check(cand_path, torch.int64, (B, cap), "cand_path")
+    _check(cand_value, torch.float64, (B, cap), "cand_value")
+    _check(cand_conf, torch.float64, (B, cap), "cand_conf")
+    _check(cand_count, torch.int32, (B,), "cand_count")
+    _check(frontier, torch.int32, (B, R), "frontier")
+    _check(frontier_count, torch.int32, (B,), "frontier_count")
+    return B, cap, R
+
+
+def spec_tree_build_init(root_token, cand_parent, cand_token, cand_path, cand_value, cand_conf, cand_count, frontier,
+                         frontier_count, stream=None):
+    B, cap, R = _check_state(cand_parent, cand_token, cand_path, cand_value, cand_conf, cand_count, frontier,
+                             frontier_count)
+    _check(root_token, torch.int32, (B,), "root_token")
+    _call("spec_tree_build_init", _ptr(root_token), B, cap, R, _ptr(cand_parent), _ptr(cand_token), _ptr(cand_path),
+          _ptr(cand_value), _ptr(cand_conf), _ptr(cand_count), _ptr(frontier), _ptr(frontier_count), _stream(stream))
+
+
+def spec_tree_expand(draft_logits, T_d, top_k, select_k, cand_parent, cand_token, cand_path, cand_value, cand_conf,
+                     cand_count, frontier, frontier_count, workspace, status=None, stream=None):
+    B, cap, R = _check_state(cand_parent, cand_token, cand_path, cand_value, cand_conf, cand_count, frontier,
+                             frontier_count)
+    V = draft_logits.shape[-1]
+    _check(draft_logits, torch.float32, (B, R, V), "draft_logits")
+    _check(workspace, torch.uint8, None, "workspace")
+    _check(status, torch.int32, (1,), "status")
+    _call("spec_tree_expand", _ptr(draft_logits), V, float(T_d), B, R, int(top_k), int(select_k), cap,
+          _ptr(cand_parent), _ptr(cand_token), _ptr(cand_path), _ptr(cand_value), _ptr(cand_conf), _ptr(cand_count),
+          _ptr(frontier), _ptr(frontier_count), _ptr(workspace), workspace.numel(), _ptr(status), _stream(stream))
+
+
+def spec_tree_rerank(cand_parent, cand_token, cand_path, cand_value, cand_count, parent, tokens, n_nodes, cand_id,
+                     status=None, stream=None):
+    B, cap = cand_parent.shape
+    n_final = parent.shape[1]
+    _check(cand_parent, torch.int32, (B, cap), "cand_parent")
+    _check(cand_token, torch.int32, (B, cap), "cand_token")
+    _check(cand_path, torch.int64, (B, cap), "cand_path")
+    _check(cand_value, torch.float64, (B, cap), "cand_value")
+    _check(cand_count, torch.int32, (B,), "cand_count")
+    for t, nm in ((parent, "parent"), (tokens, "tokens"), (cand_id, "cand_id")):
+        _check(t, torch.int32, (B, n_final), nm)
+    _check(n_nodes, torch.int32, (B,), "n_nodes")
+    _check(status, torch.int32, (1,), "status")
+    _call("spec_tree_rerank", _ptr(cand_parent), _ptr(cand_token), _ptr(cand_path), _ptr(cand_value),
+          _ptr(cand_count), B, cap, n_final, _ptr(parent), _ptr(tokens), _ptr(n_nodes), _ptr(cand_id), _ptr(status),
+          _stream(stream))

@@ -1,0 +1,610 @@
+// Draft-tree construction on the GPU: EAGLE-2 expand and rerank.
+//
+// Tree-verification notes (zhangshuibai.github.io), "Tree Verification 详解" part
+// E.2: a node's value is the product of the draft confidences on its root path;
+// each expand round takes the frontier nodes of largest value, and each of them gets
+// the top-k tokens of its draft distribution as children; the rerank keeps the N
+// nodes of largest value, which form a connected subtree because value never grows
+// along a path.  "The EAGLE Family" (consciousengines.com), "EAGLE-2: context-aware
+// dynamic trees": the kept nodes are flattened with a tree mask for verification.
+//
+// Per request the tree under construction lives in caller arrays indexed by node id
+// (parent, token, path key, value in fp64, confidence).  One expand call is one
+// round: the caller has run the drafter on the current frontier and passes one
+// logit row per frontier node.
+//   tb_topk_kernel    one workgroup per (request, frontier row, 4096-token chunk):
+//                     one read of the chunk gives its maximum, its fp64 sum of
+//                     exp((l - m_c) / T_d) and its top-k (logit, token) keys
+//   tb_expand_kernel  one workgroup per request: merges the chunk partials of each
+//                     row (a k-way merge of sorted lists), appends the children with
+//                     value = parent value x confidence, and picks the next frontier
+// The rerank is one workgroup per request: a bitonic sort of every candidate by
+// (value desc, depth asc, id asc) in LDS, the top N - 1 plus the root, then the
+// breadth-first order from each node's path key (depth, then the sibling ranks of
+// its ancestors from the root down), which orders by depth, parent position and
+// sibling order at once.
+#include "common.hpp"
+
+namespace spectree {
+
+constexpr int kTbThreads = 256;
+constexpr int kTbPer = kChunk / kTbThreads;  // 16 logits per thread
+constexpr int kTbMaxK = 16;                  // children per expanded node
+constexpr int kTbMaxFrontier = 16;           // nodes expanded per round
+constexpr int kTbMaxChunks = 64;             // vocabulary up to 64 chunks
+constexpr int kTbMaxCap = 1024;              // candidates per request (sorted in LDS)
+constexpr int kTbMaxDepth = 15;              // path keys hold 15 four-bit sibling ranks
+constexpr int kTbRerankThreads = 512;
+typedef float tb_f32x4 __attribute__((ext_vector_type(4)));
+
+inline size_t tb_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Orderable key of (logit, token): a larger logit gives a larger key, and equal
+// logits give the lower token the larger key.  Key 0 is no token.
+__device__ inline uint64_t tb_key(float x, int t) {
+  uint32_t u = __float_as_uint(x);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)t);
+}
+__device__ inline float tb_key_logit(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+__device__ inline int tb_key_token(uint64_t k) { return (int)(~(uint32_t)k); }
+
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline uint64_t max_dpp_u64(uint64_t v) {
+  const uint64_t o = (uint64_t)dpp_ll<kCtrl, kRowMask>((long long)v, (long long)v);
+  return o > v ? o : v;
+}
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+  v = max_dpp_u64<kDppQuad1032>(v);
+  v = max_dpp_u64<kDppQuad2301>(v);
+  v = max_dpp_u64<kDppHalfMirror>(v);
+  v = max_dpp_u64<kDppMirror>(v);
+  v = max_dpp_u64<kDppBcast15, 0xa>(v);
+  v = max_dpp_u64<kDppBcast31, 0xc>(v);
+  return (uint64_t)lane63_ll((long long)v);
+}
+
+// (value desc, id asc) ordering of candidates and its wave-wide maximum.
+__device__ inline bool tb_better(double v, int i, double ov, int oi) { return ov > v || (ov == v && oi < i); }
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline void best_dpp_vd(double& v, int& i) {
+  const double ov = dpp_d<kCtrl, kRowMask>(v, v);
+  const int oi = dpp_i<kCtrl, kRowMask>(i, i);
+  if (tb_better(v, i, ov, oi)) {
+    v = ov;
+    i = oi;
+  }
+}
+__device__ inline void wave_best_vd(double& v, int& i) {
+  best_dpp_vd<kDppQuad1032>(v, i);
+  best_dpp_vd<kDppQuad2301>(v, i);
+  best_dpp_vd<kDppHalfMirror>(v, i);
+  best_dpp_vd<kDppMirror>(v, i);
+  best_dpp_vd<kDppBcast15, 0xa>(v, i);
+  best_dpp_vd<kDppBcast31, 0xc>(v, i);
+  v = lane63_d(v);
+  i = lane63_i(i);
+}
+
+// This wavefront's LDS writes are visible to its own later LDS reads.
+__device__ inline void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+struct TbArgs {
+  const float* logits;  // [batch, R, vocab]
+  int32_t vocab, nch, R, K, select_k, cap;
+  double inv_t;
+  ExpScale es;
+  int32_t* parent;  // [batch, cap] ...
+  int32_t* token;
+  uint64_t* path;
+  double* value;
+  double* conf;
+  int32_t* count;     // [batch]
+  int32_t* frontier;  // [batch, R]
+  int32_t* fcount;    // [batch]
+  uint64_t* ws_keys;  // [batch, R, nch, kTbMaxK]
+  float* ws_max;      // [batch, R, nch]
+  double* ws_sum;
+  int32_t* ws_bad;
+  int32_t* status;
+};
+
+inline size_t tb_ws_bytes(int64_t batch, int32_t R, int32_t nch) {
+  const size_t n = (size_t)batch * (size_t)R * (size_t)nch;
+  return tb_align(n * kTbMaxK * 8) + tb_align(n * 4) + tb_align(n * 8) + tb_align(n * 4);
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kTbThreads) void tb_topk_kernel(TbArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t blk = blockIdx.x;
+  const int c = (int)(blk % a.nch);
+  const int64_t rowi = blk / a.nch;  // request * R + frontier row
+  const int j = (int)(rowi % a.R), b = (int)(rowi / a.R);
+  if (j >= a.fcount[b]) return;  // no node behind this row this round
+  const float* src = a.logits + rowi * (int64_t)a.vocab;
+  const int c0 = c * kChunk;
+  // element e of a thread is token c0 + ((e >> 2) * kTbThreads + tid) * 4 + (e & 3)
+  float x[kTbPer];
+  if (kVec && c0 + kChunk <= a.vocab) {
+#pragma unroll
+    for (int k = 0; k < kTbPer / 4; ++k) {
+      const tb_f32x4 f =
+          __builtin_nontemporal_load(reinterpret_cast<const tb_f32x4*>(src + c0 + (k * kTbThreads + tid) * 4));
+      x[4 * k + 0] = f[0];
+      x[4 * k + 1] = f[1];
+      x[4 * k + 2] = f[2];
+      x[4 * k + 3] = f[3];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kTbPer; ++e) {
+      const int t = c0 + ((e >> 2) * kTbThreads + tid) * 4 + (e & 3);
+      x[e] = t < a.vocab ? src[t] : -INFINITY;
+    }
+  }
+  float m = -INFINITY;
+  int bad = 0;
+#pragma unroll
+  for (int e = 0; e < kTbPer; ++e) {
+    bad |= is_bad_logit(x[e]) ? 1 : 0;
+    m = fmaxf(m, x[e]);
+  }
+  __shared__ float s_m[kTbThreads / 64];
+  __shared__ int s_b[kTbThreads / 64];
+  __shared__ double s_s[kTbThreads / 64];
+  __shared__ uint64_t s_k[kTbThreads / 64][kTbMaxK];
+  m = wave_max_f(m);
+  bad = wave_or_i(bad);
+  if (lane == 0) {
+    s_m[wid] = m;
+    s_b[wid] = bad;
+  }
+  // this wavefront's top K: K rounds of a wave maximum over the lanes' best keys
+  uint64_t key[kTbPer];
+  uint64_t best = 0;
+#pragma unroll
+  for (int e = 0; e < kTbPer; ++e) {
+    const int t = c0 + ((e >> 2) * kTbThreads + tid) * 4 + (e & 3);
+    key[e] = t < a.vocab ? tb_key(x[e], t) : 0ull;
+    best = key[e] > best ? key[e] : best;
+  }
+  for (int r = 0; r < a.K; ++r) {
+    const uint64_t w = wave_max_u64(best);
+    if (lane == 0) s_k[wid][r] = w;
+    if (best == w) {  // the owner drops it (keys of real tokens are unique)
+      best = 0;
+#pragma unroll
+      for (int e = 0; e < kTbPer; ++e) {
+        key[e] = key[e] == w ? 0ull : key[e];
+        best = key[e] > best ? key[e] : best;
+      }
+    }
+  }
+  __syncthreads();
+  float cm = s_m[0];
+  int cb = s_b[0];
+#pragma unroll
+  for (int w = 1; w < kTbThreads / 64; ++w) {
+    cm = fmaxf(cm, s_m[w]);
+    cb |= s_b[w];
+  }
+  double csum = 0.0;
+  if (cm > -INFINITY) {
+    double acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < kTbPer; ++e) acc += (double)exp_scaled(x[e] - cm, a.es);
+    acc = wave_sum_d(acc);
+    if (lane == 0) s_s[wid] = acc;
+    __syncthreads();
+    csum = s_s[0];
+#pragma unroll
+    for (int w = 1; w < kTbThreads / 64; ++w) csum += s_s[w];
+  }
+  if (wid == 0) {  // merge the four wavefronts' lists into the chunk's
+    uint64_t v = lane < 4 * a.K ? s_k[lane / a.K][lane % a.K] : 0ull;
+    uint64_t mine = 0;
+    for (int r = 0; r < a.K; ++r) {
+      const uint64_t w = wave_max_u64(v);
+      if (lane == r) mine = w;
+      if (v == w) v = 0;
+    }
+    const int64_t slot = rowi * a.nch + c;
+    if (lane < a.K) a.ws_keys[slot * kTbMaxK + lane] = mine;
+    if (lane == 0) {
+      a.ws_max[slot] = cm;
+      a.ws_sum[slot] = csum;
+      a.ws_bad[slot] = cb;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kTbThreads) void tb_expand_kernel(TbArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K = a.K;
+  __shared__ uint64_t s_list[kTbThreads / 64][kTbMaxChunks * kTbMaxK];
+  __shared__ double s_cv[kTbMaxFrontier * kTbMaxK];
+  __shared__ double s_cc[kTbMaxFrontier * kTbMaxK];
+  __shared__ int s_ct[kTbMaxFrontier * kTbMaxK];
+  __shared__ int s_fr[kTbMaxFrontier];
+  __shared__ int s_err;
+  const int fc = a.fcount[b], base = a.count[b];
+  if (fc == 0) return;  // this request is finished (or failed earlier)
+  if (tid == 0) s_err = (fc < 0 || fc > a.R || base < 1 || base > a.cap || fc * K > a.cap - base) ? 1 : 0;
+  if (tid < kTbMaxFrontier) s_fr[tid] = tid < a.R ? a.frontier[(int64_t)b * a.R + tid] : -1;
+  __syncthreads();
+  if (s_err) {
+    if (tid == 0) {
+      report(a.status, SPEC_ERR_BAD_INPUT);
+      a.fcount[b] = 0;
+    }
+    return;
+  }
+  for (int j = wid; j < fc; j += kTbThreads / 64) {
+    const int64_t rowi = (int64_t)b * a.R + j;
+    const int nd = s_fr[j];
+    const bool nd_ok = nd >= 0 && nd < base && (int)(a.path[(int64_t)b * a.cap + nd] >> 60) < kTbMaxDepth;
+    // the row's maximum and exp sum from its chunk partials (lane c: chunk c)
+    float mc = -INFINITY;
+    double sc = 0.0;
+    int bc = 0;
+    if (lane < a.nch) {
+      const int64_t slot = rowi * a.nch + lane;
+      mc = a.ws_max[slot];
+      sc = a.ws_sum[slot];
+      bc = a.ws_bad[slot];
+    }
+    const float M = wave_max_f(mc);
+    const int bad = wave_or_i(bc);
+    double S = (lane < a.nch && mc > -INFINITY) ? sc * exp(((double)mc - (double)M) * a.inv_t) : 0.0;
+    S = wave_sum_d(S);
+    // the row's top K: a K-way merge of the chunks' sorted lists (lane c: chunk c)
+    uint64_t* L = s_list[wid];
+    for (int i = lane; i < a.nch * K; i += 64) {
+      const int cc = i / K, rr = i - cc * K;
+      L[i] = a.ws_keys[(rowi * a.nch + cc) * kTbMaxK + rr];
+    }
+    wave_lds_sync();
+    int h = 0;
+    uint64_t head = lane < a.nch ? L[lane * K] : 0ull;
+    uint64_t mine = 0;
+    for (int r = 0; r < K; ++r) {
+      const uint64_t w = wave_max_u64(head);
+      if (lane == r) mine = w;
+      if (lane < a.nch && head == w) {
+        ++h;
+        head = h < K ? L[lane * K + h] : 0ull;
+      }
+    }
+    if (lane < K) {
+      // confidence = softmax(row / T_d) at the child's token, in fp64 from the merged sum
+      const double cf = exp(((double)tb_key_logit(mine) - (double)M) * a.inv_t) / S;
+      const double pv = nd_ok ? a.value[(int64_t)b * a.cap + nd] : 0.0;
+      s_cv[j * K + lane] = pv * cf;
+      s_cc[j * K + lane] = cf;
+      s_ct[j * K + lane] = tb_key_token(mine);
+    }
+    if (lane == 0 && (bad || !(M > -INFINITY) || !nd_ok)) s_err = 1;
+  }
+  __syncthreads();
+  if (s_err) {
+    if (tid == 0) {
+      report(a.status, SPEC_ERR_BAD_INPUT);
+      a.fcount[b] = 0;
+    }
+    return;
+  }
+  // append the children: ids base + j * K + r (frontier order, then top-k order)
+  const int nnew = fc * K;
+  for (int i = tid; i < nnew; i += kTbThreads) {
+    const int j = i / K, r = i - j * K;
+    const int nd = s_fr[j];
+    const int64_t o = (int64_t)b * a.cap + base + i;
+    const uint64_t pp = a.path[(int64_t)b * a.cap + nd];
+    const int d = (int)(pp >> 60) + 1;
+    a.parent[o] = nd;
+    a.token[o] = s_ct[i];
+    a.value[o] = s_cv[i];
+    a.conf[o] = s_cc[i];
+    a.path[o] = ((uint64_t)d << 60) | (pp & ((1ull << 60) - 1)) | ((uint64_t)r << (60 - 4 * d));
+  }
+  // the next frontier: the select_k new children of largest value (ties to the lower id)
+  if (wid == 0) {
+    double v[kTbMaxFrontier * kTbMaxK / 64];
+    int bi = 0x7fffffff;
+    double bv = -2.0;
+#pragma unroll
+    for (int q = 0; q < kTbMaxFrontier * kTbMaxK / 64; ++q) {
+      const int i = lane + 64 * q;
+      v[q] = i < nnew ? s_cv[i] : -1.0;
+      if (tb_better(bv, bi, v[q], i)) {
+        bv = v[q];
+        bi = i;
+      }
+    }
+    const int sk = min(a.select_k, nnew);
+    int mine = -1;
+    for (int r = 0; r < sk; ++r) {
+      double wv = bv;
+      int wi = bi;
+      wave_best_vd(wv, wi);
+      if (lane == r) mine = wi;
+      if (bi == wi) {  // the owner drops it and finds its next best
+        bv = -2.0;
+        bi = 0x7fffffff;
+#pragma unroll
+        for (int q = 0; q < kTbMaxFrontier * kTbMaxK / 64; ++q) {
+          const int i = lane + 64 * q;
+          if (i == wi) v[q] = -2.0;
+          if (tb_better(bv, bi, v[q], i)) {
+            bv = v[q];
+            bi = i;
+          }
+        }
+      }
+    }
+    if (lane < sk) a.frontier[(int64_t)b * a.R + lane] = base + mine;
+    if (lane == 0) {
+      a.fcount[b] = sk;
+      a.count[b] = base + nnew;
+    }
+  }
+}
+
+__global__ void tb_init_kernel(const int32_t* root_token, int32_t batch, int32_t cap, int32_t R, int32_t* parent,
+                               int32_t* token, uint64_t* path, double* value, double* conf, int32_t* count,
+                               int32_t* frontier, int32_t* fcount) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int64_t o = (int64_t)b * cap;
+  parent[o] = -1;
+  token[o] = root_token[b];
+  path[o] = 0;
+  value[o] = 1.0;
+  conf[o] = 1.0;
+  count[b] = 1;
+  frontier[(int64_t)b * R] = 0;
+  fcount[b] = 1;
+}
+
+struct RrArgs {
+  const int32_t *parent, *token;
+  const uint64_t* path;
+  const double* value;
+  const int32_t* count;
+  int32_t cap, n_final;
+  int32_t *out_parent, *out_token, *out_n, *out_id, *status;
+};
+
+// (value desc, then (depth, id) asc); t packs depth << 10 | id
+__device__ inline bool rr_before(double va, uint32_t ta, double vb, uint32_t tb) {
+  return va > vb || (va == vb && ta < tb);
+}
+
+__global__ __launch_bounds__(kTbRerankThreads) void tb_rerank_kernel(RrArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ double s_v[kTbMaxCap];
+  __shared__ uint32_t s_t[kTbMaxCap];
+  __shared__ int s_pos[kTbMaxCap];
+  __shared__ uint64_t s_key[64];
+  __shared__ int s_sel[64];
+  const int cnt = a.count[b];
+  const int64_t ob = (int64_t)b * a.n_final;
+  if (cnt < 1 || cnt > a.cap) {  // no tree to rank
+    for (int i = tid; i < a.n_final; i += kTbRerankThreads) {
+      a.out_parent[ob + i] = -1;
+      a.out_token[ob + i] = -1;
+      a.out_id[ob + i] = -1;
+    }
+    if (tid == 0) {
+      a.out_n[b] = 0;
+      report(a.status, SPEC_ERR_BAD_INPUT);
+    }
+    return;
+  }
+  const int m = cnt - 1;  // candidates besides the root
+  int P = 2;
+  while (P < m) P <<= 1;
+  const int64_t cb = (int64_t)b * a.cap;
+  for (int i = tid; i < P; i += kTbRerankThreads) {
+    if (i < m) {
+      const int id = i + 1;
+      s_v[i] = a.value[cb + id];
+      s_t[i] = ((uint32_t)(a.path[cb + id] >> 60) << 10) | (uint32_t)id;
+    } else {
+      s_v[i] = -1.0;
+      s_t[i] = 0xffffffffu;
+    }
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < P; i += kTbRerankThreads) {
+        const int l = i ^ jj;
+        if (l > i) {
+          const double vi = s_v[i], vl = s_v[l];
+          const uint32_t ti = s_t[i], tl = s_t[l];
+          const bool up = (i & k) == 0;
+          if (up ? rr_before(vl, tl, vi, ti) : rr_before(vi, ti, vl, tl)) {
+            s_v[i] = vl;
+            s_v[l] = vi;
+            s_t[i] = tl;
+            s_t[l] = ti;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  if (wid != 0) return;
+  // the root and the top n - 1, in breadth-first order by path key
+  const int n = min(a.n_final - 1, m) + 1;
+  int id = -1;
+  uint64_t key = ~0ull;
+  if (lane < n) {
+    id = lane == 0 ? 0 : (int)(s_t[lane - 1] & 0x3ffu);
+    if (id >= cnt) id = 0;  // (only with values that do not order, e.g. NaN: caught below as a repeated key)
+    key = a.path[cb + id];
+  }
+  s_key[lane] = key;
+  s_sel[lane] = -1;
+  wave_lds_sync();
+  int rank = 0;
+  for (int q = 0; q < n; ++q) rank += s_key[q] < key ? 1 : 0;
+  if (lane < n) {
+    s_sel[rank] = id;
+    s_pos[id] = rank;
+  }
+  wave_lds_sync();
+  int bad = 0;
+  if (lane < n) {
+    int idr = s_sel[lane];
+    int pf = -1;
+    if (idr < 0 || idr >= cnt) {  // two kept nodes with one path key: the state is not a valid tree
+      bad = 1;
+      idr = 0;
+    } else if (lane > 0) {
+      const int pp = a.parent[cb + idr];
+      const int pr = (pp >= 0 && pp < cnt) ? s_pos[pp] : -1;
+      if (pr >= 0 && pr < lane && s_sel[pr] == pp)
+        pf = pr;
+      else
+        bad = 1;  // a kept node whose parent was not kept: the state is not a valid tree
+    }
+    a.out_parent[ob + lane] = pf;
+    a.out_token[ob + lane] = a.token[cb + idr];
+    a.out_id[ob + lane] = idr;
+  } else if (lane < a.n_final) {
+    a.out_parent[ob + lane] = -1;
+    a.out_token[ob + lane] = -1;
+    a.out_id[ob + lane] = -1;
+  }
+  bad = wave_or_i(bad);
+  if (lane == 0) {
+    a.out_n[b] = bad ? 0 : n;
+    if (bad) report(a.status, SPEC_ERR_BAD_TREE);
+  }
+}
+
+inline int tb_chunks(int32_t vocab) { return (vocab + kChunk - 1) / kChunk; }
+
+}  // namespace spectree
+
+extern "C" int spec_tree_build_init(const int32_t* root_token, int32_t batch, int32_t cap, int32_t max_frontier,
+                                    int32_t* cand_parent, int32_t* cand_token, uint64_t* cand_path,
+                                    double* cand_value, double* cand_conf, int32_t* cand_count, int32_t* frontier,
+                                    int32_t* frontier_count, void* stream) {
+  using namespace spectree;
+  if (!root_token || !cand_parent || !cand_token || !cand_path || !cand_value || !cand_conf || !cand_count ||
+      !frontier || !frontier_count)
+    return SPEC_ERR_INVALID_ARG;
+  if (batch < 1 || cap < 1 || cap > kTbMaxCap || max_frontier < 1 || max_frontier > kTbMaxFrontier)
+    return SPEC_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(tb_init_kernel, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, (hipStream_t)stream,
+                     root_token, batch, cap, max_frontier, cand_parent, cand_token, cand_path, cand_value, cand_conf,
+                     cand_count, frontier, frontier_count);
+  SPEC_LAUNCH_CHECK();
+  return SPEC_OK;
+}
+
+extern "C" size_t spec_tree_expand_workspace_size(int32_t batch, int32_t max_frontier, int32_t vocab) {
+  using namespace spectree;
+  if (batch < 1 || max_frontier < 1 || max_frontier > kTbMaxFrontier || vocab < 1 ||
+      vocab > kTbMaxChunks * kChunk)
+    return 0;
+  return tb_ws_bytes(batch, max_frontier, tb_chunks(vocab));
+}
+
+extern "C" int spec_tree_expand(const float* draft_logits, int32_t vocab, float T_d, int32_t batch,
+                                int32_t max_frontier, int32_t top_k, int32_t select_k, int32_t cap,
+                                int32_t* cand_parent, int32_t* cand_token, uint64_t* cand_path, double* cand_value,
+                                double* cand_conf, int32_t* cand_count, int32_t* frontier, int32_t* frontier_count,
+                                void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
+  using namespace spectree;
+  if (!draft_logits || !cand_parent || !cand_token || !cand_path || !cand_value || !cand_conf || !cand_count ||
+      !frontier || !frontier_count)
+    return SPEC_ERR_INVALID_ARG;
+  if (batch < 1 || max_frontier < 1 || max_frontier > kTbMaxFrontier || top_k < 1 || top_k > kTbMaxK ||
+      select_k < 1 || select_k > max_frontier || cap < 1 || cap > kTbMaxCap || vocab < top_k)
+    return SPEC_ERR_INVALID_ARG;
+  if (!(T_d > 0.0f) || !isfinite(T_d)) return SPEC_ERR_INVALID_ARG;
+  if (vocab > kTbMaxChunks * kChunk) return SPEC_ERR_UNSUPPORTED;
+  const int nch = tb_chunks(vocab);
+  const size_t need = tb_ws_bytes(batch, max_frontier, nch);
+  if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
+  const int64_t blocks = (int64_t)batch * max_frontier * nch;
+  if (blocks > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+  TbArgs a;
+  a.logits = draft_logits;
+  a.vocab = vocab;
+  a.nch = nch;
+  a.R = max_frontier;
+  a.K = top_k;
+  a.select_k = select_k;
+  a.cap = cap;
+  a.inv_t = 1.0 / (double)T_d;
+  a.es = make_exp_scale(a.inv_t);
+  a.parent = cand_parent;
+  a.token = cand_token;
+  a.path = cand_path;
+  a.value = cand_value;
+  a.conf = cand_conf;
+  a.count = cand_count;
+  a.frontier = frontier;
+  a.fcount = frontier_count;
+  const size_t n = (size_t)batch * max_frontier * nch;
+  char* w = (char*)workspace;
+  a.ws_keys = (uint64_t*)w;
+  w += tb_align(n * kTbMaxK * 8);
+  a.ws_max = (float*)w;
+  w += tb_align(n * 4);
+  a.ws_sum = (double*)w;
+  w += tb_align(n * 8);
+  a.ws_bad = (int32_t*)w;
+  a.status = status;
+  hipStream_t st = (hipStream_t)stream;
+  const bool vec = vocab % 4 == 0 && (((uintptr_t)draft_logits & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL(tb_topk_kernel<true>, dim3((unsigned)blocks), dim3(kTbThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(tb_topk_kernel<false>, dim3((unsigned)blocks), dim3(kTbThreads), 0, st, a);
+  SPEC_LAUNCH_CHECK();
+  hipLaunchKernelGGL(tb_expand_kernel, dim3((unsigned)batch), dim3(kTbThreads), 0, st, a);
+  SPEC_LAUNCH_CHECK();
+  return SPEC_OK;
+}
+
+extern "C" int spec_tree_rerank(const int32_t* cand_parent, const int32_t* cand_token, const uint64_t* cand_path,
+                                const double* cand_value, const int32_t* cand_count, int32_t batch, int32_t cap,
+                                int32_t n_final, int32_t* parent, int32_t* tokens, int32_t* n_nodes,
+                                int32_t* cand_id, int32_t* status, void* stream) {
+  using namespace spectree;
+  if (!cand_parent || !cand_token || !cand_path || !cand_value || !cand_count || !parent || !tokens || !n_nodes ||
+      !cand_id)
+    return SPEC_ERR_INVALID_ARG;
+  if (batch < 1 || cap < 1 || cap > kTbMaxCap || n_final < 1 || n_final > 64) return SPEC_ERR_INVALID_ARG;
+  RrArgs a;
+  a.parent = cand_parent;
+  a.token = cand_token;
+  a.path = cand_path;
+  a.value = cand_value;
+  a.count = cand_count;
+  a.cap = cap;
+  a.n_final = n_final;
+  a.out_parent = parent;
+  a.out_token = tokens;
+  a.out_n = n_nodes;
+  a.out_id = cand_id;
+  a.status = status;
+  hipLaunchKernelGGL(tb_rerank_kernel, dim3((unsigned)batch), dim3(kTbRerankThreads), 0, (hipStream_t)stream, a);
+  SPEC_LAUNCH_CHECK();
+  return SPEC_OK;
+}

@@ -20,6 +20,7 @@ the open interval (0, 1).
 from __future__ import annotations
 
 import math
+import zlib
 
 import numpy as np
 
@@ -190,6 +191,17 @@ def topk_binary_tree(src: RowSource, Td: float, root_token: int):
 
 def chain_tree(n: int):
     return np.arange(-1, n - 1, dtype=np.int32)
+
+
+def path_row(seed: int, path, vocab: int, kind: str = "normal", scale: float = 3.0, noise: float = 1.0):
+    """Draft logits at the tree node whose root path carries the tokens ``path`` (root
+    first), seeded by the path itself, so a node gets the same row whatever order the
+    nodes are visited in.  kind "normal": N(0, scale) + N(0, noise); "student_t":
+    scale * t(3) + N(0, noise)."""
+    key = np.asarray(path, np.int64)
+    r = np.random.default_rng([seed, len(key), zlib.crc32(key.tobytes())])
+    base = r.normal(0.0, scale, vocab) if kind == "normal" else scale * r.standard_t(3.0, vocab)
+    return (base + r.normal(0.0, noise, vocab)).astype(np.float32)
 
 
 def random_tree(rng: np.random.Generator, n: int, max_branch: int = 4, max_depth: int = 8):
