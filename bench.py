@@ -257,6 +257,63 @@ def time_kv_commit(step, dev, k_src, v_src, stream, iters=200, layers=1):
                     "copy after the timed region"}
 
 
+def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60):
+    """EAGLE-2 tree construction on the GPU for the 60-node verify tree: init, six
+    expand rounds (top-10 over a 128256-token vocabulary) and the rerank, with the
+    draft rows of every round already resident (generated once, per node path).  The
+    rows a round reads are its algorithmic bytes."""
+    import torch
+
+    from tree_verification_masked_amd import synth
+    from tree_verification_masked_amd.draft_tree import DraftTree
+
+    dt = DraftTree(1, 1024, k, V)
+    root = torch.tensor([int(np.random.default_rng(seed).integers(V))], dtype=torch.int32, device="cuda")
+    dt.init(root)
+    rounds, row_bytes = [], 0
+    for _ in range(depth):  # one untimed build fixes each round's frontier and rows
+        st = dt.host_state()
+        rows = np.zeros((1, k, V), np.float32)
+        fc = int(st["frontier_count"][0])
+        for j in range(fc):
+            nd, path = int(st["frontier"][0, j]), []
+            while nd >= 0:
+                path.append(int(st["token"][0, nd]))
+                nd = int(st["parent"][0, nd])
+            rows[0, j] = synth.path_row(seed, tuple(path[::-1]), V)
+        rounds.append(torch.from_numpy(rows).cuda())
+        row_bytes += fc * V * 4
+        dt.expand(rounds[-1], 1.0, k)
+    out = dt.rerank(n_final)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out]
+
+    def build():
+        dt.init(root)
+        for r in rounds:
+            dt.expand(r, 1.0, k)
+        dt.rerank(n_final, out=out)
+
+    for _ in range(5):
+        build()
+    torch.cuda.synchronize()
+    prefill()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(iters):
+        build()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / iters
+    assert int(dt.status.item()) == 0 and all(torch.equal(a, b) for a, b in zip(out, ref))
+    return {"call": "spec_tree_build_init + 6 x spec_tree_expand + spec_tree_rerank (1 request)",
+            "workload": f"EAGLE-2 top-{k}, depth {depth}, {n_final} nodes, vocabulary {V}, T_d = 1",
+            "us_per_tree": round(us, 2), "draft_row_bytes": row_bytes,
+            "gbs": round(row_bytes / (us * 1e-6) / 1e9, 1), "iters": iters,
+            "note": "the drafter's rows are inputs (resident); its forward passes are not part of this"}
+
+
 COST_GRID = {"batch": (1, 2, 4, 8), "ctx": (1024, 4096, 16384), "n_nodes": (16, 32, 64)}
 
 
@@ -410,6 +467,7 @@ def main():
             # every layer of a 32-layer model (the Llama-3-8B depth) in one call
             "kv_commit_32_layers": time_kv_commit(step, dev, replicas[0]["k"], replicas[0]["v"], stream, layers=32),
         }
+    res.setdefault("next_rows", {})["tree_build"] = time_tree_build(args.seed)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -34,7 +34,9 @@ constexpr int kTbMaxFrontier = 16;           // nodes expanded per round
 constexpr int kTbMaxChunks = 64;             // vocabulary up to 64 chunks
 constexpr int kTbMaxCap = 1024;              // candidates per request (sorted in LDS)
 constexpr int kTbMaxDepth = 15;              // path keys hold 15 four-bit sibling ranks
-constexpr int kTbRerankThreads = 512;
+constexpr int kTbRerankThreads = kTbMaxCap;  // one candidate per thread
+constexpr int kTbExpandThreads = 64 * kTbMaxFrontier;  // one wavefront per frontier row
+constexpr int kTbCand = 128;                            // threshold candidates ranked directly
 typedef float tb_f32x4 __attribute__((ext_vector_type(4)));
 
 inline size_t tb_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -66,6 +68,28 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
   v = max_dpp_u64<kDppBcast15, 0xa>(v);
   v = max_dpp_u64<kDppBcast31, 0xc>(v);
   return (uint64_t)lane63_ll((long long)v);
+}
+
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline uint32_t max_dpp_u32(uint32_t v) {
+  const uint32_t o = (uint32_t)dpp_i<kCtrl, kRowMask>((int)v, (int)v);
+  return o > v ? o : v;
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max_dpp_u32<kDppQuad1032>(v);
+  v = max_dpp_u32<kDppQuad2301>(v);
+  v = max_dpp_u32<kDppHalfMirror>(v);
+  v = max_dpp_u32<kDppMirror>(v);
+  v = max_dpp_u32<kDppBcast15, 0xa>(v);
+  v = max_dpp_u32<kDppBcast31, 0xc>(v);
+  return (uint32_t)lane63_i((int)v);
+}
+// The same maximum in two 32-bit steps: the high words, then the low words of the
+// lanes that hold the largest high word.
+__device__ inline uint64_t wave_max_u64_2step(uint64_t v) {
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // (value desc, id asc) ordering of candidates and its wave-wide maximum.
@@ -152,108 +176,146 @@ __global__ __launch_bounds__(kTbThreads) void tb_topk_kernel(TbArgs a) {
       x[e] = t < a.vocab ? src[t] : -INFINITY;
     }
   }
-  float m = -INFINITY;
+  float lm = -INFINITY;  // this lane's maximum
   int bad = 0;
 #pragma unroll
   for (int e = 0; e < kTbPer; ++e) {
     bad |= is_bad_logit(x[e]) ? 1 : 0;
-    m = fmaxf(m, x[e]);
+    lm = fmaxf(lm, x[e]);
   }
-  __shared__ float s_m[kTbThreads / 64];
+  __shared__ float s_m[kTbThreads / 64], s_tau[kTbThreads / 64];
   __shared__ int s_b[kTbThreads / 64];
   __shared__ double s_s[kTbThreads / 64];
   __shared__ uint64_t s_k[kTbThreads / 64][kTbMaxK];
-  m = wave_max_f(m);
+  __shared__ uint64_t s_cand[kTbCand];
+  __shared__ int s_cnt;
+  // Threshold: the K-th largest lane maximum of a wavefront.  At least K of its
+  // tokens reach it, so no token below it is in the wavefront's top K, nor below the
+  // largest such threshold in the chunk's.
+  float v = lm, tw = -INFINITY;
+  for (int r = 0; r < a.K; ++r) {
+    tw = wave_max_f(v);
+    const uint64_t holders = __ballot(v == tw);
+    if (lane == __ffsll((long long)holders) - 1) v = -INFINITY;
+  }
+  const float wm = wave_max_f(lm);
   bad = wave_or_i(bad);
   if (lane == 0) {
-    s_m[wid] = m;
+    s_m[wid] = wm;
     s_b[wid] = bad;
+    s_tau[wid] = tw;
   }
-  // this wavefront's top K: K rounds of a wave maximum over the lanes' best keys
-  uint64_t key[kTbPer];
-  uint64_t best = 0;
-#pragma unroll
-  for (int e = 0; e < kTbPer; ++e) {
-    const int t = c0 + ((e >> 2) * kTbThreads + tid) * 4 + (e & 3);
-    key[e] = t < a.vocab ? tb_key(x[e], t) : 0ull;
-    best = key[e] > best ? key[e] : best;
-  }
-  for (int r = 0; r < a.K; ++r) {
-    const uint64_t w = wave_max_u64(best);
-    if (lane == 0) s_k[wid][r] = w;
-    if (best == w) {  // the owner drops it (keys of real tokens are unique)
-      best = 0;
-#pragma unroll
-      for (int e = 0; e < kTbPer; ++e) {
-        key[e] = key[e] == w ? 0ull : key[e];
-        best = key[e] > best ? key[e] : best;
-      }
-    }
-  }
+  if (tid == 0) s_cnt = 0;
   __syncthreads();
-  float cm = s_m[0];
+  float cm = s_m[0], tau = s_tau[0];
   int cb = s_b[0];
 #pragma unroll
   for (int w = 1; w < kTbThreads / 64; ++w) {
     cm = fmaxf(cm, s_m[w]);
+    tau = fmaxf(tau, s_tau[w]);
     cb |= s_b[w];
   }
-  double csum = 0.0;
+  // the chunk's exp sum, and the tokens at or above the threshold as candidates
+  double acc = 0.0;
   if (cm > -INFINITY) {
-    double acc = 0.0;
 #pragma unroll
     for (int e = 0; e < kTbPer; ++e) acc += (double)exp_scaled(x[e] - cm, a.es);
-    acc = wave_sum_d(acc);
-    if (lane == 0) s_s[wid] = acc;
-    __syncthreads();
-    csum = s_s[0];
-#pragma unroll
-    for (int w = 1; w < kTbThreads / 64; ++w) csum += s_s[w];
   }
-  if (wid == 0) {  // merge the four wavefronts' lists into the chunk's
-    uint64_t v = lane < 4 * a.K ? s_k[lane / a.K][lane % a.K] : 0ull;
-    uint64_t mine = 0;
+  acc = wave_sum_d(acc);
+  if (lane == 0) s_s[wid] = acc;
+#pragma unroll
+  for (int e = 0; e < kTbPer; ++e) {
+    const int t = c0 + ((e >> 2) * kTbThreads + tid) * 4 + (e & 3);
+    if (t < a.vocab && x[e] >= tau) {
+      const int pos = atomicAdd(&s_cnt, 1);
+      if (pos < kTbCand) s_cand[pos] = tb_key(x[e], t);
+    }
+  }
+  __syncthreads();
+  double csum = s_s[0];
+#pragma unroll
+  for (int w = 1; w < kTbThreads / 64; ++w) csum += s_s[w];
+  const int C = s_cnt;
+  const int64_t slot = rowi * a.nch + c;
+  if (C <= kTbCand) {
+    // the top K of the candidates by rank (keys are unique)
+    if (wid == 0) {
+      const uint64_t k0 = lane < C ? s_cand[lane] : 0ull, k1 = lane + 64 < C ? s_cand[lane + 64] : 0ull;
+      int r0 = 0, r1 = 0;
+      for (int q = 0; q < C; ++q) {
+        const uint64_t kq = s_cand[q];
+        r0 += kq > k0 ? 1 : 0;
+        r1 += kq > k1 ? 1 : 0;
+      }
+      if (lane < C && r0 < a.K) a.ws_keys[slot * kTbMaxK + r0] = k0;
+      if (lane + 64 < C && r1 < a.K) a.ws_keys[slot * kTbMaxK + r1] = k1;
+      if (lane >= C && lane < a.K) a.ws_keys[slot * kTbMaxK + lane] = 0ull;  // a chunk with fewer tokens than K
+    }
+  } else {
+    // many tokens tie at the threshold (e.g. a row of equal logits): K rounds of a
+    // wave maximum over every wavefront's keys, then over the four lists
+    uint64_t key[kTbPer];
+    uint64_t best = 0;
+#pragma unroll
+    for (int e = 0; e < kTbPer; ++e) {
+      const int t = c0 + ((e >> 2) * kTbThreads + tid) * 4 + (e & 3);
+      key[e] = t < a.vocab ? tb_key(x[e], t) : 0ull;
+      best = key[e] > best ? key[e] : best;
+    }
     for (int r = 0; r < a.K; ++r) {
-      const uint64_t w = wave_max_u64(v);
-      if (lane == r) mine = w;
-      if (v == w) v = 0;
+      const uint64_t w = wave_max_u64(best);
+      if (lane == 0) s_k[wid][r] = w;
+      if (best == w) {  // the owner drops it
+        best = 0;
+#pragma unroll
+        for (int e = 0; e < kTbPer; ++e) {
+          key[e] = key[e] == w ? 0ull : key[e];
+          best = key[e] > best ? key[e] : best;
+        }
+      }
     }
-    const int64_t slot = rowi * a.nch + c;
-    if (lane < a.K) a.ws_keys[slot * kTbMaxK + lane] = mine;
-    if (lane == 0) {
-      a.ws_max[slot] = cm;
-      a.ws_sum[slot] = csum;
-      a.ws_bad[slot] = cb;
+    __syncthreads();
+    if (wid == 0) {
+      uint64_t u = lane < 4 * a.K ? s_k[lane / a.K][lane % a.K] : 0ull;
+      uint64_t mine = 0;
+      for (int r = 0; r < a.K; ++r) {
+        const uint64_t w = wave_max_u64(u);
+        if (lane == r) mine = w;
+        if (u == w) u = 0;
+      }
+      if (lane < a.K) a.ws_keys[slot * kTbMaxK + lane] = mine;
     }
+  }
+  if (tid == 0) {
+    a.ws_max[slot] = cm;
+    a.ws_sum[slot] = csum;
+    a.ws_bad[slot] = cb;
   }
 }
 
-__global__ __launch_bounds__(kTbThreads) void tb_expand_kernel(TbArgs a) {
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+// One wavefront per frontier row (at most 16), all rows at once.
+__global__ __launch_bounds__(kTbExpandThreads) void tb_expand_kernel(TbArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, j = tid >> 6;
   const int K = a.K;
-  __shared__ uint64_t s_list[kTbThreads / 64][kTbMaxChunks * kTbMaxK];
   __shared__ double s_cv[kTbMaxFrontier * kTbMaxK];
   __shared__ double s_cc[kTbMaxFrontier * kTbMaxK];
   __shared__ int s_ct[kTbMaxFrontier * kTbMaxK];
   __shared__ int s_fr[kTbMaxFrontier];
-  __shared__ int s_err;
+  __shared__ uint64_t s_pp[kTbMaxFrontier];
+  __shared__ int s_werr[kTbMaxFrontier];
   const int fc = a.fcount[b], base = a.count[b];
   if (fc == 0) return;  // this request is finished (or failed earlier)
-  if (tid == 0) s_err = (fc < 0 || fc > a.R || base < 1 || base > a.cap || fc * K > a.cap - base) ? 1 : 0;
-  if (tid < kTbMaxFrontier) s_fr[tid] = tid < a.R ? a.frontier[(int64_t)b * a.R + tid] : -1;
-  __syncthreads();
-  if (s_err) {
+  if (fc < 0 || fc > a.R || base < 1 || base > a.cap || fc * K > a.cap - base) {
     if (tid == 0) {
       report(a.status, SPEC_ERR_BAD_INPUT);
       a.fcount[b] = 0;
     }
     return;
   }
-  for (int j = wid; j < fc; j += kTbThreads / 64) {
+  if (j < fc) {
     const int64_t rowi = (int64_t)b * a.R + j;
-    const int nd = s_fr[j];
-    const bool nd_ok = nd >= 0 && nd < base && (int)(a.path[(int64_t)b * a.cap + nd] >> 60) < kTbMaxDepth;
-    // the row's maximum and exp sum from its chunk partials (lane c: chunk c)
+    const int nd = a.frontier[rowi];
+    // every load of the row is issued before any result is needed
     float mc = -INFINITY;
     double sc = 0.0;
     int bc = 0;
@@ -263,40 +325,53 @@ __global__ __launch_bounds__(kTbThreads) void tb_expand_kernel(TbArgs a) {
       sc = a.ws_sum[slot];
       bc = a.ws_bad[slot];
     }
+    // lane c holds chunk c's sorted list (entries past K are not part of it)
+    uint64_t list[kTbMaxK];
+    if (lane < a.nch) {
+      const uint64_t* src = a.ws_keys + (rowi * a.nch + lane) * kTbMaxK;
+#pragma unroll
+      for (int q = 0; q < kTbMaxK; ++q) list[q] = src[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kTbMaxK; ++q)
+      if (lane >= a.nch || q >= K) list[q] = 0ull;
+    const bool nd_in = nd >= 0 && nd < base;
+    const uint64_t pp = nd_in ? a.path[(int64_t)b * a.cap + nd] : 0ull;
+    const double pv = nd_in ? a.value[(int64_t)b * a.cap + nd] : 0.0;
+    const bool nd_ok = nd_in && (int)(pp >> 60) < kTbMaxDepth;
     const float M = wave_max_f(mc);
     const int bad = wave_or_i(bc);
     double S = (lane < a.nch && mc > -INFINITY) ? sc * exp(((double)mc - (double)M) * a.inv_t) : 0.0;
     S = wave_sum_d(S);
-    // the row's top K: a K-way merge of the chunks' sorted lists (lane c: chunk c)
-    uint64_t* L = s_list[wid];
-    for (int i = lane; i < a.nch * K; i += 64) {
-      const int cc = i / K, rr = i - cc * K;
-      L[i] = a.ws_keys[(rowi * a.nch + cc) * kTbMaxK + rr];
-    }
-    wave_lds_sync();
-    int h = 0;
-    uint64_t head = lane < a.nch ? L[lane * K] : 0ull;
+    // the row's top K: a K-way merge of the chunks' sorted lists (keys are unique;
+    // the lane holding the maximum pops its list)
     uint64_t mine = 0;
     for (int r = 0; r < K; ++r) {
-      const uint64_t w = wave_max_u64(head);
+      const uint64_t w = wave_max_u64_2step(list[0]);
       if (lane == r) mine = w;
-      if (lane < a.nch && head == w) {
-        ++h;
-        head = h < K ? L[lane * K + h] : 0ull;
+      if (w != 0ull && list[0] == w) {
+#pragma unroll
+        for (int q = 0; q < kTbMaxK - 1; ++q) list[q] = list[q + 1];
+        list[kTbMaxK - 1] = 0ull;
       }
     }
     if (lane < K) {
       // confidence = softmax(row / T_d) at the child's token, in fp64 from the merged sum
       const double cf = exp(((double)tb_key_logit(mine) - (double)M) * a.inv_t) / S;
-      const double pv = nd_ok ? a.value[(int64_t)b * a.cap + nd] : 0.0;
       s_cv[j * K + lane] = pv * cf;
       s_cc[j * K + lane] = cf;
       s_ct[j * K + lane] = tb_key_token(mine);
     }
-    if (lane == 0 && (bad || !(M > -INFINITY) || !nd_ok)) s_err = 1;
+    if (lane == 0) {
+      s_fr[j] = nd;
+      s_pp[j] = pp;
+      s_werr[j] = (bad || !(M > -INFINITY) || !nd_ok) ? 1 : 0;
+    }
   }
   __syncthreads();
-  if (s_err) {
+  int err = 0;
+  for (int q = 0; q < fc; ++q) err |= s_werr[q];
+  if (err) {
     if (tid == 0) {
       report(a.status, SPEC_ERR_BAD_INPUT);
       a.fcount[b] = 0;
@@ -305,20 +380,19 @@ __global__ __launch_bounds__(kTbThreads) void tb_expand_kernel(TbArgs a) {
   }
   // append the children: ids base + j * K + r (frontier order, then top-k order)
   const int nnew = fc * K;
-  for (int i = tid; i < nnew; i += kTbThreads) {
-    const int j = i / K, r = i - j * K;
-    const int nd = s_fr[j];
+  for (int i = tid; i < nnew; i += kTbExpandThreads) {
+    const int jj = i / K, r = i - jj * K;
     const int64_t o = (int64_t)b * a.cap + base + i;
-    const uint64_t pp = a.path[(int64_t)b * a.cap + nd];
+    const uint64_t pp = s_pp[jj];
     const int d = (int)(pp >> 60) + 1;
-    a.parent[o] = nd;
+    a.parent[o] = s_fr[jj];
     a.token[o] = s_ct[i];
     a.value[o] = s_cv[i];
     a.conf[o] = s_cc[i];
     a.path[o] = ((uint64_t)d << 60) | (pp & ((1ull << 60) - 1)) | ((uint64_t)r << (60 - 4 * d));
   }
   // the next frontier: the select_k new children of largest value (ties to the lower id)
-  if (wid == 0) {
+  if (j == 0) {
     double v[kTbMaxFrontier * kTbMaxK / 64];
     int bi = 0x7fffffff;
     double bv = -2.0;
@@ -390,6 +464,8 @@ __device__ inline bool rr_before(double va, uint32_t ta, double vb, uint32_t tb)
   return va > vb || (va == vb && ta < tb);
 }
 
+// Bitonic sort of the candidates, one per thread: exchanges within a wavefront go
+// through lane shuffles, the longer ones through LDS.
 __global__ __launch_bounds__(kTbRerankThreads) void tb_rerank_kernel(RrArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   __shared__ double s_v[kTbMaxCap];
@@ -415,38 +491,41 @@ __global__ __launch_bounds__(kTbRerankThreads) void tb_rerank_kernel(RrArgs a) {
   int P = 2;
   while (P < m) P <<= 1;
   const int64_t cb = (int64_t)b * a.cap;
-  for (int i = tid; i < P; i += kTbRerankThreads) {
-    if (i < m) {
-      const int id = i + 1;
-      s_v[i] = a.value[cb + id];
-      s_t[i] = ((uint32_t)(a.path[cb + id] >> 60) << 10) | (uint32_t)id;
-    } else {
-      s_v[i] = -1.0;
-      s_t[i] = 0xffffffffu;
-    }
+  double v = -1.0;  // padding sorts last: values are >= 0
+  uint32_t t = 0xffffffffu;
+  if (tid < m) {
+    const int id = tid + 1;
+    v = a.value[cb + id];
+    t = ((uint32_t)(a.path[cb + id] >> 60) << 10) | (uint32_t)id;
   }
-  __syncthreads();
   for (int k = 2; k <= P; k <<= 1)
     for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < P; i += kTbRerankThreads) {
-        const int l = i ^ jj;
-        if (l > i) {
-          const double vi = s_v[i], vl = s_v[l];
-          const uint32_t ti = s_t[i], tl = s_t[l];
-          const bool up = (i & k) == 0;
-          if (up ? rr_before(vl, tl, vi, ti) : rr_before(vi, ti, vl, tl)) {
-            s_v[i] = vl;
-            s_v[l] = vi;
-            s_t[i] = tl;
-            s_t[l] = ti;
-          }
-        }
+      double pv;
+      uint32_t pt;
+      if (jj < 64) {
+        pv = __shfl_xor(v, jj);
+        pt = (uint32_t)__shfl_xor((int)t, jj);
+      } else {
+        s_v[tid] = v;
+        s_t[tid] = t;
+        __syncthreads();
+        pv = s_v[tid ^ jj];
+        pt = s_t[tid ^ jj];
+        __syncthreads();
       }
-      __syncthreads();
+      // in a rising run the lower index keeps the earlier element, in a falling run the later
+      const bool keep_first = ((tid & k) == 0) == ((tid & jj) == 0);
+      const bool partner_first = rr_before(pv, pt, v, t);
+      if (partner_first == keep_first) {
+        v = pv;
+        t = pt;
+      }
     }
+  const int n = min(a.n_final - 1, m) + 1;  // the root and the top n - 1
+  if (tid < n - 1) s_t[tid] = t;
+  __syncthreads();
   if (wid != 0) return;
-  // the root and the top n - 1, in breadth-first order by path key
-  const int n = min(a.n_final - 1, m) + 1;
+  // breadth-first order by path key
   int id = -1;
   uint64_t key = ~0ull;
   if (lane < n) {
@@ -577,7 +656,7 @@ extern "C" int spec_tree_expand(const float* draft_logits, int32_t vocab, float 
   else
     hipLaunchKernelGGL(tb_topk_kernel<false>, dim3((unsigned)blocks), dim3(kTbThreads), 0, st, a);
   SPEC_LAUNCH_CHECK();
-  hipLaunchKernelGGL(tb_expand_kernel, dim3((unsigned)batch), dim3(kTbThreads), 0, st, a);
+  hipLaunchKernelGGL(tb_expand_kernel, dim3((unsigned)batch), dim3(kTbExpandThreads), 0, st, a);
   SPEC_LAUNCH_CHECK();
   return SPEC_OK;
 }
