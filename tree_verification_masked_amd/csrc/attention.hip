@@ -15,11 +15,13 @@
 // element type of the inputs) go to the workspace and
 // a combine kernel merges the splits with a log-sum-exp rescale.
 //
-//  * MFMA path (bf16, >= 16 rows per KV head): four waves of 32 rows each.  Scores
-//    are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so each
-//    lane ends up owning one query row; that accumulator layout is exactly the B
-//    operand of O^T = V^T P^T for a fixed permutation of the 16 keys of a step, and
-//    V is staged transposed in LDS in that key order.
+//  * MFMA path (bf16, >= 16 rows per KV head): eight waves, four row blocks of 32
+//    rows, each block done by two waves that take the two 32-key halves of every
+//    tile (their partial softmax states merge in LDS at the end).  Scores are
+//    computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so each lane
+//    ends up owning one query row; that accumulator layout is exactly the B operand
+//    of O^T = V^T P^T for a fixed permutation of the 16 keys of a step, and V is
+//    read transposed out of LDS in that key order.
 //  * Shuffle path (fp32, or fewer than 16 rows): lane j of a wave scores key j of
 //    the tile against one row, the row softmax uses wave reductions, and P V is
 //    accumulated with one lane per head dimension.

@@ -48,46 +48,54 @@ __device__ inline int64_t commit_off(const CommitArgs& a, int b, int t, int g) {
   return row * a.head_dim * a.elem;
 }
 
-// Whether request b's commit is valid: the path must be a walk from the root inside
-// the tree, and every position of the tree must exist in the cache.
-__device__ inline bool commit_valid(const CommitArgs& a, int b) {
+// Whether request b's commit is valid (one wavefront, every lane gets the answer):
+// the path must be a walk from the root inside the tree, and every position of the
+// tree must exist in the cache.  Lane i checks path entry i (L < n <= 64) and the
+// i-th page slot of the tree's span (at most 64 slots: n <= 64 positions).
+__device__ inline bool commit_valid(const CommitArgs& a, int b, int lane) {
   const int L = a.accept_len[b], n = a.n_nodes[b], ctx = a.ctx_len[b];
   const int32_t* path = a.path_nodes + (int64_t)b * a.n_max;
-  bool ok = L >= 0 && n >= 1 && n <= a.n_max && L < n && ctx >= 0 && path[0] == 0;
-  for (int i = 1; ok && i <= L; ++i) ok = path[i] > path[i - 1] && path[i] < n;
-  if (ok) {
-    const int64_t end = (int64_t)ctx + n;
-    if (!a.block_table) {
-      ok = end <= a.kv_capacity;
-    } else {
-      ok = end <= (int64_t)a.kv_capacity * a.page_size;
-      for (int s = ctx / a.page_size; ok && s < (int)((end + a.page_size - 1) / a.page_size); ++s) {
-        const int pg = a.block_table[(int64_t)b * a.kv_capacity + s];
-        ok = pg >= 0 && pg < a.n_pages;
-      }
+  const bool head = L >= 0 && n >= 1 && n <= a.n_max && L < n && ctx >= 0;
+  if (!head) return false;
+  bool ok = true;
+  if (lane <= L) {
+    const int p = path[lane];
+    ok = lane == 0 ? p == 0 : (p > path[lane - 1] && p < n);
+  }
+  const int64_t end = (int64_t)ctx + n;
+  if (!a.block_table) {
+    ok = ok && end <= a.kv_capacity;
+  } else {
+    ok = ok && end <= (int64_t)a.kv_capacity * a.page_size;
+    const int s = ctx / a.page_size + lane;
+    if (ok && s < (int)((end + a.page_size - 1) / a.page_size)) {
+      const int pg = a.block_table[(int64_t)b * a.kv_capacity + s];
+      ok = pg >= 0 && pg < a.n_pages;
     }
   }
-  return ok;
+  return __all(ok) != 0;
 }
 
-// The per-request end of a commit (one thread): new length, error report, page
-// release.  Runs only after every layer of the request has read its sources.
-__device__ inline void commit_finish(const CommitArgs& a, int b, bool ok) {
+// The per-request end of a commit (one wavefront): new length, error report, page
+// release (lane i releases the i-th freed slot).  Runs only after every layer of the
+// request has read its sources.
+__device__ inline void commit_finish(const CommitArgs& a, int b, bool ok, int lane) {
   const int L = a.accept_len[b], n = a.n_nodes[b], ctx = a.ctx_len[b];
   if (!ok) {
-    a.new_len[b] = -1;
-    if (L >= 0) report(a.status, SPEC_ERR_BAD_INPUT);  // (accept_len < 0: a request already refused)
+    if (lane == 0) {
+      a.new_len[b] = -1;
+      if (L >= 0) report(a.status, SPEC_ERR_BAD_INPUT);  // (accept_len < 0: a request already refused)
+    }
     return;
   }
   const int nl = ctx + 1 + L;
-  a.new_len[b] = nl;
+  if (lane == 0) a.new_len[b] = nl;
   if (a.block_table) {  // release the pages left holding only freed positions
     int32_t* tab = a.block_table + (int64_t)b * a.kv_capacity;
     const int first = (nl + a.page_size - 1) / a.page_size, end = (ctx + n + a.page_size - 1) / a.page_size;
-    int j = 0;
-    for (int s = first; s < end; ++s) {
-      if (a.freed) a.freed[(int64_t)b * kMaxFreed + j] = tab[s];
-      ++j;
+    const int s = first + lane;
+    if (s < end) {
+      if (a.freed) a.freed[(int64_t)b * kMaxFreed + lane] = tab[s];
       tab[s] = -1;
     }
   }
@@ -98,15 +106,14 @@ template <bool FINISH>
 __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitArgs a) {
   __shared__ __attribute__((aligned(16))) int4 s_buf[kCommitLds / 16];
   __shared__ int s_ok;
-  const int tid = threadIdx.x, b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, b = blockIdx.x;
   const int L = a.accept_len[b], ctx = a.ctx_len[b];
   const int32_t* path = a.path_nodes + (int64_t)b * a.n_max;
-  if (FINISH && a.freed)
-    for (int j = tid; j < kMaxFreed; j += kCommitThreads) a.freed[(int64_t)b * kMaxFreed + j] = -1;
-  if (tid == 0) {
-    const bool ok = commit_valid(a, b);
-    s_ok = ok;
-    if (FINISH && !ok) commit_finish(a, b, false);
+  if (wid == 0) {
+    if (FINISH && a.freed) a.freed[(int64_t)b * kMaxFreed + lane] = -1;
+    const bool ok = commit_valid(a, b, lane);
+    if (lane == 0) s_ok = ok;
+    if (FINISH && !ok) commit_finish(a, b, false, lane);
   }
   __syncthreads();
   if (!s_ok) return;
@@ -133,16 +140,14 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitArgs a)
     }
     __syncthreads();  // the buffer is reused and the next chunk's sources are read after these writes
   }
-  if (FINISH && tid == 0) commit_finish(a, b, true);
+  if (FINISH && wid == 0) commit_finish(a, b, true, lane);
 }
 
-// After the moves of every layer: one workgroup per request.
+// After the moves of every layer: one wavefront per request.
 __global__ __launch_bounds__(64) void kv_commit_finish_kernel(CommitArgs a) {
-  const int b = blockIdx.x;
-  if (a.freed)
-    for (int j = threadIdx.x; j < kMaxFreed; j += 64) a.freed[(int64_t)b * kMaxFreed + j] = -1;
-  __syncthreads();
-  if (threadIdx.x == 0) commit_finish(a, b, commit_valid(a, b));
+  const int b = blockIdx.x, lane = threadIdx.x;
+  if (a.freed) a.freed[(int64_t)b * kMaxFreed + lane] = -1;
+  commit_finish(a, b, commit_valid(a, b, lane), lane);
 }
 
 }  // namespace spectree
