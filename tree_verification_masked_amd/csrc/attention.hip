@@ -473,57 +473,78 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   for (; it < n_plain; ++it) tile(it, std::false_type{});
   for (; it < n_tiles; ++it) tile(it, std::true_type{});
   if (bad_page) report(a.status, SPEC_ERR_BAD_INPUT);
-  // ---- merge the two key halves of each row: the key-half-1 wave hands its
-  // (m, l, O) to its partner through LDS (the tiles are consumed) ----
-  constexpr int NACC = D / 32 * 16;  // accumulator values per lane
-  float* mw = reinterpret_cast<float*>(&sKV[0][0][0]) + wr * (NACC + 2) * 64;  // [NACC + 2][64]
+  // ---- merge the two key halves of each row, split by head dimension: the
+  // key-half-0 wave finishes dims [0, D/2) and the key-half-1 wave dims [D/2, D).
+  // Each hands the partner the half it does not finish, with its (m, l), through
+  // LDS (the K/V stages are consumed by then) ----
+  constexpr int NH = D / 64;            // accumulator blocks per half of the dims
+  constexpr int NV4 = NH * 16 / 4;      // float4 per lane handed over
+  float4* xw = reinterpret_cast<float4*>(&sKV[0][0][0]) + (wr * 2 + kh) * (NV4 + 1) * 64;     // written here
+  float4* xr = reinterpret_cast<float4*>(&sKV[0][0][0]) + (wr * 2 + 1 - kh) * (NV4 + 1) * 64; // partner's
   lds_barrier();  // every wave is done with the K/V stages
-  if (kh == 1) {
+  const bool lo_half = kh == 0;  // this wave finishes dims [0, D/2)
+  // (register blocks are picked with selects: the index must stay compile-time)
+  {
 #pragma unroll
-    for (int i = 0; i < NACC; ++i) mw[i * 64 + lane] = acc_o[i / 16][i % 16];
-    mw[NACC * 64 + lane] = m_run;
-    mw[(NACC + 1) * 64 + lane] = l_run;
+    for (int i = 0; i < NV4; ++i) {
+      const int blk = i / 4, e = 4 * (i % 4);
+      xw[i * 64 + lane] = make_float4(lo_half ? acc_o[NH + blk][e] : acc_o[blk][e],
+                                      lo_half ? acc_o[NH + blk][e + 1] : acc_o[blk][e + 1],
+                                      lo_half ? acc_o[NH + blk][e + 2] : acc_o[blk][e + 2],
+                                      lo_half ? acc_o[NH + blk][e + 3] : acc_o[blk][e + 3]);
+    }
+    xw[NV4 * 64 + lane] = make_float4(m_run, l_run, 0.0f, 0.0f);
   }
   lds_barrier();
-  if (kh == 0) {
-    const float mb = mw[NACC * 64 + lane], lb = mw[(NACC + 1) * 64 + lane];
+  float fin[NH][16];  // the finished half of the accumulators
+  {
+    const float4 ml = xr[NV4 * 64 + lane];
+    const float mb = ml.x, lb = ml.y;
     const float m = fmaxf(m_run, mb);
     const float wa = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
     const float wb = mb == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - m);
     l_run = l_run * wa + lb * wb;
-#pragma unroll
-    for (int i = 0; i < NACC; ++i) acc_o[i / 16][i % 16] = acc_o[i / 16][i % 16] * wa + mw[i * 64 + lane] * wb;
     m_run = m;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const float4 o = xr[i * 64 + lane];
+      const int blk = i / 4, e = 4 * (i % 4);
+      fin[blk][e] = (lo_half ? acc_o[blk][e] : acc_o[NH + blk][e]) * wa + o.x * wb;
+      fin[blk][e + 1] = (lo_half ? acc_o[blk][e + 1] : acc_o[NH + blk][e + 1]) * wa + o.y * wb;
+      fin[blk][e + 2] = (lo_half ? acc_o[blk][e + 2] : acc_o[NH + blk][e + 2]) * wa + o.z * wb;
+      fin[blk][e + 3] = (lo_half ? acc_o[blk][e + 3] : acc_o[NH + blk][e + 3]) * wa + o.w * wb;
+    }
   }
-  lds_barrier();  // the merge area is free again
-  if (kh == 1) return;
-  // ---- write this split's partials: the wave's 32 rows go through LDS so that
-  // the normalised outputs leave as whole rows ----
+  // ---- write this split's partials: the wave's 32 rows x D/2 dims go through LDS
+  // (the partner's hand-over area, read by now) so that they leave as whole
+  // 16-byte row pieces ----
   const bool row_out = r < G && node < a.n_max;
   const int64_t prow = (((int64_t)s * a.batch + b) * a.n_max + node) * a.hq + h;
-  if (row_out && lane < 32) {
+  if (kh == 0 && row_out && lane < 32) {
     a.mpart[prow] = m_run;
     a.lpart[prow] = l_run;
   }
-  constexpr int OROW = D * 2 + 16;  // bytes per staged row (padded)
-  char* so = &sKV[0][0][0] + wr * 32 * OROW;
+  constexpr int HB = D;               // bytes of half a row in bf16
+  constexpr int OROW = HB + 16;       // bytes per staged half row (padded)
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the hand-over reads are done
+  char* so = reinterpret_cast<char*>(xr);
   {
     const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NH; ++db)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int d = db * 32 + 8 * e4 + 4 * (lane >> 5);
+        const int d = db * 32 + 8 * e4 + 4 * (lane >> 5);  // within the half
         bf16x4 o4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(acc_o[db][4 * e4 + i] * inv_l);
+        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(fin[db][4 * e4 + i] * inv_l);
         *reinterpret_cast<bf16x4*>(so + (lane & 31) * OROW + d * 2) = o4;
       }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
   // 16-byte pieces: lane covers piece (lane % CPR) of rows lane / CPR + rpi * j
-  constexpr int CPR = D * 2 / 16;  // pieces per row
+  constexpr int CPR = HB / 16;     // pieces per half row
   constexpr int RPI = 64 / CPR;    // rows per wave instruction
 #pragma unroll
   for (int j = 0; j < 32 / RPI; ++j) {
@@ -533,7 +554,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     if (rg < G && nd2 < a.n_max) {
       const int64_t prow2 = (((int64_t)s * a.batch + b) * a.n_max + nd2) * a.hq + g * hpg + rg % hpg;
       const int4 v = *reinterpret_cast<const int4*>(so + rl * OROW + (lane % CPR) * 16);
-      *reinterpret_cast<int4*>((char*)a.opart + prow2 * D * 2 + (lane % CPR) * 16) = v;
+      *reinterpret_cast<int4*>((char*)a.opart + prow2 * D * 2 + kh * HB + (lane % CPR) * 16) = v;
     }
   }
 }
