@@ -14,10 +14,12 @@
 // logit row per frontier node.
 //   tb_topk_kernel    one workgroup per (request, frontier row, 4096-token chunk):
 //                     one read of the chunk gives its maximum, its fp64 sum of
-//                     exp((l - m_c) / T_d) and its top-k (logit, token) keys
-//   tb_expand_kernel  one workgroup per request: merges the chunk partials of each
-//                     row (a k-way merge of sorted lists), appends the children with
-//                     value = parent value x confidence, and picks the next frontier
+//                     exp((l - m_c) / T_d) and its top-k (logit, token) keys; the
+//                     row's last workgroup to finish (agent-scope counter) merges the
+//                     row's chunks and writes its children (value = parent value x
+//                     confidence), so the rows merge on different CUs
+//   tb_select_kernel  one workgroup per request: appends the children and picks
+//                     the next frontier
 // The rerank is one workgroup per request: a bitonic sort of every candidate by
 // (value desc, depth asc, id asc) in LDS, the top N - 1 plus the root, then the
 // breadth-first order from each node's path key (depth, then the sibling ranks of
@@ -35,8 +37,8 @@ constexpr int kTbMaxChunks = 64;             // vocabulary up to 64 chunks
 constexpr int kTbMaxCap = 1024;              // candidates per request (sorted in LDS)
 constexpr int kTbMaxDepth = 15;              // path keys hold 15 four-bit sibling ranks
 constexpr int kTbRerankThreads = kTbMaxCap;  // one candidate per thread
-constexpr int kTbExpandThreads = 64 * kTbMaxFrontier;  // one wavefront per frontier row
 constexpr int kTbCand = 128;                            // threshold candidates ranked directly
+static_assert(kTbMaxFrontier * kTbMaxK <= kTbThreads, "one thread per new child");
 typedef float tb_f32x4 __attribute__((ext_vector_type(4)));
 
 inline size_t tb_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -135,16 +137,130 @@ struct TbArgs {
   int32_t* count;     // [batch]
   int32_t* frontier;  // [batch, R]
   int32_t* fcount;    // [batch]
-  uint64_t* ws_keys;  // [batch, R, nch, kTbMaxK]
+  uint64_t* ws_keys;  // [batch, R, nch, kTbMaxK]  chunk partials
   float* ws_max;      // [batch, R, nch]
   double* ws_sum;
   int32_t* ws_bad;
+  uint32_t* row_cnt;  // [batch, R]  chunk workgroups of the row done (0 between calls)
+  double* row_val;    // [batch, R, kTbMaxK]  the row's children: value, confidence, token
+  double* row_conf;
+  int32_t* row_tok;
+  int32_t* row_node;  // [batch, R]  the expanded node, its path key, an error flag
+  uint64_t* row_path;
+  int32_t* row_bad;
   int32_t* status;
 };
 
 inline size_t tb_ws_bytes(int64_t batch, int32_t R, int32_t nch) {
-  const size_t n = (size_t)batch * (size_t)R * (size_t)nch;
-  return tb_align(n * kTbMaxK * 8) + tb_align(n * 4) + tb_align(n * 8) + tb_align(n * 4);
+  const size_t n = (size_t)batch * (size_t)R * (size_t)nch, rows = (size_t)batch * (size_t)R;
+  return tb_align(n * kTbMaxK * 8) + tb_align(n * 4) + tb_align(n * 8) + tb_align(n * 4) + tb_align(rows * 4) +
+         2 * tb_align(rows * kTbMaxK * 8) + tb_align(rows * kTbMaxK * 4) + tb_align(rows * 4) + tb_align(rows * 8) +
+         tb_align(rows * 4);
+}
+
+// Top K of the union of up to 64 lists sorted in decreasing order (lane c holds list
+// c, 0 = no key; nonzero keys are unique), by one wavefront; lane r < K gets the
+// r-th largest.  The K-th largest list head bounds the answer from below, so only
+// the keys at or above it are ranked (one pass over them per lane); when more than
+// 64 keys reach it, K rounds of a wave maximum pop the list heads instead.
+// s_h: 64 entries of LDS, s_c: 64 entries of LDS (this wavefront's).
+__device__ inline uint64_t merge_sorted_lists(uint64_t (&list)[kTbMaxK], int K, int lane, uint64_t* s_h,
+                                              uint64_t* s_c) {
+  const uint64_t head = list[0];
+  s_h[lane] = head;
+  wave_lds_sync();
+  int g = 0;  // heads larger than this lane's (LDS reads in batches of 16)
+  for (int q0 = 0; q0 < 64; q0 += 16) {
+    uint64_t hq[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) hq[q] = s_h[q0 + q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) g += hq[q] > head ? 1 : 0;
+  }
+  const uint64_t tau = wave_max_u64_2step(g == K - 1 ? head : 0ull);
+  int cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kTbMaxK; ++q) cnt += (list[q] != 0ull && list[q] >= tau) ? 1 : 0;
+  const int incl = wave_incl_scan_i(cnt);
+  const int C = __builtin_amdgcn_readlane(incl, 63);
+  uint64_t mine = 0;
+  if (C <= 64) {
+    const int off = incl - cnt;
+#pragma unroll
+    for (int q = 0; q < kTbMaxK; ++q)
+      if (q < cnt) s_c[off + q] = list[q];  // a sorted list: its candidates are a prefix
+    wave_lds_sync();
+    const uint64_t key = lane < C ? s_c[lane] : 0ull;
+    int rank = 0;
+    for (int q0 = 0; q0 < C; q0 += 8) {
+      uint64_t cq[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) cq[q] = s_c[q0 + q];  // (entries past C: stale keys, not counted)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rank += (int)((q0 + q < C) & (cq[q] > key));
+    }
+    wave_lds_sync();  // every lane has read the candidates
+    if (lane < C && rank < K) s_c[rank] = key;
+    wave_lds_sync();
+    mine = lane < K && lane < C ? s_c[lane] : 0ull;
+  } else {
+    for (int r = 0; r < K; ++r) {
+      const uint64_t w = wave_max_u64_2step(list[0]);
+      if (lane == r) mine = w;
+      if (w != 0ull && list[0] == w) {
+#pragma unroll
+        for (int q = 0; q < kTbMaxK - 1; ++q) list[q] = list[q + 1];
+        list[kTbMaxK - 1] = 0ull;
+      }
+    }
+  }
+  return mine;
+}
+
+// The row's top K from its chunks' partials, by one wavefront of the row's last
+// chunk workgroup: a k-way merge of the chunks' sorted lists (lane c holds chunk c's
+// list in registers; keys are unique and the lane holding the maximum pops its list),
+// the confidences in fp64 from the merged exp sum, and the children's values.
+__device__ void tb_merge_row(const TbArgs& a, int b, int64_t rowi, int lane, uint64_t* s_h, uint64_t* s_c) {
+  const int K = a.K, base = a.count[b];
+  const int nd = a.frontier[rowi];
+  float mc = -INFINITY;
+  double sc = 0.0;
+  int bc = 0;
+  uint64_t list[kTbMaxK];
+#pragma unroll
+  for (int q = 0; q < kTbMaxK; ++q) list[q] = 0ull;
+  if (lane < a.nch) {  // the other workgroups' partials: agent-scope loads
+    const int64_t slot = rowi * a.nch + lane;
+    mc = __uint_as_float(pub_load(reinterpret_cast<const uint32_t*>(a.ws_max) + slot));
+    sc = __longlong_as_double((long long)pub_load(reinterpret_cast<const uint64_t*>(a.ws_sum) + slot));
+    bc = pub_load(a.ws_bad + slot);
+#pragma unroll
+    for (int q = 0; q < kTbMaxK; ++q)
+      if (q < K) list[q] = pub_load(a.ws_keys + slot * kTbMaxK + q);
+  }
+  const bool nd_in = nd >= 0 && nd < base && base <= a.cap;
+  const uint64_t pp = nd_in ? a.path[(int64_t)b * a.cap + nd] : 0ull;
+  const double pv = nd_in ? a.value[(int64_t)b * a.cap + nd] : 0.0;
+  const bool nd_ok = nd_in && (int)(pp >> 60) < kTbMaxDepth;
+  const float M = wave_max_f(mc);
+  const int bad = wave_or_i(bc);
+  double S = (lane < a.nch && mc > -INFINITY) ? sc * exp(((double)mc - (double)M) * a.inv_t) : 0.0;
+  S = wave_sum_d(S);
+  const uint64_t mine = merge_sorted_lists(list, K, lane, s_h, s_c);
+  if (lane < K) {
+    // confidence = softmax(row / T_d) at the child's token
+    const double cf = exp(((double)tb_key_logit(mine) - (double)M) * a.inv_t) / S;
+    const int64_t o = rowi * kTbMaxK + lane;
+    a.row_val[o] = pv * cf;
+    a.row_conf[o] = cf;
+    a.row_tok[o] = tb_key_token(mine);
+  }
+  if (lane == 0) {
+    a.row_node[rowi] = nd;
+    a.row_path[rowi] = pp;
+    a.row_bad[rowi] = (bad || !(M > -INFINITY) || !nd_ok) ? 1 : 0;
+  }
 }
 
 template <bool kVec>
@@ -192,12 +308,19 @@ __global__ __launch_bounds__(kTbThreads) void tb_topk_kernel(TbArgs a) {
   // Threshold: the K-th largest lane maximum of a wavefront.  At least K of its
   // tokens reach it, so no token below it is in the wavefront's top K, nor below the
   // largest such threshold in the chunk's.
-  float v = lm, tw = -INFINITY;
-  for (int r = 0; r < a.K; ++r) {
-    tw = wave_max_f(v);
-    const uint64_t holders = __ballot(v == tw);
-    if (lane == __ffsll((long long)holders) - 1) v = -INFINITY;
+  __shared__ float s_lm[kTbThreads];
+  s_lm[tid] = lm;
+  wave_lds_sync();
+  int gl = 0;  // lane maxima of the wavefront above this lane's
+  for (int q0 = 0; q0 < 64; q0 += 16) {
+    float mq[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mq[q] = s_lm[wid * 64 + q0 + q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) gl += mq[q] > lm ? 1 : 0;
   }
+  // the K-th largest lane maximum: the largest value with at least K - 1 above it
+  const float tw = wave_max_f(gl >= a.K - 1 ? lm : -INFINITY);
   const float wm = wave_max_f(lm);
   bad = wave_or_i(bad);
   if (lane == 0) {
@@ -247,9 +370,9 @@ __global__ __launch_bounds__(kTbThreads) void tb_topk_kernel(TbArgs a) {
         r0 += kq > k0 ? 1 : 0;
         r1 += kq > k1 ? 1 : 0;
       }
-      if (lane < C && r0 < a.K) a.ws_keys[slot * kTbMaxK + r0] = k0;
-      if (lane + 64 < C && r1 < a.K) a.ws_keys[slot * kTbMaxK + r1] = k1;
-      if (lane >= C && lane < a.K) a.ws_keys[slot * kTbMaxK + lane] = 0ull;  // a chunk with fewer tokens than K
+      if (lane < C && r0 < a.K) pub_store(a.ws_keys + slot * kTbMaxK + r0, k0);
+      if (lane + 64 < C && r1 < a.K) pub_store(a.ws_keys + slot * kTbMaxK + r1, k1);
+      if (lane >= C && lane < a.K) pub_store(a.ws_keys + slot * kTbMaxK + lane, (uint64_t)0);  // fewer tokens than K
     }
   } else {
     // many tokens tie at the threshold (e.g. a row of equal logits): K rounds of a
@@ -283,26 +406,36 @@ __global__ __launch_bounds__(kTbThreads) void tb_topk_kernel(TbArgs a) {
         if (lane == r) mine = w;
         if (u == w) u = 0;
       }
-      if (lane < a.K) a.ws_keys[slot * kTbMaxK + lane] = mine;
+      if (lane < a.K) pub_store(a.ws_keys + slot * kTbMaxK + lane, mine);
     }
   }
   if (tid == 0) {
-    a.ws_max[slot] = cm;
-    a.ws_sum[slot] = csum;
-    a.ws_bad[slot] = cb;
+    pub_store(reinterpret_cast<uint32_t*>(a.ws_max) + slot, __float_as_uint(cm));
+    pub_store(reinterpret_cast<uint64_t*>(a.ws_sum) + slot, (uint64_t)__double_as_longlong(csum));
+    pub_store(a.ws_bad + slot, cb);
   }
+  // ---- the row's last chunk workgroup to finish merges the row ----
+  __shared__ int s_last;
+  stores_done();
+  __syncthreads();
+  if (tid == 0) s_last = pub_arrive(&a.row_cnt[rowi]) == (uint32_t)(a.nch - 1);
+  __syncthreads();
+  if (!s_last || wid != 0) return;
+  if (lane == 0) pub_store(&a.row_cnt[rowi], 0u);
+  tb_merge_row(a, b, rowi, lane, s_cand, s_cand + 64);
 }
 
-// One wavefront per frontier row (at most 16), all rows at once.
-__global__ __launch_bounds__(kTbExpandThreads) void tb_expand_kernel(TbArgs a) {
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, j = tid >> 6;
+// One workgroup per request, after every row is merged: append the children (ids
+// base + j * K + r: frontier order, then top-k order) and pick the next frontier.
+__global__ __launch_bounds__(kTbThreads) void tb_select_kernel(TbArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int K = a.K;
   __shared__ double s_cv[kTbMaxFrontier * kTbMaxK];
   __shared__ double s_cc[kTbMaxFrontier * kTbMaxK];
   __shared__ int s_ct[kTbMaxFrontier * kTbMaxK];
   __shared__ int s_fr[kTbMaxFrontier];
   __shared__ uint64_t s_pp[kTbMaxFrontier];
-  __shared__ int s_werr[kTbMaxFrontier];
+  __shared__ int s_err;
   const int fc = a.fcount[b], base = a.count[b];
   if (fc == 0) return;  // this request is finished (or failed earlier)
   if (fc < 0 || fc > a.R || base < 1 || base > a.cap || fc * K > a.cap - base) {
@@ -312,75 +445,31 @@ __global__ __launch_bounds__(kTbExpandThreads) void tb_expand_kernel(TbArgs a) {
     }
     return;
   }
-  if (j < fc) {
-    const int64_t rowi = (int64_t)b * a.R + j;
-    const int nd = a.frontier[rowi];
-    // every load of the row is issued before any result is needed
-    float mc = -INFINITY;
-    double sc = 0.0;
-    int bc = 0;
-    if (lane < a.nch) {
-      const int64_t slot = rowi * a.nch + lane;
-      mc = a.ws_max[slot];
-      sc = a.ws_sum[slot];
-      bc = a.ws_bad[slot];
-    }
-    // lane c holds chunk c's sorted list (entries past K are not part of it)
-    uint64_t list[kTbMaxK];
-    if (lane < a.nch) {
-      const uint64_t* src = a.ws_keys + (rowi * a.nch + lane) * kTbMaxK;
-#pragma unroll
-      for (int q = 0; q < kTbMaxK; ++q) list[q] = src[q];
-    }
-#pragma unroll
-    for (int q = 0; q < kTbMaxK; ++q)
-      if (lane >= a.nch || q >= K) list[q] = 0ull;
-    const bool nd_in = nd >= 0 && nd < base;
-    const uint64_t pp = nd_in ? a.path[(int64_t)b * a.cap + nd] : 0ull;
-    const double pv = nd_in ? a.value[(int64_t)b * a.cap + nd] : 0.0;
-    const bool nd_ok = nd_in && (int)(pp >> 60) < kTbMaxDepth;
-    const float M = wave_max_f(mc);
-    const int bad = wave_or_i(bc);
-    double S = (lane < a.nch && mc > -INFINITY) ? sc * exp(((double)mc - (double)M) * a.inv_t) : 0.0;
-    S = wave_sum_d(S);
-    // the row's top K: a K-way merge of the chunks' sorted lists (keys are unique;
-    // the lane holding the maximum pops its list)
-    uint64_t mine = 0;
-    for (int r = 0; r < K; ++r) {
-      const uint64_t w = wave_max_u64_2step(list[0]);
-      if (lane == r) mine = w;
-      if (w != 0ull && list[0] == w) {
-#pragma unroll
-        for (int q = 0; q < kTbMaxK - 1; ++q) list[q] = list[q + 1];
-        list[kTbMaxK - 1] = 0ull;
-      }
-    }
-    if (lane < K) {
-      // confidence = softmax(row / T_d) at the child's token, in fp64 from the merged sum
-      const double cf = exp(((double)tb_key_logit(mine) - (double)M) * a.inv_t) / S;
-      s_cv[j * K + lane] = pv * cf;
-      s_cc[j * K + lane] = cf;
-      s_ct[j * K + lane] = tb_key_token(mine);
-    }
-    if (lane == 0) {
-      s_fr[j] = nd;
-      s_pp[j] = pp;
-      s_werr[j] = (bad || !(M > -INFINITY) || !nd_ok) ? 1 : 0;
-    }
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+  const int nnew = fc * K;
+  for (int i = tid; i < nnew; i += kTbThreads) {
+    const int j = i / K, r = i - j * K;
+    const int64_t o = ((int64_t)b * a.R + j) * kTbMaxK + r;
+    s_cv[i] = a.row_val[o];
+    s_cc[i] = a.row_conf[o];
+    s_ct[i] = a.row_tok[o];
+  }
+  if (tid < fc) {
+    const int64_t rowi = (int64_t)b * a.R + tid;
+    s_fr[tid] = a.row_node[rowi];
+    s_pp[tid] = a.row_path[rowi];
+    if (a.row_bad[rowi]) s_err = 1;
   }
   __syncthreads();
-  int err = 0;
-  for (int q = 0; q < fc; ++q) err |= s_werr[q];
-  if (err) {
+  if (s_err) {
     if (tid == 0) {
       report(a.status, SPEC_ERR_BAD_INPUT);
       a.fcount[b] = 0;
     }
     return;
   }
-  // append the children: ids base + j * K + r (frontier order, then top-k order)
-  const int nnew = fc * K;
-  for (int i = tid; i < nnew; i += kTbExpandThreads) {
+  for (int i = tid; i < nnew; i += kTbThreads) {
     const int jj = i / K, r = i - jj * K;
     const int64_t o = (int64_t)b * a.cap + base + i;
     const uint64_t pp = s_pp[jj];
@@ -391,46 +480,28 @@ __global__ __launch_bounds__(kTbExpandThreads) void tb_expand_kernel(TbArgs a) {
     a.conf[o] = s_cc[i];
     a.path[o] = ((uint64_t)d << 60) | (pp & ((1ull << 60) - 1)) | ((uint64_t)r << (60 - 4 * d));
   }
-  // the next frontier: the select_k new children of largest value (ties to the lower id)
-  if (j == 0) {
-    double v[kTbMaxFrontier * kTbMaxK / 64];
-    int bi = 0x7fffffff;
-    double bv = -2.0;
+  // the next frontier: the select_k new children of largest value (ties to the lower
+  // id), each child ranked against all new children by its own thread (branch-free
+  // comparisons over broadcast LDS reads)
+  const int sk = min(a.select_k, nnew);
+  if (tid < nnew) {
+    const double v = s_cv[tid];
+    int rank = 0;
+    for (int q0 = 0; q0 < nnew; q0 += 8) {
+      double vq[8];
 #pragma unroll
-    for (int q = 0; q < kTbMaxFrontier * kTbMaxK / 64; ++q) {
-      const int i = lane + 64 * q;
-      v[q] = i < nnew ? s_cv[i] : -1.0;
-      if (tb_better(bv, bi, v[q], i)) {
-        bv = v[q];
-        bi = i;
+      for (int q = 0; q < 8; ++q) vq[q] = s_cv[min(q0 + q, nnew - 1)];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = q0 + q;
+        rank += (int)((i < nnew) & ((vq[q] > v) | ((vq[q] == v) & (i < tid))));
       }
     }
-    const int sk = min(a.select_k, nnew);
-    int mine = -1;
-    for (int r = 0; r < sk; ++r) {
-      double wv = bv;
-      int wi = bi;
-      wave_best_vd(wv, wi);
-      if (lane == r) mine = wi;
-      if (bi == wi) {  // the owner drops it and finds its next best
-        bv = -2.0;
-        bi = 0x7fffffff;
-#pragma unroll
-        for (int q = 0; q < kTbMaxFrontier * kTbMaxK / 64; ++q) {
-          const int i = lane + 64 * q;
-          if (i == wi) v[q] = -2.0;
-          if (tb_better(bv, bi, v[q], i)) {
-            bv = v[q];
-            bi = i;
-          }
-        }
-      }
-    }
-    if (lane < sk) a.frontier[(int64_t)b * a.R + lane] = base + mine;
-    if (lane == 0) {
-      a.fcount[b] = sk;
-      a.count[b] = base + nnew;
-    }
+    if (rank < sk) a.frontier[(int64_t)b * a.R + rank] = base + tid;
+  }
+  if (tid == 0) {
+    a.fcount[b] = sk;
+    a.count[b] = base + nnew;
   }
 }
 
@@ -648,6 +719,21 @@ extern "C" int spec_tree_expand(const float* draft_logits, int32_t vocab, float 
   a.ws_sum = (double*)w;
   w += tb_align(n * 8);
   a.ws_bad = (int32_t*)w;
+  w += tb_align(n * 4);
+  const size_t rows = (size_t)batch * max_frontier;
+  a.row_cnt = (uint32_t*)w;
+  w += tb_align(rows * 4);
+  a.row_val = (double*)w;
+  w += tb_align(rows * kTbMaxK * 8);
+  a.row_conf = (double*)w;
+  w += tb_align(rows * kTbMaxK * 8);
+  a.row_tok = (int32_t*)w;
+  w += tb_align(rows * kTbMaxK * 4);
+  a.row_node = (int32_t*)w;
+  w += tb_align(rows * 4);
+  a.row_path = (uint64_t*)w;
+  w += tb_align(rows * 8);
+  a.row_bad = (int32_t*)w;
   a.status = status;
   hipStream_t st = (hipStream_t)stream;
   const bool vec = vocab % 4 == 0 && (((uintptr_t)draft_logits & 15) == 0);
@@ -656,7 +742,7 @@ extern "C" int spec_tree_expand(const float* draft_logits, int32_t vocab, float 
   else
     hipLaunchKernelGGL(tb_topk_kernel<false>, dim3((unsigned)blocks), dim3(kTbThreads), 0, st, a);
   SPEC_LAUNCH_CHECK();
-  hipLaunchKernelGGL(tb_expand_kernel, dim3((unsigned)batch), dim3(kTbExpandThreads), 0, st, a);
+  hipLaunchKernelGGL(tb_select_kernel, dim3((unsigned)batch), dim3(kTbThreads), 0, st, a);
   SPEC_LAUNCH_CHECK();
   return SPEC_OK;
 }
