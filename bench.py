@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tree-verify steps/sec + attn/sampling HBM GB/s (8B-shape, 60-node tree, 4k ctx)"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 COPY_ELEMS = 1 << 27  # fp32: 512 MiB read and 512 MiB written per copy
 # HBM bytes per call measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by the
 # same counters on a plain copy); valid only while the sources listed there are unchanged
@@ -69,7 +70,14 @@ def measured_traffic():
     return out
 
 
-def roofline_entry(kernel, nbytes, us, traffic):
+def roofline_entry(kernel, nbytes, us, traffic, flops=0):
+    """HBM roofline entry, or the bf16 MFMA one when the call's arithmetic intensity is
+    above the ridge (peak FLOP/s / peak bytes/s)."""
+    if flops and flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        tf = flops / (us * 1e-6) / 1e12
+        return {"kernel": kernel, "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "flops_per_launch": int(flops), "bytes_per_launch": int(nbytes), "avg_launch_us": round(float(us), 3)}
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "bytes_per_launch": int(nbytes),
@@ -106,6 +114,14 @@ def algorithmic_bytes(inp):
     logits = B * n_max * inp["V"] * 4
     sampling = logits * (2 if inp["T"] > 0 else 1)
     return attn, logits, sampling
+
+
+def attention_flops(inp):
+    """Matrix FLOPs of the attention call: S = Q K^T and O = P V for every node and query
+    head against every key of its request (prompt and tree; ancestors are masked after
+    the product), 2 FLOPs per multiply-add."""
+    n = inp["n_nodes"].astype(np.int64)
+    return int(4 * inp["hq"] * inp["d"] * np.sum(n * (inp["ctx_len"].astype(np.int64) + n)))
 
 
 def copy_calibration():
@@ -481,7 +497,7 @@ def main():
         # avg_launch_us: the call timed back to back on its own (time_calls); stage_us
         # holds the same calls inside the step, each bracketed by events
         "roofline": roofline_entry("spec_tree_attention call: attn_mfma_kernel<128> + attn_combine_kernel",
-                                   attn_b, attn_us, traffic.get("spec_tree_attention")),
+                                   attn_b, attn_us, traffic.get("spec_tree_attention"), attention_flops(inp)),
         "stage_roofline": {
             "softmax_pair": roofline_entry("spec_tree_softmax_pair call: softmax_stats_kernel + softmax_merge_kernel",
                                            samp_b, pair_us, traffic.get("spec_tree_softmax_pair")),
