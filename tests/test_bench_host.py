@@ -1,0 +1,47 @@
+"""Host-side pieces of bench.py: algorithmic bytes and FLOPs, the roofline entry, the
+measured-traffic parser and the deepest-path construction used for the KV-commit
+timing.  No GPU."""
+import os
+import sys
+
+import numpy as np
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+from tree_verification_masked_amd import synth  # noqa: E402
+
+
+def test_algorithmic_bytes_and_flops_of_the_60_node_step():
+    inp = synth.make_config(2, seed=0, with_kv=False)
+    attn, logits, sampling = bench.algorithmic_bytes(inp)
+    kv = 2 * (4096 + 60) * 8 * 128 * 2            # K and V of every position, bf16
+    qo = 2 * 60 * 32 * 128 * 2                    # Q in, O out
+    assert attn == kv + qo == 18006016
+    assert logits == 60 * 128256 * 4 and sampling == 2 * logits
+    assert bench.attention_flops(inp) == 4 * 32 * 128 * 60 * (4096 + 60)
+
+
+def test_roofline_switches_to_mfma_above_the_ridge():
+    e = bench.roofline_entry("k", 1_000_000, 10.0, None, flops=0)
+    assert e["bound"] == "hbm" and e["unit"] == "GB/s" and abs(e["achieved"] - 100.0) < 1e-9
+    ridge = bench.MFMA_BF16_PEAK_TFLOPS * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
+    below = bench.roofline_entry("k", 1_000_000, 10.0, None, flops=int(0.9 * ridge * 1_000_000))
+    above = bench.roofline_entry("k", 1_000_000, 10.0, None, flops=int(1.1 * ridge * 1_000_000))
+    assert below["bound"] == "hbm" and above["bound"] == "mfma" and above["unit"] == "TFLOP/s"
+    assert abs(above["frac"] - above["achieved"] / bench.MFMA_BF16_PEAK_TFLOPS) < 1e-3
+
+
+def test_deepest_paths():
+    parent = np.array([[-1, 0, 0, 1, 3, 2, -1], [-1, 0, -1, -1, -1, -1, -1]], np.int32)
+    path, L = bench.deepest_paths(parent, np.array([6, 2]))
+    assert L.tolist() == [3, 1]
+    assert path[0, :4].tolist() == [0, 1, 3, 4] and path[1, :2].tolist() == [0, 1]
+
+
+def test_measured_traffic_matches_the_committed_sources():
+    # the committed counter summary lists the sources' hashes; bench reports traffic only
+    # while they match, and the values are per-call byte counts
+    t = bench.measured_traffic()
+    for call in ("spec_tree_attention", "spec_tree_softmax_pair"):
+        assert call in t
+        assert t[call] is None or t[call] > 10_000_000
