@@ -22,6 +22,13 @@ The pages leave these steps open; the readings taken here:
   value = value(parent) * c.
 * Node ids.  Children get consecutive ids as they are created: expanded nodes in
   frontier order, each node's children in top-k order.
+* Best-first (the DDTree variant of the same notes, part E.4).  The frontier is kept
+  as a max-heap over every node not yet expanded, whatever its depth, and the node of
+  largest value is expanded next.  Reading: a round expands the ``select_k`` best
+  nodes of that frontier (``select_k`` = 1 is the one-pop heap); since every expanded
+  node gets children, the unexpanded nodes are exactly the leaves of the candidate
+  tree.  Leaves at depth ``MAX_DEPTH`` are not expanded (the GPU's path key holds 15
+  levels).
 * Rerank.  Keep the root and the ``n_final - 1`` other nodes of largest value (ties
   to the shallower node, then the lower id).  Value never increases along a path and
   a parent precedes its child on ties, so the kept set is a connected subtree.
@@ -37,6 +44,7 @@ from __future__ import annotations
 import numpy as np
 
 TIE_REL = 1e-5
+MAX_DEPTH = 15
 
 
 def softmax_f64(row, T):
@@ -72,8 +80,10 @@ class TreeBuild:
         self.ties = []  # (stage, round) of every decision inside the near-tie band
         self.rounds = 0
 
-    def expand(self, rows, T_d: float, top_k: int, select_k: int):
-        """One round.  ``rows[j]`` is the draft row (logits) at ``frontier[j]``."""
+    def expand(self, rows, T_d: float, top_k: int, select_k: int, policy: str = "layer"):
+        """One round.  ``rows[j]`` is the draft row (logits) at ``frontier[j]``.
+        policy "layer": the next frontier is chosen among this round's children (EAGLE-2);
+        "best_first": among every leaf of the candidate tree (DDTree)."""
         assert len(rows) == len(self.frontier)
         new = []
         for j, nd in enumerate(self.frontier):
@@ -86,7 +96,12 @@ class TreeBuild:
                 self.value.append(self.value[nd] * float(p[t]))
                 self.rank.append(r)
                 new.append(len(self.parent) - 1)
-        order = sorted(new, key=lambda i: (-self.value[i], i))
+        if policy == "best_first":
+            has_kids = set(self.parent[1:])
+            pool = [i for i in range(len(self.parent)) if i not in has_kids and self.depth[i] < MAX_DEPTH]
+        else:
+            pool = new
+        order = sorted(pool, key=lambda i: (-self.value[i], i))
         # the next frontier and its order (the order fixes the next round's ids)
         cut = min(select_k, len(order))
         for a, b in zip(order[:cut], order[1:cut + 1]):
@@ -137,15 +152,17 @@ def expand_values(frontier_values, select_k, child_confidences):
     return kept, np.array(vals), np.array(par, np.int64)
 
 
-def build_tree(row_of, root_token, T_d, top_k, depth, n_final, select_k=None):
-    """A whole EAGLE-2 tree: ``depth`` expand rounds, then rerank and flatten.
+def build_tree(row_of, root_token, T_d, top_k, depth, n_final, select_k=None, policy="layer"):
+    """A whole tree: ``depth`` expand rounds, then rerank and flatten.
     ``row_of(tokens_on_path)`` returns the draft logits at the node whose root path
     carries those tokens (root token first)."""
     select_k = top_k if select_k is None else select_k
     t = TreeBuild(root_token)
     for _ in range(depth):
+        if not t.frontier:
+            break
         rows = [row_of(path_tokens(t, nd)) for nd in t.frontier]
-        t.expand(rows, T_d, top_k, select_k)
+        t.expand(rows, T_d, top_k, select_k, policy)
     parent, tokens, ids = t.rerank(n_final)
     return t, parent, tokens, ids
 

@@ -137,3 +137,56 @@ def test_near_ties_are_recorded():
     tr2 = tb.TreeBuild(0)
     tr2.expand([np.log(np.array([0.6, 0.3, 0.1])).astype(np.float32)], 1.0, 2, 1)
     assert tr2.ties == []
+
+
+def _prob_rows(table):
+    return {k: np.log(np.array(v, np.float64)).astype(np.float32) for k, v in table.items()}
+
+
+def test_best_first_returns_to_a_shallower_leaf_by_hand():
+    # root children 0.6, 0.4; the 0.6 node's children 0.5 x 0.6 = 0.3 each.  The next
+    # frontier (select_k 1): EAGLE-2 picks among the new children (a 0.3 node); the
+    # best-first heap picks the older 0.4 leaf at depth 1
+    rows = _prob_rows({(7,): [0.6, 0.4, 1e-12, 1e-12], (7, 0): [0.5, 0.5, 1e-12, 1e-12],
+                       (7, 1): [0.9, 0.1, 1e-12, 1e-12]})
+    lay, bf = tb.TreeBuild(7), tb.TreeBuild(7)
+    for t, pol in ((lay, "layer"), (bf, "best_first")):
+        t.expand([rows[(7,)]], 1.0, 2, 1, pol)
+        assert t.frontier == [1]  # the 0.6 child
+        t.expand([rows[(7, 0)]], 1.0, 2, 1, pol)
+    assert lay.frontier == [3] and bf.frontier == [2]  # ids: 3 = first 0.3 child, 2 = the 0.4 leaf
+    bf.expand([rows[(7, 1)]], 1.0, 2, 1, "best_first")
+    assert bf.value[5] == pytest.approx(0.4 * 0.9, rel=1e-6) and bf.frontier == [5]  # 0.36 > 0.3
+
+
+def _full_values(row_of, root, top_k, depth):
+    """Every node of the candidate tree to ``depth`` (brute force): path -> value."""
+    out, level = {}, [((root,), 1.0)]
+    for _ in range(depth):
+        nxt = []
+        for path, v in level:
+            p = tb.softmax_f64(row_of(path), 1.0)
+            for t in tb.topk_tokens(row_of(path), top_k):
+                nxt.append((path + (int(t),), v * float(p[t])))
+        out.update(nxt)
+        level = nxt
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_best_first_pops_the_best_nodes_of_the_whole_candidate_tree(seed):
+    # one pop per round: the expanded nodes are the r most valuable nodes of the full
+    # candidate tree (values never grow along a path), popped in non-increasing order
+    V, k, r = 12, 3, 9
+    row_of = _rows_from_seed(seed, V, scale=2.0)
+    t = tb.TreeBuild(0)
+    popped = []
+    for _ in range(r):
+        popped.append(t.frontier[0])
+        t.expand([row_of(tb.path_tokens(t, t.frontier[0]))], 1.0, k, 1, "best_first")
+    vals = [t.value[i] for i in popped]
+    assert all(a >= b for a, b in zip(vals, vals[1:]))
+    full = _full_values(row_of, 0, k, r)
+    best = sorted(full.values(), reverse=True)[: r - 1]  # the root (value 1) is the first pop
+    assert np.allclose(sorted(vals[1:], reverse=True), best, rtol=1e-12)
+    assert t.ties == []
