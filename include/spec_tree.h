@@ -309,21 +309,28 @@ int spec_tree_build_init(const int32_t* root_token, int32_t batch, int32_t cap, 
  * frontier_count[b] are not read).  Each such node gets as children its top_k
  * tokens by logit (ties to the lower token id), with confidence
  * c = softmax(row / T_d)[token] (fp32 exponentials summed in fp64; c itself in
- * fp64) and value = value(node) * c.  The new frontier is the select_k new children
- * of largest value (ties to the lower id).  One read of every row.
+ * fp64) and value = value(node) * c.  The new frontier is the select_k nodes of
+ * largest value (ties to the lower id) among
+ *   policy 0  this round's children (EAGLE-2, layer by layer), or
+ *   policy 1  every node without children below depth 15 (the best-first heap of
+ *             DDTree, tree notes part E.4: whatever its depth, the most valuable
+ *             unexpanded node is grown next; select_k 1 is the one-pop heap).
+ * One read of every row.
  * Device errors (SPEC_ERR_BAD_INPUT in status; the request's frontier_count becomes
  * 0 and nothing is appended): a row with NaN or +inf or only -inf, a frontier entry
  * that is not an existing node or sits at depth 15, frontier_count above
  * max_frontier, or more than cap nodes.
  * Host errors: null pointers; batch < 1; max_frontier outside [1, 16]; top_k
- * outside [1, 16]; select_k outside [1, max_frontier]; cap outside [1, 1024];
+ * outside [1, 16]; select_k outside [1, max_frontier]; policy not 0 or 1; cap
+ * outside [1, 1024];
  * vocab < top_k; T_d not finite and positive; SPEC_ERR_UNSUPPORTED for vocab above
  * 262144; SPEC_ERR_WORKSPACE for a workspace smaller than
  * spec_tree_expand_workspace_size(batch, max_frontier, vocab) (0 = bad sizes).
  */
 size_t spec_tree_expand_workspace_size(int32_t batch, int32_t max_frontier, int32_t vocab);
 int spec_tree_expand(const float* draft_logits, int32_t vocab, float T_d, int32_t batch, int32_t max_frontier,
-                     int32_t top_k, int32_t select_k, int32_t cap, int32_t* cand_parent, int32_t* cand_token,
+                     int32_t top_k, int32_t select_k, int32_t policy, int32_t cap, int32_t* cand_parent,
+                     int32_t* cand_token,
                      uint64_t* cand_path, double* cand_value, double* cand_conf, int32_t* cand_count,
                      int32_t* frontier, int32_t* frontier_count, void* workspace, size_t workspace_bytes,
                      int32_t* status, void* stream);

@@ -63,7 +63,7 @@ def compare_state(st, b, o, tag):
 
 
 def run_build(Bn, V, k, depth, n_final, T_d, kind, seed, select_k=None, cap=1024, scale=3.0, noise=1.0,
-              row_hook=None):
+              row_hook=None, policy="layer"):
     sk = k if select_k is None else select_k
     R = max(sk, 1)
     rng = np.random.default_rng(seed)
@@ -84,8 +84,9 @@ def run_build(Bn, V, k, depth, n_final, T_d, kind, seed, select_k=None, cap=1024
             for j in range(int(st["frontier_count"][b])):
                 rows[b, j] = row(gpu_path_tokens(st, b, int(st["frontier"][b, j])))
         for b, o in enumerate(orc):
-            o.expand([row(otb.path_tokens(o, nd)) for nd in o.frontier], T_d, k, sk)
-        dt.expand(torch.from_numpy(rows).cuda(), T_d, k, sk)
+            if o.frontier:
+                o.expand([row(otb.path_tokens(o, nd)) for nd in o.frontier], T_d, k, sk, policy)
+        dt.expand(torch.from_numpy(rows).cuda(), T_d, k, sk, policy=policy)
         st = dt.host_state()
         assert st["status"][0] == 0
         for b, o in enumerate(orc):
@@ -221,3 +222,34 @@ def test_bad_row_stops_only_its_request():
     assert st["status"][0] == BAD_INPUT
     assert st["count"][1] == 1 and st["frontier_count"][1] == 0
     compare_state(st, 0, o, "healthy request beside a bad one")
+
+
+@pytest.mark.parametrize("Bn,V,k,sk,rounds,n", [
+    (2, 3000, 4, 1, 12, 24),      # the one-pop heap
+    (3, 1000, 3, 2, 10, 30),      # scalar loads, two pops per round
+    (1, 128256, 8, 4, 8, 64),     # full vocabulary
+])
+def test_best_first_parity(Bn, V, k, sk, rounds, n):
+    say("tree build best-first", Bn, V, k, sk, rounds, n)
+    _, _, orc, tied = run_build(Bn, V, k, rounds, n, 1.0, "normal", seed=V + sk, select_k=sk, policy="best_first")
+    assert len(tied) == 0
+    # the heap goes back to shallower nodes: some expanded node is not on the last
+    # round's depth (unlike the layer policy)
+    depths = [o.depth[i] for o in orc for i in set(o.parent[1:])]
+    assert len(set(depths)) > 1
+
+
+def test_best_first_stops_at_the_depth_limit():
+    say("tree build best-first: depth 15")
+    V = 64
+    dt = DraftTree(1, 1024, 1, V)
+    dt.init(torch.tensor([3], dtype=torch.int32, device="cuda"))
+    rows = _empty_rows(dt)
+    rows[0, 0] = torch.arange(V, dtype=torch.float32, device="cuda")
+    for _ in range(15):  # a chain: its only leaf reaches depth 15, which is not grown
+        dt.expand(rows, 1.0, 1, policy="best_first")
+    st = dt.host_state()
+    assert st["status"][0] == 0 and st["count"][0] == 16 and st["frontier_count"][0] == 0
+    dt.expand(rows, 1.0, 1, policy="best_first")  # nothing left to grow: a no-op
+    st = dt.host_state()
+    assert st["status"][0] == 0 and st["count"][0] == 16

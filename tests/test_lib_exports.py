@@ -162,9 +162,9 @@ def test_host_errors_tree_build(lib):
     assert f(P, 1, 64, 17, P, P, P, P, P, P, P, P, None) == -1   # frontier above 16
     assert f(None, 1, 64, 4, P, P, P, P, P, P, P, P, None) == -1
     g = lib.spec_tree_expand
-    #       lg V     T    B  R  k  sk cap par tok path val conf cnt fr fc ws wsb      st    s
-    args = [P, 1000, 1.0, 1, 4, 4, 4, 64, P, P, P, P, P, P, P, P, P, 1 << 30, None, None]
-    for i, bad in ((2, 0.0), (2, float("inf")), (5, 17), (5, 0), (6, 5), (1, 3), (7, 2000), (4, 17)):
+    #       lg V     T    B  R  k  sk pol cap par tok path val conf cnt fr fc ws wsb      st    s
+    args = [P, 1000, 1.0, 1, 4, 4, 4, 0,  64, P, P, P, P, P, P, P, P, P, 1 << 30, None, None]
+    for i, bad in ((2, 0.0), (2, float("inf")), (5, 17), (5, 0), (6, 5), (1, 3), (8, 2000), (4, 17), (7, 2)):
         a = list(args)
         a[i] = bad
         assert g(*a) == -1, (i, bad)
@@ -172,7 +172,7 @@ def test_host_errors_tree_build(lib):
     a[1] = 64 * 4096 + 1  # vocabulary above 64 chunks
     assert g(*a) == -2
     a = list(args)
-    a[17] = 16
+    a[18] = 16
     assert g(*a) == -5
     assert binding.spec_tree_expand_workspace_size(1, 4, 1000) > 4 * 16 * 8
     assert binding.spec_tree_expand_workspace_size(1, 17, 1000) == 0

@@ -53,8 +53,8 @@ _SIGNATURES = {
                             _I32, _VP, _VP, _VP, _VP],
     "spec_tree_build_init": [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_expand_workspace_size": [_I32, _I32, _I32],
-    "spec_tree_expand": [_VP, _I32, _F32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                         _SZ, _VP, _VP],
+    "spec_tree_expand": [_VP, _I32, _F32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                         _VP, _SZ, _VP, _VP],
     "spec_tree_rerank": [_VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_version": [],
 }
@@ -349,15 +349,18 @@ def spec_tree_build_init(root_token, cand_parent, cand_token, cand_path, cand_va
           _ptr(cand_value), _ptr(cand_conf), _ptr(cand_count), _ptr(frontier), _ptr(frontier_count), _stream(stream))
 
 
+EXPAND_LAYER, EXPAND_BEST_FIRST = 0, 1
+
+
 def spec_tree_expand(draft_logits, T_d, top_k, select_k, cand_parent, cand_token, cand_path, cand_value, cand_conf,
-                     cand_count, frontier, frontier_count, workspace, status=None, stream=None):
+                     cand_count, frontier, frontier_count, workspace, status=None, stream=None, policy=EXPAND_LAYER):
     B, cap, R = _check_state(cand_parent, cand_token, cand_path, cand_value, cand_conf, cand_count, frontier,
                              frontier_count)
     V = draft_logits.shape[-1]
     _check(draft_logits, torch.float32, (B, R, V), "draft_logits")
     _check(workspace, torch.uint8, None, "workspace")
     _check(status, torch.int32, (1,), "status")
-    _call("spec_tree_expand", _ptr(draft_logits), V, float(T_d), B, R, int(top_k), int(select_k), cap,
+    _call("spec_tree_expand", _ptr(draft_logits), V, float(T_d), B, R, int(top_k), int(select_k), int(policy), cap,
           _ptr(cand_parent), _ptr(cand_token), _ptr(cand_path), _ptr(cand_value), _ptr(cand_conf), _ptr(cand_count),
           _ptr(frontier), _ptr(frontier_count), _ptr(workspace), workspace.numel(), _ptr(status), _stream(stream))
 

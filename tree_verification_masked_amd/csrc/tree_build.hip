@@ -94,6 +94,11 @@ __device__ inline uint64_t wave_max_u64_2step(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// (value desc, then t asc): t is depth << 10 | id in the rerank, the id in the best-first frontier
+__device__ inline bool rr_before(double va, uint32_t ta, double vb, uint32_t tb) {
+  return va > vb || (va == vb && ta < tb);
+}
+
 // (value desc, id asc) ordering of candidates and its wave-wide maximum.
 __device__ inline bool tb_better(double v, int i, double ov, int oi) { return ov > v || (ov == v && oi < i); }
 template <int kCtrl, int kRowMask = 0xf>
@@ -127,6 +132,7 @@ __device__ inline void wave_lds_sync() {
 struct TbArgs {
   const float* logits;  // [batch, R, vocab]
   int32_t vocab, nch, R, K, select_k, cap;
+  int32_t policy;  // 0: next frontier among this round's children; 1: among every leaf
   double inv_t;
   ExpScale es;
   int32_t* parent;  // [batch, cap] ...
@@ -482,9 +488,9 @@ __global__ __launch_bounds__(kTbThreads) void tb_select_kernel(TbArgs a) {
   }
   // the next frontier: the select_k new children of largest value (ties to the lower
   // id), each child ranked against all new children by its own thread (branch-free
-  // comparisons over broadcast LDS reads)
+  // comparisons over broadcast LDS reads).  Best-first: tb_frontier_kernel picks it.
   const int sk = min(a.select_k, nnew);
-  if (tid < nnew) {
+  if (a.policy == 0 && tid < nnew) {
     const double v = s_cv[tid];
     int rank = 0;
     for (int q0 = 0; q0 < nnew; q0 += 8) {
@@ -503,6 +509,59 @@ __global__ __launch_bounds__(kTbThreads) void tb_select_kernel(TbArgs a) {
     a.fcount[b] = sk;
     a.count[b] = base + nnew;
   }
+}
+
+// Best-first policy, after the children are appended: the next frontier is the
+// select_k leaves of largest value (ties to the lower id) among every node of the
+// request that has no children and sits above the depth limit.  One thread per node,
+// a bitonic sort as in the rerank.
+__global__ __launch_bounds__(kTbMaxCap) void tb_frontier_kernel(TbArgs a) {
+  __shared__ int s_kid[kTbMaxCap];
+  __shared__ double s_v[kTbMaxCap];
+  __shared__ uint32_t s_t[kTbMaxCap];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (a.fcount[b] == 0) return;  // finished, failed, or refused this round
+  const int cnt = a.count[b];
+  if (cnt < 1 || cnt > a.cap) return;  // (the select kernel has refused such a state)
+  const int64_t cb = (int64_t)b * a.cap;
+  s_kid[tid] = 0;
+  __syncthreads();
+  if (tid >= 1 && tid < cnt) {
+    const int p = a.parent[cb + tid];
+    if (p >= 0 && p < cnt) s_kid[p] = 1;
+  }
+  __syncthreads();
+  const bool leaf = tid < cnt && !s_kid[tid] && (int)(a.path[cb + tid] >> 60) < kTbMaxDepth;
+  double v = leaf ? a.value[cb + tid] : -1.0;  // values are >= 0: non-leaves sort last
+  uint32_t t = leaf ? (uint32_t)tid : 0xffffffffu;
+  const int n_leaves = __syncthreads_count(leaf);
+  int P = 2;
+  while (P < cnt) P <<= 1;
+  for (int k = 2; k <= P; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      double pv;
+      uint32_t pt;
+      if (jj < 64) {
+        pv = __shfl_xor(v, jj);
+        pt = (uint32_t)__shfl_xor((int)t, jj);
+      } else {
+        s_v[tid] = v;
+        s_t[tid] = t;
+        __syncthreads();
+        pv = s_v[tid ^ jj];
+        pt = s_t[tid ^ jj];
+        __syncthreads();
+      }
+      const bool keep_first = ((tid & k) == 0) == ((tid & jj) == 0);
+      const bool partner_first = rr_before(pv, pt, v, t);
+      if (partner_first == keep_first) {
+        v = pv;
+        t = pt;
+      }
+    }
+  const int sk = min(a.select_k, n_leaves);
+  if (tid < sk) a.frontier[(int64_t)b * a.R + tid] = (int)t;
+  if (tid == 0) a.fcount[b] = sk;
 }
 
 __global__ void tb_init_kernel(const int32_t* root_token, int32_t batch, int32_t cap, int32_t R, int32_t* parent,
@@ -530,10 +589,6 @@ struct RrArgs {
   int32_t *out_parent, *out_token, *out_n, *out_id, *status;
 };
 
-// (value desc, then (depth, id) asc); t packs depth << 10 | id
-__device__ inline bool rr_before(double va, uint32_t ta, double vb, uint32_t tb) {
-  return va > vb || (va == vb && ta < tb);
-}
 
 // Bitonic sort of the candidates, one per thread: exchanges within a wavefront go
 // through lane shuffles, the longer ones through LDS.
@@ -674,7 +729,7 @@ extern "C" size_t spec_tree_expand_workspace_size(int32_t batch, int32_t max_fro
 }
 
 extern "C" int spec_tree_expand(const float* draft_logits, int32_t vocab, float T_d, int32_t batch,
-                                int32_t max_frontier, int32_t top_k, int32_t select_k, int32_t cap,
+                                int32_t max_frontier, int32_t top_k, int32_t select_k, int32_t policy, int32_t cap,
                                 int32_t* cand_parent, int32_t* cand_token, uint64_t* cand_path, double* cand_value,
                                 double* cand_conf, int32_t* cand_count, int32_t* frontier, int32_t* frontier_count,
                                 void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
@@ -683,7 +738,8 @@ extern "C" int spec_tree_expand(const float* draft_logits, int32_t vocab, float 
       !frontier || !frontier_count)
     return SPEC_ERR_INVALID_ARG;
   if (batch < 1 || max_frontier < 1 || max_frontier > kTbMaxFrontier || top_k < 1 || top_k > kTbMaxK ||
-      select_k < 1 || select_k > max_frontier || cap < 1 || cap > kTbMaxCap || vocab < top_k)
+      select_k < 1 || select_k > max_frontier || cap < 1 || cap > kTbMaxCap || vocab < top_k ||
+      (policy != 0 && policy != 1))
     return SPEC_ERR_INVALID_ARG;
   if (!(T_d > 0.0f) || !isfinite(T_d)) return SPEC_ERR_INVALID_ARG;
   if (vocab > kTbMaxChunks * kChunk) return SPEC_ERR_UNSUPPORTED;
@@ -699,6 +755,7 @@ extern "C" int spec_tree_expand(const float* draft_logits, int32_t vocab, float 
   a.R = max_frontier;
   a.K = top_k;
   a.select_k = select_k;
+  a.policy = policy;
   a.cap = cap;
   a.inv_t = 1.0 / (double)T_d;
   a.es = make_exp_scale(a.inv_t);
@@ -744,6 +801,10 @@ extern "C" int spec_tree_expand(const float* draft_logits, int32_t vocab, float 
   SPEC_LAUNCH_CHECK();
   hipLaunchKernelGGL(tb_select_kernel, dim3((unsigned)batch), dim3(kTbThreads), 0, st, a);
   SPEC_LAUNCH_CHECK();
+  if (policy == 1) {
+    hipLaunchKernelGGL(tb_frontier_kernel, dim3((unsigned)batch), dim3(kTbMaxCap), 0, st, a);
+    SPEC_LAUNCH_CHECK();
+  }
   return SPEC_OK;
 }
 

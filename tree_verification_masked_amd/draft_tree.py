@@ -40,10 +40,14 @@ class DraftTree:
     def init(self, root_tokens, stream=None):
         B.spec_tree_build_init(root_tokens, *self.state(), stream=stream)
 
-    def expand(self, draft_logits, T_d: float, top_k: int, select_k: int | None = None, stream=None):
-        """draft_logits [batch, max_frontier, vocab] fp32: row j = the drafter at frontier[b][j]."""
+    def expand(self, draft_logits, T_d: float, top_k: int, select_k: int | None = None, stream=None,
+               policy: str = "layer"):
+        """draft_logits [batch, max_frontier, vocab] fp32: row j = the drafter at frontier[b][j].
+        policy "layer" (EAGLE-2: the next frontier among this round's children) or
+        "best_first" (DDTree: among every unexpanded node)."""
+        pol = {"layer": B.EXPAND_LAYER, "best_first": B.EXPAND_BEST_FIRST}[policy]
         B.spec_tree_expand(draft_logits, T_d, top_k, top_k if select_k is None else select_k, *self.state(),
-                           self.workspace, status=self.status, stream=stream)
+                           self.workspace, status=self.status, stream=stream, policy=pol)
 
     def rerank(self, n_final: int, out=None, stream=None):
         """Returns (parent, tokens, n_nodes, cand_id) of the flattened trees."""
