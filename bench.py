@@ -294,23 +294,24 @@ def time_kv_commit(step, dev, k_src, v_src, stream, iters=200, layers=1):
                     "copy after the timed region"}
 
 
-def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60):
-    """EAGLE-2 tree construction on the GPU for the 60-node verify tree: init, six
-    expand rounds (top-10 over a 128256-token vocabulary) and the rerank, with the
-    draft rows of every round already resident (generated once, per node path).  The
-    rows a round reads are its algorithmic bytes."""
+def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60, select_k=None, policy="layer"):
+    """Draft-tree construction on the GPU for the 60-node verify tree: init, the expand
+    rounds (top-10 over a 128256-token vocabulary; EAGLE-2 layer rounds or best-first
+    pops) and the rerank, with the draft rows of every round already resident
+    (generated once, per node path).  The rows a round reads are its algorithmic bytes."""
+    sk = k if select_k is None else select_k
     import torch
 
     from tree_verification_masked_amd import synth
     from tree_verification_masked_amd.draft_tree import DraftTree
 
-    dt = DraftTree(1, 1024, k, V)
+    dt = DraftTree(1, 1024, sk, V)
     root = torch.tensor([int(np.random.default_rng(seed).integers(V))], dtype=torch.int32, device="cuda")
     dt.init(root)
     rounds, row_bytes = [], 0
     for _ in range(depth):  # one untimed build fixes each round's frontier and rows
         st = dt.host_state()
-        rows = np.zeros((1, k, V), np.float32)
+        rows = np.zeros((1, sk, V), np.float32)
         fc = int(st["frontier_count"][0])
         for j in range(fc):
             nd, path = int(st["frontier"][0, j]), []
@@ -320,7 +321,7 @@ def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60):
             rows[0, j] = synth.path_row(seed, tuple(path[::-1]), V)
         rounds.append(torch.from_numpy(rows).cuda())
         row_bytes += fc * V * 4
-        dt.expand(rounds[-1], 1.0, k)
+        dt.expand(rounds[-1], 1.0, k, sk, policy=policy)
     out = dt.rerank(n_final)
     torch.cuda.synchronize()
     ref = [t.clone() for t in out]
@@ -328,7 +329,7 @@ def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60):
     def build():
         dt.init(root)
         for r in rounds:
-            dt.expand(r, 1.0, k)
+            dt.expand(r, 1.0, k, sk, policy=policy)
         dt.rerank(n_final, out=out)
 
     for _ in range(5):
@@ -344,8 +345,10 @@ def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60):
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / iters
     assert int(dt.status.item()) == 0 and all(torch.equal(a, b) for a, b in zip(out, ref))
-    return {"call": "spec_tree_build_init + 6 x spec_tree_expand + spec_tree_rerank (1 request)",
-            "workload": f"EAGLE-2 top-{k}, depth {depth}, {n_final} nodes, vocabulary {V}, T_d = 1",
+    kind = f"EAGLE-2 top-{k}, depth {depth}" if policy == "layer" else \
+        f"best-first top-{k}, {depth} rounds of {sk} pops"
+    return {"call": f"spec_tree_build_init + {depth} x spec_tree_expand + spec_tree_rerank (1 request)",
+            "workload": f"{kind}, {n_final} nodes, vocabulary {V}, T_d = 1",
             "us_per_tree": round(us, 2), "draft_row_bytes": row_bytes,
             "gbs": round(row_bytes / (us * 1e-6) / 1e9, 1), "iters": iters,
             "note": "the drafter's rows are inputs (resident); its forward passes are not part of this"}
@@ -510,6 +513,9 @@ def main():
             "kv_commit_32_layers": time_kv_commit(step, dev, replicas[0]["k"], replicas[0]["v"], stream, layers=32),
         }
     res.setdefault("next_rows", {})["tree_build"] = time_tree_build(args.seed)
+    # the best-first (heap) variant: 16 rounds of 4 pops, top-8 children
+    res["next_rows"]["tree_build_best_first"] = time_tree_build(args.seed, k=8, depth=16, select_k=4,
+                                                                policy="best_first")
 
     if not args.no_cpu_baseline:
         import oracle
