@@ -94,6 +94,10 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="issue the whole step on one stream (default: mask + attention on a second stream)")
+    ap.add_argument("--fork", choices=("start", "after_softmax"), default="start",
+                    help="where the second stream branches off: at the step's start or after the logit pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cost-table", metavar="PREFIX", default=None,
                     help="sweep (batch, context, nodes) and write PREFIX.json and PREFIX.md: the verify-latency "
@@ -402,7 +406,7 @@ def cost_table(args):
                                      "v": vf[:Bn, : ctx + N].clone(), "tgt_logits": pt["tgt_logits"].clone(),
                                      "dft_logits": pt["dft_logits"].clone()})
                 pt.update(q=replicas[0]["q"], k=replicas[0]["k"], v=replicas[0]["v"])
-                step = VerifyStep(pt)
+                step = VerifyStep(pt).overlap()
                 ms, st = time_steps(step, replicas, stream, args.steps, args.warmup)
                 rows.append({"batch": Bn, "ctx": ctx, "n_nodes": N, "step_us": round(ms * 1e3, 2),
                              "attention_us": round(float(st[1]), 2),
@@ -454,6 +458,8 @@ def main():
     inp = synth.make_config(args.config, seed=args.seed, T=T)
     dev = to_device(inp)
     step = VerifyStep(dev)
+    if not args.serial:
+        step.overlap(fork=args.fork)  # mask + attention on a second stream
     big = [k for k in ("q", "k", "v", "tgt_logits", "dft_logits") if k in dev]
     replicas = [{k: dev[k].clone() for k in big} for _ in range(args.replicas)]
     stream = torch.cuda.current_stream()
@@ -487,7 +493,10 @@ def main():
         "config": {
             "workload": synth.CONFIGS[args.config], "batch": inp["B"], "n_nodes": int(inp["n_nodes"].max()),
             "ctx": int(inp["ctx_len"].max()), "hq": inp["hq"], "hkv": inp["hkv"], "head_dim": inp["d"],
-            "vocab": inp["V"], "T": inp["T"], "replicas": args.replicas, "launch": "stream (no graph)",
+            "vocab": inp["V"], "T": inp["T"], "replicas": args.replicas,
+            "launch": "one stream (no graph)" if args.serial or step.side is None else
+                      ("two streams: mask + attention beside softmax + sampling (no graph)" if step.fork == "start"
+                       else "two streams: mask + attention beside the sampling, after the logit pass (no graph)"),
         },
         "step_bytes": step_b,
         "step_gbs": round(step_b / (ms_per_step * 1e-3) / 1e9, 1),

@@ -458,7 +458,7 @@ def test_full_step(cfg, T):
     say("full step", cfg, T)
     inp = synth.make_config(cfg, seed=11, T=T)
     d = to_device(inp)
-    st = VerifyStep(d)
+    st = VerifyStep(d).overlap()  # mask + attention on a second stream, as the benchmark runs it
     st.run()
     got = st.results()
     assert got["status"][0] == 0
@@ -481,3 +481,37 @@ def test_full_step(cfg, T):
     sep = st.results()
     for k in fused:
         assert np.array_equal(fused[k], sep[k]), k
+
+
+@pytest.mark.parametrize("cfg,fork", [(2, "start"), (2, "after_softmax"), (4, "after_softmax")])
+def test_two_stream_step_equals_one_stream_step(cfg, fork):
+    """The step with mask + attention on a second stream gives, bit for bit, what the
+    one-stream step gives, over consecutive steps that rotate input copies (each
+    step's side branch must wait for the previous step, and the caller's stream for
+    the side branch)."""
+    say("two-stream step", cfg, fork)
+    inp = synth.make_config(cfg, seed=5, T=1.0)
+    d = to_device(inp)
+    reps = [{k: d[k].clone() for k in ("q", "k", "v", "tgt_logits", "dft_logits")} for _ in range(3)]
+    reps[1]["q"].mul_(-1)  # three different inputs
+    reps[2]["tgt_logits"].add_(0.25 * torch.randn_like(reps[2]["tgt_logits"]))
+    keys = ("anc", "attn", "tmax", "tsum", "dsum", "accepted_child", "term_token", "path_nodes", "out_tokens",
+            "accept_len", "status")
+    serial = VerifyStep(d)
+    want = []
+    for r in reps:
+        serial.run(replica=r)
+        want.append({k: v for k, v in serial.results().items() if k in keys})
+    two = VerifyStep(d).overlap(fork=fork)
+    names = {"anc": "anc", "attn": "attn_out"}
+    for rnd in range(2):
+        for i, r in enumerate(reps):
+            two.run(replica=r)
+            # copies on the caller's stream only (no device-wide synchronisation): the
+            # join must already cover the side branch
+            got = {k: getattr(two, names.get(k, k)).cpu() for k in keys}
+            got["anc"] = got["anc"].numpy().view(np.uint64)
+            got["attn"] = got["attn"].float().numpy()
+            for k in keys:
+                g = got[k] if isinstance(got[k], np.ndarray) else got[k].numpy()
+                assert np.array_equal(g, want[i][k]), (rnd, i, k)
