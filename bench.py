@@ -226,6 +226,35 @@ def time_calls(call, replicas, iters=200):
     return t0.elapsed_time(t1) * 1e3 / iters
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def step_percentiles(step, replicas, stream, steps, first=0):
+    """Per-step durations (us) of the clean step sequence from one event at every step
+    boundary on the caller's stream (which the step joins), as p10 / p50 / p90; each
+    event adds its own small cost to the step it closes."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    prefill()
+    ev[0].record(stream)
+    for i in range(steps):
+        step.run(replica=replicas[(first + i) % len(replicas)])
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e3
+    return {"p10": round(float(np.percentile(d, 10)), 2), "p50": round(float(np.percentile(d, 50)), 2),
+            "p90": round(float(np.percentile(d, 90)), 2), "mean": round(float(d.mean()), 2), "steps": steps}
+
+
 def deepest_paths(parent, n_nodes):
     """Per request, the root-to-leaf path to the first deepest node (a full accept)."""
     B, n_max = parent.shape
@@ -467,6 +496,7 @@ def main():
     # warm-up, the clean timed region, then an instrumented pass with events around
     # every stage of every step
     ms_per_step, st_mean = time_steps(step, replicas, stream, args.steps, args.warmup)
+    pct = step_percentiles(step, replicas, stream, args.steps)
     names = ["mask_build", "attention", "softmax_pair", "-", "reject_sample", "-"]
 
     attn_b, logit_b, samp_b = algorithmic_bytes(inp)
@@ -498,6 +528,9 @@ def main():
                       ("two streams: mask + attention beside softmax + sampling (no graph)" if step.fork == "start"
                        else "two streams: mask + attention beside the sampling, after the logit pass (no graph)"),
         },
+        # one event per step boundary: the distribution of single steps (the events'
+        # own cost included, so the mean sits a little above ms_per_step)
+        "step_us_percentiles": pct,
         "step_bytes": step_b,
         "step_gbs": round(step_b / (ms_per_step * 1e-3) / 1e9, 1),
         "step_frac_of_hbm": round(step_b / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -539,7 +572,18 @@ def main():
         el = time.perf_counter() - t_start
         res["cpu_baseline"] = {"value": round(n / el, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
                                "sample": f"{n} full steps of the same workload (all attention rows, lazy walk), "
-                                         f"{el:.1f} s"}
+                                         f"{el:.1f} s", "cpu": cpu_model(), "host_cores": os.cpu_count()}
+        # the same oracle on one thread, a few steps (about 1 / threads of the rate)
+        oracle.set_threads(1)
+        n1, t_start = 0, time.perf_counter()
+        while True:
+            oracle.verify_step(inp)
+            n1 += 1
+            if time.perf_counter() - t_start >= args.cpu_seconds / 2:
+                break
+        el1 = time.perf_counter() - t_start
+        res["cpu_baseline"]["single_thread"] = {"value": round(n1 / el1, 4), "unit": "steps/s", "cores": 1,
+                                                "sample": f"{n1} full steps, {el1:.1f} s"}
     print(json.dumps(res))
 
 
