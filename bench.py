@@ -274,6 +274,45 @@ def deepest_paths(parent, n_nodes):
     return path, L
 
 
+def time_layers_step(step, dev, replicas, stream, layers=32, iters=20, warmup=3):
+    """The 32-layer-equivalent step: mask, then one attention call per layer over its
+    own KV buffers (the same Q), beside one sampling pass (two streams, as the step).
+    Returns us per step and the attention bytes' rate."""
+    import torch
+
+    kv = [(torch.randn_like(dev["k"]), torch.randn_like(dev["v"])) for _ in range(layers)]
+    side = step.side if step.side is not None else stream
+
+    def one(r):
+        if side is not stream:
+            step.ev_fork.record(stream)
+            side.wait_event(step.ev_fork)
+        step.mask(side)
+        for k, v in kv:
+            step.attention(side, r["q"], k, v)
+        if side is not stream:
+            step.ev_join.record(side)
+        step.softmax(stream, r["tgt_logits"], r.get("dft_logits"))
+        step.reject(stream, r["tgt_logits"], r.get("dft_logits"))
+        if side is not stream:
+            stream.wait_event(step.ev_join)
+
+    for i in range(warmup):
+        one(replicas[i % len(replicas)])
+    torch.cuda.synchronize()
+    prefill()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(iters):
+        one(replicas[i % len(replicas)])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / iters
+    del kv
+    return us
+
+
 def time_kv_commit(step, dev, k_src, v_src, stream, iters=200, layers=1):
     """The commit after the step (``layers`` layers' K and V, in one call: one layer, or
     a whole model's cache stacked on a leading axis) along each tree's deepest path
@@ -556,6 +595,13 @@ def main():
         }
     res.setdefault("next_rows", {})["tree_build"] = time_tree_build(args.seed)
     # the best-first (heap) variant: 16 rounds of 4 pops, top-8 children
+    if step.with_attention and dev.get("block_table") is None:
+        us32 = time_layers_step(step, dev, replicas, stream)
+        res["step_32_layers"] = {
+            "what": "mask + 32 attention calls (one per layer, each over its own KV buffers) beside one sampling "
+                    "pass; the pages name no layer count, so this is a secondary figure",
+            "us_per_step": round(us32, 2), "steps_per_s": round(1e6 / us32, 1),
+            "attention_gbs": round(32 * attn_b / (us32 * 1e-6) / 1e9, 1)}
     res["next_rows"]["tree_build_best_first"] = time_tree_build(args.seed, k=8, depth=16, select_k=4,
                                                                 policy="best_first")
 

@@ -378,6 +378,7 @@ def test_attention_full_size_sampled_rows(cfg):
 
 
 def _custom_attention_case(rng, B_, n_max, hq, hkv, d, ctxs, n_nodes, bf16, paged=False):
+    page = paged if paged not in (True, False) else 16  # paged: True (16-token pages) or a page size
     parent = np.full((B_, n_max), -1, np.int32)
     for b in range(B_):
         for i in range(1, n_nodes[b]):
@@ -388,7 +389,6 @@ def _custom_attention_case(rng, B_, n_max, hq, hkv, d, ctxs, n_nodes, bf16, page
                tgt_logits=np.zeros((B_, n_max, 16), np.float32), block_table=None, page_size=0, n_pages=0)
     q = rng.standard_normal((B_, n_max, hq, d), dtype=np.float32)
     if paged:
-        page = 16
         need = [-(-(int(ctxs[b]) + n_max) // page) for b in range(B_)]
         n_pages = sum(need) + 2
         perm = rng.permutation(n_pages).astype(np.int32)
@@ -419,6 +419,10 @@ def _custom_attention_case(rng, B_, n_max, hq, hkv, d, ctxs, n_nodes, bf16, page
     ("padded trees bf16", 4, 40, 16, 4, 128, [10, 200, 1, 1500], [40, 17, 2, 33], True, False),
     ("paged ragged bf16", 3, 12, 16, 4, 128, [1, 47, 1000], [12, 5, 9], True, True),
     ("paged fp32 d64", 2, 5, 4, 4, 64, [31, 100], [5, 4], False, True),
+    ("paged 64-token pages bf16 mfma", 2, 24, 32, 8, 128, [3000, 77], [24, 11], True, 64),
+    ("paged 128-token pages bf16 d64", 3, 8, 16, 2, 64, [1, 600, 2049], [8, 8, 2], True, 128),
+    ("gqa 8 per group, 64 nodes", 1, 64, 64, 8, 128, [777], [64], True, False),
+    ("mha 1 per group bf16 mfma", 1, 30, 4, 4, 128, [1234], [30], True, False),
     ("empty prompt", 2, 10, 8, 8, 64, [0, 0], [10, 1], True, False),
     # one KV head, long context: more key splits than a wavefront has lanes
     ("many splits fp32 shuffle", 1, 4, 1, 1, 64, [12800], [4], False, False),
