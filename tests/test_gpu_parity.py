@@ -250,6 +250,24 @@ def test_sampling_many_small_vocab_trees(cfg):
     assert ties <= max(2, n // 20)
 
 
+@pytest.mark.parametrize("cfg,V", [(2, 4097), (2, 10003), (4, 9001), (5, 12292)])
+def test_sampling_ragged_vocab(cfg, V):
+    """Vocabularies whose last chunk is partial and (but for 12292) not a multiple of
+    four tokens: the sampler's scalar load paths and its partial last chunk, several
+    seeds, against the oracle."""
+    ties, n = 0, 0
+    for seed in range(6 if cfg != 4 else 2):
+        say("sampling ragged vocab", cfg, V, seed)
+        inp = synth.make_config(cfg, seed=200 + seed, with_kv=False, vocab_override=V)
+        got = _sampling_gpu(inp)
+        ref = _oracle_sampling(inp)
+        assert got["status"][0] == 0
+        ties += _compare_sampling(got, ref, inp["n_nodes"])
+        n += inp["B"]
+    print(f"near ties: {ties} / {n}")
+    assert ties <= max(2, n // 10)
+
+
 @pytest.mark.parametrize("qkind,k", [("noisy", 1), ("noisy", 4), ("zeros", 2), ("onehot", 3), ("equal", 2)])
 def test_sampling_star_trials(qkind, k):
     """10^5 tiny stars in one batched call, bit-exact against the oracle; the emitted
