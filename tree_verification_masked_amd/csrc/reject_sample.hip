@@ -1118,21 +1118,23 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
                                (uint32_t)rl_i((int)(uint32_t)v, l));
           };
           auto rl_d = [&](double v, int l) { return __longlong_as_double(rl_ll(__double_as_longlong(v), l)); };
+          // The thresholds depend only on earlier rejections, not on the tests'
+          // outcomes, so the serial pass carries the (c, W) recursion alone, for every
+          // level, and lane l keeps the state child l is tested with; the tests then
+          // run in parallel and the first accepted level wins.  The same arithmetic as
+          // testing level by level, without the division on the serial path.
           double c = 0.0, W = 1.0;
-          int acc0 = SPEC_NODE_NONE, lvl = 0, zl = 0, pend = 0;
-          uint64_t m = 0;
+          int zl = 0, pend_at = kk;  // pend_at: the first transition that leaves its interval
+          double c_my = 0.0, W_my = 1.0;
           for (int l = 0; l < kk; ++l) {
-            m = (uint64_t)rl_ll((long long)rest_l, l);
-            const float u = __int_as_float(rl_i(__float_as_int(u_l), l));
-            if ((double)u < accept_ratio(rl_d(px_l, l), rl_d(qx_l, l), c, W)) {
-              acc0 = rl_i(ci_l, l);
-              break;
+            if (lane == l) {
+              c_my = c;
+              W_my = W;
             }
-            ++lvl;  // cn = c + W is the threshold after this rejection
-            const double cn = c + W;
+            const double cn = c + W;  // the threshold after a rejection at this level
             const double ia = rl_d(ia_l, l), ib = rl_d(ib_l, l);
             if (!(cn >= ia && cn <= ib)) {
-              pend = 1;
+              pend_at = l;
               break;
             }
             long long lp = rl_ll(lp_l, l), lq = rl_ll(lq_l, l);
@@ -1149,6 +1151,24 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
             } else {
               zl = 1;  // the residual keeps its previous threshold
             }
+          }
+          // levels 0 .. min(kk, pend_at + 1) - 1 have their test inputs
+          const bool ok = lane < min(kk, pend_at + 1) && (double)u_l < accept_ratio(px_l, qx_l, c_my, W_my);
+          const uint64_t okm = __ballot(ok);
+          int acc0 = SPEC_NODE_NONE, lvl, pend = 0;
+          uint64_t m;
+          if (okm) {  // the first accepted level (the state is not used after an acceptance)
+            const int l = __ffsll((unsigned long long)okm) - 1;
+            acc0 = rl_i(ci_l, l);
+            lvl = l;
+            m = (uint64_t)rl_ll((long long)rest_l, l);
+          } else if (pend_at < kk) {  // every tested child rejected, then a transition to finish directly
+            lvl = pend_at + 1;
+            pend = 1;
+            m = (uint64_t)rl_ll((long long)rest_l, pend_at);
+          } else {  // every child rejected
+            lvl = kk;
+            m = (uint64_t)rl_ll((long long)rest_l, kk - 1);
           }
           if (lane == 0) s_st = SibState{m, c, W, acc0, lvl, zl, pend};
         }
