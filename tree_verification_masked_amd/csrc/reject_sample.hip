@@ -36,7 +36,9 @@
 //       list, and per-chunk sums for the terminal draw.  Only tokens in buckets
 //       that straddle an interval end get an exact fp64 ratio.
 //   R3  one workgroup per node: sibling tests with exact W(c_j) from R2's sums and
-//       list, terminal draws located by exact chunk sums and one chunk scan; the
+//       list (the thresholds c_j follow from the rejections alone, so they are
+//       computed first and the tests then run side by side), terminal draws
+//       located by exact chunk sums and one chunk scan; the
 //       last workgroup of a request walks from the root and writes the outputs.
 //       Each node clears the chain state it consumed, so the next call finds the
 //       workspace ready without any cross-workgroup wait.
