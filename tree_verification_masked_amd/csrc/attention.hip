@@ -106,7 +106,6 @@ __device__ inline int kv_swz(int key) {
   return ((((key & 3) << 1) | ((key >> 2) & 1) | (key & 8))) & (CH - 1);
 }
 typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 __device__ inline float xor32_f(float v) {  // the value of lane l ^ 32
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -131,24 +130,7 @@ __device__ inline void lds_barrier() {
 __device__ inline uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
-// Eight 16-byte reads and their wait, likewise: read 2j at ad[j], read 2j+1 at
-// ad[j] + OFF1 (the same K chunk of the second 32-key block).
 typedef int v4i __attribute__((ext_vector_type(4)));
-template <int OFF1>
-__device__ inline void ds_read_b128_x8(v4i (&r)[8], const uint32_t (&ad)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n"
-      "ds_read_b128 %1, %8 offset:%12\n"
-      "ds_read_b128 %2, %9\n"
-      "ds_read_b128 %3, %9 offset:%12\n"
-      "ds_read_b128 %4, %10\n"
-      "ds_read_b128 %5, %10 offset:%12\n"
-      "ds_read_b128 %6, %11\n"
-      "ds_read_b128 %7, %11 offset:%12\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "n"(OFF1));
-}
 // Four 16-byte reads and their wait.
 __device__ inline void ds_read_b128_x4(v4i (&r)[4], const uint32_t (&ad)[4]) {
   asm volatile(
