@@ -1,9 +1,12 @@
 """Benchmark of one tree-verification step on one MI355X.
 
-A step is the whole hot path over one input set, issued on one HIP stream:
+A step is the whole hot path over one input set:
     spec_tree_mask_build, spec_tree_attention (one layer's KV), spec_tree_softmax
     (target rows, and draft rows at T > 0), spec_tree_reject_sample (whose final walk
     also writes the accepted path, the result of spec_accept_path).
+The first two share no data with the last two, so by default they run on a second
+HIP stream, forked from and joined back into the timing stream by events
+(``--serial``: all four on one stream).
 Workload (default): the Llama-3-8B-shaped step -- one request, a 60-node EAGLE-2
 tree (top-k 10, depth 6), 4096 cached tokens, 32 query / 8 KV heads, head_dim 128,
 bf16 KV, fp32 logits over a 128256-token vocabulary, T = 1.  Synthetic, seeded.
@@ -17,9 +20,12 @@ per-stage durations.  The call holding the longest kernel (tree attention) gives
 roofline entry and the logit softmax a second one; each is timed back to back on its
 own, so no event sits between its kernels.  Measured HBM traffic per call comes
 from the committed counter summary under profiles/ while the kernel sources match.  The CPU oracle is timed on the host on full steps of the same
-workload.  After the timed regions the KV commit that follows a step (one layer, the
-deepest path of the tree) is timed on a scratch copy of the cache and reported under
-"next_rows".  Prints one JSON line.
+workload (multi-threaded, and on one thread).  A third pass with one event per step
+boundary gives the p10 / p50 / p90 of single steps.  After the timed regions come a
+32-layer-equivalent step (32 attention calls over their own KV beside one sampling
+pass), and, under "next_rows", the KV commit that follows a step (one layer, and 32
+layers in one call, the deepest path of the tree, on a scratch copy of the cache) and
+the draft-tree construction (EAGLE-2 and best-first).  Prints one JSON line.
 
 ``--cost-table PREFIX`` instead sweeps the step over (batch, context, nodes) and writes
 the verify-latency table (PREFIX.json, PREFIX.md) that cost_table.CostTable reads.
