@@ -518,35 +518,69 @@ __global__ __launch_bounds__(64) void plan_kernel(RejArgs a, NodeWs w, int chunk
 // ---------------------------------------------------------------------------
 // R1: ratio histogram
 // ---------------------------------------------------------------------------
-// Items are (active node, chunk) pairs, item = slot * nch + chunk, visited
-// grid-stride.  The first item's node id is read together with the item count.
+// Items are (active node, group of cg consecutive chunks) pairs, item = slot *
+// ngroups + group, visited grid-stride; a workgroup accumulates its group's chunks in
+// LDS and merges them into the node's histogram with one set of integer atomics.
+// Those atomics are what limits the launch when many nodes are active (every node's
+// buckets receive one per group), so cg grows with the active (node, chunk) count --
+// about 512 items, one round of resident workgroups -- up to four chunks.  Every
+// workgroup derives the same cg from the count.  The first item's node id is read
+// together with the count.
+constexpr int kMaxCg = 4;  // chunks per R1 item at most
 __global__ __launch_bounds__(kCThreads) void chain_hist_kernel(RejArgs a, NodeWs w) {
   __shared__ unsigned long long s_P[4][kHN], s_Q[4][kHN];  // copy (wave % 4): few lanes ever meet
   const int tid = threadIdx.x, cp = (tid >> 6) & 3;
   const int nodes = a.batch * a.n_max;
-  const int items = (int)(*w.act_count) * a.nch;
-  const int first_nd = w.act_list[min((int)blockIdx.x / a.nch, nodes - 1)];
+  const int act = (int)(*w.act_count);
+  const int cg = min(kMaxCg, max(1, (act * a.nch + 511) / 512));
+  const int ng = cg == 1 ? a.nch : (a.nch + cg - 1) / cg;  // groups per node
+  const int items = act * ng;
+  const int first_nd = w.act_list[min((int)blockIdx.x / ng, nodes - 1)];
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int nd = it == (int)blockIdx.x ? first_nd : w.act_list[it / a.nch];
-    const int chunk = it % a.nch;
+    const int nd = it == (int)blockIdx.x ? first_nd : w.act_list[it / ng];
+    const int c_first = (it % ng) * cg, c_last = min(a.nch, c_first + cg);
     const NodeInfo inf = w.info[nd];
     const float mt = a.tgt_max[nd], md = a.dft_max[nd];
+    const float* lt = a.tgt_logits + (int64_t)nd * a.vocab;
+    const float* ld = a.dft_logits + (int64_t)nd * a.vocab;
+    // the group's first chunk is in flight while the LDS histograms are cleared, and
+    // each later chunk while the previous one is binned
     float xl[kCPer], xd[kCPer];
-    load_chunk4(a.tgt_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xl);
-    load_chunk4(a.dft_logits + (int64_t)nd * a.vocab, chunk * kChunk, a.vocab, a.vec, xd);
+    load_chunk4(lt, c_first * kChunk, a.vocab, a.vec, xl);
+    load_chunk4(ld, c_first * kChunk, a.vocab, a.vec, xd);
     for (int i = tid; i < 4 * kHN; i += blockDim.x) {
       (&s_P[0][0])[i] = 0;
       (&s_Q[0][0])[i] = 0;
     }
     __syncthreads();
+    auto bin = [&](const float* bl, const float* bd) {
 #pragma unroll
-    for (int s2 = 0; s2 < kCPer; ++s2) {
-      const float ep = exp2_arg(xl[s2], mt, a.est), eq = exp2_arg(xd[s2], md, a.esd);
-      const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
-      const int h = est_bucket(ep, eq, pp, qq, inf.K);
-      if (h >= 0) {
-        atomicAdd(&s_P[cp][h], (unsigned long long)fx42(pp));
-        atomicAdd(&s_Q[cp][h], (unsigned long long)fx42(qq));
+      for (int s2 = 0; s2 < kCPer; ++s2) {
+        const float ep = exp2_arg(bl[s2], mt, a.est), eq = exp2_arg(bd[s2], md, a.esd);
+        const float pp = __builtin_amdgcn_exp2f(ep), qq = __builtin_amdgcn_exp2f(eq);
+        const int h = est_bucket(ep, eq, pp, qq, inf.K);
+        if (h >= 0) {
+          atomicAdd(&s_P[cp][h], (unsigned long long)fx42(pp));
+          atomicAdd(&s_Q[cp][h], (unsigned long long)fx42(qq));
+        }
+      }
+    };
+    if (cg == 1) {
+      bin(xl, xd);
+    } else {
+      for (int chunk = c_first; chunk < c_last; ++chunk) {
+        float yl[kCPer], yd[kCPer];
+        if (chunk + 1 < c_last) {
+          load_chunk4(lt, (chunk + 1) * kChunk, a.vocab, a.vec, yl);
+          load_chunk4(ld, (chunk + 1) * kChunk, a.vocab, a.vec, yd);
+        }
+        bin(xl, xd);
+        if (chunk + 1 < c_last)
+#pragma unroll
+          for (int s2 = 0; s2 < kCPer; ++s2) {
+            xl[s2] = yl[s2];
+            xd[s2] = yd[s2];
+          }
       }
     }
     __syncthreads();
