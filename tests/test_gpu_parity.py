@@ -222,7 +222,7 @@ def _oracle_sampling(inp):
 
 
 @pytest.mark.parametrize("cfg,T,seeds", [(1, 1.0, range(6)), (2, 1.0, range(3)), (2, 0.0, range(3)),
-                                         (3, None, range(2)), (4, 1.0, range(1)), (5, 1.0, range(2))])
+                                         (3, None, range(2)), (4, 1.0, range(4)), (5, 1.0, range(2))])
 def test_sampling_full_vocab(cfg, T, seeds):
     ties = 0
     for seed in seeds:
