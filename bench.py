@@ -189,23 +189,39 @@ def run_steps(step, replicas, stream, n, first=0, events=None):
         ev[6].record(stream)
 
 
-def time_steps(step, replicas, stream, steps, warmup):
-    """(ms per step over a clean timed region, mean us per stage from an instrumented pass)."""
+def host_prefill_ms(host_us_per_step, steps):
+    """A spin long enough for the host to queue `steps` steps behind it (with margin)."""
+    return max(20.0, 1.5 * host_us_per_step * steps / 1e3 + 5.0)
+
+
+def time_steps(step, replicas, stream, steps, warmup, info=None):
+    """(ms per step over a clean timed region, mean us per stage from an instrumented pass).
+    The spin kernel ahead of each timed region is sized from the host's measured
+    queueing time per step, so the GPU never waits for the host inside the region;
+    `info` (a dict) receives that time and whether the host finished queueing first."""
     import torch
 
+    h = time.perf_counter()
     run_steps(step, replicas, stream, warmup)
+    host_us = (time.perf_counter() - h) * 1e6 / max(warmup, 1)
     torch.cuda.synchronize()
-    prefill()
+    pre = host_prefill_ms(host_us, steps)
+    prefill(pre)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
+    h = time.perf_counter()
     run_steps(step, replicas, stream, steps, first=warmup)
+    queued_ms = (time.perf_counter() - h) * 1e3
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / steps
+    if info is not None:
+        info.update(host_queue_us_per_step=round(queued_ms * 1e3 / steps, 2), spin_ms=round(pre, 1),
+                    host_ahead=bool(queued_ms < pre))
     assert int(step.status.item()) == 0, f"device status {int(step.status.item())}"
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
-    prefill()
+    prefill(2 * pre)  # this pass records seven events per step as well
     run_steps(step, replicas, stream, steps, first=0, events=evs)
     torch.cuda.synchronize()
     stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(6)] for e in evs]) * 1e3  # us
@@ -250,7 +266,10 @@ def step_percentiles(step, replicas, stream, steps, first=0):
     import torch
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    prefill()
+    h = time.perf_counter()
+    step.run(replica=replicas[first % len(replicas)])
+    torch.cuda.synchronize()
+    prefill(host_prefill_ms((time.perf_counter() - h) * 1e6, steps))
     ev[0].record(stream)
     for i in range(steps):
         step.run(replica=replicas[(first + i) % len(replicas)])
@@ -540,7 +559,8 @@ def main():
 
     # warm-up, the clean timed region, then an instrumented pass with events around
     # every stage of every step
-    ms_per_step, st_mean = time_steps(step, replicas, stream, args.steps, args.warmup)
+    timing = {}
+    ms_per_step, st_mean = time_steps(step, replicas, stream, args.steps, args.warmup, timing)
     pct = step_percentiles(step, replicas, stream, args.steps)
     names = ["mask_build", "attention", "softmax_pair", "-", "reject_sample", "-"]
 
@@ -576,6 +596,8 @@ def main():
         # one event per step boundary: the distribution of single steps (the events'
         # own cost included, so the mean sits a little above ms_per_step)
         "step_us_percentiles": pct,
+        # the host's queueing time per step and whether it stayed ahead of the GPU
+        "host_queue": timing,
         "step_bytes": step_b,
         "step_gbs": round(step_b / (ms_per_step * 1e-3) / 1e9, 1),
         "step_frac_of_hbm": round(step_b / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
