@@ -194,6 +194,31 @@ def host_prefill_ms(host_us_per_step, steps):
     return max(20.0, 1.5 * host_us_per_step * steps / 1e3 + 5.0)
 
 
+def gpu_time_us(fn, iters, warmup, stream=None):
+    """GPU time per call of fn() (us), fn issued `iters` times back to back after
+    `warmup` untimed calls, queued behind a spin sized from the host's measured
+    queueing time per call.  Returns (us per call, host us per call, host ahead)."""
+    import torch
+
+    h = time.perf_counter()
+    for i in range(warmup):
+        fn(i)
+    host_us = (time.perf_counter() - h) * 1e6 / max(warmup, 1)
+    torch.cuda.synchronize()
+    pre = host_prefill_ms(host_us, iters)
+    prefill(pre)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    h = time.perf_counter()
+    for i in range(iters):
+        fn(i)
+    queued_ms = (time.perf_counter() - h) * 1e3
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / iters, queued_ms * 1e3 / iters, queued_ms < pre
+
+
 def time_steps(step, replicas, stream, steps, warmup, info=None):
     """(ms per step over a clean timed region, mean us per stage from an instrumented pass).
     The spin kernel ahead of each timed region is sized from the host's measured
@@ -232,20 +257,8 @@ def time_calls(call, replicas, iters=200):
     """Average duration (us) of one library call issued back to back, rotating over the
     input replicas, queued behind a spin kernel: the call's kernels and the gaps
     between them, without the per-stage events of the instrumented pass."""
-    import torch
-
-    for i in range(10):
-        call(replicas[i % len(replicas)])
-    torch.cuda.synchronize()
-    prefill()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(iters):
-        call(replicas[i % len(replicas)])
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) * 1e3 / iters
+    us, _, _ = gpu_time_us(lambda i: call(replicas[i % len(replicas)]), iters, 10)
+    return us
 
 
 def cpu_model():
@@ -322,18 +335,7 @@ def time_layers_step(step, dev, replicas, stream, layers=32, iters=20, warmup=3)
         if side is not stream:
             stream.wait_event(step.ev_join)
 
-    for i in range(warmup):
-        one(replicas[i % len(replicas)])
-    torch.cuda.synchronize()
-    prefill()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(iters):
-        one(replicas[i % len(replicas)])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    us = t0.elapsed_time(t1) * 1e3 / iters
+    us, _, _ = gpu_time_us(lambda i: one(replicas[i % len(replicas)]), iters, warmup, stream)
     del kv
     return us
 
@@ -365,18 +367,7 @@ def time_kv_commit(step, dev, k_src, v_src, stream, iters=200, layers=1):
     def call():
         Bd.spec_tree_kv_commit(k, v, dev["ctx_len"], dev["n_nodes"], path, acc, new_len, status=status)
 
-    for _ in range(10):
-        call()
-    torch.cuda.synchronize()
-    prefill()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(iters):
-        call()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    us = t0.elapsed_time(t1) * 1e3 / iters
+    us, _, _ = gpu_time_us(lambda i: call(), iters, 10, stream)
     L = L.astype(np.int64)
     assert int(status.item()) == 0, f"device status {int(status.item())}"
     assert np.array_equal(new_len.cpu().numpy(), dev["ctx_len"].cpu().numpy() + 1 + L)
@@ -429,24 +420,14 @@ def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60, select
             dt.expand(r, 1.0, k, sk, policy=policy)
         dt.rerank(n_final, out=out)
 
-    for _ in range(5):
-        build()
-    torch.cuda.synchronize()
-    prefill()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(iters):
-        build()
-    t1.record()
-    torch.cuda.synchronize()
-    us = t0.elapsed_time(t1) * 1e3 / iters
+    us, host_us, ahead = gpu_time_us(lambda i: build(), iters, 5)
     assert int(dt.status.item()) == 0 and all(torch.equal(a, b) for a, b in zip(out, ref))
     kind = f"EAGLE-2 top-{k}, depth {depth}" if policy == "layer" else \
         f"best-first top-{k}, {depth} rounds of {sk} pops"
     return {"call": f"spec_tree_build_init + {depth} x spec_tree_expand + spec_tree_rerank (1 request)",
             "workload": f"{kind}, {n_final} nodes, vocabulary {V}, T_d = 1",
-            "us_per_tree": round(us, 2), "draft_row_bytes": row_bytes,
+            "us_per_tree": round(us, 2), "host_queue_us_per_tree": round(host_us, 1), "host_ahead": bool(ahead),
+            "draft_row_bytes": row_bytes,
             "gbs": round(row_bytes / (us * 1e-6) / 1e9, 1), "iters": iters,
             "note": "the drafter's rows are inputs (resident); its forward passes are not part of this"}
 
