@@ -537,3 +537,32 @@ def test_two_stream_step_equals_one_stream_step(cfg, fork):
             for k in keys:
                 g = got[k] if isinstance(got[k], np.ndarray) else got[k].numpy()
                 assert np.array_equal(g, want[i][k]), (rnd, i, k)
+
+
+@pytest.mark.parametrize("cfg,overlap", [(2, True), (2, False), (4, True)])
+def test_recorded_step_replay_equals_run(cfg, overlap):
+    """VerifyStep.compile() records each replica's library calls; run_fast(i) replays
+    them and must give, bit for bit, what run() gives on the same replica."""
+    say("replayed step", cfg, overlap)
+    inp = synth.make_config(cfg, seed=9, T=1.0)
+    d = to_device(inp)
+    reps = [{k: d[k].clone() for k in ("q", "k", "v", "tgt_logits", "dft_logits")} for _ in range(2)]
+    reps[1]["tgt_logits"].add_(0.5 * torch.randn_like(reps[1]["tgt_logits"]))
+    reps[1]["q"].mul_(-1)
+    keys = ("anc", "attn", "tmax", "tsum", "dsum", "accepted_child", "term_token", "path_nodes", "out_tokens",
+            "accept_len", "status")
+    ref = VerifyStep(d)
+    want = []
+    for r in reps:
+        ref.run(replica=r)
+        want.append({k: v for k, v in ref.results().items() if k in keys})
+    st = VerifyStep(d)
+    if overlap:
+        st.overlap()
+    st.compile(reps)
+    for rnd in range(2):
+        for i in (1, 0):
+            st.run_fast(i)
+            got = st.results()
+            for k in keys:
+                assert np.array_equal(got[k], want[i][k]), (rnd, i, k)

@@ -114,11 +114,42 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
+_recording = None  # a list while record_calls() is active
+
+
 def _call(name, *args):
-    rc = getattr(lib(), name)(*args)
+    fn = getattr(lib(), name)
+    rc = fn(*args)
     if rc != SPEC_OK:
         raise SpecTreeError(name, rc)
+    if _recording is not None:  # the call with its arguments already converted to C types
+        _recording.append((name, fn, tuple(None if a is None else t(a) for t, a in zip(fn.argtypes, args))))
     return rc
+
+
+class record_calls:
+    """Context manager: the library calls made inside it (after their checks, with the
+    same pointers, sizes and streams) are kept in the list it returns, for replay()."""
+
+    def __enter__(self):
+        global _recording
+        _recording = []
+        return _recording
+
+    def __exit__(self, *exc):
+        global _recording
+        _recording = None
+        return False
+
+
+def replay(calls):
+    """Issue recorded calls again, as recorded: no argument checks or conversions, so
+    the host queues them at a fraction of the cost.  The tensors behind the recorded
+    pointers must still be alive; the calls' own host errors are still raised."""
+    for name, fn, args in calls:
+        rc = fn(*args)
+        if rc != SPEC_OK:
+            raise SpecTreeError(name, rc)
 
 
 def spec_tree_version() -> str:

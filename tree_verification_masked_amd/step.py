@@ -161,6 +161,48 @@ class VerifyStep:
         self.softmax(stream, r.get("tgt_logits"), r.get("dft_logits"))
         self.reject(stream, r.get("tgt_logits"), r.get("dft_logits"))  # and the accepted path
 
+    def compile(self, replicas, stream=None):
+        """Record the step's library calls for each input replica (running each once),
+        so that run_fast(i) issues replica i's step with the recorded arguments and no
+        per-call checks.  The recorded streams are the caller's (current) stream and
+        this step's side stream.  Returns self."""
+        main = torch.cuda.current_stream() if stream is None else stream
+        self._main = main
+        self._plans = []
+        torch.cuda.synchronize()
+        for r in replicas:
+            if self.side is not None:
+                with B.record_calls() as side_calls:
+                    self.mask(self.side)
+                    self.attention(self.side, r.get("q"), r.get("k"), r.get("v"))
+                with B.record_calls() as main_calls:  # one softmax call, then the sampler
+                    self.softmax(main, r.get("tgt_logits"), r.get("dft_logits"))
+                    self.reject(main, r.get("tgt_logits"), r.get("dft_logits"))
+                self._plans.append((list(side_calls), list(main_calls)))
+            else:
+                with B.record_calls() as calls:
+                    self.run(main, r)
+                self._plans.append(([], list(calls)))
+            torch.cuda.synchronize()
+        return self
+
+    def run_fast(self, i):
+        """The step of recorded replica i (compile()), forked and joined as run() does."""
+        side_calls, main_calls = self._plans[i]
+        main = self._main
+        if self.side is not None:
+            if self.fork == "after_softmax":  # the side branch waits for the logit pass
+                B.replay(main_calls[:1])
+                main_calls = main_calls[1:]
+            self.ev_fork.record(main)
+            self.side.wait_event(self.ev_fork)
+            B.replay(side_calls)
+            self.ev_join.record(self.side)
+            B.replay(main_calls)
+            main.wait_event(self.ev_join)
+        else:
+            B.replay(main_calls)
+
     def results(self) -> dict:
         torch.cuda.synchronize()
         out = {k: getattr(self, k).cpu().numpy() for k in
