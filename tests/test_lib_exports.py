@@ -180,3 +180,18 @@ def test_host_errors_tree_build(lib):
     assert h(P, P, P, P, P, 1, 64, 65, P, P, P, P, None, None) == -1  # n_final above 64
     assert h(P, P, P, P, P, 1, 0, 8, P, P, P, P, None, None) == -1
     assert h(P, P, None, P, P, 1, 64, 8, P, P, P, P, None, None) == -1
+
+
+def test_record_calls_keeps_only_accepted_calls(lib):
+    """A call the library refuses raises and is not recorded; the recording ends with
+    its block, also when the block raises; replaying nothing issues nothing."""
+    with binding.record_calls() as rec:
+        with pytest.raises(binding.SpecTreeError):
+            binding._call("spec_tree_mask_build", None, P, 1, 7, P, P, P, None, None)
+    assert rec == []
+    assert binding._recording is None
+    with pytest.raises(RuntimeError):
+        with binding.record_calls():
+            raise RuntimeError("inside the block")
+    assert binding._recording is None
+    binding.replay([])

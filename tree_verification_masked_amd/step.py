@@ -165,10 +165,13 @@ class VerifyStep:
         """Record the step's library calls for each input replica (running each once),
         so that run_fast(i) issues replica i's step with the recorded arguments and no
         per-call checks.  The recorded streams are the caller's (current) stream and
-        this step's side stream.  Returns self."""
+        this step's side stream.  The recorded calls hold raw device addresses, so the
+        replicas (and this step's own buffers) are kept alive with the plans; a buffer
+        replaced afterwards needs a new compile().  Returns self."""
         main = torch.cuda.current_stream() if stream is None else stream
         self._main = main
         self._plans = []
+        self._replicas = list(replicas)  # keeps every recorded address valid
         torch.cuda.synchronize()
         for r in replicas:
             if self.side is not None:
