@@ -47,7 +47,9 @@
  *    Each call leaves its workspace zero-filled where that matters, so one buffer
  *    can be reused by consecutive calls of the same entry point on one stream.
  *    Calls that run concurrently need separate workspaces.
- *  - gfx950 only.  The library is stateless and reentrant across streams.
+ *  - gfx950 only.  The library is stateless and reentrant across streams, except
+ *    spec_tree_attention_noalloc, whose library-owned array is shared by every call
+ *    on one GPU.
  */
 #ifndef SPEC_TREE_H
 #define SPEC_TREE_H
@@ -130,6 +132,28 @@ int spec_tree_attention(const void* q, const void* k, const void* v, int32_t dty
                         const int32_t* n_nodes, const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq,
                         int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale, void* out, void* workspace,
                         size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
+ * spec_tree_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, results and errors as spec_tree_attention, without the workspace: the
+ * split partials go to a library-owned device array of
+ * SPEC_TREE_ATTENTION_SCRATCH_BYTES per GPU (its address is resolved on the first
+ * call on each device and kept; the array lives until the process ends).  Nothing
+ * is allocated or freed by the call.  The array needs no clearing: every partial is
+ * written before it is read.
+ * Returns SPEC_ERR_WORKSPACE when the split partials of these sizes would exceed
+ * the array (spec_tree_attention_workspace_size is an upper bound of what they
+ * need), SPEC_ERR_HIP when the array's device address cannot be resolved.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams) race and must be serialised by the caller.
+ */
+#define SPEC_TREE_ATTENTION_SCRATCH_BYTES (16u << 20)
+int spec_tree_attention_noalloc(const void* q, const void* k, const void* v, int32_t dtype,
+                                const int32_t* block_table, int32_t page_size, int32_t kv_capacity, int32_t n_pages,
+                                const int32_t* ctx_len, const int32_t* n_nodes, const uint64_t* anc_mask,
+                                int32_t batch, int32_t n_max, int32_t hq, int32_t hkv, int32_t head_dim,
+                                int32_t max_kv_len, float scale, void* out, int32_t* status, void* stream);
 
 /*
  * Per-row vocabulary softmax statistics at temperature T ("The EAGLE Family",

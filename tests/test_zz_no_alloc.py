@@ -1,0 +1,104 @@
+"""spec_tree_attention_noalloc: the attention call whose split partials live in the
+library's own per-GPU array instead of a caller workspace.
+
+It runs the same kernels as spec_tree_attention, so on the same inputs its output
+must equal spec_tree_attention's bit for bit; both are also held to the oracle at
+the attention bar (max-abs 2e-2 in bf16, 1e-4 in fp32) on sampled rows.  Two calls
+in a row share the array: the Llama-3-8B-shaped call (60-node tree, 4k context, the
+benchmark's launch) and then a smaller one (the 7-node fp32 tree), whose partials
+overwrite only part of what the first call left there.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_verification_masked_amd import binding as B
+from tree_verification_masked_amd import synth
+from tree_verification_masked_amd.step import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _masks(d):
+    Bn, n_max = d["parent"].shape
+    anc = torch.zeros((Bn, n_max), dtype=torch.int64, device="cuda")
+    child, depth = torch.zeros_like(anc), torch.zeros((Bn, n_max), dtype=torch.int32, device="cuda")
+    B.spec_tree_mask_build(d["parent"], d["n_nodes"], anc, child, depth)
+    return anc
+
+
+def _both(inp):
+    """(noalloc output, workspace output, anc) for one input set, noalloc first."""
+    d = to_device(inp)
+    anc = _masks(d)
+    kw = dict(hkv=d["hkv"], max_kv_len=d["max_kv_len"], block_table=d.get("block_table"),
+              page_size=d.get("page_size", 0), n_pages=d.get("n_pages", 0))
+    st_a = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out_a = torch.full_like(d["q"], float("nan"))
+    B.spec_tree_attention_noalloc(d["q"], d["k"], d["v"], d["ctx_len"], d["n_nodes"], anc, out_a, status=st_a, **kw)
+    ws = torch.zeros(B.spec_tree_attention_workspace_size(d["B"], d["n_max"], d["hq"], d["hkv"], d["d"],
+                                                          d["max_kv_len"]), dtype=torch.uint8, device="cuda")
+    st_b = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out_b = torch.full_like(d["q"], float("nan"))
+    B.spec_tree_attention(d["q"], d["k"], d["v"], d["ctx_len"], d["n_nodes"], anc, out_b, ws, status=st_b, **kw)
+    torch.cuda.synchronize()
+    assert st_a.item() == 0 and st_b.item() == 0
+    return out_a.float().cpu().numpy(), out_b.float().cpu().numpy(), anc.cpu().numpy().view(np.uint64)
+
+
+def _oracle_rows(inp, anc, got, n_rows, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.array(sorted({(int(rng.integers(inp["B"])), int(rng.integers(int(inp["n_nodes"].max()))),
+                             int(rng.integers(inp["hq"]))) for _ in range(n_rows)}), np.int32)
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], inp["n_nodes"], anc, inp["hq"],
+                                inp["hkv"], rows=rows, block_table=inp["block_table"], page_size=inp["page_size"],
+                                n_pages=inp["n_pages"], bf16=inp["bf16"])
+    return np.abs(got[rows[:, 0], rows[:, 1], rows[:, 2]] - ref).max()
+
+
+def test_noalloc_matches_workspace_call_twice():
+    # first call: the 8B-shaped workload in the launch the benchmark times (MFMA path)
+    say("noalloc attention: 60-node tree, ctx 4096, 32/8 heads, bf16")
+    big = synth.make_config(2, seed=5, vocab_override=64)
+    need = B.spec_tree_attention_workspace_size(1, big["n_max"], big["hq"], big["hkv"], big["d"],
+                                                int(big["ctx_len"].max()) + big["n_max"])
+    assert need <= B.ATTENTION_SCRATCH_BYTES
+    a, b, anc = _both(big)
+    assert np.array_equal(a, b)  # same kernels, same partials: identical bits
+    err = _oracle_rows(big, anc, a, 48, 0)
+    assert err <= 2e-2, err
+    # second call, smaller: the 7-node fp32 tree (shuffle path) over what the first left behind
+    say("noalloc attention: 7-node tree, ctx 128, fp32")
+    small = synth.make_config(1, seed=6)
+    a2, b2, anc2 = _both(small)
+    assert np.array_equal(a2, b2)
+    ref = oracle.tree_attention(small["q"], small["k"], small["v"], small["ctx_len"], small["n_nodes"], anc2,
+                                small["hq"], small["hkv"], bf16=small["bf16"])
+    assert np.abs(a2.reshape(ref.shape) - ref).max() <= 1e-4
+
+
+def test_noalloc_refuses_sizes_beyond_its_array():
+    say("noalloc attention: size limit")
+    q = torch.zeros((8, 64, 64, 128), dtype=torch.bfloat16, device="cuda")  # 8 x 64 nodes x 64 heads, 32k ctx
+    kv = torch.zeros((8, 16, 8, 128), dtype=torch.bfloat16, device="cuda")  # never read: refused on the host
+    i32 = dict(dtype=torch.int32, device="cuda")
+    with pytest.raises(B.SpecTreeError) as e:
+        B.spec_tree_attention_noalloc(q, kv, kv, torch.zeros(8, **i32), torch.ones(8, **i32),
+                                      torch.zeros((8, 64), dtype=torch.int64, device="cuda"), torch.empty_like(q),
+                                      hkv=8, max_kv_len=32768 + 64)
+    assert e.value.code == -5

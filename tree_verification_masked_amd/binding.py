@@ -17,6 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspectree.so")
 
 SPEC_OK = 0
+ATTENTION_SCRATCH_BYTES = 16 << 20  # SPEC_TREE_ATTENTION_SCRATCH_BYTES of spec_tree.h
 SPEC_F32 = 0
 SPEC_BF16 = 1
 NODE_NONE = -1
@@ -39,6 +40,8 @@ _SIGNATURES = {
     "spec_tree_attention_workspace_size": [_I32, _I32, _I32, _I32, _I32, _I32],
     "spec_tree_attention": [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                             _I32, _F32, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_attention_noalloc": [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
+                                    _I32, _I32, _F32, _VP, _VP, _VP],
     "spec_tree_softmax_chunk": [],
     "spec_tree_softmax_workspace_size": [_I64, _I32],
     "spec_tree_softmax": [_VP, _I64, _I32, _F32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
@@ -193,8 +196,10 @@ def spec_tree_mask_build(parent, n_nodes, anc_mask, child_mask, depth, status=No
           _ptr(depth), _ptr(status), _stream(stream))
 
 
-def spec_tree_attention(q, k, v, ctx_len, n_nodes, anc_mask, out, workspace, *, hkv, max_kv_len,
-                        block_table=None, page_size=0, n_pages=0, scale=None, status=None, stream=None):
+def _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, block_table, page_size, n_pages,
+                    scale, status):
+    """The argument list shared by spec_tree_attention and spec_tree_attention_noalloc
+    (everything before their workspace / status arguments), after the checks."""
     B, n_max, hq, D = q.shape
     if q.dtype == torch.bfloat16:
         dtype = SPEC_BF16
@@ -223,9 +228,25 @@ def spec_tree_attention(q, k, v, ctx_len, n_nodes, anc_mask, out, workspace, *, 
         n_pages = k.shape[0] if not n_pages else n_pages
     if scale is None:
         scale = D ** -0.5
-    _call("spec_tree_attention", _ptr(q), _ptr(k), _ptr(v), dtype, _ptr(block_table), page_size, kv_capacity,
-          n_pages, _ptr(ctx_len), _ptr(n_nodes), _ptr(anc_mask), B, n_max, hq, hkv, D, max_kv_len, scale, _ptr(out),
-          _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream))
+    return (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(block_table), page_size, kv_capacity, n_pages, _ptr(ctx_len),
+            _ptr(n_nodes), _ptr(anc_mask), B, n_max, hq, hkv, D, max_kv_len, scale, _ptr(out))
+
+
+def spec_tree_attention(q, k, v, ctx_len, n_nodes, anc_mask, out, workspace, *, hkv, max_kv_len,
+                        block_table=None, page_size=0, n_pages=0, scale=None, status=None, stream=None):
+    args = _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, block_table, page_size,
+                           n_pages, scale, status)
+    _call("spec_tree_attention", *args, _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _ptr(status), _stream(stream))
+
+
+def spec_tree_attention_noalloc(q, k, v, ctx_len, n_nodes, anc_mask, out, *, hkv, max_kv_len, block_table=None,
+                                page_size=0, n_pages=0, scale=None, status=None, stream=None):
+    """spec_tree_attention with the split partials in the library's own per-GPU array
+    (SPEC_TREE_ATTENTION_SCRATCH_BYTES): no workspace argument, nothing allocated."""
+    args = _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, block_table, page_size,
+                           n_pages, scale, status)
+    _call("spec_tree_attention_noalloc", *args, _ptr(status), _stream(stream))
 
 
 def spec_tree_softmax(logits, temperature, row_max, row_sumexp, row_argmax, workspace, probs=None, chunk_max=None,

@@ -26,6 +26,7 @@
 //    the tile against one row, the row softmax uses wave reductions, and P V is
 //    accumulated with one lane per head dimension.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -790,13 +791,15 @@ extern "C" size_t spec_tree_attention_workspace_size(int32_t batch, int32_t n_ma
   return std::max(attn_ws_bytes(p0, batch, n_max, hq, head_dim), attn_ws_bytes(p1, batch, n_max, hq, head_dim));
 }
 
-extern "C" int spec_tree_attention(const void* q, const void* k, const void* v, int32_t dtype,
-                                   const int32_t* block_table, int32_t page_size, int32_t kv_capacity,
-                                   int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes,
-                                   const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
-                                   int32_t head_dim, int32_t max_kv_len, float scale, void* out, void* workspace,
-                                   size_t workspace_bytes, int32_t* status, void* stream) {
-  using namespace spectree;
+namespace spectree {
+
+// Checks the arguments and launches the attention kernel and the split combine, with
+// the split partials in `workspace` (workspace_bytes long).
+static int attention_launch(const void* q, const void* k, const void* v, int32_t dtype, const int32_t* block_table,
+                            int32_t page_size, int32_t kv_capacity, int32_t n_pages, const int32_t* ctx_len,
+                            const int32_t* n_nodes, const uint64_t* anc_mask, int32_t batch, int32_t n_max,
+                            int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale, void* out,
+                            void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
   if (!q || !k || !v || !ctx_len || !n_nodes || !anc_mask || !out) return SPEC_ERR_INVALID_ARG;
   if (batch < 1 || n_max < 1 || n_max > 64 || hq < 1 || hkv < 1 || hq % hkv != 0) return SPEC_ERR_INVALID_ARG;
   if (kv_capacity < 1 || max_kv_len < 1 || !(scale > 0.0f) || isinf(scale)) return SPEC_ERR_INVALID_ARG;
@@ -871,4 +874,63 @@ extern "C" int spec_tree_attention(const void* q, const void* k, const void* v, 
   }
   SPEC_LAUNCH_CHECK();
   return SPEC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned split partials for spec_tree_attention_noalloc
+// ---------------------------------------------------------------------------
+// One array per GPU the library runs on, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address is
+// looked up once per device with hipGetSymbolAddress and only that address is
+// handed to kernels.
+constexpr size_t kAttnScratchBytes = (size_t)SPEC_TREE_ATTENTION_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kAttnScratchBytes];
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of the current device's array (nullptr if it cannot be resolved).
+static void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace spectree
+
+extern "C" int spec_tree_attention(const void* q, const void* k, const void* v, int32_t dtype,
+                                   const int32_t* block_table, int32_t page_size, int32_t kv_capacity,
+                                   int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes,
+                                   const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
+                                   int32_t head_dim, int32_t max_kv_len, float scale, void* out, void* workspace,
+                                   size_t workspace_bytes, int32_t* status, void* stream) {
+  return spectree::attention_launch(q, k, v, dtype, block_table, page_size, kv_capacity, n_pages, ctx_len, n_nodes,
+                                    anc_mask, batch, n_max, hq, hkv, head_dim, max_kv_len, scale, out, workspace,
+                                    workspace_bytes, status, stream);
+}
+
+extern "C" int spec_tree_attention_noalloc(const void* q, const void* k, const void* v, int32_t dtype,
+                                           const int32_t* block_table, int32_t page_size, int32_t kv_capacity,
+                                           int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes,
+                                           const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq,
+                                           int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale, void* out,
+                                           int32_t* status, void* stream) {
+  using namespace spectree;
+  // the size check needs only the host-side plan: refuse before touching the device
+  if (batch >= 1 && n_max >= 1 && n_max <= 64 && hq >= 1 && hkv >= 1 && hq % hkv == 0 && max_kv_len >= 1 &&
+      (head_dim == 64 || head_dim == 128) && (dtype == SPEC_F32 || dtype == SPEC_BF16) &&
+      attn_ws_bytes(make_plan(batch, n_max, hq, hkv, max_kv_len, dtype), batch, n_max, hq, head_dim) >
+          kAttnScratchBytes)
+    return SPEC_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return SPEC_ERR_HIP;
+  return attention_launch(q, k, v, dtype, block_table, page_size, kv_capacity, n_pages, ctx_len, n_nodes, anc_mask,
+                          batch, n_max, hq, hkv, head_dim, max_kv_len, scale, out, ws, kAttnScratchBytes, status,
+                          stream);
 }
