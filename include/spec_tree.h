@@ -164,10 +164,12 @@ int spec_tree_attention_noalloc(const void* q, const void* k, const void* v, int
  *   probs[r,x]    = exp((logits[r,x] - row_max[r]) / T) / row_sumexp (nullable,
  *                   T > 0; meant for tests)
  *   chunk_max[r,c], chunk_sum[r,c] (nullable, both or neither): for chunk c of
- *                   spec_tree_softmax_chunk() tokens, the chunk's maximum m_c and
+ *                   spec_tree_softmax_chunk() tokens, the chunk's maximum m_c (NaN
+ *                   if the chunk holds NaN or +inf) and
  *                   sum_x exp((logits[r,x] - m_c) / T) in fp64 -- the rejection
- *                   sampler uses them to draw bonus tokens at leaves without
- *                   another pass over the row.  [rows, ceil(vocab / chunk)].
+ *                   sampler merges its rows from them and draws bonus tokens at
+ *                   leaves without another pass over the row.
+ *                   [rows, ceil(vocab / chunk)].
  * logits: fp32 [rows, vocab].  -inf logits are probability 0.  A row holding NaN
  * or +inf, or only -inf, gets row_max = NaN and SPEC_ERR_BAD_INPUT in status.
  * T == 0 computes row_max and row_argmax only.
@@ -180,18 +182,25 @@ int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float te
                       void* workspace, size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
- * The same statistics for the target rows (temperature T, with argmax and chunk
- * partials) and the draft rows (temperature T_d) of a step in one launch, so the
- * two vocabulary passes share the GPU instead of running back to back.  Both
- * arrays are fp32 [rows, vocab]; T > 0 and T_d > 0.  tgt_argmax, tgt_chunk_max
- * and tgt_chunk_sum are nullable (the chunk pair both or neither).
+ * The same statistics for the target rows (temperature T) and the draft rows
+ * (temperature T_d) of a step in one launch, so the two vocabulary passes share
+ * the GPU instead of running back to back.  Both arrays are fp32 [rows, vocab];
+ * T > 0 and T_d > 0.
+ *   chunk partials  tgt_chunk_max / tgt_chunk_sum and dft_chunk_max / dft_chunk_sum
+ *                   [rows, ceil(vocab / chunk)] as spec_tree_softmax defines them
+ *                   (each pair both or neither); a chunk holding NaN or +inf gets
+ *                   maximum NaN.  These are what spec_tree_reject_sample reads.
+ *   row statistics  tgt_max, tgt_sumexp, dft_max, dft_sumexp (all four or none) and
+ *                   tgt_argmax (nullable) as spec_tree_softmax defines them.  With
+ *                   none, no row merge is launched and both chunk pairs are required
+ *                   -- the single vocabulary pass of a verification step.
  */
 size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vocab);
 int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
                            float draft_temperature, int64_t rows, int32_t vocab, float* tgt_max, float* tgt_sumexp,
                            int32_t* tgt_argmax, float* tgt_chunk_max, double* tgt_chunk_sum, float* dft_max,
-                           float* dft_sumexp, void* workspace, size_t workspace_bytes, int32_t* status,
-                           void* stream);
+                           float* dft_sumexp, float* dft_chunk_max, double* dft_chunk_sum, void* workspace,
+                           size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
  * Tree rejection sampling (gingerlabs page, "Target-model decoding is serial";
@@ -206,13 +215,15 @@ int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const flo
  * running sum exceeds u * total); at a leaf it is drawn from p_n the same way.
  * q(x) == 0 gives ratio +inf when r(x) > 0, else 0.
  * T == 0 is greedy: the first child whose token equals the target argmax is
- * accepted, the terminal token is that argmax; draft inputs and uniforms may be
- * NULL.
- * Inputs: tgt_logits, dft_logits fp32 [batch, n_max, vocab]; the row statistics
- * of spec_tree_softmax over the same rows (tgt_argmax needed only at T == 0;
- * tgt_chunk_max / tgt_chunk_sum optional, both or neither, from the same call);
- * tokens, parent int32 [batch, n_max]; n_nodes int32 [batch]; u_accept, u_sample
- * fp32 [batch, n_max] in (0, 1).
+ * accepted, the terminal token is that argmax; it reads tgt_max and tgt_argmax
+ * (spec_tree_softmax at T = 0; a NaN maximum marks an invalid row) and the draft
+ * and chunk inputs, uniforms and workspace may be NULL.
+ * T > 0 reads the chunk partials of both arrays (spec_tree_softmax_pair or
+ * spec_tree_softmax, same chunking) and merges each row's statistics itself;
+ * tgt_max and tgt_argmax are not read.
+ * Inputs: tgt_logits, dft_logits fp32 [batch, n_max, vocab]; tokens, parent int32
+ * [batch, n_max]; n_nodes int32 [batch]; u_accept, u_sample fp32 [batch, n_max] in
+ * [0, 1).
  * Outputs int32 [batch, n_max]: accepted_child[b,n] = accepted child,
  * SPEC_NODE_NONE, or SPEC_NODE_NOT_EVALUATED for nodes off the walk;
  * term_token[b,n] = the terminal token of the last node of the walk, else
@@ -222,25 +233,31 @@ int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const flo
  * path_nodes, out_tokens [batch, n_max] and accept_len [batch] (int32, all three
  * or none, NULL to skip): the accepted path, exactly as spec_accept_path would
  * derive it from accepted_child and term_token, written by the same walk.
- * T > 0 needs the workspace of spec_tree_reject_sample_workspace_size
- * (zero-filled once; every call leaves it ready for the next).  Each node is
- * evaluated in parallel and the last workgroup of a request walks the results;
- * vocabularies of more than one chunk add a ratio-histogram launch and an
- * exact-sum launch first, so no workgroup waits on another.  At T == 0 the
- * workspace may be NULL.
+ * T > 0 needs the workspace of spec_tree_reject_sample_workspace_size, zero-filled
+ * once; every call leaves it ready for the next.  Its first 16 bytes are uint32
+ * diagnostics, cumulative over calls (the caller may zero them between calls):
+ * word 0 counts the nodes of a multi-chunk vocabulary that were finished by
+ * direct passes over their rows (their exact-sum path could not guarantee its
+ * result: a list or queue overflow, a threshold beyond the ratio histogram, a
+ * zero-mass step); words 1-3 are reserved (0).  Launches: a plan launch (one
+ * workgroup per node: row statistics merged from the chunk partials, children,
+ * first-child test), for vocabularies of two or more chunks a ratio-histogram
+ * launch and an exact-sum launch over the nodes whose first child is rejected,
+ * and a node launch (sibling tests and terminal draws; the last node of a request
+ * walks).  No workgroup waits on another.
  * Host errors: T < 0 or NaN, T > 0 with T_d <= 0, null required pointers, only
- * some of the path outputs, sizes, workspace.
+ * some of the path outputs, sizes, workspace; SPEC_ERR_UNSUPPORTED for a
+ * vocabulary above 256 chunks.
  */
 size_t spec_tree_reject_sample_workspace_size(int32_t batch, int32_t n_max, int32_t vocab);
-int spec_tree_reject_sample(const float* tgt_logits, const float* tgt_max, const float* tgt_sumexp,
+int spec_tree_reject_sample(const float* tgt_logits, float temperature, const float* tgt_max,
                             const int32_t* tgt_argmax, const float* tgt_chunk_max, const double* tgt_chunk_sum,
-                            float temperature, const float* dft_logits,
-                            const float* dft_max, const float* dft_sumexp, float draft_temperature,
-                            const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
-                            const float* u_accept, const float* u_sample, int32_t batch, int32_t n_max, int32_t vocab,
-                            int32_t* accepted_child, int32_t* term_token, int32_t* path_nodes, int32_t* out_tokens,
-                            int32_t* accept_len, void* workspace, size_t workspace_bytes, int32_t* status,
-                            void* stream);
+                            const float* dft_logits, float draft_temperature, const float* dft_chunk_max,
+                            const double* dft_chunk_sum, const int32_t* tokens, const int32_t* parent,
+                            const int32_t* n_nodes, const float* u_accept, const float* u_sample, int32_t batch,
+                            int32_t n_max, int32_t vocab, int32_t* accepted_child, int32_t* term_token,
+                            int32_t* path_nodes, int32_t* out_tokens, int32_t* accept_len, void* workspace,
+                            size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
  * Accepted path plus bonus token (tree notes, parts C and G; gingerlabs page, "A

@@ -63,9 +63,24 @@ def test_host_errors_softmax(lib):
     assert f(P, 4, 100, 1.0, P, P, P, None, None, None, P, 8, None, None) == -5              # workspace
     assert f(P, 4, 100, 1.0, P, P, P, None, None, None, None, 0, None, None) == -5
     g = lib.spec_tree_softmax_pair
-    assert g(P, 1.0, P, 0.0, 4, 100, P, P, P, None, None, P, P, P, 1 << 20, None, None) == -1  # T_d = 0
-    assert g(P, 1.0, None, 1.0, 4, 100, P, P, P, None, None, P, P, P, 1 << 20, None, None) == -1
-    assert g(P, 1.0, P, 1.0, 4, 100, P, P, P, None, None, P, P, P, 8, None, None) == -5
+    #          tl T    dl Td   R  V    tmx tse tam tcm tcs dmx dse dcm dcs ws wsb st s
+    ok_rows = [P, 1.0, P, 1.0, 4, 100, P, P, P, None, None, P, P, None, None, P, 1 << 20, None, None]
+    ok_chunks = [P, 1.0, P, 1.0, 4, 100, None, None, None, P, P, None, None, P, P, P, 1 << 20, None, None]
+
+    def pair(base, **kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return g(*a)
+
+    assert pair(ok_rows, a3=0.0) == -1                      # T_d = 0
+    assert pair(ok_rows, a2=None) == -1                     # draft logits
+    assert pair(ok_rows, a16=8) == -5                       # workspace
+    assert pair(ok_rows, a7=None) == -1                     # row outputs all or none
+    assert pair(ok_chunks, a10=None) == -1                  # a chunk pair is both or neither
+    assert pair(ok_chunks, a13=None, a14=None) == -1        # chunk pass only: both pairs needed
+    assert pair(ok_chunks, a8=P) == -1                      # the argmax needs the row merge
+    assert pair(ok_chunks, a16=8) == -5
     assert lib.spec_tree_softmax_chunk() == 4096
 
 
@@ -90,36 +105,44 @@ def test_host_errors_attention(lib):
 
 def test_host_errors_reject(lib):
     f = lib.spec_tree_reject_sample
-    #       tl mx se am cmx csm T    dl mx se Td   tok par nn ua us B  nmax V    acc term pn ot al ws wsb st s
-    args = [P, P, P, P, None, None, 1.0, P, P, P, 1.0, P, P, P, P, P, 1, 8, 100, P, P, None, None, None, None, 0,
+    #       tl T    tmx tam tcm tcs dl Td   dcm dcs tok par nn ua us B  nmax V    acc term pn ot al ws wsb st s
+    args = [P, 1.0, None, None, P, P, P, 1.0, P, P, P, P, P, P, P, 1, 8, 100, P, P, None, None, None, None, 0,
             None, None]
     a = list(args)
-    a[6] = -0.5
+    a[1] = -0.5
     assert f(*a) == -1
     a = list(args)
-    a[10] = 0.0  # T_d must be positive when T > 0
+    a[7] = 0.0  # T_d must be positive when T > 0
     assert f(*a) == -1
     a = list(args)
-    a[6], a[3] = 0.0, None  # greedy needs the argmax
+    a[1] = 0.0  # greedy needs the row maxima and the argmax
+    assert f(*a) == -1
+    a[2] = P
     assert f(*a) == -1
     a = list(args)
     a[14] = None  # stochastic needs uniforms
     assert f(*a) == -1
     a = list(args)
-    a[17] = 65
+    a[16] = 65
     assert f(*a) == -1
     a = list(args)
-    a[4] = P  # chunk partials come as a pair
+    a[5] = None  # T > 0 reads the target chunk partials
     assert f(*a) == -1
     a = list(args)
-    a[21] = P  # the path outputs come together
+    a[9] = None  # and the draft ones
     assert f(*a) == -1
-    a[22], a[23] = P, P
+    a = list(args)
+    a[20] = P  # the path outputs come together
+    assert f(*a) == -1
+    a[21], a[22] = P, P
     assert f(*a) == -5  # all three given: accepted, then the missing workspace
     assert f(*args) == -5  # T > 0 needs the workspace (per-node results)
     a = list(args)
-    a[18] = 100000
+    a[17] = 100000
     assert f(*a) == -5
+    a = list(args)
+    a[17] = 256 * 4096 + 1  # more than 256 chunks
+    assert f(*a) == -2
     assert 0 < binding.spec_tree_reject_sample_workspace_size(1, 60, 4096) < 16384
     assert binding.spec_tree_reject_sample_workspace_size(1, 65, 4096) == 0
     assert binding.spec_tree_reject_sample_workspace_size(1, 60, 128256) > 60 * 4096 * 32

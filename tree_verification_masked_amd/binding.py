@@ -46,10 +46,10 @@ _SIGNATURES = {
     "spec_tree_softmax_workspace_size": [_I64, _I32],
     "spec_tree_softmax": [_VP, _I64, _I32, _F32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_tree_softmax_pair_workspace_size": [_I64, _I32],
-    "spec_tree_softmax_pair": [_VP, _F32, _VP, _F32, _I64, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
-                               _VP],
+    "spec_tree_softmax_pair": [_VP, _F32, _VP, _F32, _I64, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                               _SZ, _VP, _VP],
     "spec_tree_reject_sample_workspace_size": [_I32, _I32, _I32],
-    "spec_tree_reject_sample": [_VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _I32,
+    "spec_tree_reject_sample": [_VP, _F32, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32,
                                 _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_kv_commit": [_VP, _VP, _I32, _I32, _I64, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
@@ -273,31 +273,56 @@ def spec_tree_softmax(logits, temperature, row_max, row_sumexp, row_argmax, work
           workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream))
 
 
+def _check_rows(t, dtype, rows, name):
+    """A per-row array (None allowed): dtype and one entry per row."""
+    _check(t, dtype, None, name)
+    if t is not None and t.numel() != rows:
+        raise ValueError(f"{name} must have one entry per logit row ({rows}), got {t.numel()}")
+
+
+def _check_chunks(cmax, csum, rows, vocab, prefix):
+    """A chunk-partials pair (both or neither): fp32 maxima and fp64 sums, [rows, nch]."""
+    if (cmax is None) != (csum is None):
+        raise ValueError(f"{prefix}_chunk_max and {prefix}_chunk_sum come together")
+    _check(cmax, torch.float32, None, f"{prefix}_chunk_max")
+    _check(csum, torch.float64, None, f"{prefix}_chunk_sum")
+    nch = -(-vocab // spec_tree_softmax_chunk())
+    for t, nm in ((cmax, "max"), (csum, "sum")):
+        if t is not None and t.numel() != rows * nch:
+            raise ValueError(f"{prefix}_chunk_{nm} must be [rows, ceil(vocab / chunk)] = [{rows}, {nch}]")
+
+
 def spec_tree_softmax_pair(tgt_logits, temperature, dft_logits, draft_temperature, tgt_max, tgt_sumexp, tgt_argmax,
-                           tgt_chunk_max, tgt_chunk_sum, dft_max, dft_sumexp, workspace, status=None, stream=None):
+                           tgt_chunk_max, tgt_chunk_sum, dft_max, dft_sumexp, workspace, status=None, stream=None,
+                           dft_chunk_max=None, dft_chunk_sum=None):
+    """Row statistics (tgt_max, tgt_sumexp, dft_max, dft_sumexp: all or none; tgt_argmax
+    optional) and / or chunk partials of both logit arrays in one launch; with no row
+    statistics only the chunk pass runs (both chunk pairs required)."""
     V = tgt_logits.shape[-1]
     R = tgt_logits.numel() // V
     _check(tgt_logits, torch.float32, None, "tgt_logits")
     _check(dft_logits, torch.float32, tuple(tgt_logits.shape), "dft_logits")
     for t, nm in ((tgt_max, "tgt_max"), (tgt_sumexp, "tgt_sumexp"), (dft_max, "dft_max"), (dft_sumexp, "dft_sumexp")):
-        _check(t, torch.float32, None, nm)
-        if t.numel() != R:
-            raise ValueError(f"{nm} must have one entry per row")
-    _check(tgt_argmax, torch.int32, None, "tgt_argmax")
-    _check(tgt_chunk_max, torch.float32, None, "tgt_chunk_max")
-    _check(tgt_chunk_sum, torch.float64, None, "tgt_chunk_sum")
+        _check_rows(t, torch.float32, R, nm)
+    _check_rows(tgt_argmax, torch.int32, R, "tgt_argmax")
+    _check_chunks(tgt_chunk_max, tgt_chunk_sum, R, V, "tgt")
+    _check_chunks(dft_chunk_max, dft_chunk_sum, R, V, "dft")
     _check(status, torch.int32, (1,), "status")
     _call("spec_tree_softmax_pair", _ptr(tgt_logits), float(temperature), _ptr(dft_logits), float(draft_temperature),
           R, V, _ptr(tgt_max), _ptr(tgt_sumexp), _ptr(tgt_argmax), _ptr(tgt_chunk_max), _ptr(tgt_chunk_sum),
-          _ptr(dft_max), _ptr(dft_sumexp), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status),
-          _stream(stream))
+          _ptr(dft_max), _ptr(dft_sumexp), _ptr(dft_chunk_max), _ptr(dft_chunk_sum), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream))
 
 
-def spec_tree_reject_sample(tgt_logits, tgt_max, tgt_sumexp, tgt_argmax, temperature, dft_logits, dft_max,
-                            dft_sumexp, draft_temperature, tokens, parent, n_nodes, u_accept, u_sample,
-                            accepted_child, term_token, workspace=None, status=None, stream=None,
-                            tgt_chunk_max=None, tgt_chunk_sum=None, path_nodes=None, out_tokens=None, accept_len=None):
+def spec_tree_reject_sample(tgt_logits, temperature, tokens, parent, n_nodes, accepted_child, term_token, *,
+                            tgt_max=None, tgt_argmax=None, tgt_chunk_max=None, tgt_chunk_sum=None, dft_logits=None,
+                            draft_temperature=1.0, dft_chunk_max=None, dft_chunk_sum=None, u_accept=None,
+                            u_sample=None, workspace=None, status=None, stream=None, path_nodes=None,
+                            out_tokens=None, accept_len=None):
+    """T == 0 reads tgt_max / tgt_argmax; T > 0 the chunk partials of both arrays, the
+    draft logits, the uniforms and the workspace."""
     B, n_max, V = tgt_logits.shape
+    R = B * n_max
     _check(tgt_logits, torch.float32, (B, n_max, V), "tgt_logits")
     _check(dft_logits, torch.float32, (B, n_max, V), "dft_logits")
     for t, nm in ((tokens, "tokens"), (parent, "parent"), (accepted_child, "accepted_child"),
@@ -306,18 +331,26 @@ def spec_tree_reject_sample(tgt_logits, tgt_max, tgt_sumexp, tgt_argmax, tempera
     _check(n_nodes, torch.int32, (B,), "n_nodes")
     _check(u_accept, torch.float32, (B, n_max), "u_accept")
     _check(u_sample, torch.float32, (B, n_max), "u_sample")
-    _check(tgt_chunk_max, torch.float32, None, "tgt_chunk_max")
-    _check(tgt_chunk_sum, torch.float64, None, "tgt_chunk_sum")
+    _check_rows(tgt_max, torch.float32, R, "tgt_max")
+    _check_rows(tgt_argmax, torch.int32, R, "tgt_argmax")
+    _check_chunks(tgt_chunk_max, tgt_chunk_sum, R, V, "tgt")
+    _check_chunks(dft_chunk_max, dft_chunk_sum, R, V, "dft")
     _check(status, torch.int32, (1,), "status")
     _check(path_nodes, torch.int32, (B, n_max), "path_nodes")
     _check(out_tokens, torch.int32, (B, n_max), "out_tokens")
     _check(accept_len, torch.int32, (B,), "accept_len")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("spec_tree_reject_sample", _ptr(tgt_logits), _ptr(tgt_max), _ptr(tgt_sumexp), _ptr(tgt_argmax),
-          _ptr(tgt_chunk_max), _ptr(tgt_chunk_sum), float(temperature), _ptr(dft_logits), _ptr(dft_max),
-          _ptr(dft_sumexp), float(draft_temperature), _ptr(tokens), _ptr(parent), _ptr(n_nodes), _ptr(u_accept),
-          _ptr(u_sample), B, n_max, V, _ptr(accepted_child), _ptr(term_token), _ptr(path_nodes), _ptr(out_tokens),
-          _ptr(accept_len), _ptr(workspace), ws_bytes, _ptr(status), _stream(stream))
+    _call("spec_tree_reject_sample", _ptr(tgt_logits), float(temperature), _ptr(tgt_max), _ptr(tgt_argmax),
+          _ptr(tgt_chunk_max), _ptr(tgt_chunk_sum), _ptr(dft_logits), float(draft_temperature), _ptr(dft_chunk_max),
+          _ptr(dft_chunk_sum), _ptr(tokens), _ptr(parent), _ptr(n_nodes), _ptr(u_accept), _ptr(u_sample), B, n_max, V,
+          _ptr(accepted_child), _ptr(term_token), _ptr(path_nodes), _ptr(out_tokens), _ptr(accept_len),
+          _ptr(workspace), ws_bytes, _ptr(status), _stream(stream))
+
+
+def reject_sample_diagnostics(workspace) -> dict:
+    """The sampler workspace's cumulative diagnostics word (synchronises): nodes of a
+    multi-chunk vocabulary finished by direct vocabulary passes."""
+    return {"direct_nodes": int(workspace[:4].view(torch.int32).item())}
 
 
 def spec_accept_path(accepted_child, term_token, tokens, n_nodes, path_nodes, out_tokens, accept_len, status=None,

@@ -20,9 +20,11 @@
 // Every node is evaluated in parallel (the uniforms are indexed by node and child,
 // so a node's outcome does not depend on how the walk reached it); the walk from
 // the root then only follows the per-node results.  Launches (T > 0):
-//   P   one wavefront per request: validity, children, the tested tokens' p and q
-//       at their parents (fp64), the first-child test of every node, and the list
-//       of nodes whose first child is rejected ("active": only they need W(c)).
+//   P   one workgroup per node: the row statistics of the node's target and draft
+//       rows, merged from the logit pass's chunk partials (max and sum of
+//       exponentials), its children and their tested tokens' p and q (fp64), its
+//       first-child test, and the list of nodes whose first child is rejected
+//       ("active": only they need W(c)).
 //   R1  (two or more vocabulary chunks) every (active node, 4096-token chunk):
 //       histogram of rho over 128 buckets per octave on [1, 16), two more just
 //       below 1 and one for rho >= 16 or q == 0, with exact fixed-point sums of p
@@ -87,6 +89,7 @@ struct NodeInfo {     // written by P for every node slot
   int32_t active;     // first child rejected: the chain is needed
   int32_t verdict;    // the request's tree / token verdict (0 = fine)
   float K;            // log2(Z_d / Z_t), the bucket estimate's row constant
+  float mt, md;       // row maxima of the target and draft rows (NaN: invalid row)
   int32_t pad;
   double izt, izd;    // 1 / Z_t, 1 / Z_d
 };
@@ -104,7 +107,10 @@ struct BucketRec {
   long long SP, SQ;
 };
 
+constexpr int kDiagDirect = 0;  // diagnostics word: nodes finished by direct vocabulary passes
+
 struct NodeWs {            // nd = b * n_max + n
+  uint32_t* diag;          // [4]           cumulative counters (kDiag*)
   NodeRes* res;            // [nd]          R3 -> its request's last workgroup
   uint32_t* req_count;     // [batch]       self-resetting
   NodeInfo* info;          // [nd]          P -> R1, R2, R3
@@ -120,11 +126,11 @@ struct NodeWs {            // nd = b * n_max + n
 };
 
 struct RejArgs {
-  const float *tgt_logits, *tgt_max, *tgt_sumexp;
-  const int32_t* tgt_argmax;
-  const float* tgt_chunk_max;
-  const double* tgt_chunk_sum;
-  const float *dft_logits, *dft_max, *dft_sumexp;
+  const float *tgt_logits, *tgt_max;   // tgt_max: T == 0 (NaN marks an invalid row)
+  const int32_t* tgt_argmax;           // T == 0
+  const float *tgt_chunk_max, *dft_chunk_max;    // T > 0: chunk maxima (NaN: invalid chunk)
+  const double *tgt_chunk_sum, *dft_chunk_sum;   // T > 0: chunk sums of exp((l - m_c) / T)
+  const float* dft_logits;
   double inv_t, inv_td;
   ExpScale est, esd;
   const int32_t *tokens, *parent, *n_nodes;
@@ -446,72 +452,120 @@ __device__ inline double block_excl_scan_d(double v, double* s_w, double* total)
 }
 
 // ---------------------------------------------------------------------------
-// P: per-request plan
+// P: per-node plan
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void plan_kernel(RejArgs a, NodeWs w, int chunked) {
-  __shared__ unsigned long long s_kids[64];
-  const int lane = threadIdx.x, b = blockIdx.x;
-  s_kids[lane] = 0;
+// One wavefront merges a row's chunk partials in chunk order: m = max_c m_c,
+// Z = sum_c s_c exp((m_c - m) / T); a NaN chunk maximum (a chunk holding NaN or
+// +inf) or an all -inf row makes the row invalid.
+__device__ inline void merge_row(const float* cm, const double* cs, int nch, double inv, float* m_out, double* z_out,
+                                 int* ok_out) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kC = 4;  // chunks per lane (256 at most)
+  float mc[kC];
+  double sc[kC];
+#pragma unroll
+  for (int j = 0; j < kC; ++j) {
+    const int c = lane + 64 * j;
+    mc[j] = c < nch ? cm[c] : -INFINITY;
+    sc[j] = c < nch ? cs[c] : 0.0;
+  }
+  int bad = 0;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kC; ++j) {
+    bad |= isnan(mc[j]) ? 1 : 0;
+    mx = fmaxf(mx, mc[j]);
+  }
+  bad = wave_or_i(bad);
+  const float m = wave_max_f(mx);
+  double z = 0.0;
+#pragma unroll
+  for (int j = 0; j < kC; ++j) {
+    const int c = lane + 64 * j;
+    if (!bad && c < nch && mc[j] > -INFINITY) z += sc[j] * exp(((double)mc[j] - (double)m) * inv);
+  }
+  z = wave_sum_d(z);
+  *m_out = m;
+  *z_out = z;
+  *ok_out = !bad && m > -INFINITY && z > 0.0;
+}
+
+// One workgroup (three waves) per node slot: wave 0 reads the request's tree and
+// uniforms while waves 1 and 2 merge the node's target and draft rows; then wave 0
+// finds the node's children, their tested tokens' p and q at this row (fp64, for
+// R3) and the first-child test, and lists the node as active when that child is
+// rejected (the list order is free: every node's outcome is its own).
+__global__ __launch_bounds__(192) void plan_kernel(RejArgs a, NodeWs w, int chunked) {
+  __shared__ int s_par[64], s_tok[64];
+  __shared__ float s_ua[64];
+  __shared__ double s_z[2];
+  __shared__ float s_m[2];
+  __shared__ int s_ok[2], s_nb;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nd = blockIdx.x;
+  const int b = nd / a.n_max, n = nd % a.n_max;
   const int64_t base = (int64_t)b * a.n_max;
-  const bool in = lane < a.n_max;
-  const int nb = a.n_nodes[b];
-  const int par = in ? a.parent[base + lane] : -2;
-  const int tok = in ? a.tokens[base + lane] : 0;
-  const float ua = in ? a.u_accept[base + lane] : 0.0f;
-  const float mt = in ? a.tgt_max[base + lane] : 0.0f, md = in ? a.dft_max[base + lane] : 0.0f;
-  const float zt = in ? a.tgt_sumexp[base + lane] : 1.0f, zd = in ? a.dft_sumexp[base + lane] : 1.0f;
+  if (wv == 0) {
+    const bool in = lane < a.n_max;
+    s_par[lane] = in ? a.parent[base + lane] : -2;
+    s_tok[lane] = in ? a.tokens[base + lane] : 0;
+    s_ua[lane] = in ? a.u_accept[base + lane] : 0.0f;
+    if (lane == 0) s_nb = a.n_nodes[b];
+  } else {
+    const bool tg = wv == 1;
+    float m;
+    double z;
+    int ok;
+    merge_row((tg ? a.tgt_chunk_max : a.dft_chunk_max) + (int64_t)nd * a.nch,
+              (tg ? a.tgt_chunk_sum : a.dft_chunk_sum) + (int64_t)nd * a.nch, a.nch, tg ? a.inv_t : a.inv_td, &m, &z,
+              &ok);
+    if (lane == 0) {
+      s_m[wv - 1] = m;
+      s_z[wv - 1] = z;
+      s_ok[wv - 1] = ok;
+    }
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  const int nb = s_nb;
   const bool n_ok = nb >= 1 && nb <= a.n_max;
   const bool live = n_ok && lane < nb;
+  const int par = s_par[lane], tok = s_tok[lane];
   const bool bad_link = live && (lane == 0 ? par != -1 : (par < 0 || par >= lane));
   const bool bad_tok = live && lane > 0 && (tok < 0 || tok >= a.vocab);
   const unsigned long long m_link = __ballot(bad_link), m_tok = __ballot(bad_tok);
   const int verdict = (!n_ok || m_link) ? SPEC_ERR_BAD_TREE : (m_tok ? SPEC_ERR_BAD_INPUT : 0);
   const bool tree_ok = verdict == 0;
-  // children: every live non-root node sets its bit in its parent's mask
-  if (tree_ok && live && lane > 0) atomicOr(&s_kids[par], 1ull << lane);
-  __syncthreads();
-  const uint64_t kids = tree_ok && live ? s_kids[lane] : 0ull;
-  const bool row_ok = !isnan(mt) && !isnan(md);
-  const double izt = 1.0 / (double)zt, izd = 1.0 / (double)zd;
-  // the tested token of child `lane`, at its parent's row
-  const bool child = tree_ok && live && lane > 0;
-  const int pl = child ? par : 0;
-  const float pmt = __shfl(mt, pl), pmd = __shfl(md, pl);
-  const double pizt = __shfl(izt, pl), pizd = __shfl(izd, pl);
+  const bool row_ok = s_ok[0] && s_ok[1];
+  const float mt = s_m[0], md = s_m[1];
+  const double izt = row_ok ? 1.0 / s_z[0] : 0.0, izd = row_ok ? 1.0 / s_z[1] : 0.0;
+  // the children of this node, and each one's tested token's p and q at this row
+  const bool is_kid = tree_ok && live && lane > 0 && par == n;
+  const uint64_t kids = __ballot(is_kid);
   double px = 0.0, qx = 0.0;
-  if (child) {
-    const int64_t prow = base + par;
-    const float lt = a.tgt_logits[prow * a.vocab + tok], ld = a.dft_logits[prow * a.vocab + tok];
-    px = exp(((double)lt - (double)pmt) * a.inv_t) * pizt;
-    qx = exp(((double)ld - (double)pmd) * a.inv_td) * pizd;
+  if (is_kid && row_ok) {
+    const int64_t o = (int64_t)nd * a.vocab + tok;
+    px = exp(((double)a.tgt_logits[o] - (double)mt) * a.inv_t) * izt;
+    qx = exp(((double)a.dft_logits[o] - (double)md) * a.inv_td) * izd;
   }
-  // first-child test of node `lane`
+  if (is_kid) w.kid[base + lane] = KidInfo{px, qx};
+  // first-child test of this node
   const int fc = kids ? __ffsll((unsigned long long)kids) - 1 : 0;
   const double fpx = __shfl(px, fc), fqx = __shfl(qx, fc);
-  const float fua = __shfl(ua, fc);
-  const bool active = tree_ok && live && kids && row_ok && !((double)fua < accept_ratio(fpx, fqx, 0.0, 1.0));
-  if (in) {
+  const bool active = tree_ok && n < nb && kids && row_ok && !((double)s_ua[fc] < accept_ratio(fpx, fqx, 0.0, 1.0));
+  if (lane == 0) {
     NodeInfo inf;
     inf.kids = kids;
     inf.active = active;
     inf.verdict = verdict;
-    inf.K = (float)(log2((double)zd) - log2((double)zt));
+    inf.K = row_ok ? (float)(log2(s_z[1]) - log2(s_z[0])) : 0.0f;
+    inf.mt = row_ok ? mt : NAN;
+    inf.md = row_ok ? md : NAN;
     inf.pad = 0;
     inf.izt = izt;
     inf.izd = izd;
-    w.info[base + lane] = inf;
-    w.kid[base + lane] = KidInfo{px, qx};
-  }
-  if (chunked) {
-    const unsigned long long m = __ballot(active);
-    int at = 0;
-    if (gridDim.x == 1) {  // one request: its nodes are the whole list
-      if (lane == 0) *w.act_count = (uint32_t)__popcll(m);
-    } else {
-      if (lane == 0 && m) at = (int)atomicAdd(w.act_count, (uint32_t)__popcll(m));
-      at = __shfl(at, 0);
-    }
-    if (active) w.act_list[at + __popcll(m & ((1ull << lane) - 1ull))] = (int)(base + lane);
+    w.info[nd] = inf;
+    if (chunked && active) w.act_list[atomicAdd(w.act_count, 1u)] = nd;
   }
 }
 
@@ -540,7 +594,7 @@ __global__ __launch_bounds__(kCThreads) void chain_hist_kernel(RejArgs a, NodeWs
     const int nd = it == (int)blockIdx.x ? first_nd : w.act_list[it / ng];
     const int c_first = (it % ng) * cg, c_last = min(a.nch, c_first + cg);
     const NodeInfo inf = w.info[nd];
-    const float mt = a.tgt_max[nd], md = a.dft_max[nd];
+    const float mt = inf.mt, md = inf.md;
     const float* lt = a.tgt_logits + (int64_t)nd * a.vocab;
     const float* ld = a.dft_logits + (int64_t)nd * a.vocab;
     // the group's first chunk is in flight while the LDS histograms are cleared, and
@@ -626,7 +680,7 @@ __global__ __launch_bounds__(kXThreads) void chain_exact_kernel(RejArgs a, NodeW
     const int chunk = it % a.nch;
     const NodeInfo inf = w.info[nd];
     const int k = __popcll(inf.kids);
-    const float mt = a.tgt_max[nd], md = a.dft_max[nd];
+    const float mt = inf.mt, md = inf.md;
     // merged histogram -> suffix sums S[h] = sum_{h' >= h} hist[h'], S[kHN] = 0; it is
     // loaded before the chunk's logits, which are only needed after the intervals
     // (thread t holds bucket t < kHB; the kHN - kHB top buckets are added to every suffix)
@@ -1061,8 +1115,8 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
   RowView rv;
   rv.lt = a.tgt_logits + row * (int64_t)a.vocab;
   rv.ld = a.dft_logits + row * (int64_t)a.vocab;
-  rv.mt = a.tgt_max[row];
-  rv.md = a.dft_max[row];
+  rv.mt = inf.mt;
+  rv.md = inf.md;
   rv.izt = inf.izt;
   rv.izd = inf.izd;
   const float us = a.u_sample[row];
@@ -1097,6 +1151,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
   }
   __syncthreads();
   NodeRes res{SPEC_NODE_NOT_EVALUATED, SPEC_NODE_NOT_EVALUATED, 0, 0};
+  bool used_direct = false;  // a direct vocabulary pass (counted for multi-chunk vocabularies)
   if (node_ok) {
     if (isnan(rv.mt) || isnan(rv.md)) {
       res.err = 1;
@@ -1285,6 +1340,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
           if (st.pending) {
             const double cn = c + W;
             const double Wn = direct_W(a, rv, cn, s_red);
+            used_direct = true;
             if (Wn > 0.0) {
               c = cn;
               W = Wn;
@@ -1301,6 +1357,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
             }
             const double cn = c + W;
             const double Wn = direct_W(a, rv, cn, s_red);
+            used_direct = true;
             if (Wn > 0.0) {
               c = cn;
               W = Wn;
@@ -1338,6 +1395,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
             }
           } else {
             term = direct_draw(a, rv, c, u, s_red, s_w, &s_pick);
+            used_direct = true;
           }
         }
       }
@@ -1345,6 +1403,7 @@ __global__ __launch_bounds__(kRjThreads) void node_kernel(RejArgs a, NodeWs w, i
       res.term = acc >= 0 ? SPEC_NODE_NOT_EVALUATED : term;
     }
   }
+  if (used_direct && chunked && tid == 0) atomicAdd(&w.diag[kDiagDirect], 1u);
   if (chain) {  // the chain state of this node is consumed: clear it for the next call
     __syncthreads();
     long long* hw = w.hist + (int64_t)nd * 2 * kHN;
@@ -1481,6 +1540,7 @@ inline size_t node_ws_layout(int64_t batch, int64_t nodes, int nch, char* base, 
     return p;
   };
   NodeWs t{};
+  t.diag = (uint32_t*)take(16);
   t.res = (NodeRes*)take((size_t)nodes * sizeof(NodeRes));
   t.req_count = (uint32_t*)take((size_t)batch * 4);
   t.info = (NodeInfo*)take((size_t)nodes * sizeof(NodeInfo));
@@ -1508,42 +1568,41 @@ extern "C" size_t spec_tree_reject_sample_workspace_size(int32_t batch, int32_t 
   return node_ws_layout(batch, (int64_t)batch * n_max, nch, nullptr, nullptr);
 }
 
-extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt_max, const float* tgt_sumexp,
+extern "C" int spec_tree_reject_sample(const float* tgt_logits, float temperature, const float* tgt_max,
                                        const int32_t* tgt_argmax, const float* tgt_chunk_max,
-                                       const double* tgt_chunk_sum, float temperature, const float* dft_logits,
-                                       const float* dft_max, const float* dft_sumexp, float draft_temperature,
-                                       const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
-                                       const float* u_accept, const float* u_sample, int32_t batch, int32_t n_max,
-                                       int32_t vocab, int32_t* accepted_child, int32_t* term_token,
-                                       int32_t* path_nodes, int32_t* out_tokens, int32_t* accept_len, void* workspace,
-                                       size_t workspace_bytes, int32_t* status, void* stream) {
+                                       const double* tgt_chunk_sum, const float* dft_logits,
+                                       float draft_temperature, const float* dft_chunk_max,
+                                       const double* dft_chunk_sum, const int32_t* tokens, const int32_t* parent,
+                                       const int32_t* n_nodes, const float* u_accept, const float* u_sample,
+                                       int32_t batch, int32_t n_max, int32_t vocab, int32_t* accepted_child,
+                                       int32_t* term_token, int32_t* path_nodes, int32_t* out_tokens,
+                                       int32_t* accept_len, void* workspace, size_t workspace_bytes,
+                                       int32_t* status, void* stream) {
   using namespace spectree;
   if (!(temperature >= 0.0f) || isinf(temperature)) return SPEC_ERR_INVALID_ARG;
   const bool greedy = temperature == 0.0f;
-  if (!tgt_logits || !tgt_max || !tokens || !parent || !n_nodes || !accepted_child || !term_token)
-    return SPEC_ERR_INVALID_ARG;
-  if (greedy && !tgt_argmax) return SPEC_ERR_INVALID_ARG;
+  if (!tgt_logits || !tokens || !parent || !n_nodes || !accepted_child || !term_token) return SPEC_ERR_INVALID_ARG;
   if ((path_nodes == nullptr) != (out_tokens == nullptr) || (path_nodes == nullptr) != (accept_len == nullptr))
     return SPEC_ERR_INVALID_ARG;  // the path outputs come together
+  if (greedy && (!tgt_max || !tgt_argmax)) return SPEC_ERR_INVALID_ARG;
   if (!greedy) {
-    if (!tgt_sumexp || !dft_logits || !dft_max || !dft_sumexp || !u_accept || !u_sample) return SPEC_ERR_INVALID_ARG;
+    if (!tgt_chunk_max || !tgt_chunk_sum || !dft_logits || !dft_chunk_max || !dft_chunk_sum || !u_accept ||
+        !u_sample)
+      return SPEC_ERR_INVALID_ARG;
     if (!(draft_temperature > 0.0f) || isinf(draft_temperature)) return SPEC_ERR_INVALID_ARG;
-    if ((tgt_chunk_max == nullptr) != (tgt_chunk_sum == nullptr)) return SPEC_ERR_INVALID_ARG;
   }
   if (batch < 1 || n_max < 1 || n_max > 64 || vocab < 1) return SPEC_ERR_INVALID_ARG;
   const int nch = (vocab + kChunk - 1) / kChunk;
   if (nch > 256) return SPEC_ERR_UNSUPPORTED;
-  const bool chunked = !greedy && nch >= 2;
   RejArgs a{};
   a.tgt_logits = tgt_logits;
+  a.dft_logits = dft_logits;
   a.tgt_max = tgt_max;
-  a.tgt_sumexp = tgt_sumexp;
   a.tgt_argmax = tgt_argmax;
   a.tgt_chunk_max = tgt_chunk_max;
   a.tgt_chunk_sum = tgt_chunk_sum;
-  a.dft_logits = dft_logits;
-  a.dft_max = dft_max;
-  a.dft_sumexp = dft_sumexp;
+  a.dft_chunk_max = dft_chunk_max;
+  a.dft_chunk_sum = dft_chunk_sum;
   a.inv_t = greedy ? 0.0 : 1.0 / (double)temperature;
   a.inv_td = greedy ? 0.0 : 1.0 / (double)draft_temperature;
   a.est = make_exp_scale(a.inv_t);
@@ -1573,9 +1632,10 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, const float* tgt
   const int64_t nodes = (int64_t)batch * n_max;
   if (!workspace || workspace_bytes < node_ws_layout(batch, nodes, nch, nullptr, nullptr)) return SPEC_ERR_WORKSPACE;
   if (nodes > 0x7fffffffLL || nodes * nch > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+  const bool chunked = nch >= 2;
   NodeWs w{};
   node_ws_layout(batch, nodes, nch, (char*)workspace, &w);
-  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)batch), dim3(64), 0, st, a, w, chunked ? 1 : 0);
+  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)nodes), dim3(192), 0, st, a, w, chunked ? 1 : 0);
   SPEC_LAUNCH_CHECK();
   if (chunked) {
     // grid-stride over (active node, chunk) items; the item count is known on the device only

@@ -169,7 +169,8 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSe
   }
   if (tid == 0) {
     const int64_t slot = row * nch + chunk;
-    S.cmax[slot] = cm;
+    S.cmax[slot] = cb ? NAN : cm;  // an invalid chunk is marked in its maximum too
+    if (cb) report(status, SPEC_ERR_BAD_INPUT);
     S.csum[slot] = csum;
     S.carg[slot] = ca;
     S.cbad[slot] = cb;
@@ -247,7 +248,9 @@ inline SmSet make_set(const float* logits, int64_t rows, float t, float* mx, flo
   return s;
 }
 
-inline int launch_stats(const SmSet& A, const SmSet& B, int32_t vocab, int32_t* status, hipStream_t st) {
+// The chunk pass, then (merge) the row merge.
+inline int launch_stats(const SmSet& A, const SmSet& B, int32_t vocab, int32_t* status, hipStream_t st,
+                        bool merge = true) {
   const int nch = sm_chunks(vocab);
   const int64_t blocks = (A.rows + B.rows) * nch;
   if (blocks > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
@@ -260,6 +263,7 @@ inline int launch_stats(const SmSet& A, const SmSet& B, int32_t vocab, int32_t* 
     hipLaunchKernelGGL(softmax_stats_kernel<false>, dim3((unsigned)blocks), dim3(kSmThreads), 0, st, A, B, vocab,
                        nch, status);
   SPEC_LAUNCH_CHECK();
+  if (!merge) return SPEC_OK;  // invalid rows were reported by the chunk pass
   const int64_t rows = A.rows + B.rows;
   hipLaunchKernelGGL(softmax_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, A, B, nch, status);
   SPEC_LAUNCH_CHECK();
@@ -308,10 +312,17 @@ extern "C" size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vo
 extern "C" int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
                                       float draft_temperature, int64_t rows, int32_t vocab, float* tgt_max,
                                       float* tgt_sumexp, int32_t* tgt_argmax, float* tgt_chunk_max,
-                                      double* tgt_chunk_sum, float* dft_max, float* dft_sumexp, void* workspace,
-                                      size_t workspace_bytes, int32_t* status, void* stream) {
+                                      double* tgt_chunk_sum, float* dft_max, float* dft_sumexp, float* dft_chunk_max,
+                                      double* dft_chunk_sum, void* workspace, size_t workspace_bytes,
+                                      int32_t* status, void* stream) {
   using namespace spectree;
-  if (!tgt_logits || !dft_logits || !tgt_max || !tgt_sumexp || !dft_max || !dft_sumexp) return SPEC_ERR_INVALID_ARG;
+  if (!tgt_logits || !dft_logits) return SPEC_ERR_INVALID_ARG;
+  const bool row_out = tgt_max || tgt_sumexp || dft_max || dft_sumexp;
+  if (row_out && !(tgt_max && tgt_sumexp && dft_max && dft_sumexp)) return SPEC_ERR_INVALID_ARG;  // all or none
+  if ((tgt_chunk_max == nullptr) != (tgt_chunk_sum == nullptr)) return SPEC_ERR_INVALID_ARG;
+  if ((dft_chunk_max == nullptr) != (dft_chunk_sum == nullptr)) return SPEC_ERR_INVALID_ARG;
+  if (!row_out && (!tgt_chunk_max || !dft_chunk_max)) return SPEC_ERR_INVALID_ARG;  // nothing to write
+  if (!row_out && tgt_argmax) return SPEC_ERR_INVALID_ARG;  // the argmax comes from the row merge
   if (rows < 1 || vocab < 1) return SPEC_ERR_INVALID_ARG;
   if (!(temperature > 0.0f) || isinf(temperature) || !(draft_temperature > 0.0f) || isinf(draft_temperature))
     return SPEC_ERR_INVALID_ARG;
@@ -320,6 +331,6 @@ extern "C" int spec_tree_softmax_pair(const float* tgt_logits, float temperature
   SmSet A = make_set(tgt_logits, rows, temperature, tgt_max, tgt_sumexp, tgt_argmax);
   SmSet B = make_set(dft_logits, rows, draft_temperature, dft_max, dft_sumexp, nullptr);
   sm_set_carve((char*)workspace, rows, vocab, &A, tgt_chunk_max, tgt_chunk_sum);
-  sm_set_carve((char*)workspace + one, rows, vocab, &B, nullptr, nullptr);
-  return launch_stats(A, B, vocab, status, (hipStream_t)stream);
+  sm_set_carve((char*)workspace + one, rows, vocab, &B, dft_chunk_max, dft_chunk_sum);
+  return launch_stats(A, B, vocab, status, (hipStream_t)stream, row_out);
 }

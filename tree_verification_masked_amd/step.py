@@ -4,9 +4,10 @@
 once, outputs, workspaces, the status word) so that ``run()`` allocates nothing
 and only issues the library calls, in order, on one stream:
 
-    spec_tree_mask_build -> spec_tree_attention -> spec_tree_softmax_pair (target
-    and draft rows in one launch; spec_tree_softmax on the target rows at T = 0)
-    -> spec_tree_reject_sample -> spec_accept_path
+    spec_tree_mask_build -> spec_tree_attention -> spec_tree_softmax_pair (the chunk
+    partials of the target and draft rows in one launch, no row merge;
+    spec_tree_softmax with row statistics on the target rows at T = 0)
+    -> spec_tree_reject_sample (which merges each row itself) -> spec_accept_path
 
 The attention output is not an input of the sampling half (the target logits are
 given), so the step's dependence graph has two branches after its start: mask ->
@@ -68,6 +69,8 @@ class VerifyStep:
         nch = -(-V // B.spec_tree_softmax_chunk())
         self.tcmax = torch.zeros((R, nch), **f32)
         self.tcsum = torch.zeros((R, nch), dtype=torch.float64, device=cuda)
+        self.dcmax = torch.zeros((R, nch), **f32)
+        self.dcsum = torch.zeros((R, nch), dtype=torch.float64, device=cuda)
         self.sm_ws = torch.zeros(B.spec_tree_softmax_pair_workspace_size(R, V), dtype=torch.uint8, device=cuda)
         rj = B.spec_tree_reject_sample_workspace_size(Bn, n_max, V)
         self.rj_ws = torch.zeros(max(rj, 256), dtype=torch.uint8, device=cuda)
@@ -105,13 +108,19 @@ class VerifyStep:
                               block_table=d.get("block_table"), page_size=d.get("page_size", 0),
                               n_pages=d.get("n_pages", 0), status=self.status, stream=stream)
 
-    def softmax(self, stream=None, tgt=None, dft=None):
+    def softmax(self, stream=None, tgt=None, dft=None, rows=False):
+        """T > 0: the chunk partials of both logit arrays (one launch); with rows, the
+        row statistics as well (a second, merging launch the sampler does not need).
+        T = 0: the target rows' maximum and argmax."""
         d = self.d
         tgt = d["tgt_logits"] if tgt is None else tgt
         if self.T > 0:
-            B.spec_tree_softmax_pair(tgt, self.T, d["dft_logits"] if dft is None else dft, self.Td, self.tmax,
-                                     self.tsum, self.targ, self.tcmax, self.tcsum, self.dmax, self.dsum, self.sm_ws,
-                                     status=self.status, stream=stream)
+            B.spec_tree_softmax_pair(tgt, self.T, d["dft_logits"] if dft is None else dft, self.Td,
+                                     self.tmax if rows else None, self.tsum if rows else None,
+                                     self.targ if rows else None, self.tcmax, self.tcsum,
+                                     self.dmax if rows else None, self.dsum if rows else None, self.sm_ws,
+                                     status=self.status, stream=stream, dft_chunk_max=self.dcmax,
+                                     dft_chunk_sum=self.dcsum)
         else:
             B.spec_tree_softmax(tgt, 0.0, self.tmax, self.tsum, self.targ, self.sm_ws, status=self.status,
                                 stream=stream)
@@ -120,17 +129,20 @@ class VerifyStep:
         """Rejection sampling; with_path: the same walk also writes the accepted path
         (path_nodes, out_tokens, accept_len), the result spec_accept_path gives."""
         d = self.d
-        greedy = self.T == 0
-        B.spec_tree_reject_sample(d["tgt_logits"] if tgt is None else tgt, self.tmax, self.tsum, self.targ, self.T,
-                                  None if greedy else (d["dft_logits"] if dft is None else dft),
-                                  None if greedy else self.dmax, None if greedy else self.dsum, self.Td,
-                                  d["tokens"], d["parent"], d["n_nodes"], None if greedy else d["u_accept"],
-                                  None if greedy else d["u_sample"], self.accepted_child, self.term_token,
-                                  self.rj_ws, self.status, stream, tgt_chunk_max=None if greedy else self.tcmax,
-                                  tgt_chunk_sum=None if greedy else self.tcsum,
-                                  path_nodes=self.path_nodes if with_path else None,
-                                  out_tokens=self.out_tokens if with_path else None,
-                                  accept_len=self.accept_len if with_path else None)
+        tgt = d["tgt_logits"] if tgt is None else tgt
+        path = dict(path_nodes=self.path_nodes, out_tokens=self.out_tokens, accept_len=self.accept_len) \
+            if with_path else {}
+        if self.T == 0:
+            B.spec_tree_reject_sample(tgt, 0.0, d["tokens"], d["parent"], d["n_nodes"], self.accepted_child,
+                                      self.term_token, tgt_max=self.tmax, tgt_argmax=self.targ, status=self.status,
+                                      stream=stream, **path)
+            return
+        B.spec_tree_reject_sample(tgt, self.T, d["tokens"], d["parent"], d["n_nodes"], self.accepted_child,
+                                  self.term_token, tgt_chunk_max=self.tcmax, tgt_chunk_sum=self.tcsum,
+                                  dft_logits=d["dft_logits"] if dft is None else dft, draft_temperature=self.Td,
+                                  dft_chunk_max=self.dcmax, dft_chunk_sum=self.dcsum, u_accept=d["u_accept"],
+                                  u_sample=d["u_sample"], workspace=self.rj_ws, status=self.status, stream=stream,
+                                  **path)
 
     def path(self, stream=None):
         d = self.d
@@ -209,8 +221,8 @@ class VerifyStep:
     def results(self) -> dict:
         torch.cuda.synchronize()
         out = {k: getattr(self, k).cpu().numpy() for k in
-               ("anc", "child", "depth", "tmax", "tsum", "targ", "dmax", "dsum", "accepted_child", "term_token",
-                "path_nodes", "out_tokens", "accept_len", "status")}
+               ("anc", "child", "depth", "tmax", "tsum", "targ", "dmax", "dsum", "tcmax", "tcsum", "dcmax", "dcsum",
+                "accepted_child", "term_token", "path_nodes", "out_tokens", "accept_len", "status")}
         out["anc"] = out["anc"].view(np.uint64)
         out["child"] = out["child"].view(np.uint64)
         if self.with_attention:
