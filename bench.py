@@ -396,7 +396,7 @@ def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60, select
     sk = k if select_k is None else select_k
     import torch
 
-    from tree_verification_masked_amd import synth
+    import synth
     from tree_verification_masked_amd.draft_tree import DraftTree
 
     dt = DraftTree(1, 1024, sk, V)
@@ -438,6 +438,43 @@ def time_tree_build(seed, iters=100, V=128256, k=10, depth=6, n_final=60, select
             "note": "the drafter's rows are inputs (resident); its forward passes are not part of this"}
 
 
+def gpu_tree_builder(row_of, root_token, T_d, top_k, depth, n_final):
+    """The EAGLE-2 tree of a workload built on the GPU by the library's own calls
+    (spec_tree_build_init, ``depth`` spec_tree_expand rounds, spec_tree_rerank), the
+    drafter's rows supplied per frontier node by ``row_of(path)``; returns the
+    flattened tree and each node's root path (the input hook of synth.make_config)."""
+    import torch
+
+    from tree_verification_masked_amd.draft_tree import DraftTree
+
+    V = int(np.asarray(row_of((int(root_token),))).shape[0])
+    dt = DraftTree(1, 1024, top_k, V)
+    dt.init(torch.tensor([int(root_token)], dtype=torch.int32, device="cuda"))
+
+    def path_of(st, nd):
+        out = []
+        while nd >= 0:
+            out.append(int(st["token"][0, nd]))
+            nd = int(st["parent"][0, nd])
+        return tuple(out[::-1])
+
+    for _ in range(depth):
+        st = dt.host_state()
+        fc = int(st["frontier_count"][0])
+        if fc == 0:
+            break
+        rows = np.zeros((1, top_k, V), np.float32)
+        for j in range(fc):
+            rows[0, j] = row_of(path_of(st, int(st["frontier"][0, j])))
+        dt.expand(torch.from_numpy(rows).cuda(), T_d, top_k, top_k)
+    parent, tokens, n_nodes, cand_id = dt.rerank(n_final)
+    st = dt.host_state()
+    assert int(st["status"][0]) == 0, f"tree build status {int(st['status'][0])}"
+    n = int(n_nodes[0].item())
+    ids = cand_id[0, :n].cpu().numpy()
+    return parent[0, :n].cpu().numpy(), tokens[0, :n].cpu().numpy(), [path_of(st, int(i)) for i in ids]
+
+
 COST_GRID = {"batch": (1, 2, 4, 8), "ctx": (1024, 4096, 16384), "n_nodes": (16, 32, 64)}
 
 
@@ -449,7 +486,7 @@ def cost_table(args):
     context C, each in enough replicas to exceed the last-level cache."""
     import torch
 
-    from tree_verification_masked_amd import synth
+    import synth
     from tree_verification_masked_amd.step import VerifyStep, to_device
 
     torch.cuda.set_device(0)
@@ -530,12 +567,12 @@ def main():
         sys.exit(2)
     import torch
 
-    from tree_verification_masked_amd import synth
+    import synth
     from tree_verification_masked_amd.step import VerifyStep, to_device
 
     torch.cuda.set_device(0)
     T = args.temperature if args.config != 3 else None
-    inp = synth.make_config(args.config, seed=args.seed, T=T)
+    inp = synth.make_config(args.config, seed=args.seed, T=T, tree_builder=gpu_tree_builder)
     dev = to_device(inp)
     step = VerifyStep(dev)
     if not args.serial:

@@ -1,11 +1,13 @@
-"""Seeded synthetic inputs for the tree-verification step.
+"""Seeded synthetic inputs for the tree-verification step (test and benchmark support).
 
 This module only *makes inputs*: draft trees, token ids, logits, Q/K/V activations,
-paged block tables and uniforms.  It contains none of the verification arithmetic
-(no masks, no attention, no rejection rule) and is shared by the tests, the
-benchmark and the oracle-side checks alike.  Where a generator needs draft
-probabilities to shape a tree (EAGLE-2 confidences, i.i.d. sibling draws) it
-computes them here with plain numpy, as part of making the input.
+paged block tables and uniforms.  It holds none of the verification arithmetic (no
+masks, no attention, no rejection rule) and no tree-construction method: the
+EAGLE-2 trees of workloads 2 and 5 come from a tree builder the caller passes in
+(the tests pass the CPU oracle's, the benchmark builds them on the GPU with the
+library's own expand / rerank calls).  Where an input's statistics are defined by a
+draft distribution (i.i.d. sibling draws, the top-2 children of the 7-node tree) the
+generator evaluates that distribution with plain numpy as part of making the input.
 
 Workloads follow the shapes the pages discuss: Llama-3-8B-like GQA heads and
 128k vocabularies, EAGLE-2 expand/rerank trees of 60 nodes, 16-token DFlash
@@ -102,80 +104,6 @@ class RowSource:
 # --------------------------------------------------------------------------
 
 
-def expand_step(frontier_values, k, child_confidences):
-    """One EAGLE-2 expand round on a frontier.
-
-    Keeps the k frontier nodes with the largest value (ties to the earlier node),
-    and gives each kept node the children whose confidences are listed for it in
-    ``child_confidences`` (a list aligned with the kept nodes, in value order).
-    A child's value is its parent's value times its own confidence.
-    Returns (kept_indices, child_values, child_parent_positions).
-    """
-    fv = np.asarray(frontier_values, np.float64)
-    order = np.lexsort((np.arange(fv.size), -fv))[:k]
-    vals, parents = [], []
-    for pos, fi in enumerate(order):
-        for c in child_confidences[pos]:
-            vals.append(fv[fi] * c)
-            parents.append(int(fi))
-    return order, np.array(vals), np.array(parents)
-
-
-def eagle2_tree(src: RowSource, k: int, depth: int, n_final: int, Td: float, root_token: int):
-    """EAGLE-2 expand/rerank tree built from the draft rows of ``src``.
-
-    Expand: round 1 expands the root; each later round expands the k frontier
-    nodes of largest value.  An expanded node's children are the top-k tokens of
-    its draft distribution, each with confidence q(token) and value parent*conf.
-    Rerank: keep the n_final - 1 candidates of largest value (ties to the
-    shallower, then the earlier node) plus the root.  Flatten breadth-first,
-    siblings in descending confidence.
-    Returns parent, tokens (int32 [n_final]), uid per flattened node, values.
-    """
-    nodes = [dict(uid=0, parent=-1, depth=0, token=root_token, conf=1.0, value=1.0)]
-    frontier = [0]
-    for rnd in range(depth):
-        if rnd == 0:
-            expand = [0]
-        else:
-            fv = [nodes[i]["value"] for i in frontier]
-            kept, _, _ = expand_step(fv, k, [[] for _ in range(min(k, len(fv)))])
-            expand = [frontier[j] for j in kept]
-        new = []
-        for ni in expand:
-            _, dft = src.rows(nodes[ni]["uid"])
-            q = _draft_probs(dft, Td)
-            for tok in _topk_desc(dft.astype(np.float64), k):
-                nodes.append(dict(uid=len(nodes), parent=ni, depth=nodes[ni]["depth"] + 1, token=int(tok),
-                                  conf=float(q[tok]), value=nodes[ni]["value"] * float(q[tok])))
-                new.append(len(nodes) - 1)
-        frontier = new
-    cand = list(range(1, len(nodes)))
-    cand.sort(key=lambda i: (-nodes[i]["value"], nodes[i]["depth"], i))
-    keep = set([0] + cand[: n_final - 1])
-    for i in keep:  # rerank keeps a connected subtree
-        assert nodes[i]["parent"] == -1 or nodes[i]["parent"] in keep
-    # breadth-first flatten: by depth, then parent's flattened index, then descending confidence
-    flat = [0]
-    pos = {0: 0}
-    level = [0]
-    while level:
-        nxt = []
-        for pi in level:
-            kids = [i for i in keep if nodes[i]["parent"] == pi]
-            kids.sort(key=lambda i: (-nodes[i]["conf"], i))
-            for c in kids:
-                pos[c] = len(flat)
-                flat.append(c)
-                nxt.append(c)
-        level = nxt
-    parent = np.array([-1] + [pos[nodes[i]["parent"]] for i in flat[1:]], np.int32)
-    tokens = np.array([nodes[i]["token"] for i in flat], np.int32)
-    uids = [nodes[i]["uid"] for i in flat]
-    values = np.array([nodes[i]["value"] for i in flat])
-    return parent, tokens, uids, values
-
-
 def topk_binary_tree(src: RowSource, Td: float, root_token: int):
     """Depth-2 complete binary tree (7 nodes, BFS), children = top-2 draft tokens of the parent."""
     parent = np.array([-1, 0, 0, 1, 1, 2, 2], np.int32)
@@ -193,15 +121,34 @@ def chain_tree(n: int):
     return np.arange(-1, n - 1, dtype=np.int32)
 
 
-def path_row(seed: int, path, vocab: int, kind: str = "normal", scale: float = 3.0, noise: float = 1.0):
-    """Draft logits at the tree node whose root path carries the tokens ``path`` (root
-    first), seeded by the path itself, so a node gets the same row whatever order the
-    nodes are visited in.  kind "normal": N(0, scale) + N(0, noise); "student_t":
-    scale * t(3) + N(0, noise)."""
+def path_rows(seed: int, path, vocab: int, kind: str = "normal", scale: float = 3.0, noise: float = 1.0):
+    """(target, draft) logit rows at the tree node whose root path carries the tokens
+    ``path`` (root first), seeded by the path itself, so a node gets the same rows
+    whatever builds the tree and in whatever order it visits the nodes.  kind "normal":
+    target ~ N(0, scale); "student_t": target = scale * t(3); draft = target + N(0, noise)."""
     key = np.asarray(path, np.int64)
     r = np.random.default_rng([seed, len(key), zlib.crc32(key.tobytes())])
     base = r.normal(0.0, scale, vocab) if kind == "normal" else scale * r.standard_t(3.0, vocab)
-    return (base + r.normal(0.0, noise, vocab)).astype(np.float32)
+    return base.astype(np.float32), (base + r.normal(0.0, noise, vocab)).astype(np.float32)
+
+
+def path_row(seed: int, path, vocab: int, kind: str = "normal", scale: float = 3.0, noise: float = 1.0):
+    """The draft row of ``path_rows``."""
+    return path_rows(seed, path, vocab, kind, scale, noise)[1]
+
+
+class PathRows:
+    """``path_rows`` of one workload, cached per path (a RowSource keyed by paths)."""
+
+    def __init__(self, seed: int, vocab: int, kind: str, scale: float, noise: float):
+        self.seed, self.vocab, self.kind, self.scale, self.noise = seed, vocab, kind, scale, noise
+        self._cache: dict = {}
+
+    def rows(self, path):
+        path = tuple(int(t) for t in path)
+        if path not in self._cache:
+            self._cache[path] = path_rows(self.seed, path, self.vocab, self.kind, self.scale, self.noise)
+        return self._cache[path]
 
 
 def random_tree(rng: np.random.Generator, n: int, max_branch: int = 4, max_depth: int = 8):
@@ -260,13 +207,19 @@ def _activations(rng, B, n_max, hq, hkv, d, s_cap, bf16):
 
 
 def make_config(cfg: int, seed: int = 0, T: float | None = None, with_kv: bool = True,
-                ctx_override: int | None = None, vocab_override: int | None = None, grid=None):
+                ctx_override: int | None = None, vocab_override: int | None = None, grid=None, tree_builder=None):
     """Build one input set for workload ``cfg`` (1..6).  Returns a dict of numpy arrays
     and scalars.  ``ctx_override`` / ``vocab_override`` shrink a workload for fast tests
     while keeping its tree generator and head geometry.  Workload 6 takes
     ``grid = (B, ctx, N)``: workload 4's trees, tokens and logits with N nodes per tree,
     every request at context ``ctx`` and contiguous KV (see ``grid_point`` for cutting
-    smaller points out of one such input)."""
+    smaller points out of one such input).
+
+    Workloads 2 and 5 need ``tree_builder(row_of, root_token, T_d, top_k, depth,
+    n_final) -> (parent, tokens, paths)``: an EAGLE-2 expand / rerank over the draft
+    rows ``row_of(path)`` (path = the tokens on a node's root path, root first),
+    returning the flattened tree and each node's path; every node's target and draft
+    rows are then ``path_rows`` of its path."""
     rng = rng_for(seed, cfg, 1)
     inp: dict = {"cfg": cfg, "seed": seed, "page_size": 0, "n_pages": 0, "block_table": None}
     if cfg == 1:
@@ -280,19 +233,21 @@ def make_config(cfg: int, seed: int = 0, T: float | None = None, with_kv: bool =
         Td, bf16, B = T_ if T_ > 0 else 1.0, False, 1
         ctxs = [ctx]
     elif cfg in (2, 5):
+        if tree_builder is None:
+            raise ValueError("workloads 2 and 5 take their EAGLE-2 tree from a tree_builder")
         if cfg == 2:
             V, hq, hkv, d, ctx, k, depth, n = 128256, 32, 8, 128, 4096, 10, 6, 60
-            src_kw = dict(kind="normal", sigma_t=3.0, sigma_d=1.0)
+            src_kw = dict(kind="normal", scale=3.0, noise=1.0)
         else:
             V, hq, hkv, d, ctx, k, depth, n = 152064, 64, 8, 128, 32768, 8, 8, 64
-            src_kw = dict(kind="student_t", scale_t=2.0, sigma_d=1.5)
+            src_kw = dict(kind="student_t", scale=2.0, noise=1.5)
         V = vocab_override or V
         ctx = ctx_override or ctx
         T_ = 1.0 if T is None else T
         Td = T_ if T_ > 0 else 1.0
-        src = RowSource(seed * 7919 + cfg, V, **src_kw)
-        parent, tokens, uids, _ = eagle2_tree(src, k, depth, n, Td, root_token=int(rng.integers(V)))
-        trees = [(parent, tokens, uids)]
+        src = PathRows(seed * 7919 + cfg, V, **src_kw)
+        parent, tokens, paths = tree_builder(lambda path: src.rows(path)[1], int(rng.integers(V)), Td, k, depth, n)
+        trees = [(np.asarray(parent, np.int32), np.asarray(tokens, np.int32), [tuple(p) for p in paths])]
         bf16, B = True, 1
         ctxs = [ctx]
     elif cfg == 3:

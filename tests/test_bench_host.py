@@ -6,13 +6,15 @@ import sys
 
 import numpy as np
 
+import support
+
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import bench  # noqa: E402
-from tree_verification_masked_amd import synth  # noqa: E402
+import synth  # noqa: E402
 
 
 def test_algorithmic_bytes_and_flops_of_the_60_node_step():
-    inp = synth.make_config(2, seed=0, with_kv=False)
+    inp = support.make_config(2, seed=0, with_kv=False)
     attn, logits, sampling = bench.algorithmic_bytes(inp)
     kv = 2 * (4096 + 60) * 8 * 128 * 2            # K and V of every position, bf16
     qo = 2 * 60 * 32 * 128 * 2                    # Q in, O out

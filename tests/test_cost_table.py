@@ -4,7 +4,8 @@ import json
 import numpy as np
 import pytest
 
-from tree_verification_masked_amd import synth
+import synth
+import support
 from tree_verification_masked_amd.cost_table import CostTable
 
 B_AX, C_AX, N_AX = (1, 2, 4, 8), (1024, 4096, 16384), (16, 32, 64)
@@ -68,7 +69,7 @@ def test_single_point_axes():
 
 
 def test_grid_workload_prefixes_are_trees():
-    inp = synth.make_config(6, seed=3, with_kv=True, grid=(2, 96, 24), vocab_override=64)
+    inp = support.make_config(6, seed=3, with_kv=True, grid=(2, 96, 24), vocab_override=64)
     assert inp["block_table"] is None and inp["kv_capacity"] == 96 + 24
     assert np.all(inp["ctx_len"] == 96) and np.all(inp["n_nodes"] == 24)
     for n in (1, 2, 7, 24):

@@ -9,7 +9,8 @@ import torch
 
 import oracle
 from tree_verification_masked_amd import binding as B
-from tree_verification_masked_amd import synth
+import synth
+import support
 from tree_verification_masked_amd.step import VerifyStep, to_device
 
 pytestmark = pytest.mark.gpu
@@ -129,7 +130,7 @@ def test_kv_commit_parity(bf16, paged, d, hkv, page, layers):
 def test_kv_commit_after_the_full_step(cfg):
     """The step's own path, committed on the step's cache (config 4 is paged)."""
     say("kv_commit after step", cfg)
-    inp = synth.make_config(cfg, seed=5, T=1.0)
+    inp = support.make_config(cfg, seed=5, T=1.0)
     d = to_device(inp)
     st = VerifyStep(d)
     st.run()

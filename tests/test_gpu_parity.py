@@ -14,7 +14,8 @@ import torch
 
 import oracle
 from tree_verification_masked_amd import binding as B
-from tree_verification_masked_amd import synth
+import synth
+import support
 from tree_verification_masked_amd.step import VerifyStep, to_device
 
 pytestmark = pytest.mark.gpu
@@ -227,7 +228,7 @@ def test_sampling_full_vocab(cfg, T, seeds):
     ties = 0
     for seed in seeds:
         say("sampling", cfg, T, seed)
-        inp = synth.make_config(cfg, seed=seed, T=T, with_kv=False)
+        inp = support.make_config(cfg, seed=seed, T=T, with_kv=False)
         got = _sampling_gpu(inp)
         ref = _oracle_sampling(inp)
         assert got["status"][0] == 0
@@ -241,7 +242,7 @@ def test_sampling_many_small_vocab_trees(cfg):
     ties, n = 0, 0
     for seed in range(40 if cfg != 4 else 10):
         say("sampling small vocab", cfg, seed)
-        inp = synth.make_config(cfg, seed=100 + seed, with_kv=False, vocab_override=4096)
+        inp = support.make_config(cfg, seed=100 + seed, with_kv=False, vocab_override=4096)
         got = _sampling_gpu(inp)
         ref = _oracle_sampling(inp)
         ties += _compare_sampling(got, ref, inp["n_nodes"])
@@ -258,7 +259,7 @@ def test_sampling_ragged_vocab(cfg, V):
     ties, n = 0, 0
     for seed in range(6 if cfg != 4 else 2):
         say("sampling ragged vocab", cfg, V, seed)
-        inp = synth.make_config(cfg, seed=200 + seed, with_kv=False, vocab_override=V)
+        inp = support.make_config(cfg, seed=200 + seed, with_kv=False, vocab_override=V)
         got = _sampling_gpu(inp)
         ref = _oracle_sampling(inp)
         assert got["status"][0] == 0
@@ -380,7 +381,7 @@ def _check_attention(inp, got, anc, n_rows=None, seed=0):
 @pytest.mark.parametrize("cfg,ctx", [(1, None), (2, 1000), (3, 777), (4, 300), (5, 515)])
 def test_attention_small_context_all_rows(cfg, ctx):
     say("attention all rows", cfg, ctx)
-    inp = synth.make_config(cfg, seed=3, ctx_override=ctx, vocab_override=64)
+    inp = support.make_config(cfg, seed=3, ctx_override=ctx, vocab_override=64)
     got, st, anc = _attention_gpu(inp)
     assert st == 0
     _check_attention(inp, got, anc)
@@ -389,7 +390,7 @@ def test_attention_small_context_all_rows(cfg, ctx):
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_attention_full_size_sampled_rows(cfg):
     say("attention full size", cfg)
-    inp = synth.make_config(cfg, seed=0, vocab_override=64)
+    inp = support.make_config(cfg, seed=0, vocab_override=64)
     got, st, anc = _attention_gpu(inp)
     assert st == 0
     _check_attention(inp, got, anc, n_rows=96)
@@ -478,7 +479,7 @@ def test_full_step(cfg, T):
     """The five calls in the order and launch configuration the benchmark times, at
     the workload's full size (attention on sampled rows)."""
     say("full step", cfg, T)
-    inp = synth.make_config(cfg, seed=11, T=T)
+    inp = support.make_config(cfg, seed=11, T=T)
     d = to_device(inp)
     st = VerifyStep(d).overlap()  # mask + attention on a second stream, as the benchmark runs it
     st.run()
@@ -519,7 +520,7 @@ def test_two_stream_step_equals_one_stream_step(cfg, fork):
     step's side branch must wait for the previous step, and the caller's stream for
     the side branch)."""
     say("two-stream step", cfg, fork)
-    inp = synth.make_config(cfg, seed=5, T=1.0)
+    inp = support.make_config(cfg, seed=5, T=1.0)
     d = to_device(inp)
     reps = [{k: d[k].clone() for k in ("q", "k", "v", "tgt_logits", "dft_logits")} for _ in range(3)]
     reps[1]["q"].mul_(-1)  # three different inputs
@@ -551,7 +552,7 @@ def test_recorded_step_replay_equals_run(cfg, overlap):
     """VerifyStep.compile() records each replica's library calls; run_fast(i) replays
     them and must give, bit for bit, what run() gives on the same replica."""
     say("replayed step", cfg, overlap)
-    inp = synth.make_config(cfg, seed=9, T=1.0)
+    inp = support.make_config(cfg, seed=9, T=1.0)
     d = to_device(inp)
     reps = [{k: d[k].clone() for k in ("q", "k", "v", "tgt_logits", "dft_logits")} for _ in range(2)]
     reps[1]["tgt_logits"].add_(0.5 * torch.randn_like(reps[1]["tgt_logits"]))

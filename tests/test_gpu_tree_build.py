@@ -12,7 +12,7 @@ import torch
 
 from oracle import tree_build as otb
 from tree_verification_masked_amd import binding as B
-from tree_verification_masked_amd import synth
+import synth
 from tree_verification_masked_amd.draft_tree import DraftTree
 
 pytestmark = pytest.mark.gpu

@@ -9,7 +9,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from tree_verification_masked_amd import synth
+import synth
 
 
 def _path(parent, i):

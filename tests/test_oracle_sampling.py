@@ -21,7 +21,7 @@ import pytest
 import scipy.stats
 
 import oracle
-from tree_verification_masked_amd import synth
+import synth
 
 TRIALS = 1_000_000
 

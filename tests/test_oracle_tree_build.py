@@ -190,3 +190,12 @@ def test_best_first_pops_the_best_nodes_of_the_whole_candidate_tree(seed):
     best = sorted(full.values(), reverse=True)[: r - 1]  # the root (value 1) is the first pop
     assert np.allclose(sorted(vals[1:], reverse=True), best, rtol=1e-12)
     assert t.ties == []
+
+
+def test_worked_example_values_follow_the_product_rule():
+    # tree notes part G: node values are products of the draft confidences on the root path
+    g = _golden("worked_example.json")["printed_by_the_page"]
+    conf = g["draft_confidence"]
+    _, lvl1, _ = tb.expand_values([1.0], 1, [[conf["1"], conf["2"]]])
+    _, lvl2, _ = tb.expand_values(list(lvl1), 2, [[conf["3"], conf["4"]], [conf["5"], conf["6"]]])
+    np.testing.assert_allclose([1.0] + list(lvl1) + list(lvl2), g["node_values"], rtol=0, atol=1e-12)

@@ -16,7 +16,8 @@ import torch
 
 import oracle
 from tree_verification_masked_amd import binding as B
-from tree_verification_masked_amd import synth
+import synth
+import support
 from tree_verification_masked_amd.step import to_device
 
 pytestmark = pytest.mark.gpu
@@ -74,7 +75,7 @@ def _oracle_rows(inp, anc, got, n_rows, seed):
 def test_noalloc_matches_workspace_call_twice():
     # first call: the 8B-shaped workload in the launch the benchmark times (MFMA path)
     say("noalloc attention: 60-node tree, ctx 4096, 32/8 heads, bf16")
-    big = synth.make_config(2, seed=5, vocab_override=64)
+    big = support.make_config(2, seed=5, vocab_override=64)
     need = B.spec_tree_attention_workspace_size(1, big["n_max"], big["hq"], big["hkv"], big["d"],
                                                 int(big["ctx_len"].max()) + big["n_max"])
     assert need <= B.ATTENTION_SCRATCH_BYTES
@@ -84,7 +85,7 @@ def test_noalloc_matches_workspace_call_twice():
     assert err <= 2e-2, err
     # second call, smaller: the 7-node fp32 tree (shuffle path) over what the first left behind
     say("noalloc attention: 7-node tree, ctx 128, fp32")
-    small = synth.make_config(1, seed=6)
+    small = support.make_config(1, seed=6)
     a2, b2, anc2 = _both(small)
     assert np.array_equal(a2, b2)
     ref = oracle.tree_attention(small["q"], small["k"], small["v"], small["ctx_len"], small["n_nodes"], anc2,

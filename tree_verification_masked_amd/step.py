@@ -24,7 +24,7 @@ from . import binding as B
 
 
 def to_device(inp: dict, device="cuda") -> dict:
-    """Copy a synthetic input set (numpy, see synth.make_config) to the GPU."""
+    """Copy a synthetic input set (numpy dict of arrays and scalars, as synth.make_config makes it) to the GPU."""
     d = {}
     for key in ("parent", "tokens", "n_nodes", "ctx_len", "block_table"):
         if inp.get(key) is not None:
