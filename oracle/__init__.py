@@ -142,6 +142,19 @@ def softmax(logits, T, want_probs=True):
     return {"probs": probs, "max": mx, "sumexp": se, "argmax": am, "valid": valid}
 
 
+def acceptance_rate(tgt_logits, dft_logits, T, Td):
+    """Per-row acceptance rate alpha = sum_x min(p(x), q(x)) of one drafted token
+    drawn from q and verified against p (fp64), with p = softmax(target / T) and
+    q = softmax(draft / Td).  Tree-verification notes, "Tree Verification 详解"
+    parts A and D.1: a chain token passes with probability alpha, so P(L >= k) is the
+    product of the first k levels' alpha when the rows do not depend on the drafted
+    tokens.  Rows [..., V] fp32; returns an array of the leading shape."""
+    p = softmax(tgt_logits, T)["probs"]
+    q = softmax(dft_logits, Td)["probs"]
+    shape = np.shape(tgt_logits)[:-1]
+    return np.minimum(p, q).sum(axis=-1).reshape(shape)
+
+
 def reject_sample(tgt_logits, dft_logits, T, Td, tokens, parent, n_nodes, u_accept, u_sample,
                   eps=1e-6, mode="lazy"):
     """Tree rejection sampling.  Logits [B, n_max, V] fp32.  Returns dict of

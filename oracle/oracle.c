@@ -27,8 +27,11 @@
  *   oracle_mask             pinned (hand-built 7-node tree, chain, star)
  *   oracle_tree_attention   pinned (causal equivalence vs a library attention)
  *   oracle_softmax          pinned (library softmax, row sums)
- *   oracle_reject_sample    pinned (worked example, chi-square, alpha^d, greedy vs
- *                           target-only decode, special cases)
+ *   oracle_reject_sample    pinned (worked example, chi-square, alpha^d, product of
+ *                           per-level alphas, greedy vs target-only decode, special
+ *                           cases; near-tie bands: hand-derived first-order widths of
+ *                           a later-sibling test and of draws from p and from a
+ *                           residual, each probed just inside and just outside)
  *   oracle_accept_path      pinned (worked example)
  *   oracle_kv_commit        pinned (hand-checked moves on a small cache, both
  *                           layouts; untouched positions; page release)

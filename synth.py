@@ -15,9 +15,9 @@ blocks verified as chains, a batch of small random trees over a paged KV cache,
 and a long-context 64/8-head shard with heavy-tailed logits.  No public
 benchmark item is used; every value is drawn from a seeded PCG64 stream.
 
-Uniform convention: every uniform is (2k + 1) * 2**-24 for an integer k drawn
-uniformly from [0, 2**23), so it is exactly representable in fp32 and lies in
-the open interval (0, 1).
+Uniform convention: every uniform is k * 2**-24 for an integer k drawn uniformly
+from [0, 2**24), so it is exactly representable in fp32 and lies in [0, 1)
+(0 included).
 """
 from __future__ import annotations
 
@@ -37,8 +37,8 @@ def rng_for(*key: int) -> np.random.Generator:
 
 
 def uniforms(rng: np.random.Generator, shape) -> np.ndarray:
-    k = rng.integers(0, 1 << 23, size=shape, dtype=np.int64)
-    return ((2 * k + 1).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+    k = rng.integers(0, 1 << 24, size=shape, dtype=np.int64)
+    return (k.astype(np.float64) * 2.0 ** -24).astype(np.float32)
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -476,6 +476,21 @@ def chain_trials(rng, p, q, depth, n_trials):
     dft = np.broadcast_to(log_probs_f32(q), (n_trials, n, V)).copy()
     return dict(parent=parent, tokens=tokens, n_nodes=np.full(n_trials, n, np.int32), tgt_logits=tgt,
                 dft_logits=dft, u_accept=uniforms(rng, (n_trials, n)), u_sample=uniforms(rng, (n_trials, n)))
+
+
+def chain_redraw(tgt_rows, dft_rows, Td: float, root_token: int, n_trials: int, rng):
+    """Trials on one chain whose logit rows are fixed (tgt_rows, dft_rows: [n, V]):
+    every trial draws its own tokens, token i from the draft distribution of row
+    i - 1 at temperature Td, and its own uniforms.  Returns the tree arrays
+    ([n_trials, n]); the rows are the caller's to broadcast."""
+    n, V = tgt_rows.shape
+    tokens = np.zeros((n_trials, n), np.int32)
+    tokens[:, 0] = root_token
+    for i in range(1, n):
+        cdf = np.cumsum(_draft_probs(dft_rows[i - 1], Td))
+        tokens[:, i] = np.minimum(np.searchsorted(cdf, rng.random(n_trials) * cdf[-1], side="right"), V - 1)
+    return dict(parent=np.tile(chain_tree(n), (n_trials, 1)), tokens=tokens, n_nodes=np.full(n_trials, n, np.int32),
+                u_accept=uniforms(rng, (n_trials, n)), u_sample=uniforms(rng, (n_trials, n)))
 
 
 def path_keyed_logits(seed: int, path_tokens, vocab: int) -> np.ndarray:

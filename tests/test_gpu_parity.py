@@ -197,20 +197,50 @@ def _sampling_gpu(inp):
     return got
 
 
-def _compare_sampling(got, ref, n_nodes):
-    """Bit-exact on every request whose committed path carries no near-tie flag."""
+def _check_walk(got, inp, b):
+    """The outputs of request b form a valid walk of its tree: root first, each next
+    node a child of the previous one, the emitted tokens those of the accepted
+    children followed by the terminal token of the last node, all in [0, V)."""
+    V, nb = inp["V"], int(inp["n_nodes"][b])
+    par, tok = inp["parent"][b], inp["tokens"][b]
+    L = int(got["accept_len"][b])
+    pn, ot = got["path_nodes"][b], got["out_tokens"][b]
+    acc, term = got["accepted_child"][b], got["term_token"][b]
+    assert 0 <= L < nb, (b, L)
+    assert pn[0] == 0 and (pn[L + 1:] == -1).all() and (ot[L + 1:] == -1).all(), b
+    for i in range(1, L + 1):
+        assert pn[i - 1] < pn[i] < nb and par[pn[i]] == pn[i - 1], (b, i)
+        assert acc[pn[i - 1]] == pn[i] and ot[i - 1] == tok[pn[i]], (b, i)
+    last = pn[L]
+    assert acc[last] == B.NODE_NONE and 0 <= term[last] < V and ot[L] == term[last], b
+    assert ((0 <= ot[:L + 1]) & (ot[:L + 1] < V)).all(), b
+
+
+def _compare_sampling(got, ref, inp, max_exempt):
+    """Bit-exact on every request whose committed path carries no near-tie flag.  A
+    request with a flag is exempt from bit-exactness but must still be a valid walk
+    that agrees with the oracle's path up to its first flagged node (the decisions
+    before it are not near ties); at most ``max_exempt`` requests may be exempt.
+    Returns the exempt count."""
     ties = 0
-    for b in range(len(n_nodes)):
+    for b in range(len(inp["n_nodes"])):
         pn = ref["path_nodes"][b]
         nodes = pn[pn >= 0]
         if ref["accept_len"][b] >= 0 and ref["tie_flags"][b][nodes].any():
             ties += 1
+            first = int(np.nonzero(ref["tie_flags"][b][nodes])[0][0])
+            assert np.array_equal(got["path_nodes"][b][:first + 1], pn[:first + 1]), b
+            _check_walk(got, inp, b)
             continue
         assert got["accept_len"][b] == ref["accept_len"][b], b
         assert np.array_equal(got["path_nodes"][b], ref["path_nodes"][b]), b
         assert np.array_equal(got["out_tokens"][b], ref["out_tokens"][b]), b
         assert np.array_equal(got["accepted_child"][b], ref["accepted_child"][b]), b
         assert np.array_equal(got["term_token"][b], ref["term_token"][b]), b
+        if ref["accept_len"][b] >= 0:
+            _check_walk(got, inp, b)
+    print(f"near-tie exempt requests: {ties} of {len(inp['n_nodes'])}")
+    assert ties <= max_exempt, (ties, max_exempt)
     return ties
 
 
@@ -232,8 +262,9 @@ def test_sampling_full_vocab(cfg, T, seeds):
         got = _sampling_gpu(inp)
         ref = _oracle_sampling(inp)
         assert got["status"][0] == 0
-        ties += _compare_sampling(got, ref, inp["n_nodes"])
+        ties += _compare_sampling(got, ref, inp, max_exempt=inp["B"])
     print("near ties:", ties)
+    assert ties <= 1 + sum(1 for _ in seeds) // 3
 
 
 @pytest.mark.parametrize("cfg", [2, 4, 5])
@@ -245,7 +276,7 @@ def test_sampling_many_small_vocab_trees(cfg):
         inp = support.make_config(cfg, seed=100 + seed, with_kv=False, vocab_override=4096)
         got = _sampling_gpu(inp)
         ref = _oracle_sampling(inp)
-        ties += _compare_sampling(got, ref, inp["n_nodes"])
+        ties += _compare_sampling(got, ref, inp, max_exempt=inp["B"])
         n += inp["B"]
     print(f"near ties: {ties} / {n}")
     assert ties <= max(2, n // 20)
@@ -263,7 +294,7 @@ def test_sampling_ragged_vocab(cfg, V):
         got = _sampling_gpu(inp)
         ref = _oracle_sampling(inp)
         assert got["status"][0] == 0
-        ties += _compare_sampling(got, ref, inp["n_nodes"])
+        ties += _compare_sampling(got, ref, inp, max_exempt=inp["B"])
         n += inp["B"]
     print(f"near ties: {ties} / {n}")
     assert ties <= max(2, n // 10)
@@ -282,8 +313,7 @@ def test_sampling_star_trials(qkind, k):
     inp = dict(tr, B=100_000, n_max=k + 1, V=16, T=1.0, Td=1.0, ctx_len=np.zeros(100_000, np.int32))
     got = _sampling_gpu(inp)
     ref = _oracle_sampling(inp)
-    ties = _compare_sampling(got, ref, inp["n_nodes"])
-    assert ties < 50
+    _compare_sampling(got, ref, inp, max_exempt=50)
     counts = np.bincount(got["out_tokens"][:, 0], minlength=16)
     exp = p * counts.sum()
     keep = exp >= 5
@@ -297,7 +327,7 @@ def test_sampling_chain_alpha():
     inp = dict(tr, B=100_000, n_max=9, V=16, T=1.0, Td=1.0, ctx_len=np.zeros(100_000, np.int32))
     got = _sampling_gpu(inp)
     ref = _oracle_sampling(inp)
-    assert _compare_sampling(got, ref, inp["n_nodes"]) < 20
+    _compare_sampling(got, ref, inp, max_exempt=20)
     L = got["accept_len"]
     for dd in range(1, 9):
         sd = np.sqrt(0.7 ** dd * (1 - 0.7 ** dd) / L.size)
@@ -331,6 +361,204 @@ def test_sampling_bad_requests():
     assert got["accept_len"].tolist()[1:] == [-1, -1, -1] and got["accept_len"][0] >= 0
     assert (got["accepted_child"][1:, 0] == B.NODE_BAD_REQUEST).all()
     assert got["status"][0] != 0
+
+
+def _star_case(rng, p_root, q_root, n_children, n_trials, child_tokens=None):
+    """Stars with the given root rows (probability vectors, zeros as -inf logits); the
+    children's tokens i.i.d. from q_root unless ``child_tokens`` ([n_trials, k]) fixes
+    them."""
+    V = p_root.size
+    tr = synth.star_trials(rng, p_root, q_root, n_children, n_trials)
+    if child_tokens is not None:
+        tr["tokens"][:, 1:] = child_tokens
+    return dict(tr, B=n_trials, n_max=n_children + 1, V=V, T=1.0, Td=1.0, ctx_len=np.zeros(n_trials, np.int32))
+
+
+def _sampling_gpu_diag(inp):
+    """_sampling_gpu plus the number of nodes the sampler finished with direct
+    vocabulary passes (its workspace counter, read before and after the call)."""
+    d = to_device(dict(inp, q=None))
+    st = VerifyStep(d, with_attention=False)
+    before = B.reject_sample_diagnostics(st.rj_ws)["direct_nodes"]
+    st.softmax()
+    st.reject()
+    torch.cuda.synchronize()
+    after = B.reject_sample_diagnostics(st.rj_ws)["direct_nodes"]
+    return st.results(), after - before
+
+
+@pytest.mark.parametrize("k,fallback", [(20, True), (12, False)])
+def test_sampling_threshold_beyond_histogram(k, fallback):
+    """Disjoint supports (p on the first half of a 10007-token vocabulary, q on the
+    second): every drafted token has p = 0 and is rejected, and after j rejections
+    the threshold is c_j = j.  With 20 children c passes the ratio histogram's range
+    (16), so every root must finish with direct vocabulary passes (the workspace
+    counter shows it); with 12 it stays inside and no node does.  The bonus is drawn
+    from the untouched p."""
+    say("sampling threshold beyond histogram", k)
+    rng = synth.rng_for(58, k)
+    V, h = 10007, 5003
+    p = np.zeros(V)
+    q = np.zeros(V)
+    p[:h] = rng.dirichlet(np.full(h, 0.5))
+    q[h:] = rng.dirichlet(np.full(V - h, 0.5))
+    inp = _star_case(rng, p, q, k, 256)
+    got, direct = _sampling_gpu_diag(inp)
+    ref = _oracle_sampling(inp)
+    assert got["status"][0] == 0
+    _compare_sampling(got, ref, inp, max_exempt=8)
+    assert (got["accepted_child"][:, 0] == B.NODE_NONE).all() and (got["accept_len"] == 0).all()
+    assert (got["out_tokens"][:, 0] < h).all()
+    print("direct nodes", direct)
+    assert direct == (inp["B"] if fallback else 0)
+
+
+def test_sampling_interval_list_overflow():
+    """6000 tokens whose ratio equals the threshold after two rejections exactly.
+    Groups of tokens, all logits 0 where present: E (6000, in both rows), Z (6000,
+    draft only), H (2000, target only), plus 3 tokens absent from both.  Then
+    Z_t = 8000 and Z_d = 12000, E has rho = 1.5, and after two rejected Z children
+    c = 1 + W(1) = 1 + (0.75 - 0.5 + 0.25) = 1.5: all of E sits inside that level's
+    interval, more than a node's list holds, so the node must fall back to direct
+    passes.  A third rejection gives c = 1.75 and the bonus is uniform over H."""
+    say("sampling list overflow")
+    V, nB = 14003, 32
+    rng = synth.rng_for(59)
+    ps, qs, kids = [], [], []
+    for b in range(nB):
+        perm = rng.permutation(V)
+        E, Z, H = perm[:6000], perm[6000:12000], perm[12000:14000]
+        p = np.zeros(V)
+        q = np.zeros(V)
+        p[E] = p[H] = 1 / 8000
+        q[E] = q[Z] = 1 / 12000
+        ps.append(p)
+        qs.append(q)
+        kids.append(rng.choice(Z, 3, replace=False))
+    inp = _star_case(rng, ps[0], qs[0], 3, nB, child_tokens=np.array(kids, np.int32))
+    for b in range(nB):
+        inp["tgt_logits"][b, 0] = synth.log_probs_f32(ps[b]) + np.float32(np.log(8000.0))  # 0 or -inf
+        inp["dft_logits"][b, 0] = synth.log_probs_f32(qs[b]) + np.float32(np.log(12000.0))
+    assert set(np.unique(inp["tgt_logits"][:, 0])) <= {0.0, -np.inf}
+    assert set(np.unique(inp["dft_logits"][:, 0])) <= {0.0, -np.inf}
+    got, direct = _sampling_gpu_diag(inp)
+    ref = _oracle_sampling(inp)
+    assert got["status"][0] == 0
+    _compare_sampling(got, ref, inp, max_exempt=2)
+    assert (got["accept_len"] == 0).all()
+    for b in range(nB):
+        assert ps[b][got["out_tokens"][b, 0]] > 0 and qs[b][got["out_tokens"][b, 0]] == 0  # a token of H
+    print("direct nodes", direct)
+    assert direct == nB
+
+
+def test_sampling_zero_mass_residual():
+    """p one-hot at token t, q = 1/2 on t and on s, 60 children that all draft s.
+    Each child has ratio 0 and is rejected; W(c) = 1 - c/2 halves at every level
+    and reaches exactly zero in fp64 after 53 rejections (c rounds to 2), a
+    zero-mass step that leaves the residual at one-hot t.  The bonus must be t."""
+    say("sampling zero-mass residual")
+    V, nB = 8199, 16
+    rng = synth.rng_for(60)
+    ts = rng.choice(V, nB, replace=False)
+    ss = (ts + 1 + rng.integers(0, V - 1, nB)) % V
+    inp = _star_case(rng, np.full(V, 1 / V), np.full(V, 1 / V), 60, nB,
+                     child_tokens=np.repeat(ss[:, None], 60, axis=1).astype(np.int32))
+    for b in range(nB):
+        inp["tgt_logits"][b, 0] = -np.inf
+        inp["tgt_logits"][b, 0, ts[b]] = 0.0
+        inp["dft_logits"][b, 0] = -np.inf
+        inp["dft_logits"][b, 0, [ts[b], ss[b]]] = 0.0
+    got, _ = _sampling_gpu_diag(inp)
+    ref = _oracle_sampling(inp)
+    assert got["status"][0] == 0
+    for r in (got, ref):
+        assert (r["accepted_child"][:, 0] == B.NODE_NONE).all() and (r["accept_len"] == 0).all()
+        assert np.array_equal(r["out_tokens"][:, 0], ts)
+    for b in range(nB):
+        _check_walk(got, inp, b)
+
+
+@pytest.mark.parametrize("cfg,V", [(4, None), (2, 4096)])
+def test_sampling_zero_uniforms(cfg, V):
+    """Every uniform 0: a child is accepted whenever its ratio is positive (here every
+    first child), and a draw takes the smallest token with positive mass (token 0).
+    Both sides must give exactly that walk."""
+    say("sampling zero uniforms", cfg, V)
+    inp = support.make_config(cfg, seed=17, with_kv=False, vocab_override=V)
+    inp["u_accept"][:] = 0.0
+    inp["u_sample"][:] = 0.0
+    got = _sampling_gpu(inp)
+    ref = _oracle_sampling(inp)
+    for b in range(inp["B"]):
+        nb, par = int(inp["n_nodes"][b]), inp["parent"][b]
+        walk = [0]
+        while True:
+            kids = [c for c in range(walk[-1] + 1, nb) if par[c] == walk[-1]]
+            if not kids:
+                break
+            walk.append(kids[0])
+        want = [int(inp["tokens"][b, c]) for c in walk[1:]] + [0]
+        for r in (got, ref):
+            L = int(r["accept_len"][b])
+            assert r["path_nodes"][b, :L + 1].tolist() == walk, b
+            assert r["out_tokens"][b, :L + 1].tolist() == want, b
+        _check_walk(got, inp, b)
+
+
+def test_sampling_chain_lengths_follow_the_product_of_level_rates():
+    """Workload 3 at its full 151936-token vocabulary: the 16 rows of each level are
+    fixed, every trial redraws the drafted tokens from the draft rows and the
+    uniforms.  The GPU's acceptance lengths over 8000 trials must follow
+    P(L >= k) = prod_{i <= k} alpha_i with the oracle's per-level rates, and the
+    first 100 trials must match the oracle bit for bit."""
+    import scipy.stats
+    say("chain lengths vs product of alphas")
+    inp = synth.make_config(3, seed=4, with_kv=False)
+    T, Td, V = inp["T"], inp["Td"], inp["V"]
+    tgt, dft = inp["tgt_logits"][0], inp["dft_logits"][0]
+    n = tgt.shape[0]
+    alpha = oracle.acceptance_rate(tgt[:-1], dft[:-1], T, Td)
+    pred = np.concatenate([[1.0], np.cumprod(alpha)])
+    tgt_d, dft_d = torch.from_numpy(tgt).cuda(), torch.from_numpy(dft).cuda()
+    Ls = []
+    nb = 500
+    for batch in range(16):
+        tr = synth.chain_redraw(tgt, dft, Td, int(inp["tokens"][0, 0]), nb, synth.rng_for(61, batch))
+        small = dict(tr, B=nb, n_max=n, V=V, T=T, Td=Td, ctx_len=np.zeros(nb, np.int32))
+        d = to_device(small)
+        d["tgt_logits"] = tgt_d.expand(nb, n, V).contiguous()
+        d["dft_logits"] = dft_d.expand(nb, n, V).contiguous()
+        st = VerifyStep(d, with_attention=False)
+        st.softmax()
+        st.reject()
+        got = st.results()
+        assert got["status"][0] == 0
+        if batch == 0:
+            m = 100
+            sub = {k: (v[:m] if isinstance(v, np.ndarray) else v) for k, v in small.items()}
+            sub.update(B=m, tgt_logits=np.broadcast_to(tgt, (m, n, V)), dft_logits=np.broadcast_to(dft, (m, n, V)))
+            ref = _oracle_sampling(sub)
+            gsub = {k: got[k][:m] for k in ("accept_len", "path_nodes", "out_tokens", "accepted_child", "term_token")}
+            _compare_sampling(gsub, ref, sub, max_exempt=3)
+        for b in range(nb):
+            _check_walk(got, small, b)
+        Ls.append(got["accept_len"].copy())
+        del d, st
+    L = np.concatenate(Ls)
+    for k in range(1, n):
+        sd = np.sqrt(pred[k] * (1 - pred[k]) / L.size)
+        assert abs((L >= k).mean() - pred[k]) < 5 * sd + 1e-12, (k, (L >= k).mean(), pred[k])
+    probs = np.append(pred[:-1] - pred[1:], pred[-1])
+    obs = np.bincount(L, minlength=n).astype(np.float64)
+    exp = probs * L.size
+    keep = exp >= 5
+    o, e = obs[keep], exp[keep]
+    if (~keep).any():
+        o, e = np.append(o, obs[~keep].sum()), np.append(e, exp[~keep].sum())
+    assert scipy.stats.chisquare(o, e * o.sum() / e.sum()).pvalue > 0.01
+    print("P(L>=k) measured", np.round([(L >= k).mean() for k in range(1, 6)], 4), "predicted",
+          np.round(pred[1:6], 4))
 
 
 # ---------------------------------------------------------------- a2: attention
@@ -388,12 +616,13 @@ def test_attention_small_context_all_rows(cfg, ctx):
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_attention_full_size_sampled_rows(cfg):
+def test_attention_full_size_all_rows(cfg):
+    """Every output row at the workload's full context and head count."""
     say("attention full size", cfg)
     inp = support.make_config(cfg, seed=0, vocab_override=64)
     got, st, anc = _attention_gpu(inp)
     assert st == 0
-    _check_attention(inp, got, anc, n_rows=96)
+    _check_attention(inp, got, anc)
 
 
 def _custom_attention_case(rng, B_, n_max, hq, hkv, d, ctxs, n_nodes, bf16, paged=False):
@@ -487,7 +716,7 @@ def test_full_step(cfg, T):
     assert got["status"][0] == 0
     anc_r, child_r, depth_r, _ = oracle.mask(inp["parent"], inp["n_nodes"])
     assert np.array_equal(got["anc"], anc_r) and np.array_equal(got["depth"], depth_r)
-    _check_attention(inp, got["attn"], anc_r, n_rows=None if cfg == 1 else 48, seed=cfg)
+    _check_attention(inp, got["attn"], anc_r)  # every row
     ref_t = oracle.softmax(inp["tgt_logits"], inp["T"], want_probs=False)
     if inp["T"] > 0:
         # the step's logit pass leaves chunk partials only: merged on the host they
@@ -503,7 +732,7 @@ def test_full_step(cfg, T):
         assert np.array_equal(got["tmax"].astype(np.float64), ref_t["max"])
         assert np.array_equal(got["targ"], ref_t["argmax"])
     ref = _oracle_sampling(inp)
-    ties = _compare_sampling(got, ref, inp["n_nodes"])
+    ties = _compare_sampling(got, ref, inp, max_exempt=max(1, inp["B"] // 4))
     print("accept_len", got["accept_len"].tolist(), "near ties", ties)
     # the path the sampler's walk wrote equals what spec_accept_path derives
     fused = {k: got[k].copy() for k in ("path_nodes", "out_tokens", "accept_len")}

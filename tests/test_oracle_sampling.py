@@ -258,3 +258,150 @@ def test_near_ties_are_flagged():
     tr["u_accept"][0, 1] = np.float32(0.5 + 2 ** -20)
     r = _run(tr)
     assert r["tie_flags"][0, 0] & oracle.TIE_TEST
+
+
+# ---------------------------------------------------------------- near-tie bands
+#
+# The oracle flags a decision when its uniform falls inside the decision boundary's
+# range over relative perturbations of every probability by at most eps (1e-6).
+# Each case below derives that range's half-width by hand, to first order in eps,
+# places the uniform at 0.8 and at 1.25 times it (the literal 1e-5 band of accept
+# tests lying inside the first), and asserts the flag set and unset.
+
+EPS = 1e-6
+
+
+def _star3(p, q, child_tokens, u_acc, u_draw, leaf_p=None):
+    tr = synth.star_trials(synth.rng_for(32, len(child_tokens)), np.asarray(p), np.asarray(q), len(child_tokens), 1,
+                           leaf_p=None if leaf_p is None else np.asarray(leaf_p))
+    tr["tokens"][0, 1:] = child_tokens
+    tr["u_accept"][0, 1:] = np.float32(u_acc)
+    tr["u_sample"][0, 0] = np.float32(u_draw)
+    return tr
+
+
+def _probs64(p):
+    """p as the oracle sees it: the fp64 softmax of the fp32 logits that encode it."""
+    e = np.exp(synth.log_probs_f32(np.asarray(p)).astype(np.float64))
+    return e / e.sum()
+
+
+P3 = (0.1, 0.5, 0.4)
+Q3 = (0.4, 0.45, 0.15)
+
+
+@pytest.mark.parametrize("side", [-1, 1])
+def test_later_sibling_test_band(side):
+    """Second child, after the first was rejected.  With c_1 = 1 the ratio is
+    (p1 - q1) / (W q1), W = sum over p > q of (p - q) = 0.3.  Over the box:
+    p1 - c q1 moves by eps (p1 + 2 q1) / (p1 - q1) = 28 eps relative (c itself is
+    1 +- eps), W by eps * sum over p > q of (p + 2 q) / W = 7 eps, and q1 by eps:
+    half-width 36 eps times the ratio, 1.33e-5 here."""
+    p, q = _probs64(P3), _probs64(Q3)
+    W = (p - q)[p > q].sum()
+    ratio = (p[1] - q[1]) / (W * q[1])
+    half = 36 * EPS * ratio
+    assert 1e-5 < 0.8 * half  # the enclosure, not the literal band, decides the inside probe
+    for frac, flagged in ((0.8, True), (1.25, False)):
+        u = ratio + side * frac * half
+        tr = _star3(P3, Q3, [0, 1], 0.9, 0.5)
+        tr["u_accept"][0, 2] = np.float32(u)
+        r = _run(tr)
+        assert r["accepted_child"][0, 0] == (2 if side < 0 else oracle.NONE)
+        assert bool(r["tie_flags"][0, 0] & oracle.TIE_TEST) == flagged, (frac, side)
+
+
+@pytest.mark.parametrize("side", [-1, 1])
+def test_leaf_draw_band(side):
+    """A root without children draws from p.  The edge between tokens 0 and 1 sits at
+    F = p0; over the box F / (F + (1 - F)) moves by 2 F (1 - F) eps."""
+    p = _probs64((0.2, 0.3, 0.5))
+    F = p[0]
+    half = 2 * F * (1 - F) * EPS
+    for frac, flagged in ((0.8, True), (1.25, False)):
+        tr = _star3((0.2, 0.3, 0.5), (0.2, 0.3, 0.5), [], 0.5, F + side * frac * half)
+        r = _run(tr)
+        assert r["term_token"][0, 0] == (0 if side < 0 else 1)
+        assert bool(r["tie_flags"][0, 0] & oracle.TIE_DRAW) == flagged, (frac, side)
+        assert not r["tie_flags"][0, 0] & oracle.TIE_TEST
+
+
+@pytest.mark.parametrize("side", [-1, 1])
+def test_residual_draw_band(side):
+    """One child (token 0, ratio 0.25) rejected; the bonus comes from the residual
+    max(0, p - q) / W = (0, 0.05, 0.25) / 0.3, with its edge at F = 1/6.  Over the box
+    the masses 0.05 and 0.25 move by 1.4 eps and 0.7 eps (p + 2 q each, c = 1 +- eps),
+    so F moves by (28 - 7/3) eps relative."""
+    p, q = _probs64(P3), _probs64(Q3)
+    w = np.maximum(0.0, p - q)
+    F = w[1] / w.sum()
+    half = F * (28 - 7 / 3) * EPS
+    for frac, flagged in ((0.8, True), (1.25, False)):
+        tr = _star3(P3, Q3, [0], 0.9, F + side * frac * half)
+        r = _run(tr)
+        assert r["accepted_child"][0, 0] == oracle.NONE
+        assert r["term_token"][0, 0] == (1 if side < 0 else 2)
+        assert bool(r["tie_flags"][0, 0] & oracle.TIE_DRAW) == flagged, (frac, side)
+        assert not r["tie_flags"][0, 0] & oracle.TIE_TEST
+
+
+def test_zero_uniforms():
+    """u = 0 (the uniform grid k * 2^-24 includes it): a test accepts exactly when its
+    ratio is positive, and a draw returns the smallest token with positive mass, a
+    decision the oracle flags (u sits on the first bin's lower edge)."""
+    p, q = (0.0, 0.3, 0.7), (0.5, 0.25, 0.25)
+    tr = _star3(p, q, [0, 2], 0.0, 0.0, leaf_p=(0.0, 0.5, 0.5))
+    tr["u_sample"][:] = 0.0
+    r = _run(tr)
+    assert r["accepted_child"][0, 0] == 2       # token 0 has ratio 0: rejected; token 2 accepted
+    assert r["term_token"][0, 2] == 1           # leaf draw at u = 0: first token with mass
+    assert r["out_tokens"][0, :2].tolist() == [2, 1]
+    assert r["tie_flags"][0, 2] & oracle.TIE_DRAW
+    tr = _star3(p, q, [0], 0.0, 0.0)
+    r = _run(tr)
+    assert r["accepted_child"][0, 0] == oracle.NONE and r["term_token"][0, 0] == 1
+
+
+# ---------------------------------------------------------------- acceptance rates
+
+def test_acceptance_rate_special_cases():
+    for a in (0.0, 0.3, 0.7, 1.0):
+        p, q = synth.alpha_pq(a)
+        got = oracle.acceptance_rate(synth.log_probs_f32(p), synth.log_probs_f32(q), 1.0, 1.0)
+        assert abs(got - a) < 1e-6, (a, got)
+    rng = synth.rng_for(33)
+    l = rng.normal(0, 2, (3, 50)).astype(np.float32)
+    assert np.allclose(oracle.acceptance_rate(l, l, 0.8, 0.8), 1.0, atol=1e-12)
+    # the same rows at different temperatures: 1 - total variation distance
+    p = oracle.softmax(l, 0.5)["probs"]
+    q = oracle.softmax(l, 1.5)["probs"]
+    assert np.allclose(oracle.acceptance_rate(l, l, 0.5, 1.5), 1 - 0.5 * np.abs(p - q).sum(-1), atol=1e-12)
+
+
+def test_chain_lengths_follow_the_product_of_level_rates():
+    """Workload 3's generator (16-node chain, T = 0.7 against a draft at T_d = 1, draft =
+    target + N(0, 0.5)), with the vocabulary cut to 4096: the logit rows of each level
+    are fixed, while every trial redraws the drafted tokens from the draft rows and
+    the uniforms.  The rows do not depend on the drafted tokens, so levels pass
+    independently and P(L >= k) = prod_{i <= k} alpha_i, alpha_i the acceptance rate
+    of level i's rows."""
+    inp = synth.make_config(3, seed=4, with_kv=False, vocab_override=4096)
+    T, Td = inp["T"], inp["Td"]
+    tgt, dft = inp["tgt_logits"][0], inp["dft_logits"][0]
+    n = tgt.shape[0]
+    alpha = oracle.acceptance_rate(tgt[:-1], dft[:-1], T, Td)
+    pred = np.concatenate([[1.0], np.cumprod(alpha)])  # P(L >= k), k = 0 .. n - 1
+    L = []
+    for batch in range(16):
+        tr = synth.chain_redraw(tgt, dft, Td, int(inp["tokens"][0, 0]), 625, synth.rng_for(34, batch))
+        r = _run(dict(tr, tgt_logits=np.broadcast_to(tgt, (625,) + tgt.shape),
+                      dft_logits=np.broadcast_to(dft, (625,) + dft.shape)), T=T, Td=Td)
+        L.append(r["accept_len"])
+    L = np.concatenate(L)
+    assert (L >= 0).all()
+    for k in range(1, n):
+        emp = (L >= k).mean()
+        sd = np.sqrt(pred[k] * (1 - pred[k]) / L.size)
+        assert abs(emp - pred[k]) < 5 * sd + 1e-12, (k, emp, pred[k])
+    probs = np.append(pred[:-1] - pred[1:], pred[-1])  # P(L = k)
+    assert _chi2_p(np.bincount(L, minlength=n), probs) > 0.01

@@ -12,11 +12,13 @@ import synth
 import support
 
 
-def test_uniforms_are_exact_and_open():
-    u = synth.uniforms(synth.rng_for(1), 1 << 20)
-    assert u.dtype == np.float32 and (u > 0).all() and (u < 1).all()
-    k = (u.astype(np.float64) * 2 ** 24 - 1) / 2
+def test_uniforms_are_exact_and_half_open():
+    u = synth.uniforms(synth.rng_for(1), 1 << 22)
+    assert u.dtype == np.float32 and (u >= 0).all() and (u < 1).all()
+    k = u.astype(np.float64) * 2 ** 24
     assert np.array_equal(k, np.round(k))
+    assert (k % 2 == 0).any() and (k % 2 == 1).any()  # the whole 2^-24 grid, not every other point
+    assert k.min() < 2 ** 8 and k.max() > 2 ** 24 - 2 ** 8
 
 
 def test_bf16_rounding_matches_torch():
