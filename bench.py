@@ -1,12 +1,14 @@
 """Benchmark of one tree-verification step on one MI355X.
 
 A step is the whole hot path over one input set:
-    spec_tree_mask_build, spec_tree_attention (one layer's KV), spec_tree_softmax
-    (target rows, and draft rows at T > 0), spec_tree_reject_sample (whose final walk
-    also writes the accepted path, the result of spec_accept_path).
-The first two share no data with the last two, so by default they run on a second
+    spec_tree_attention (one layer's KV; given the parent links, the launch builds
+    the ancestor rows of spec_tree_mask_build itself), spec_tree_softmax_pair
+    (target and draft rows at T > 0; spec_tree_softmax at T = 0),
+    spec_tree_reject_sample (whose final walk also writes the accepted path, the
+    result of spec_accept_path).
+The attention shares no data with the other two, so by default it runs on a second
 HIP stream, forked from and joined back into the timing stream by events
-(``--serial``: all four on one stream).
+(``--serial``: all on one stream).
 Workload (default): the Llama-3-8B-shaped step -- one request, a 60-node EAGLE-2
 tree (top-k 10, depth 6), 4096 cached tokens, 32 query / 8 KV heads, head_dim 128,
 bf16 KV, fp32 logits over a 128256-token vocabulary, T = 1.  Synthetic, seeded.
@@ -19,8 +21,14 @@ are HBM numbers.  A second timed pass records events around every stage to repor
 per-stage durations.  The call holding the longest kernel (tree attention) gives the
 roofline entry and the logit softmax a second one; each is timed back to back on its
 own, so no event sits between its kernels.  Measured HBM traffic per call comes
-from the committed counter summary under profiles/ while the kernel sources match.  The CPU oracle is timed on the host on full steps of the same
-workload (multi-threaded, and on one thread).  A third pass with one event per step
+from the committed counter summary under profiles/ while the kernel sources match.
+The sampling branch (logit pass + sampler), the step's critical path, is timed the
+same way and reported with its own roofline entry.  A host-driven loop (no spin
+ahead of it) gives the rate a serving loop on this host sees.  The request is then
+verified under 2048 independent uniform sets for the accepted-length distribution
+(tau, per-depth acceptance).  The CPU oracle is timed on the host on full steps of the same
+workload (multi-threaded, and on one thread), and checks the first 32 of those
+trials (near-tie and identical counts).  A third pass with one event per step
 boundary gives the p10 / p50 / p90 of single steps.  After the timed regions come a
 32-layer-equivalent step (32 attention calls over their own KV beside one sampling
 pass), and, under "next_rows", the KV commit that follows a step (one layer, and 32
@@ -168,7 +176,8 @@ def prefill(ms=20.0):
 
 def run_steps(step, replicas, stream, n, first=0, events=None):
     """n steps, rotating over the input replicas; with events, 7 events per step
-    bracket the stages (mask, attention, softmax, -, reject + path, -)."""
+    bracket the stages (mask build unless the attention builds the ancestor rows
+    itself, attention, softmax, -, reject + path, -)."""
     for i in range(n):
         r = replicas[(first + i) % len(replicas)]
         if events is None:
@@ -179,7 +188,8 @@ def run_steps(step, replicas, stream, n, first=0, events=None):
             continue
         ev = events[i]
         ev[0].record(stream)
-        step.mask()
+        if not step.fold_mask:  # (folded: the attention call builds the ancestor rows itself)
+            step.mask()
         ev[1].record(stream)
         if step.with_attention:
             step.attention(None, r["q"], r["k"], r["v"])
@@ -319,8 +329,8 @@ def deepest_paths(parent, n_nodes):
 
 
 def time_layers_step(step, dev, replicas, stream, layers=32, iters=20, warmup=3):
-    """The 32-layer-equivalent step: mask, then one attention call per layer over its
-    own KV buffers (the same Q), beside one sampling pass (two streams, as the step).
+    """The 32-layer-equivalent step: one attention call per layer over its own KV
+    buffers (the same Q), beside one sampling pass (two streams, as the step).
     Returns us per step and the attention bytes' rate."""
     import torch
 
@@ -331,7 +341,8 @@ def time_layers_step(step, dev, replicas, stream, layers=32, iters=20, warmup=3)
         if side is not stream:
             step.ev_fork.record(stream)
             side.wait_event(step.ev_fork)
-        step.mask(side)
+        if not step.fold_mask:
+            step.mask(side)
         for k, v in kv:
             step.attention(side, r["q"], k, v)
         if side is not stream:
@@ -553,6 +564,90 @@ def cost_table(args):
     print(json.dumps({"cost_table": args.cost_table, "points": len(rows)}))
 
 
+def acceptance_trials(inp, dev, n_trials=2048, batch=256, seed=0):
+    """The step's request verified under n_trials independent sets of uniforms (the
+    tree, its tokens and logit rows fixed): the distribution of the accepted length
+    L and of tau = L + 1 tokens per step (the bonus included).  Runs the library's
+    softmax and sampling calls on `batch` copies of the request at a time.  Returns
+    (summary dict, first batch's inputs and outputs for the oracle check)."""
+    import torch
+
+    import synth
+    from tree_verification_masked_amd.step import VerifyStep
+
+    n, V = inp["n_max"], inp["V"]
+    rows = {k: dev[k][:1].expand(batch, n, V).contiguous() for k in ("tgt_logits", "dft_logits") if k in dev}
+    small = dict(parent=np.repeat(inp["parent"][:1], batch, 0), tokens=np.repeat(inp["tokens"][:1], batch, 0),
+                 n_nodes=np.repeat(inp["n_nodes"][:1], batch, 0), ctx_len=np.zeros(batch, np.int32))
+    d = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in small.items()}
+    d.update(rows, B=batch, n_max=n, V=V, T=inp["T"], Td=inp["Td"], max_kv_len=n)
+    st = VerifyStep(d, with_attention=False)
+    Ls, first = [], None
+    for i in range(-(-n_trials // batch)):
+        rng = synth.rng_for(seed, 12345, i)
+        ua, us = synth.uniforms(rng, (batch, n)), synth.uniforms(rng, (batch, n))
+        d["u_accept"], d["u_sample"] = torch.from_numpy(ua).cuda(), torch.from_numpy(us).cuda()
+        st.softmax()
+        st.reject()
+        r = st.results()
+        assert int(r["status"][0]) == 0
+        Ls.append(r["accept_len"].copy())
+        if first is None:
+            first = dict(small, u_accept=ua, u_sample=us, out=r)
+    L = np.concatenate(Ls)[:n_trials]
+    depth = np.zeros(n, np.int64)
+    for i in range(1, int(inp["n_nodes"][0])):
+        depth[i] = depth[inp["parent"][0, i]] + 1
+    D = int(depth.max())
+    ge = [float((L >= k).mean()) for k in range(D + 1)]
+    return {
+        "trials": int(L.size),
+        "what": "the timed request under independent uniform sets (tree, tokens and logits fixed)",
+        "mean_accept_len": round(float(L.mean()), 4),
+        "tau_mean": round(float(L.mean()) + 1, 4),
+        "accept_len_hist": np.bincount(L, minlength=D + 1).tolist(),
+        "p_accept_len_ge": [round(x, 4) for x in ge[1:]],
+        "per_depth_acceptance": [round(ge[k] / ge[k - 1], 4) if ge[k - 1] > 0 else None for k in range(1, D + 1)],
+    }, first
+
+
+def oracle_check(inp, first, m=32):
+    """The oracle on the first m of the acceptance trials: near-tie requests (flag on
+    the oracle's path) and requests whose GPU outputs equal the oracle's."""
+    import oracle
+
+    sub = {k: first[k][:m] for k in ("parent", "tokens", "n_nodes", "u_accept", "u_sample")}
+    tgt = np.broadcast_to(inp["tgt_logits"][:1], (m,) + inp["tgt_logits"].shape[1:])
+    dft = np.broadcast_to(inp["dft_logits"][:1], (m,) + inp["dft_logits"].shape[1:]) if inp["T"] > 0 else None
+    r = oracle.reject_sample(tgt, dft, inp["T"], inp["Td"], sub["tokens"], sub["parent"], sub["n_nodes"],
+                             sub["u_accept"] if inp["T"] > 0 else None, sub["u_sample"] if inp["T"] > 0 else None)
+    r.update(oracle.accept_path(r["accepted_child"], r["term_token"], sub["tokens"], sub["n_nodes"]))
+    g = first["out"]
+    ties = same = 0
+    for b in range(m):
+        pn = r["path_nodes"][b]
+        if r["tie_flags"][b][pn[pn >= 0]].any():
+            ties += 1
+        if all(np.array_equal(g[k][b], r[k][b]) for k in ("path_nodes", "out_tokens", "accepted_child",
+                                                          "term_token")):
+            same += 1
+    return {"trials": m, "near_tie_requests": ties, "identical_to_oracle": same}
+
+
+def host_driven(step, replicas, steps):
+    """Steps/s of a loop that the host drives with no spin ahead of it: the host's
+    issue time included (the replayed calls of compile())."""
+    import torch
+
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(steps):
+        step.run_fast(i % len(replicas))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t
+    return {"steps_per_s": round(steps / el, 1), "us_per_step": round(el * 1e6 / steps, 2), "steps": steps}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -576,7 +671,7 @@ def main():
     dev = to_device(inp)
     step = VerifyStep(dev)
     if not args.serial:
-        step.overlap(fork=args.fork)  # mask + attention on a second stream
+        step.overlap(fork=args.fork)  # the attention on a second stream
     big = [k for k in ("q", "k", "v", "tgt_logits", "dft_logits") if k in dev]
     replicas = [{k: dev[k].clone() for k in big} for _ in range(args.replicas)]
     stream = torch.cuda.current_stream()
@@ -587,7 +682,7 @@ def main():
     timing = {}
     ms_per_step, st_mean = time_steps(step, replicas, stream, args.steps, args.warmup, timing)
     pct = step_percentiles(step, replicas, stream, args.steps)
-    names = ["mask_build", "attention", "softmax_pair", "-", "reject_sample", "-"]
+    names = ["mask_build" if not step.fold_mask else "-", "attention", "softmax_pair", "-", "reject_sample", "-"]
 
     attn_b, logit_b, samp_b = algorithmic_bytes(inp)
     traffic = measured_traffic()
@@ -595,8 +690,16 @@ def main():
     attn_us = time_calls(lambda r: step.attention(None, r["q"], r["k"], r["v"]), replicas) \
         if step.with_attention else float("nan")
     pair_us = time_calls(lambda r: step.softmax(None, r["tgt_logits"], r.get("dft_logits")), replicas)
+
+    def branch(r):  # the sampling branch: the logit pass, then the sampler (with its walk)
+        step.softmax(None, r["tgt_logits"], r.get("dft_logits"))
+        step.reject(None, r["tgt_logits"], r.get("dft_logits"))
+
+    branch_us = time_calls(branch, replicas)
+    reject_us = time_calls(lambda r: step.reject(None, r["tgt_logits"], r.get("dft_logits")), replicas)
     step_b = attn_b + samp_b
     samp_us = st_mean[2] + st_mean[4] + st_mean[5]
+    hd = host_driven(step, replicas, args.steps)
     res = {
         "metric": METRIC,
         "value": round(1e3 / ms_per_step, 1),
@@ -615,8 +718,9 @@ def main():
             "ctx": int(inp["ctx_len"].max()), "hq": inp["hq"], "hkv": inp["hkv"], "head_dim": inp["d"],
             "vocab": inp["V"], "T": inp["T"], "replicas": args.replicas,
             "launch": "one stream (no graph)" if args.serial or step.side is None else
-                      ("two streams: mask + attention beside softmax + sampling (no graph)" if step.fork == "start"
-                       else "two streams: mask + attention beside the sampling, after the logit pass (no graph)"),
+                      ("two streams: the attention (ancestor rows built in its launch) beside softmax + sampling "
+                       "(no graph)" if step.fork == "start"
+                       else "two streams: the attention beside the sampling, after the logit pass (no graph)"),
         },
         # one event per step boundary: the distribution of single steps (the events'
         # own cost included, so the mean sits a little above ms_per_step)
@@ -636,10 +740,30 @@ def main():
         "roofline": roofline_entry("spec_tree_attention call: attn_mfma_kernel<128> + attn_combine_kernel",
                                    attn_b, attn_us, traffic.get("spec_tree_attention"), attention_flops(inp)),
         "stage_roofline": {
-            "softmax_pair": roofline_entry("spec_tree_softmax_pair call: softmax_stats_kernel + softmax_merge_kernel",
+            # the logit pass alone: chunk partials of both logit arrays, one launch
+            "softmax_pair": roofline_entry("spec_tree_softmax_pair call: softmax_stats_kernel (target and draft "
+                                           "rows, chunk partials only)",
                                            samp_b, pair_us, traffic.get("spec_tree_softmax_pair")),
+            # the critical path of the two-stream step: the logit pass and the sampler,
+            # against the bytes of one pass over both logit arrays
+            "sampling_branch": roofline_entry("spec_tree_softmax_pair + spec_tree_reject_sample calls: "
+                                              "softmax_stats_kernel, plan_kernel, chain_hist_kernel, "
+                                              "chain_exact_kernel, node_kernel",
+                                              samp_b, branch_us, traffic.get("sampling_branch")),
         },
+        "critical_path": {
+            "branch": "softmax_pair + reject_sample (the attention branch runs beside it)",
+            "us": round(branch_us, 2), "share_of_step": round(branch_us / (ms_per_step * 1e3), 3),
+            "reject_sample_us": round(reject_us, 2), "softmax_pair_us": round(pair_us, 2),
+            "side_branch_us": round(float(st_mean[1] + (st_mean[0] if not step.fold_mask else 0.0)), 2),
+            "attention_call_us": round(attn_us, 2),
+        },
+        # the same replayed steps driven by the host with nothing queued ahead: what a
+        # serving loop on this host gets, host issue time included
+        "host_driven": hd,
     }
+    acc, first = acceptance_trials(inp, dev, seed=args.seed)
+    res["acceptance"] = acc
     if "k" in dev and dev.get("block_table") is None:
         res["next_rows"] = {
             "kv_commit": time_kv_commit(step, dev, replicas[0]["k"], replicas[0]["v"], stream),
@@ -651,7 +775,7 @@ def main():
     if step.with_attention and dev.get("block_table") is None:
         us32 = time_layers_step(step, dev, replicas, stream)
         res["step_32_layers"] = {
-            "what": "mask + 32 attention calls (one per layer, each over its own KV buffers) beside one sampling "
+            "what": "32 attention calls (one per layer, each over its own KV buffers) beside one sampling "
                     "pass; the pages name no layer count, so this is a secondary figure",
             "us_per_step": round(us32, 2), "steps_per_s": round(1e6 / us32, 1),
             "attention_gbs": round(32 * attn_b / (us32 * 1e-6) / 1e9, 1)}
@@ -683,6 +807,8 @@ def main():
         el1 = time.perf_counter() - t_start
         res["cpu_baseline"]["single_thread"] = {"value": round(n1 / el1, 4), "unit": "steps/s", "cores": 1,
                                                 "sample": f"{n1} full steps, {el1:.1f} s"}
+        oracle.set_threads(threads)
+        res["acceptance"]["oracle_check"] = oracle_check(inp, first)
     print(json.dumps(res))
 
 

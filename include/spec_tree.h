@@ -98,7 +98,15 @@ int spec_tree_mask_build(const int32_t* parent, const int32_t* n_nodes, int32_t 
  * Tree-masked attention (tree notes, parts B and D.2).  For request b, node
  * i < n_nodes[b] and query head h (KV head g = h / (hq / hkv)):
  *   visible keys = logical positions [0, ctx_len[b]) plus ctx_len[b] + j for
- *                  every bit j of anc_mask[b,i]
+ *                  every node j that is node i or one of its ancestors
+ * The ancestor sets come from exactly one of two inputs (the other is NULL):
+ *   parent   int32 [batch, n_max]: the tree's parent links; the launch builds the
+ *            ancestor sets itself (those spec_tree_mask_build would write), so no
+ *            separate mask launch is needed.  A request whose links are not a tree
+ *            rooted at node 0 (parent[b,0] = -1, 0 <= parent[b,i] < i) gets zero
+ *            rows and SPEC_ERR_BAD_TREE.
+ *   anc_mask uint64 [batch, n_max]: the ancestor rows, bit j of anc_mask[b,i] set
+ *            when node j is visible to node i (as spec_tree_mask_build writes them).
  *   out[b,i,h,:] = softmax(scale * q . k) . v over the visible keys
  * The tree's own K/V rows sit at logical positions ctx_len[b] + j (node j), so the
  * caller writes them before this call.  Q and K carry RoPE already (node i at
@@ -120,7 +128,7 @@ int spec_tree_mask_build(const int32_t* parent, const int32_t* n_nodes, int32_t 
  * unspecified (page 0 is read in its place, so no memory outside the pool is
  * touched).  A node whose ancestor mask lacks its own bit (the all-zero masks
  * spec_tree_mask_build writes for a bad tree) gets a zero row.
- * Host errors: null pointers, hq % hkv != 0, n_max outside [1, 64], page_size < 1
+ * Host errors: null pointers, both or neither of parent and anc_mask, hq % hkv != 0, n_max outside [1, 64], page_size < 1
  * with a block table, scale not finite and positive, workspace too small;
  * SPEC_ERR_UNSUPPORTED for head_dim not 64/128, another dtype, or a block table
  * with pages of fewer than 16 tokens on the MFMA path (bf16, G >= 16).
@@ -129,9 +137,9 @@ size_t spec_tree_attention_workspace_size(int32_t batch, int32_t n_max, int32_t 
                                           int32_t max_kv_len);
 int spec_tree_attention(const void* q, const void* k, const void* v, int32_t dtype, const int32_t* block_table,
                         int32_t page_size, int32_t kv_capacity, int32_t n_pages, const int32_t* ctx_len,
-                        const int32_t* n_nodes, const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq,
-                        int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale, void* out, void* workspace,
-                        size_t workspace_bytes, int32_t* status, void* stream);
+                        const int32_t* n_nodes, const int32_t* parent, const uint64_t* anc_mask, int32_t batch,
+                        int32_t n_max, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale,
+                        void* out, void* workspace, size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
  * spec_tree_attention for callers that cannot allocate device memory: code under
@@ -151,9 +159,10 @@ int spec_tree_attention(const void* q, const void* k, const void* v, int32_t dty
 #define SPEC_TREE_ATTENTION_SCRATCH_BYTES (16u << 20)
 int spec_tree_attention_noalloc(const void* q, const void* k, const void* v, int32_t dtype,
                                 const int32_t* block_table, int32_t page_size, int32_t kv_capacity, int32_t n_pages,
-                                const int32_t* ctx_len, const int32_t* n_nodes, const uint64_t* anc_mask,
-                                int32_t batch, int32_t n_max, int32_t hq, int32_t hkv, int32_t head_dim,
-                                int32_t max_kv_len, float scale, void* out, int32_t* status, void* stream);
+                                const int32_t* ctx_len, const int32_t* n_nodes, const int32_t* parent,
+                                const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
+                                int32_t head_dim, int32_t max_kv_len, float scale, void* out, int32_t* status,
+                                void* stream);
 
 /*
  * Per-row vocabulary softmax statistics at temperature T ("The EAGLE Family",

@@ -563,13 +563,18 @@ def test_sampling_chain_lengths_follow_the_product_of_level_rates():
 
 # ---------------------------------------------------------------- a2: attention
 
-def _attention_gpu(inp):
+def _attention_gpu(inp, fold=True):
+    """The attention call (from the parent links by default, else from the rows of
+    spec_tree_mask_build); returns its output, the status and the oracle's ancestor
+    rows."""
     d = to_device(inp)
-    st = VerifyStep(d)
-    st.mask()
+    st = VerifyStep(d, fold_mask=fold)
+    if not fold:
+        st.mask()
     st.attention()
     r = st.results()
-    return r["attn"], int(r["status"][0]), r["anc"]
+    anc, _, _, _ = oracle.mask(inp["parent"], inp["n_nodes"])
+    return r["attn"], int(r["status"][0]), anc
 
 
 def _rows_sample(inp, n_rows, rng):
@@ -684,6 +689,46 @@ def test_attention_edge_cases(name, B_, n_max, hq, hkv, d, ctxs, nn, bf16, paged
     _check_attention(inp, got, anc)
 
 
+@pytest.mark.parametrize("case", ["cfg1 fp32 shuffle", "cfg2 mfma", "cfg4 paged mfma", "small G bf16 shuffle"])
+def test_attention_parent_links_equal_ancestor_rows(case):
+    """The attention launch given the parent links builds the ancestor rows itself:
+    its output must equal, bit for bit, the launch that reads the rows of
+    spec_tree_mask_build."""
+    say("attention from parent links", case)
+    if case.startswith("cfg"):
+        inp = support.make_config(int(case[3]), seed=2, ctx_override=600 if case[3] != "1" else None,
+                                  vocab_override=64)
+    else:
+        inp = _custom_attention_case(np.random.default_rng(7), 3, 7, 4, 2, 128, [5, 64, 130], [7, 3, 1], True)
+    a_fold, st_fold, _ = _attention_gpu(inp, fold=True)
+    a_mask, st_mask, _ = _attention_gpu(inp, fold=False)
+    assert st_fold == 0 and st_mask == 0
+    assert np.array_equal(a_fold, a_mask)
+
+
+@pytest.mark.parametrize("mfma", [True, False])
+def test_attention_parent_links_bad_tree(mfma):
+    """A request whose parent links are not a tree: its rows are zero and the status
+    says SPEC_ERR_BAD_TREE; the other requests are untouched (equal to the launch
+    that reads spec_tree_mask_build's rows, which are zero for that request too)."""
+    say("attention bad tree", mfma)
+    hq, d = (16, 128) if mfma else (2, 64)  # 9 x 8 rows per KV head (MFMA tiles) or 9 x 1 (shuffle path)
+    inp = _custom_attention_case(np.random.default_rng(8), 3, 9, hq, 2, d, [40, 300, 77], [9, 9, 5], True)
+    inp["parent"][1, 4] = 6  # a parent behind its child
+    a_fold, st_fold, _ = _attention_gpu(inp, fold=True)
+    a_mask, st_mask, _ = _attention_gpu(inp, fold=False)
+    assert st_fold == -3 and st_mask == -3  # SPEC_ERR_BAD_TREE
+    assert (a_fold[1] == 0).all()
+    assert np.array_equal(a_fold, a_mask)
+    ok = [0, 2]
+    anc, _, _, _ = oracle.mask(inp["parent"], inp["n_nodes"])
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], inp["n_nodes"], anc, hq, 2,
+                                rows=np.array([(b, i, h) for b in ok for i in range(inp["n_nodes"][b])
+                                               for h in range(hq)], np.int32), bf16=True)
+    got = np.concatenate([a_fold[b, :inp["n_nodes"][b]].reshape(-1, d) for b in ok])
+    assert np.abs(got - ref).max() < 2e-2
+
+
 def test_attention_rejects_out_of_range_lengths():
     say("attention bad lengths")
     inp = _custom_attention_case(np.random.default_rng(1), 2, 8, 8, 2, 128, [100, 50], [8, 8], True)
@@ -710,8 +755,9 @@ def test_full_step(cfg, T):
     say("full step", cfg, T)
     inp = support.make_config(cfg, seed=11, T=T)
     d = to_device(inp)
-    st = VerifyStep(d).overlap()  # mask + attention on a second stream, as the benchmark runs it
+    st = VerifyStep(d).overlap()  # the attention on a second stream, as the benchmark runs it
     st.run()
+    st.mask()  # the standalone mask build (the step's attention built its ancestor rows itself)
     got = st.results()
     assert got["status"][0] == 0
     anc_r, child_r, depth_r, _ = oracle.mask(inp["parent"], inp["n_nodes"])

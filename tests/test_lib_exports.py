@@ -86,8 +86,8 @@ def test_host_errors_softmax(lib):
 
 def test_host_errors_attention(lib):
     f = lib.spec_tree_attention
-    base = dict(q=P, k=P, v=P, dtype=1, bt=None, ps=0, cap=100, npg=0, ctx=P, n=P, anc=P, B=1, nmax=8, hq=8, hkv=2,
-                D=128, maxlen=100, scale=0.1, out=P, ws=P, wsb=1 << 30, st=None, s=None)
+    base = dict(q=P, k=P, v=P, dtype=1, bt=None, ps=0, cap=100, npg=0, ctx=P, n=P, par=None, anc=P, B=1, nmax=8,
+                hq=8, hkv=2, D=128, maxlen=100, scale=0.1, out=P, ws=P, wsb=1 << 30, st=None, s=None)
 
     def call(**kw):
         a = dict(base, **kw)
@@ -100,6 +100,9 @@ def test_host_errors_attention(lib):
     assert call(q=None) == -1
     assert call(scale=0.0) == -1
     assert call(bt=P, ps=0) == -1
+    assert call(par=P) == -1            # both the parent links and the ancestor rows
+    assert call(anc=None) == -1         # neither
+    assert call(par=P, anc=None, wsb=16) == -5  # the parent links alone are accepted
     assert call(wsb=16) == -5
 
 

@@ -38,10 +38,10 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "spec_tree_mask_build": [_VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_attention_workspace_size": [_I32, _I32, _I32, _I32, _I32, _I32],
-    "spec_tree_attention": [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
-                            _I32, _F32, _VP, _VP, _SZ, _VP, _VP],
-    "spec_tree_attention_noalloc": [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
-                                    _I32, _I32, _F32, _VP, _VP, _VP],
+    "spec_tree_attention": [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
+                            _I32, _I32, _F32, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_attention_noalloc": [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
+                                    _I32, _I32, _I32, _F32, _VP, _VP, _VP],
     "spec_tree_softmax_chunk": [],
     "spec_tree_softmax_workspace_size": [_I64, _I32],
     "spec_tree_softmax": [_VP, _I64, _I32, _F32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
@@ -197,9 +197,10 @@ def spec_tree_mask_build(parent, n_nodes, anc_mask, child_mask, depth, status=No
 
 
 def _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, block_table, page_size, n_pages,
-                    scale, status):
+                    scale, status, parent):
     """The argument list shared by spec_tree_attention and spec_tree_attention_noalloc
-    (everything before their workspace / status arguments), after the checks."""
+    (everything before their workspace / status arguments), after the checks.  The
+    ancestor sets come from exactly one of anc_mask and parent."""
     B, n_max, hq, D = q.shape
     if q.dtype == torch.bfloat16:
         dtype = SPEC_BF16
@@ -213,6 +214,9 @@ def _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, b
     _check(ctx_len, torch.int32, (B,), "ctx_len")
     _check(n_nodes, torch.int32, (B,), "n_nodes")
     _check(anc_mask, torch.int64, (B, n_max), "anc_mask")
+    _check(parent, torch.int32, (B, n_max), "parent")
+    if (anc_mask is None) == (parent is None):
+        raise ValueError("give exactly one of anc_mask and parent")
     _check(status, torch.int32, (1,), "status")
     if block_table is None:
         if k.shape[0] != B or k.shape[2] != hkv or k.shape[3] != D or k.shape != v.shape:
@@ -229,23 +233,25 @@ def _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, b
     if scale is None:
         scale = D ** -0.5
     return (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(block_table), page_size, kv_capacity, n_pages, _ptr(ctx_len),
-            _ptr(n_nodes), _ptr(anc_mask), B, n_max, hq, hkv, D, max_kv_len, scale, _ptr(out))
+            _ptr(n_nodes), _ptr(parent), _ptr(anc_mask), B, n_max, hq, hkv, D, max_kv_len, scale, _ptr(out))
 
 
 def spec_tree_attention(q, k, v, ctx_len, n_nodes, anc_mask, out, workspace, *, hkv, max_kv_len,
-                        block_table=None, page_size=0, n_pages=0, scale=None, status=None, stream=None):
+                        block_table=None, page_size=0, n_pages=0, scale=None, status=None, stream=None, parent=None):
+    """anc_mask: the ancestor rows; or anc_mask=None and parent= the parent links, from
+    which the launch builds them itself."""
     args = _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, block_table, page_size,
-                           n_pages, scale, status)
+                           n_pages, scale, status, parent)
     _call("spec_tree_attention", *args, _ptr(workspace), workspace.numel() * workspace.element_size(),
           _ptr(status), _stream(stream))
 
 
 def spec_tree_attention_noalloc(q, k, v, ctx_len, n_nodes, anc_mask, out, *, hkv, max_kv_len, block_table=None,
-                                page_size=0, n_pages=0, scale=None, status=None, stream=None):
+                                page_size=0, n_pages=0, scale=None, status=None, stream=None, parent=None):
     """spec_tree_attention with the split partials in the library's own per-GPU array
     (SPEC_TREE_ATTENTION_SCRATCH_BYTES): no workspace argument, nothing allocated."""
     args = _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, block_table, page_size,
-                           n_pages, scale, status)
+                           n_pages, scale, status, parent)
     _call("spec_tree_attention_noalloc", *args, _ptr(status), _stream(stream))
 
 

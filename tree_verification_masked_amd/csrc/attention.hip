@@ -51,7 +51,8 @@ struct AttnArgs {
   int32_t page_size, kv_capacity, n_pages;
   const int32_t* ctx_len;
   const int32_t* n_nodes;
-  const uint64_t* anc;
+  const int32_t* parent;  // the tree's parent links (ancestor rows built in the launch), or
+  const uint64_t* anc;    // the ancestor rows themselves: exactly one is given
   int32_t batch, n_max, hq, hkv, head_dim, max_kv_len;
   float scale_log2;  // scale * log2(e): scores live in the log2 domain
   int32_t S, split_len, qblocks;
@@ -188,6 +189,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   static_assert(LOADS >= 1 && LOADS * 8 * 1024 == TILE_B, "tile split over the eight waves");
   __shared__ __attribute__((aligned(1024))) char sKV[kStages][2][TILE_B];
   __shared__ int s_page[kMaxSplitPages];
+  __shared__ uint64_t s_anc[64];
+  __shared__ int s_tree_ok;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wid & 3, kh = wid >> 2;  // row block, key half
@@ -243,7 +246,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int node = r / hpg;
   const int node_c = min(node, a.n_max - 1);
   const int h = g * hpg + r % hpg;
-  const uint64_t anc_raw = a.anc[(int64_t)b * a.n_max + node_c];
+  uint64_t anc_raw = a.anc ? a.anc[(int64_t)b * a.n_max + node_c] : 0ull;
+  // with parent links, wave 0 holds node `lane`'s link (built into ancestor rows below)
+  const int plink = (a.parent && wid == 0 && lane < a.n_max) ? a.parent[(int64_t)b * a.n_max + lane] : -1;
   // Q fragments: lane holds row r, dims kk*16 + 8*(lane/32) .. +8
   bf16x8 qf[D / 16];
   {
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int len = request_len(a, b);
   const int n = a.n_nodes[b];
   const int ctx = a.ctx_len[b];
-  const bool row_live = len >= 0 && r < G && node < n;
+  bool row_live = len >= 0 && r < G && node < n;
   const int k_end = min(k_begin + a.split_len, len < 0 ? 0 : len);
   const int n_tiles = k_end > k_begin ? (k_end - k_begin + kTile - 1) / kTile : 0;
 
@@ -311,6 +316,17 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   // anc_row and Q are in registers before the loop (with the first tiles, which the
   // first iteration needs anyway), so no wait inside the loop is for them
   vm_wait<0>();
+  if (a.parent) {  // ancestor rows of this request from its parent links, shared through LDS
+    if (wid == 0) {
+      bool ok;
+      s_anc[lane] = tree_ancestors_wave(plink, n, a.n_max, &ok);
+      if (lane == 0) s_tree_ok = ok;
+      if (lane == 0 && !ok && len >= 0 && g == 0 && qb == 0 && s == 0) report(a.status, SPEC_ERR_BAD_TREE);
+    }
+    lds_barrier();
+    anc_raw = s_anc[node_c];
+    row_live = row_live && s_tree_ok;  // a request that is not a tree gets zero rows
+  }
   const uint64_t anc_row = row_live ? anc_raw : 0ull;
   if (!row_live)
 #pragma unroll
@@ -551,6 +567,8 @@ __global__ __launch_bounds__(256) void attn_shfl_kernel(AttnArgs a) {
   __shared__ float sQ[kShflRowsPerWg * D];
   __shared__ float sK[kTile * (D + 1)];
   __shared__ float sV[kTile * D];
+  __shared__ uint64_t s_anc[64];
+  __shared__ int s_tree_ok;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int blk = blockIdx.x;
   const int s = blk % a.S;
@@ -577,6 +595,18 @@ __global__ __launch_bounds__(256) void attn_shfl_kernel(AttnArgs a) {
     if (rr < G && node < n && len >= 0) val = (float)qg[(((int64_t)b * a.n_max + node) * a.hq + h) * D + x % D];
     sQ[x] = val;
   }
+  bool tree_ok = true;
+  if (a.parent) {  // ancestor rows of this request from its parent links, shared through LDS
+    if (wid == 0) {
+      const int p = lane < a.n_max ? a.parent[(int64_t)b * a.n_max + lane] : -1;
+      bool ok;
+      s_anc[lane] = tree_ancestors_wave(p, n, a.n_max, &ok);
+      if (lane == 0) s_tree_ok = ok;
+      if (lane == 0 && !ok && len >= 0 && g == 0 && qb == 0 && s == 0) report(a.status, SPEC_ERR_BAD_TREE);
+    }
+    __syncthreads();
+    tree_ok = s_tree_ok;
+  }
   // per-wave rows: wid, wid + 4, wid + 8, wid + 12
   float m_run[4], l_run[4], o[4][NV];
   uint64_t anc_row[4];
@@ -585,8 +615,8 @@ __global__ __launch_bounds__(256) void attn_shfl_kernel(AttnArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int rr = qb * kShflRowsPerWg + wid + 4 * j;
     const int node = rr / hpg;
-    live[j] = len >= 0 && rr < G && node < n;
-    anc_row[j] = live[j] ? a.anc[(int64_t)b * a.n_max + node] : 0ull;
+    live[j] = len >= 0 && rr < G && node < n && tree_ok;
+    anc_row[j] = live[j] ? (a.parent ? s_anc[node] : a.anc[(int64_t)b * a.n_max + node]) : 0ull;
     m_run[j] = -INFINITY;
     l_run[j] = 0.0f;
 #pragma unroll
@@ -689,7 +719,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* __rest
   // outputs (every row of every split is written by the attention launch, so these
   // addresses are valid whether or not the row turns out live).
   const int len = request_len(a, b);
-  const uint64_t anc_row = a.anc[(int64_t)b * a.n_max + node];
+  // (built from parent links, the ancestor rows of a request that is not a tree were
+  // all dead in the attention launch, so their partial sums are zero)
+  const uint64_t anc_row = a.anc ? a.anc[(int64_t)b * a.n_max + node] : (1ull << node);
   const int nb = a.n_nodes[b];
   const int sl = min(lane, a.S - 1);
   const float m_l = a.mpart[sl * stride + rowid], l_l = a.lpart[sl * stride + rowid];
@@ -797,10 +829,12 @@ namespace spectree {
 // the split partials in `workspace` (workspace_bytes long).
 static int attention_launch(const void* q, const void* k, const void* v, int32_t dtype, const int32_t* block_table,
                             int32_t page_size, int32_t kv_capacity, int32_t n_pages, const int32_t* ctx_len,
-                            const int32_t* n_nodes, const uint64_t* anc_mask, int32_t batch, int32_t n_max,
+                            const int32_t* n_nodes, const int32_t* parent, const uint64_t* anc_mask, int32_t batch,
+                            int32_t n_max,
                             int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale, void* out,
                             void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
-  if (!q || !k || !v || !ctx_len || !n_nodes || !anc_mask || !out) return SPEC_ERR_INVALID_ARG;
+  if (!q || !k || !v || !ctx_len || !n_nodes || !out) return SPEC_ERR_INVALID_ARG;
+  if ((parent == nullptr) == (anc_mask == nullptr)) return SPEC_ERR_INVALID_ARG;  // exactly one of the two
   if (batch < 1 || n_max < 1 || n_max > 64 || hq < 1 || hkv < 1 || hq % hkv != 0) return SPEC_ERR_INVALID_ARG;
   if (kv_capacity < 1 || max_kv_len < 1 || !(scale > 0.0f) || isinf(scale)) return SPEC_ERR_INVALID_ARG;
   if (block_table && (page_size < 1 || n_pages < 1)) return SPEC_ERR_INVALID_ARG;
@@ -823,6 +857,7 @@ static int attention_launch(const void* q, const void* k, const void* v, int32_t
   a.n_pages = n_pages;
   a.ctx_len = ctx_len;
   a.n_nodes = n_nodes;
+  a.parent = parent;
   a.anc = anc_mask;
   a.batch = batch;
   a.n_max = n_max;
@@ -907,20 +942,22 @@ static void* device_scratch() {
 extern "C" int spec_tree_attention(const void* q, const void* k, const void* v, int32_t dtype,
                                    const int32_t* block_table, int32_t page_size, int32_t kv_capacity,
                                    int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes,
-                                   const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
-                                   int32_t head_dim, int32_t max_kv_len, float scale, void* out, void* workspace,
-                                   size_t workspace_bytes, int32_t* status, void* stream) {
+                                   const int32_t* parent, const uint64_t* anc_mask, int32_t batch, int32_t n_max,
+                                   int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale,
+                                   void* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                                   void* stream) {
   return spectree::attention_launch(q, k, v, dtype, block_table, page_size, kv_capacity, n_pages, ctx_len, n_nodes,
-                                    anc_mask, batch, n_max, hq, hkv, head_dim, max_kv_len, scale, out, workspace,
-                                    workspace_bytes, status, stream);
+                                    parent, anc_mask, batch, n_max, hq, hkv, head_dim, max_kv_len, scale, out,
+                                    workspace, workspace_bytes, status, stream);
 }
 
 extern "C" int spec_tree_attention_noalloc(const void* q, const void* k, const void* v, int32_t dtype,
                                            const int32_t* block_table, int32_t page_size, int32_t kv_capacity,
                                            int32_t n_pages, const int32_t* ctx_len, const int32_t* n_nodes,
-                                           const uint64_t* anc_mask, int32_t batch, int32_t n_max, int32_t hq,
-                                           int32_t hkv, int32_t head_dim, int32_t max_kv_len, float scale, void* out,
-                                           int32_t* status, void* stream) {
+                                           const int32_t* parent, const uint64_t* anc_mask, int32_t batch,
+                                           int32_t n_max, int32_t hq, int32_t hkv, int32_t head_dim,
+                                           int32_t max_kv_len, float scale, void* out, int32_t* status,
+                                           void* stream) {
   using namespace spectree;
   // the size check needs only the host-side plan: refuse before touching the device
   if (batch >= 1 && n_max >= 1 && n_max <= 64 && hq >= 1 && hkv >= 1 && hq % hkv == 0 && max_kv_len >= 1 &&
@@ -930,7 +967,7 @@ extern "C" int spec_tree_attention_noalloc(const void* q, const void* k, const v
     return SPEC_ERR_WORKSPACE;
   void* ws = device_scratch();
   if (!ws) return SPEC_ERR_HIP;
-  return attention_launch(q, k, v, dtype, block_table, page_size, kv_capacity, n_pages, ctx_len, n_nodes, anc_mask,
-                          batch, n_max, hq, hkv, head_dim, max_kv_len, scale, out, ws, kAttnScratchBytes, status,
-                          stream);
+  return attention_launch(q, k, v, dtype, block_table, page_size, kv_capacity, n_pages, ctx_len, n_nodes, parent,
+                          anc_mask, batch, n_max, hq, hkv, head_dim, max_kv_len, scale, out, ws, kAttnScratchBytes,
+                          status, stream);
 }

@@ -146,6 +146,35 @@ __device__ inline uint64_t shfl_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Ancestor set of a flattened draft tree, one wavefront per tree ("Tree Verification
+// 详解" part B: a node sees itself and its ancestors).  Lane i passes node i's parent
+// link p (-1 past n_max) and gets the bitmask of node i and its ancestors (0 for
+// lanes at or past n).  *ok: n lies in [1, n_max] and the links form a tree rooted
+// at node 0 with every parent ahead of its child (wave-uniform).  The sets come
+// from pointer jumping: six doubling steps cover depth 63.
+__device__ inline uint64_t tree_ancestors_wave(int p, int n, int n_max, bool* ok) {
+  const int lane = threadIdx.x & 63;
+  const bool n_ok = n >= 1 && n <= n_max;
+  const bool node = n_ok && lane < n;
+  const bool link_ok = !node || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
+  *ok = n_ok && __all(link_ok);
+  if (!*ok) return 0ull;
+  // a: ancestors at distance < 2^t (self included); jp: the ancestor at distance 2^t
+  uint64_t a = node ? (1ull << lane) : 0ull;
+  int jp = node ? p : -1;
+#pragma unroll
+  for (int t = 0; t < 6; ++t) {
+    const int src = jp < 0 ? lane : jp;
+    const uint64_t a_src = shfl_u64(a, src);
+    const int jp_src = __shfl(jp, src);
+    if (jp >= 0) {
+      a |= a_src;
+      jp = jp_src;
+    }
+  }
+  return a;
+}
+
 // exp(d / T) for d <= 0 written as 2^(d * log2(e) / T); the scale is carried as an
 // fp32 pair (hi + lo) so that its rounding does not bias every element the same way.
 struct ExpScale {

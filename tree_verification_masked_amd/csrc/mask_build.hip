@@ -3,9 +3,10 @@
 // Tree-verification notes (zhangshuibai.github.io), "Tree Verification 详解" part B:
 // the tree is flattened breadth-first and every node may attend only to itself and
 // its ancestors.  One wavefront handles one tree: lane i owns node i, validity is a
-// wave vote, the ancestor sets come from pointer jumping over the parent links
-// (six doubling steps cover depth 63), and every node sets its bit in its parent's
-// child mask with one LDS atomic.
+// wave vote and the ancestor sets come from pointer jumping over the parent links
+// (tree_ancestors_wave, which the attention launch also uses when it is given the
+// parent links), and every node sets its bit in its parent's child mask with one
+// LDS atomic.
 #include "common.hpp"
 
 namespace spectree {
@@ -22,12 +23,11 @@ __global__ __launch_bounds__(256) void mask_build_kernel(const int32_t* __restri
   s_kids[wv][lane] = 0;
   const int64_t base = (int64_t)b * n_max;
   const int n = n_nodes[b];
-  const bool n_ok = n >= 1 && n <= n_max;
   const bool in_row = lane < n_max;
   const int p = in_row ? parent[base + lane] : -1;
-  const bool node = n_ok && lane < n;
-  const bool link_ok = !node || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
-  const bool ok = n_ok && __all(link_ok);
+  bool ok;
+  const uint64_t a = tree_ancestors_wave(p, n, n_max, &ok);
+  const bool node = lane < n;
   if (!ok) {
     if (in_row) {
       anc_mask[base + lane] = 0;
@@ -36,19 +36,6 @@ __global__ __launch_bounds__(256) void mask_build_kernel(const int32_t* __restri
     }
     if (lane == 0) report(status, SPEC_ERR_BAD_TREE);
     return;
-  }
-  // a: ancestors at distance < 2^t (self included); jp: ancestor at distance 2^t.
-  uint64_t a = node ? (1ull << lane) : 0ull;
-  int jp = node ? p : -1;
-#pragma unroll
-  for (int t = 0; t < 6; ++t) {
-    const int src = jp < 0 ? lane : jp;
-    const uint64_t a_src = shfl_u64(a, src);
-    const int jp_src = __shfl(jp, src);
-    if (jp >= 0) {
-      a |= a_src;
-      jp = jp_src;
-    }
   }
   // the wavefront's own LDS row: in-order LDS operations of one wavefront need no barrier
   if (node && lane > 0) atomicOr(&s_kids[wv][p], 1ull << lane);

@@ -4,13 +4,18 @@
 once, outputs, workspaces, the status word) so that ``run()`` allocates nothing
 and only issues the library calls, in order, on one stream:
 
-    spec_tree_mask_build -> spec_tree_attention -> spec_tree_softmax_pair (the chunk
-    partials of the target and draft rows in one launch, no row merge;
-    spec_tree_softmax with row statistics on the target rows at T = 0)
-    -> spec_tree_reject_sample (which merges each row itself) -> spec_accept_path
+    spec_tree_attention (given the parent links, it builds the ancestor rows
+    itself) -> spec_tree_softmax_pair (the chunk partials of the target and draft
+    rows in one launch, no row merge; spec_tree_softmax with row statistics on the
+    target rows at T = 0) -> spec_tree_reject_sample (which merges each row itself
+    and writes the accepted path, the result of spec_accept_path)
+
+With ``fold_mask=False`` the step runs spec_tree_mask_build first and the attention
+reads its ancestor rows.  ``mask()`` and ``path()`` also run the standalone
+spec_tree_mask_build and spec_accept_path calls.
 
 The attention output is not an input of the sampling half (the target logits are
-given), so the step's dependence graph has two branches after its start: mask ->
+given), so the step's dependence graph has two branches after its start: the
 attention, and softmax -> rejection sampling (which checks the tree itself).  With
 ``overlap()`` the first branch runs on a second stream, forked from and joined back
 into the caller's stream by events, so the two branches' latencies overlap.
@@ -47,8 +52,9 @@ def to_device(inp: dict, device="cuda") -> dict:
 
 
 class VerifyStep:
-    def __init__(self, dev: dict, with_attention: bool = True):
+    def __init__(self, dev: dict, with_attention: bool = True, fold_mask: bool = True):
         self.d = dev
+        self.fold_mask = fold_mask  # the attention builds the ancestor rows from the parent links
         Bn, n_max, V = dev["B"], dev["n_max"], dev["V"]
         cuda = dev["parent"].device
         i32 = dict(dtype=torch.int32, device=cuda)
@@ -103,10 +109,11 @@ class VerifyStep:
     def attention(self, stream=None, q=None, k=None, v=None, out=None):
         d = self.d
         B.spec_tree_attention(d["q"] if q is None else q, d["k"] if k is None else k, d["v"] if v is None else v,
-                              d["ctx_len"], d["n_nodes"], self.anc, self.attn_out if out is None else out,
-                              self.attn_ws, hkv=d["hkv"], max_kv_len=d["max_kv_len"],
-                              block_table=d.get("block_table"), page_size=d.get("page_size", 0),
-                              n_pages=d.get("n_pages", 0), status=self.status, stream=stream)
+                              d["ctx_len"], d["n_nodes"], None if self.fold_mask else self.anc,
+                              self.attn_out if out is None else out, self.attn_ws, hkv=d["hkv"],
+                              max_kv_len=d["max_kv_len"], block_table=d.get("block_table"),
+                              page_size=d.get("page_size", 0), n_pages=d.get("n_pages", 0), status=self.status,
+                              stream=stream, parent=d["parent"] if self.fold_mask else None)
 
     def softmax(self, stream=None, tgt=None, dft=None, rows=False):
         """T > 0: the chunk partials of both logit arrays (one launch); with rows, the
@@ -159,7 +166,8 @@ class VerifyStep:
                 self.softmax(main, r.get("tgt_logits"), r.get("dft_logits"))
             self.ev_fork.record(main)  # the side branch starts after the caller's earlier work
             self.side.wait_event(self.ev_fork)
-            self.mask(self.side)
+            if not self.fold_mask:
+                self.mask(self.side)
             self.attention(self.side, r.get("q"), r.get("k"), r.get("v"))
             self.ev_join.record(self.side)
             if self.fork == "start":
@@ -167,8 +175,9 @@ class VerifyStep:
             self.reject(main, r.get("tgt_logits"), r.get("dft_logits"))
             main.wait_event(self.ev_join)  # the whole step is done when the caller's stream is
             return
-        self.mask(stream)
         if self.with_attention:
+            if not self.fold_mask:
+                self.mask(stream)
             self.attention(stream, r.get("q"), r.get("k"), r.get("v"))
         self.softmax(stream, r.get("tgt_logits"), r.get("dft_logits"))
         self.reject(stream, r.get("tgt_logits"), r.get("dft_logits"))  # and the accepted path
@@ -188,7 +197,8 @@ class VerifyStep:
         for r in replicas:
             if self.side is not None:
                 with B.record_calls() as side_calls:
-                    self.mask(self.side)
+                    if not self.fold_mask:
+                        self.mask(self.side)
                     self.attention(self.side, r.get("q"), r.get("k"), r.get("v"))
                 with B.record_calls() as main_calls:  # one softmax call, then the sampler
                     self.softmax(main, r.get("tgt_logits"), r.get("dft_logits"))
