@@ -57,7 +57,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 COPY_ELEMS = 1 << 27  # fp32: 512 MiB read and 512 MiB written per copy
 # HBM bytes per call measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by the
 # same counters on a plain copy); valid only while the sources listed there are unchanged
-COUNTERS_MD = os.path.join(ROOT, "profiles", "attention_softmax_llama8b_60node_ctx4096_hbm_counters.md")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "verify_step_llama8b_60node_ctx4096_hbm_counters.md")
 
 
 def measured_traffic():
