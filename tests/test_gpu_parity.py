@@ -320,6 +320,54 @@ def test_sampling_star_trials(qkind, k):
     assert scipy.stats.chisquare(counts[keep], exp[keep] * counts[keep].sum() / exp[keep].sum()).pvalue > 0.01
 
 
+def test_sampling_statistics_million_trees():
+    """10^6 two-level trees in one call (root with 2 i.i.d. children from q, each with
+    2 i.i.d. children from its own draft row; rows keyed by the path): the first
+    emitted token is distributed as p at the root and, given an accepted first token
+    t1, the second as the target row of t1 (chi-square on the GPU's own outputs); the
+    first 10^4 trees also bit for bit against the oracle."""
+    import scipy.stats
+    say("statistics: 10^6 two-level trees")
+    V, n_tr = 16, 1_000_000
+    rng = synth.rng_for(62)
+    p_root = rng.dirichlet(np.ones(V))
+    q_root = synth.q_variant("noisy", p_root, rng)
+    P2 = rng.dirichlet(np.ones(V), size=V)
+    Q2 = np.stack([synth.q_variant("noisy", P2[t], rng) for t in range(V)])
+    tr = synth.depth2_trials(rng, p_root, q_root, P2, Q2, 2, 2, n_tr)
+    n = tr["parent"].shape[1]
+    inp = dict(tr, B=n_tr, n_max=n, V=V, T=1.0, Td=1.0, ctx_len=np.zeros(n_tr, np.int32))
+    got = _sampling_gpu(inp)
+    assert got["status"][0] == 0
+    m = 10_000
+    sub = {k: (v[:m] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    sub["B"] = m
+    ref = _oracle_sampling(sub)
+    _compare_sampling({k: got[k][:m] for k in ("accept_len", "path_nodes", "out_tokens", "accepted_child",
+                                                "term_token")}, ref, sub, max_exempt=5)
+    first = got["out_tokens"][:, 0]
+    obs = np.bincount(first, minlength=V).astype(float)
+    exp = p_root * n_tr
+    keep = exp >= 5
+    assert scipy.stats.chisquare(obs[keep], exp[keep] * obs[keep].sum() / exp[keep].sum()).pvalue > 0.01
+    ok = got["accept_len"] >= 1
+    pairs = np.stack([got["out_tokens"][ok, 0], got["out_tokens"][ok, 1]], 1)
+    stat, dof = 0.0, 0
+    for t1 in range(V):
+        sel = pairs[pairs[:, 0] == t1, 1]
+        if sel.size < 50:
+            continue
+        o = np.bincount(sel, minlength=V).astype(float)
+        e = P2[t1] * sel.size
+        k = e >= 5
+        oo = list(o[k]) + ([o[~k].sum()] if (~k).any() else [])
+        ee = list(e[k]) + ([e[~k].sum()] if (~k).any() else [])
+        stat += sum((a - b) ** 2 / b for a, b in zip(oo, ee))
+        dof += len(oo) - 1
+    print("pairs", len(pairs), "chi2 dof", dof)
+    assert dof > 100 and scipy.stats.chi2.sf(stat, dof) > 0.01
+
+
 def test_sampling_chain_alpha():
     say("chain alpha")
     p, q = synth.alpha_pq(0.7)
