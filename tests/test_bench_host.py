@@ -47,3 +47,34 @@ def test_measured_traffic_matches_the_committed_sources():
     for call in ("spec_tree_attention", "spec_tree_softmax_pair"):
         assert call in t
         assert t[call] is None or t[call] > 10_000_000
+
+
+def test_measured_traffic_covers_the_sampling_branch():
+    t = bench.measured_traffic()
+    assert "sampling_branch" in t
+    if t["sampling_branch"] is not None and t["spec_tree_softmax_pair"] is not None:
+        assert t["sampling_branch"] > t["spec_tree_softmax_pair"]  # the sampler's own traffic comes on top
+
+
+def test_oracle_check_counts_identical_and_flagged_walks():
+    """bench.oracle_check on outputs that equal the oracle's (all identical) and on
+    outputs with one request altered (one fewer); the near-tie count is the oracle's."""
+    import oracle
+
+    inp = synth.make_config(1, seed=3, with_kv=False)
+    m = 6
+    rng = synth.rng_for(70)
+    first = {k: np.repeat(inp[k][:1], m, 0) for k in ("parent", "tokens", "n_nodes")}
+    first["u_accept"] = synth.uniforms(rng, (m, inp["n_max"]))
+    first["u_sample"] = synth.uniforms(rng, (m, inp["n_max"]))
+    tgt = np.broadcast_to(inp["tgt_logits"][:1], (m,) + inp["tgt_logits"].shape[1:])
+    dft = np.broadcast_to(inp["dft_logits"][:1], (m,) + inp["dft_logits"].shape[1:])
+    r = oracle.reject_sample(tgt, dft, inp["T"], inp["Td"], first["tokens"], first["parent"], first["n_nodes"],
+                             first["u_accept"], first["u_sample"])
+    r.update(oracle.accept_path(r["accepted_child"], r["term_token"], first["tokens"], first["n_nodes"]))
+    first["out"] = {k: r[k].copy() for k in ("path_nodes", "out_tokens", "accepted_child", "term_token")}
+    got = bench.oracle_check(inp, first, m=m)
+    flagged = sum(int(r["tie_flags"][b][r["path_nodes"][b][r["path_nodes"][b] >= 0]].any()) for b in range(m))
+    assert got == {"trials": m, "near_tie_requests": flagged, "identical_to_oracle": m}
+    first["out"]["term_token"][2, 0] += 1
+    assert bench.oracle_check(inp, first, m=m)["identical_to_oracle"] == m - 1
