@@ -396,6 +396,64 @@ def test_greedy_equals_target_only_decode_on_gpu():
         assert got["out_tokens"][t, :L + 1].tolist() == seq[1:]
 
 
+def test_sampling_largest_vocabulary():
+    """The largest vocabulary the sampler takes: 256 chunks of 4096 tokens
+    (1,048,576), a 12-node tree, several seeds: the row merge at four chunks per lane
+    and the chained passes over every chunk, against the oracle."""
+    V = 256 * 4096
+    ties = 0
+    for seed in range(3):
+        say("sampling largest vocabulary", seed)
+        rng = synth.rng_for(63, seed)
+        n = 12
+        parent = np.array([-1, 0, 0, 0, 1, 1, 2, 4, 4, 4, 7, 0], np.int32)[None]
+        tgt = (3.0 * rng.standard_normal((1, n, V))).astype(np.float32)
+        dft = (tgt + rng.standard_normal((1, n, V))).astype(np.float32)
+        tokens = np.zeros((1, n), np.int32)
+        for c in range(1, n):  # drafted tokens: the parent's draft argmax region, so tests are not trivial
+            tokens[0, c] = int(np.argsort(dft[0, parent[0, c]])[-1 - (c % 3)])
+        inp = dict(B=1, n_max=n, V=V, T=1.0, Td=1.0, parent=parent, tokens=tokens, n_nodes=np.array([n], np.int32),
+                   tgt_logits=tgt, dft_logits=dft, u_accept=synth.uniforms(rng, (1, n)),
+                   u_sample=synth.uniforms(rng, (1, n)), ctx_len=np.zeros(1, np.int32))
+        got = _sampling_gpu(inp)
+        assert got["status"][0] == 0
+        ties += _compare_sampling(got, _oracle_sampling(inp), inp, max_exempt=1)
+    assert ties <= 1
+
+
+def test_sampling_mixed_batch_with_bad_requests():
+    """A chunked batch (32768-token vocabulary) of 16 requests where four are
+    malformed in different ways (a root with a parent, a parent behind its child, a
+    drafted token outside the vocabulary, a NaN logit): those are refused with the
+    bad-request marker and a status, and every other request still equals the
+    oracle."""
+    say("sampling mixed batch")
+    inp = support.make_config(4, seed=31, with_kv=False, vocab_override=32768)
+    B_ = 16
+    more = support.make_config(4, seed=32, with_kv=False, vocab_override=32768)
+    for k in ("parent", "tokens", "n_nodes", "tgt_logits", "dft_logits", "u_accept", "u_sample", "ctx_len"):
+        inp[k] = np.concatenate([inp[k], more[k]])[:B_]
+    inp["B"] = B_
+    inp["parent"][2, 0] = 0
+    inp["parent"][5, 7] = 9
+    inp["tokens"][9, 3] = inp["V"]
+    inp["tgt_logits"][13, 0, 100] = np.nan  # the root's row: read whatever the walk does
+    got = _sampling_gpu(inp)
+    ref = _oracle_sampling(inp)
+    bad = [2, 5, 9, 13]
+    assert got["status"][0] != 0
+    for b in bad:
+        assert got["accept_len"][b] == -1 and ref["accept_len"][b] == -1, b
+        assert got["accepted_child"][b, 0] == B.NODE_BAD_REQUEST, b
+    good = [b for b in range(B_) if b not in bad]
+    sub = {k: (v[good] if isinstance(v, np.ndarray) and v.shape[:1] == (B_,) else v) for k, v in inp.items()}
+    sub["B"] = len(good)
+    gsub = {k: got[k][good] for k in ("accept_len", "path_nodes", "out_tokens", "accepted_child", "term_token")}
+    rsub = {k: ref[k][good] for k in ("accept_len", "path_nodes", "out_tokens", "accepted_child", "term_token",
+                                       "tie_flags")}
+    _compare_sampling(gsub, rsub, sub, max_exempt=max(1, len(good) // 4))
+
+
 def test_sampling_bad_requests():
     say("sampling bad requests")
     rng = synth.rng_for(57)
