@@ -109,7 +109,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serial", action="store_true",
-                    help="issue the whole step on one stream (default: mask + attention on a second stream)")
+                    help="issue the whole step on one stream (default: the attention on a second stream)")
     ap.add_argument("--fork", choices=("start", "after_softmax"), default="start",
                     help="where the second stream branches off: at the step's start or after the logit pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

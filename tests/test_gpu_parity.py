@@ -896,7 +896,7 @@ def test_full_step(cfg, T):
 
 @pytest.mark.parametrize("cfg,fork", [(2, "start"), (2, "after_softmax"), (4, "after_softmax")])
 def test_two_stream_step_equals_one_stream_step(cfg, fork):
-    """The step with mask + attention on a second stream gives, bit for bit, what the
+    """The step with the attention on a second stream gives, bit for bit, what the
     one-stream step gives, over consecutive steps that rotate input copies (each
     step's side branch must wait for the previous step, and the caller's stream for
     the side branch)."""

@@ -88,12 +88,13 @@ class VerifyStep:
         self.side = None
 
     def overlap(self, side_stream=None, fork="start"):
-        """Run mask + attention on ``side_stream`` (a new default-priority stream if
-        None), concurrently with the caller's stream.  fork "start": beside softmax
-        and sampling (the faster on MI355X: 75 vs 79.5 us per 60-node / 4k step);
-        "after_softmax": beside the sampling only (the logit pass then has the memory
-        system to itself, but the sampler's launches then share the CUs with the
-        attention workgroups).  Returns self."""
+        """Run the attention (after the mask build when it is not folded) on
+        ``side_stream`` (a new default-priority stream if None), concurrently with the
+        caller's stream.  fork "start": beside softmax and sampling (the faster on
+        MI355X: 66.8 vs 72.7 us per 60-node / 4k step); "after_softmax": beside the
+        sampling only (the logit pass then has the memory system to itself, but the
+        sampler's launches then share the CUs with the attention workgroups).
+        Returns self."""
         assert fork in ("start", "after_softmax")
         if self.with_attention:
             self.side = side_stream if side_stream is not None else torch.cuda.Stream(self.d["parent"].device)
