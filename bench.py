@@ -6,9 +6,10 @@ A step is the whole hot path over one input set:
     (target and draft rows at T > 0; spec_tree_softmax at T = 0),
     spec_tree_reject_sample (whose final walk also writes the accepted path, the
     result of spec_accept_path).
-The attention shares no data with the other two, so by default it runs on a second
-HIP stream, forked from and joined back into the timing stream by events
-(``--serial``: all on one stream).
+The three calls run in order on one stream.  The attention shares no data with the
+other two, so ``--overlap`` runs it on a second HIP stream, forked from and joined
+back into the timing stream by events; on MI355X that is slower (the attention
+kernel's registers leave no room on its CUs for the other kernels' workgroups).
 Workload (default): the Llama-3-8B-shaped step -- one request, a 60-node EAGLE-2
 tree (top-k 10, depth 6), 4096 cached tokens, 32 query / 8 KV heads, head_dim 128,
 bf16 KV, fp32 logits over a 128256-token vocabulary, T = 1.  Synthetic, seeded.
@@ -108,10 +109,12 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--serial", action="store_true",
-                    help="issue the whole step on one stream (default: the attention on a second stream)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="the attention on a second stream beside the logit pass and the sampler (default: the "
+                         "whole step on one stream)")
     ap.add_argument("--fork", choices=("start", "after_softmax"), default="start",
-                    help="where the second stream branches off: at the step's start or after the logit pass")
+                    help="with --overlap: where the second stream branches off, at the step's start or after "
+                         "the logit pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cost-table", metavar="PREFIX", default=None,
                     help="sweep (batch, context, nodes) and write PREFIX.json and PREFIX.md: the verify-latency "
@@ -673,7 +676,7 @@ def main():
     inp = synth.make_config(args.config, seed=args.seed, T=T, tree_builder=gpu_tree_builder)
     dev = to_device(inp)
     step = VerifyStep(dev)
-    if not args.serial:
+    if args.overlap:
         step.overlap(fork=args.fork)  # the attention on a second stream
     big = [k for k in ("q", "k", "v", "tgt_logits", "dft_logits") if k in dev]
     replicas = [{k: dev[k].clone() for k in big} for _ in range(args.replicas)]
@@ -720,7 +723,7 @@ def main():
             "workload": synth.CONFIGS[args.config], "batch": inp["B"], "n_nodes": int(inp["n_nodes"].max()),
             "ctx": int(inp["ctx_len"].max()), "hq": inp["hq"], "hkv": inp["hkv"], "head_dim": inp["d"],
             "vocab": inp["V"], "T": inp["T"], "replicas": args.replicas,
-            "launch": "one stream (no graph)" if args.serial or step.side is None else
+            "launch": "one stream (no graph)" if step.side is None else
                       ("two streams: the attention (ancestor rows built in its launch) beside softmax + sampling "
                        "(no graph)" if step.fork == "start"
                        else "two streams: the attention beside the sampling, after the logit pass (no graph)"),
@@ -747,18 +750,21 @@ def main():
             "softmax_pair": roofline_entry("spec_tree_softmax_pair call: softmax_stats_kernel (target and draft "
                                            "rows, chunk partials only)",
                                            samp_b, pair_us, traffic.get("spec_tree_softmax_pair")),
-            # the critical path of the two-stream step: the logit pass and the sampler,
-            # against the bytes of one pass over both logit arrays
+            # the sampling half of the step: the logit pass and the sampler, against the
+            # bytes of one pass over both logit arrays
             "sampling_branch": roofline_entry("spec_tree_softmax_pair + spec_tree_reject_sample calls: "
-                                              "softmax_stats_kernel, plan_kernel, chain_hist_kernel, "
-                                              "chain_exact_kernel, node_kernel",
+                                              "softmax_stats_kernel, sample_kernel",
                                               samp_b, branch_us, traffic.get("sampling_branch")),
         },
+        # the step's parts, each timed back to back on its own: one stream runs them in
+        # turn; with --overlap the attention runs beside the sampling half
         "critical_path": {
-            "branch": "softmax_pair + reject_sample (the attention branch runs beside it)",
-            "us": round(branch_us, 2), "share_of_step": round(branch_us / (ms_per_step * 1e3), 3),
+            "branch": ("attention, then softmax_pair + reject_sample" if step.side is None else
+                       "softmax_pair + reject_sample (the attention branch runs beside it)"),
+            "us": round(branch_us + (attn_us if step.side is None else 0.0), 2),
+            "share_of_step": round((branch_us + (attn_us if step.side is None else 0.0)) / (ms_per_step * 1e3), 3),
             "reject_sample_us": round(reject_us, 2), "softmax_pair_us": round(pair_us, 2),
-            "side_branch_us": round(float(st_mean[1] + (st_mean[0] if not step.fold_mask else 0.0)), 2),
+            "sampling_half_us": round(branch_us, 2),
             "attention_call_us": round(attn_us, 2),
         },
         # the same replayed steps driven by the host with nothing queued ahead: what a

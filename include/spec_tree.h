@@ -68,7 +68,8 @@ typedef enum {
   SPEC_ERR_BAD_TREE = -3,    /* device: parent[] does not describe a tree          */
   SPEC_ERR_BAD_INPUT = -4,   /* device: token or page id out of range, NaN/+inf    */
   SPEC_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
-  SPEC_ERR_HIP = -6          /* a HIP launch failed                                */
+  SPEC_ERR_HIP = -6,         /* a HIP launch failed                                */
+  SPEC_ERR_TIMEOUT = -7      /* device: a bounded cross-workgroup wait gave up     */
 } spec_status;
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
@@ -244,16 +245,21 @@ int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const flo
  * derive it from accepted_child and term_token, written by the same walk.
  * T > 0 needs the workspace of spec_tree_reject_sample_workspace_size, zero-filled
  * once; every call leaves it ready for the next.  Its first 16 bytes are uint32
- * diagnostics, cumulative over calls (the caller may zero them between calls):
- * word 0 counts the nodes of a multi-chunk vocabulary that were finished by
- * direct passes over their rows (their exact-sum path could not guarantee its
- * result: a list or queue overflow, a threshold beyond the ratio histogram, a
- * zero-mass step); words 1-3 are reserved (0).  Launches: a plan launch (one
- * workgroup per node: row statistics merged from the chunk partials, children,
- * first-child test), for vocabularies of two or more chunks a ratio-histogram
- * launch and an exact-sum launch over the nodes whose first child is rejected,
- * and a node launch (sibling tests and terminal draws; the last node of a request
- * walks).  No workgroup waits on another.
+ * counters, cumulative over calls (the caller may zero them between calls): word 0
+ * counts the exact W(c) levels summed (one per rejected sibling, over all nodes),
+ * word 1 the cross-workgroup waits that gave up; words 2-3 are reserved (0).
+ * One kernel at T > 0 (several launches only when the grid exceeds one dispatch):
+ * one planner workgroup per node slot (row statistics merged
+ * from the chunk partials, the tree's verdict, the node's children and the
+ * first-child test; a leaf's bonus; the report of a node that needs no chain) and
+ * one workgroup per 4096-token chunk of every node, which keeps its logits in
+ * registers as exact fixed-point masses.  After each rejected sibling the chunks of
+ * a node publish their exact sums for the new threshold and read each other's (a
+ * bounded wait; the chunks of one node run on one XCD when they fit there), so every
+ * chunk takes the same next step; the terminal draw scans one chunk; the request's
+ * last reported node walks from the root.  A wait that gives up marks its node
+ * failed: SPEC_ERR_TIMEOUT in status, the request reported as SPEC_NODE_BAD_REQUEST,
+ * the call still ends normally (spec_tree_reject_sample_set_wait_limit).
  * Host errors: T < 0 or NaN, T > 0 with T_d <= 0, null required pointers, only
  * some of the path outputs, sizes, workspace; SPEC_ERR_UNSUPPORTED for a
  * vocabulary above 256 chunks.
@@ -267,6 +273,16 @@ int spec_tree_reject_sample(const float* tgt_logits, float temperature, const fl
                             int32_t n_max, int32_t vocab, int32_t* accepted_child, int32_t* term_token,
                             int32_t* path_nodes, int32_t* out_tokens, int32_t* accept_len, void* workspace,
                             size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
+ * Bound on the polls of each cross-workgroup wait of spec_tree_reject_sample at
+ * T > 0 (process-wide; 0 restores the default of 2^22).  A wait that reaches it
+ * gives up: the node's result is marked failed, status gets SPEC_ERR_TIMEOUT, the
+ * request is reported as SPEC_NODE_BAD_REQUEST, and the call still ends normally
+ * with its workspace ready for the next call.  For tests of that path; the default
+ * is never reached while the workgroups of one node can run together.
+ */
+void spec_tree_reject_sample_set_wait_limit(uint32_t polls);
 
 /*
  * Accepted path plus bonus token (tree notes, parts C and G; gingerlabs page, "A

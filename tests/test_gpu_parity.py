@@ -480,54 +480,87 @@ def _star_case(rng, p_root, q_root, n_children, n_trials, child_tokens=None):
     return dict(tr, B=n_trials, n_max=n_children + 1, V=V, T=1.0, Td=1.0, ctx_len=np.zeros(n_trials, np.int32))
 
 
-def _sampling_gpu_diag(inp):
-    """_sampling_gpu plus the number of nodes the sampler finished with direct
-    vocabulary passes (its workspace counter, read before and after the call)."""
-    d = to_device(dict(inp, q=None))
-    st = VerifyStep(d, with_attention=False)
-    before = B.reject_sample_diagnostics(st.rj_ws)["direct_nodes"]
-    st.softmax()
-    st.reject()
-    torch.cuda.synchronize()
-    after = B.reject_sample_diagnostics(st.rj_ws)["direct_nodes"]
-    return st.results(), after - before
+def _sampling_gpu_diag(inp, wait_limit=0, step=None):
+    """_sampling_gpu plus the change of the sampler's workspace counters over the call
+    (exact W(c) levels summed, waits that gave up).  wait_limit > 0 bounds every
+    cross-workgroup wait of the call to that many polls (0: the default)."""
+    if step is None:
+        d = to_device(dict(inp, q=None))
+        step = VerifyStep(d, with_attention=False)
+    before = B.reject_sample_diagnostics(step.rj_ws)
+    step.softmax()
+    B.spec_tree_reject_sample_set_wait_limit(wait_limit)
+    try:
+        step.reject()
+        torch.cuda.synchronize()
+    finally:
+        B.spec_tree_reject_sample_set_wait_limit(0)
+    after = B.reject_sample_diagnostics(step.rj_ws)
+    return step.results(), {k: after[k] - before[k] for k in after}, step
 
 
-@pytest.mark.parametrize("k,fallback", [(20, True), (12, False)])
-def test_sampling_threshold_beyond_histogram(k, fallback):
-    """Disjoint supports (p on the first half of a 10007-token vocabulary, q on the
-    second): every drafted token has p = 0 and is rejected, and after j rejections
-    the threshold is c_j = j.  With 20 children c passes the ratio histogram's range
-    (16), so every root must finish with direct vocabulary passes (the workspace
-    counter shows it); with 12 it stays inside and no node does.  The bonus is drawn
-    from the untouched p."""
-    say("sampling threshold beyond histogram", k)
-    rng = synth.rng_for(58, k)
+def _disjoint_star(k, n_req, seed):
+    """p on the first half of a 10007-token vocabulary, q on the second: every drafted
+    token has p = 0 and is rejected, W(c) = 1 for every c >= 1 (all of p lies where
+    q = 0), so after j rejections the threshold is c_j = j and the bonus comes from p."""
+    rng = synth.rng_for(58, k, seed)
     V, h = 10007, 5003
     p = np.zeros(V)
     q = np.zeros(V)
     p[:h] = rng.dirichlet(np.full(h, 0.5))
     q[h:] = rng.dirichlet(np.full(V - h, 0.5))
-    inp = _star_case(rng, p, q, k, 256)
-    got, direct = _sampling_gpu_diag(inp)
+    return _star_case(rng, p, q, k, n_req), h
+
+
+@pytest.mark.parametrize("k", [12, 40])
+def test_sampling_deep_sibling_chain(k):
+    """Disjoint supports (_disjoint_star) with 12 and 40 children: every root rejects
+    all of them, so each root sums k exact levels across its three chunks (the level
+    words cycle through both parities many times; the counters show k levels per
+    root) and draws its bonus from the untouched p."""
+    say("sampling deep sibling chain", k)
+    inp, h = _disjoint_star(k, 256, 0)
+    got, diag, _ = _sampling_gpu_diag(inp)
     ref = _oracle_sampling(inp)
     assert got["status"][0] == 0
     _compare_sampling(got, ref, inp, max_exempt=8)
     assert (got["accepted_child"][:, 0] == B.NODE_NONE).all() and (got["accept_len"] == 0).all()
     assert (got["out_tokens"][:, 0] < h).all()
-    print("direct nodes", direct)
-    assert direct == (inp["B"] if fallback else 0)
+    print("diag", diag)
+    assert diag == {"levels": k * inp["B"], "timeouts": 0}
 
 
-def test_sampling_interval_list_overflow():
+def test_sampling_wait_limit_gives_up_cleanly():
+    """Every cross-workgroup wait cut to a single poll (forced from the host): the
+    chunks of a root mostly miss each other's words, so the call reports
+    SPEC_ERR_TIMEOUT, counts the waits that gave up, and every request is still
+    either a valid walk or marked bad -- no workgroup is left waiting.  The next call
+    on the same workspace, with the default bound, is exact again (every counter and
+    word was left ready)."""
+    say("sampling wait limit")
+    inp, h = _disjoint_star(12, 256, 1)
+    got, diag, step = _sampling_gpu_diag(inp, wait_limit=1)
+    print("diag", diag, "status", int(got["status"][0]))
+    assert diag["timeouts"] > 0 and int(got["status"][0]) == B.ERR_TIMEOUT
+    bad = got["accepted_child"][:, 0] == B.NODE_BAD_REQUEST
+    assert bad.any()
+    for b in np.nonzero(~bad)[0]:
+        _check_walk(got, inp, b)
+    step.status.zero_()
+    got2, diag2, _ = _sampling_gpu_diag(inp, step=step)
+    assert got2["status"][0] == 0 and diag2 == {"levels": 12 * inp["B"], "timeouts": 0}
+    _compare_sampling(got2, _oracle_sampling(inp), inp, max_exempt=8)
+
+
+def test_sampling_tokens_exactly_at_the_threshold():
     """6000 tokens whose ratio equals the threshold after two rejections exactly.
     Groups of tokens, all logits 0 where present: E (6000, in both rows), Z (6000,
     draft only), H (2000, target only), plus 3 tokens absent from both.  Then
     Z_t = 8000 and Z_d = 12000, E has rho = 1.5, and after two rejected Z children
-    c = 1 + W(1) = 1 + (0.75 - 0.5 + 0.25) = 1.5: all of E sits inside that level's
-    interval, more than a node's list holds, so the node must fall back to direct
-    passes.  A third rejection gives c = 1.75 and the bonus is uniform over H."""
-    say("sampling list overflow")
+    c = 1 + W(1) = 1 + (0.75 - 0.5 + 0.25) = 1.5: all of E sits on that level's
+    threshold and contributes nothing.  A third rejection gives c = 1.75 and the bonus
+    is uniform over H (three levels per request)."""
+    say("sampling tokens at the threshold")
     V, nB = 14003, 32
     rng = synth.rng_for(59)
     ps, qs, kids = [], [], []
@@ -547,15 +580,15 @@ def test_sampling_interval_list_overflow():
         inp["dft_logits"][b, 0] = synth.log_probs_f32(qs[b]) + np.float32(np.log(12000.0))
     assert set(np.unique(inp["tgt_logits"][:, 0])) <= {0.0, -np.inf}
     assert set(np.unique(inp["dft_logits"][:, 0])) <= {0.0, -np.inf}
-    got, direct = _sampling_gpu_diag(inp)
+    got, diag, _ = _sampling_gpu_diag(inp)
     ref = _oracle_sampling(inp)
     assert got["status"][0] == 0
     _compare_sampling(got, ref, inp, max_exempt=2)
     assert (got["accept_len"] == 0).all()
     for b in range(nB):
         assert ps[b][got["out_tokens"][b, 0]] > 0 and qs[b][got["out_tokens"][b, 0]] == 0  # a token of H
-    print("direct nodes", direct)
-    assert direct == nB
+    print("diag", diag)
+    assert diag == {"levels": 3 * nB, "timeouts": 0}
 
 
 def test_sampling_zero_mass_residual():
@@ -575,9 +608,11 @@ def test_sampling_zero_mass_residual():
         inp["tgt_logits"][b, 0, ts[b]] = 0.0
         inp["dft_logits"][b, 0] = -np.inf
         inp["dft_logits"][b, 0, [ts[b], ss[b]]] = 0.0
-    got, _ = _sampling_gpu_diag(inp)
+    got, diag, _ = _sampling_gpu_diag(inp)
     ref = _oracle_sampling(inp)
     assert got["status"][0] == 0
+    print("diag", diag)  # every root sums its levels until W(c) is zero, then stops
+    assert diag["timeouts"] == 0 and 50 * nB <= diag["levels"] <= 60 * nB
     for r in (got, ref):
         assert (r["accepted_child"][:, 0] == B.NODE_NONE).all() and (r["accept_len"] == 0).all()
         assert np.array_equal(r["out_tokens"][:, 0], ts)

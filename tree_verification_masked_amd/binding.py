@@ -23,9 +23,10 @@ SPEC_BF16 = 1
 NODE_NONE = -1
 NODE_NOT_EVALUATED = -2
 NODE_BAD_REQUEST = -3
+ERR_TIMEOUT = -7  # a bounded cross-workgroup wait of the sampler gave up
 ERRORS = {
     0: "SPEC_OK", -1: "SPEC_ERR_INVALID_ARG", -2: "SPEC_ERR_UNSUPPORTED", -3: "SPEC_ERR_BAD_TREE",
-    -4: "SPEC_ERR_BAD_INPUT", -5: "SPEC_ERR_WORKSPACE", -6: "SPEC_ERR_HIP",
+    -4: "SPEC_ERR_BAD_INPUT", -5: "SPEC_ERR_WORKSPACE", -6: "SPEC_ERR_HIP", -7: "SPEC_ERR_TIMEOUT",
 }
 
 _lib = None
@@ -51,6 +52,7 @@ _SIGNATURES = {
     "spec_tree_reject_sample_workspace_size": [_I32, _I32, _I32],
     "spec_tree_reject_sample": [_VP, _F32, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32,
                                 _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
+    "spec_tree_reject_sample_set_wait_limit": [ctypes.c_uint32],
     "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
     "spec_tree_kv_commit": [_VP, _VP, _I32, _I32, _I64, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
                             _I32, _VP, _VP, _VP, _VP],
@@ -69,6 +71,7 @@ _RESTYPES = {
     "spec_tree_reject_sample_workspace_size": _SZ,
     "spec_tree_expand_workspace_size": _SZ,
     "spec_tree_version": ctypes.c_char_p,
+    "spec_tree_reject_sample_set_wait_limit": None,
 }
 
 
@@ -354,9 +357,14 @@ def spec_tree_reject_sample(tgt_logits, temperature, tokens, parent, n_nodes, ac
 
 
 def reject_sample_diagnostics(workspace) -> dict:
-    """The sampler workspace's cumulative diagnostics word (synchronises): nodes of a
-    multi-chunk vocabulary finished by direct vocabulary passes."""
-    return {"direct_nodes": int(workspace[:4].view(torch.int32).item())}
+    """The sampler workspace's cumulative counters (synchronises): exact W(c) levels
+    summed over all nodes, and cross-workgroup waits that gave up."""
+    w = workspace[:16].view(torch.int32).tolist()
+    return {"levels": int(w[0]), "timeouts": int(w[1])}
+
+
+def spec_tree_reject_sample_set_wait_limit(polls: int) -> None:
+    lib().spec_tree_reject_sample_set_wait_limit(int(polls))
 
 
 def spec_accept_path(accepted_child, term_token, tokens, n_nodes, path_nodes, out_tokens, accept_len, status=None,

@@ -253,7 +253,7 @@ inline int launch_stats(const SmSet& A, const SmSet& B, int32_t vocab, int32_t* 
                         bool merge = true) {
   const int nch = sm_chunks(vocab);
   const int64_t blocks = (A.rows + B.rows) * nch;
-  if (blocks > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+  if (blocks * kSmThreads > 0xffffffffLL) return SPEC_ERR_UNSUPPORTED;  // a dispatch counts work-items in 32 bits
   bool vec = vocab % 4 == 0 && (((uintptr_t)A.logits & 15) == 0);
   if (B.rows) vec = vec && (((uintptr_t)B.logits & 15) == 0);
   if (vec)

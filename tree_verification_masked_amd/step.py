@@ -90,10 +90,11 @@ class VerifyStep:
     def overlap(self, side_stream=None, fork="start"):
         """Run the attention (after the mask build when it is not folded) on
         ``side_stream`` (a new default-priority stream if None), concurrently with the
-        caller's stream.  fork "start": beside softmax and sampling (the faster on
-        MI355X: 66.8 vs 72.7 us per 60-node / 4k step); "after_softmax": beside the
-        sampling only (the logit pass then has the memory system to itself, but the
-        sampler's launches then share the CUs with the attention workgroups).
+        caller's stream.  fork "start": beside softmax and sampling; "after_softmax":
+        beside the sampling only.  On MI355X either is slower than one stream (60-node
+        / 4k step: 64.4 and 69.8 vs 60.6 us per step with the same kernels): the
+        attention kernel's registers leave no room on its CUs for the others'
+        workgroups, so the kernels mostly wait for each other.
         Returns self."""
         assert fork in ("start", "after_softmax")
         if self.with_attention:
