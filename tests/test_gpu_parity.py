@@ -821,6 +821,12 @@ def _custom_attention_case(rng, B_, n_max, hq, hkv, d, ctxs, n_nodes, bf16, page
     # one KV head, long context: more key splits than a wavefront has lanes
     ("many splits fp32 shuffle", 1, 4, 1, 1, 64, [12800], [4], False, False),
     ("many splits bf16 mfma", 1, 4, 4, 1, 128, [12000], [3], True, False),
+    # 40 (or 36) requests x 8 KV heads x one 128-row block: the plan has one key split,
+    # whose workgroups write the output rows themselves (no partials, no combine)
+    ("one split, large batch bf16 mfma", 40, 16, 32, 8, 128, [(37 * i) % 301 for i in range(40)],
+     [1 + (7 * i) % 16 for i in range(40)], True, False),
+    ("one split, paged bf16 mfma", 36, 8, 32, 8, 128, [(53 * i) % 257 for i in range(36)],
+     [1 + (5 * i) % 8 for i in range(36)], True, 16),
 ])
 def test_attention_edge_cases(name, B_, n_max, hq, hkv, d, ctxs, nn, bf16, paged):
     say("attention edge", name)
@@ -830,7 +836,8 @@ def test_attention_edge_cases(name, B_, n_max, hq, hkv, d, ctxs, nn, bf16, paged
     _check_attention(inp, got, anc)
 
 
-@pytest.mark.parametrize("case", ["cfg1 fp32 shuffle", "cfg2 mfma", "cfg4 paged mfma", "small G bf16 shuffle"])
+@pytest.mark.parametrize("case", ["cfg1 fp32 shuffle", "cfg2 mfma", "cfg4 paged mfma", "small G bf16 shuffle",
+                                  "one split mfma"])
 def test_attention_parent_links_equal_ancestor_rows(case):
     """The attention launch given the parent links builds the ancestor rows itself:
     its output must equal, bit for bit, the launch that reads the rows of
@@ -839,6 +846,9 @@ def test_attention_parent_links_equal_ancestor_rows(case):
     if case.startswith("cfg"):
         inp = support.make_config(int(case[3]), seed=2, ctx_override=600 if case[3] != "1" else None,
                                   vocab_override=64)
+    elif case == "one split mfma":  # 40 requests: one key split, outputs written directly
+        inp = _custom_attention_case(np.random.default_rng(9), 40, 12, 32, 8, 128, [(29 * i) % 200 for i in range(40)],
+                                     [1 + (5 * i) % 12 for i in range(40)], True)
     else:
         inp = _custom_attention_case(np.random.default_rng(7), 3, 7, 4, 2, 128, [5, 64, 130], [7, 3, 1], True)
     a_fold, st_fold, _ = _attention_gpu(inp, fold=True)
@@ -870,11 +880,16 @@ def test_attention_parent_links_bad_tree(mfma):
     assert np.abs(got - ref).max() < 2e-2
 
 
-def test_attention_rejects_out_of_range_lengths():
-    say("attention bad lengths")
-    inp = _custom_attention_case(np.random.default_rng(1), 2, 8, 8, 2, 128, [100, 50], [8, 8], True)
+@pytest.mark.parametrize("B_,hq,hkv", [(2, 8, 2), (40, 32, 8)])
+def test_attention_rejects_out_of_range_lengths(B_, hq, hkv):
+    """A request longer than max_kv_len: SPEC_ERR_BAD_INPUT and zero rows, the others
+    served.  40 requests x 8 KV heads: the one-split plan, whose workgroups write the
+    output rows (and report the error) themselves."""
+    say("attention bad lengths", B_)
+    ctxs = [100] + [40 + (13 * i) % 40 for i in range(1, B_)]
+    inp = _custom_attention_case(np.random.default_rng(1), B_, 8, hq, hkv, 128, ctxs, [8] * B_, True)
     d = to_device(inp)
-    d["max_kv_len"] = 90  # request 0 needs 108 positions
+    d["max_kv_len"] = 90  # request 0 needs 108 positions, the others at most 87
     st = VerifyStep(d)
     st.mask()
     st.attention()
@@ -882,9 +897,11 @@ def test_attention_rejects_out_of_range_lengths():
     assert r["status"][0] == -4
     assert (r["attn"][0] == 0).all()
     anc = r["anc"]
-    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], inp["n_nodes"], anc, 8, 2,
-                                rows=np.array([(1, i, h) for i in range(8) for h in range(8)], np.int32), bf16=True)
-    assert np.abs(r["attn"][1].reshape(-1, 128) - ref).max() < 2e-2
+    for b in (1, B_ - 1):
+        ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], inp["n_nodes"], anc, hq, hkv,
+                                    rows=np.array([(b, i, h) for i in range(8) for h in range(hq)], np.int32),
+                                    bf16=True)
+        assert np.abs(r["attn"][b].reshape(-1, 128) - ref).max() < 2e-2
 
 
 # ---------------------------------------------------------------- the whole step

@@ -61,17 +61,28 @@ struct AttnArgs {
   void* opart;     // [S, B, n_max, hq, D]  split output divided by its sum (0 if the sum is 0),
                    // in the element type of Q/K/V (bf16 or fp32)
   int32_t* status;
+  // MFMA path with one split: the split writes the output rows directly (no partials,
+  // no combine launch)
+  int32_t direct;
+  void* out;       // [B, n_max, hq, D] (direct)
 };
 
-// Length of request b's logical KV, or -1 when the request cannot be served.
-__device__ inline int request_len(const AttnArgs& a, int b) {
-  const int n = a.n_nodes[b], ctx = a.ctx_len[b];
+// A workgroup-uniform read of memory the launch never writes, through the constant
+// address space: a scalar load, which no wait for the vector loads in flight covers.
+template <typename T>
+__device__ inline T uniform_read(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+// Length of the logical KV of a request with n nodes after ctx prompt keys, or -1
+// when the request cannot be served.
+__device__ inline int request_len_of(const AttnArgs& a, int n, int ctx) {
   if (n < 1 || n > a.n_max || ctx < 0) return -1;
   const int64_t len = (int64_t)ctx + n;
   const int64_t cap = a.block_table ? (int64_t)a.kv_capacity * a.page_size : (int64_t)a.kv_capacity;
   if (len > a.max_kv_len || len > cap) return -1;
   return (int)len;
 }
+__device__ inline int request_len(const AttnArgs& a, int b) { return request_len_of(a, a.n_nodes[b], a.ctx_len[b]); }
 
 // Element offset of key t (< len) of request b, KV head g; -1 for a bad page id.
 __device__ inline int64_t kv_off(const AttnArgs& a, int b, int t, int g) {
@@ -99,7 +110,7 @@ __device__ inline bool key_visible(int t, int len, int ctx, uint64_t anc_row) {
 // the 8-byte rows addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12; addressing
 // key kb + r/4, dims d0 + 4 (r % 4) from lane r hands every lane four consecutive
 // keys of one dimension, which is the V^T operand of O^T = V^T P^T.
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 // LDS slot of 16-byte chunk c of key k is c ^ kv_swz(k): a bijection of the low key
 // bits, so 16 consecutive keys (K operand reads) hit 16 different slots, and the
 // 4 consecutive keys x 2 chunks of one transpose-read group hit 8 different slots.
@@ -159,6 +170,17 @@ __device__ inline void ds_read_b128_x8(v4i (&r)[8], const uint32_t (&ad)[8]) {
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
       : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
 }
+// One 4-byte and one 8-byte read and their wait.
+__device__ inline int ds_read_i32(uint32_t ad) {
+  int r;
+  asm volatile("ds_read_b32 %0, %1\ns_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(ad));
+  return r;
+}
+__device__ inline uint64_t ds_read_u64(uint32_t ad) {
+  uint64_t r;
+  asm volatile("ds_read_b64 %0, %1\ns_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(ad));
+  return r;
+}
 // Eight transpose reads at ad[j] + OFF and their wait.
 template <int OFF>
 __device__ inline void ds_read_tr16_x8(v4s (&r)[8], const uint32_t (&ad)[8]) {
@@ -189,8 +211,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   static_assert(LOADS >= 1 && LOADS * 8 * 1024 == TILE_B, "tile split over the eight waves");
   __shared__ __attribute__((aligned(1024))) char sKV[kStages][2][TILE_B];
   __shared__ int s_page[kMaxSplitPages];
-  __shared__ uint64_t s_anc[64];
-  __shared__ int s_tree_ok;
+  __shared__ int s_plink[64];        // the request's parent links (parent-link mode)
+  __shared__ __attribute__((aligned(16))) uint32_t s_ancin[128];  // the request's ancestor rows as 32-bit halves (row mode)
 
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wid & 3, kh = wid >> 2;  // row block, key half
@@ -211,6 +233,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int G = a.n_max * hpg;
 
   const int k_begin = s * a.split_len;
+  // the request's sizes first (scalar reads): later waits for them leave the tile
+  // loads in flight
+  const int n = uniform_read(a.n_nodes + b);
+  const int ctx = uniform_read(a.ctx_len + b);
   const __bf16* kbase = (const __bf16*)a.k;
   const __bf16* vbase = (const __bf16*)a.v;
   // tile it -> stage it % kStages; wave w issues LOADS 1 KB loads of K and of V.
@@ -231,34 +257,59 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     }
   };
   auto flat_off = [&](int t) -> int64_t { return (((int64_t)b * a.kv_capacity + t) * a.hkv + g) * D; };
-  // contiguous KV: the first tiles go out before the request's lengths are known
-  int n_spec = 0;
-  if (!a.block_table) {
-    const int cap_end = min(k_begin + a.split_len, a.kv_capacity);
-    const int cap_tiles = cap_end > k_begin ? (cap_end - k_begin + kTile - 1) / kTile : 0;
-    n_spec = min(cap_tiles, kStages - 1);
-    for (int it = 0; it < n_spec; ++it) issue_tile(it, cap_end, flat_off);
-  }
-  // Q and the ancestor row go out before the request's lengths are known: the row's
+  // Q and the ancestor row go out first, before the request's lengths are known: the row's
   // node index is clamped into [0, n_max) so the addresses are valid for every row,
   // and rows that turn out dead drop what they loaded
   const int r = qb * kMfmaRowsPerWg + wr * 32 + (lane & 31);
   const int node = r / hpg;
   const int node_c = min(node, a.n_max - 1);
   const int h = g * hpg + r % hpg;
-  uint64_t anc_raw = a.anc ? a.anc[(int64_t)b * a.n_max + node_c] : 0ull;
-  // with parent links, wave 0 holds node `lane`'s link (built into ancestor rows below)
-  const int plink = (a.parent && wid == 0 && lane < a.n_max) ? a.parent[(int64_t)b * a.n_max + lane] : -1;
-  // Q fragments: lane holds row r, dims kk*16 + 8*(lane/32) .. +8
-  bf16x8 qf[D / 16];
+  // Q, the parent links and the ancestor rows reach LDS by DMA like the K/V tiles
+  // (no register loads before the loop, so no wait for a register covers the tiles
+  // in flight).  Q rows of the block (row j: node j / hpg, head g hpg + j % hpg) go
+  // to stage kStages - 1 in the K tiles' swizzled layout; the first tile that uses
+  // that stage is issued after every wave has read its Q fragments.
   {
-    const __bf16* qrow = (const __bf16*)a.q + (((int64_t)b * a.n_max + node_c) * a.hq + h) * D;
+    constexpr int QLOADS = kMfmaRowsPerWg * ROWB / 1024 / 8;  // 1 KB loads per wave
+    static_assert(QLOADS * 8 * 1024 == 2 * TILE_B, "Q fills one stage (K and V parts)");
+    char* dq = sKV[kStages - 1][0];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + 8 * (lane >> 5));
+    for (int i = 0; i < QLOADS; ++i) {
+      const int kbi = wid * QLOADS + i;
+      const int row = kbi * KPB + lane / CH, slot = lane % CH;
+      const int rg = qb * kMfmaRowsPerWg + row;
+      const int nq = min(rg / hpg, a.n_max - 1);
+      const __bf16* src = (const __bf16*)a.q + (((int64_t)b * a.n_max + nq) * a.hq + g * hpg + rg % hpg) * D +
+                          (slot ^ kv_swz<CH>(row)) * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dq + kbi * 1024), 16, 0, 0);
+    }
+    if (wid == 0) {
+      const int64_t base = (int64_t)b * a.n_max;
+      if (a.parent) {
+        __builtin_amdgcn_global_load_lds((const void*)(a.parent + base + min(lane, a.n_max - 1)),
+                                         (__attribute__((address_space(3))) void*)s_plink, 4, 0, 0);
+      } else {
+        const uint32_t* w32 = (const uint32_t*)(a.anc + base);
+        __builtin_amdgcn_global_load_lds((const void*)(w32 + min(lane, 2 * a.n_max - 1)),
+                                         (__attribute__((address_space(3))) void*)s_ancin, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(w32 + min(lane + 64, 2 * a.n_max - 1)),
+                                         (__attribute__((address_space(3))) void*)(s_ancin + 64), 4, 0, 0);
+      }
+    }
   }
-  const int len = request_len(a, b);
-  const int n = a.n_nodes[b];
-  const int ctx = a.ctx_len[b];
+  bf16x8 qf[D / 16];  // Q fragments: lane holds row r, dims kk*16 + 8*(lane/32) .. +8
+  // Exactly kStages - 1 tiles go out before the loop, in straight-line code, so that
+  // the waits for the loads above count the tile loads issued after them and leave
+  // those in flight.  Contiguous KV: they go out now, before the request's lengths
+  // are known, keys clamped to the capacity (tiles past the split's end load valid
+  // memory that is never used).
+  constexpr int kAhead = kStages - 1;
+  if (!a.block_table) {
+    const int cap_end = min(k_begin + a.split_len, a.kv_capacity);  // >= 1: kv_capacity >= 1
+#pragma unroll
+    for (int it = 0; it < kAhead; ++it) issue_tile(it, cap_end, flat_off);
+  }
+  const int len = request_len_of(a, n, ctx);
   bool row_live = len >= 0 && r < G && node < n;
   const int k_end = min(k_begin + a.split_len, len < 0 ? 0 : len);
   const int n_tiles = k_end > k_begin ? (k_end - k_begin + kTile - 1) / kTile : 0;
@@ -280,7 +331,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int page0 = a.block_table ? k_begin / a.page_size : 0;
   auto key_off = [&](int t) -> int64_t {  // element offset of key t (< k_end) of head g
     if (!a.block_table) return (((int64_t)b * a.kv_capacity + t) * a.hkv + g) * D;
-    const int pg = s_page[t / a.page_size - page0];
+    // an empty split reads key 0 of page 0 (valid memory, never used)
+    const int pg = n_tiles > 0 ? s_page[max(t / a.page_size - page0, 0)] : 0;
     return (((int64_t)pg * a.page_size + t % a.page_size) * a.hkv + g) * D;
   };
   // Contiguous KV, a tile wholly below k_end: a uniform tile base plus per-lane 32-bit
@@ -311,26 +363,21 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       issue_tile(it, k_end, flat_off);
     }
   };
-  if (a.block_table)
-    for (int it = 0; it < kStages - 1 && it < n_tiles; ++it) issue(it);
-  // anc_row and Q are in registers before the loop (with the first tiles, which the
-  // first iteration needs anyway), so no wait inside the loop is for them
-  vm_wait<0>();
-  if (a.parent) {  // ancestor rows of this request from its parent links, shared through LDS
-    if (wid == 0) {
-      bool ok;
-      s_anc[lane] = tree_ancestors_wave(plink, n, a.n_max, &ok);
-      if (lane == 0) s_tree_ok = ok;
-      if (lane == 0 && !ok && len >= 0 && g == 0 && qb == 0 && s == 0) report(a.status, SPEC_ERR_BAD_TREE);
-    }
-    lds_barrier();
-    anc_raw = s_anc[node_c];
-    row_live = row_live && s_tree_ok;  // a request that is not a tree gets zero rows
-  }
-  const uint64_t anc_row = row_live ? anc_raw : 0ull;
-  if (!row_live)
+  if (a.block_table) {  // paged KV: the first tiles go out once the page ids are known
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = bf16x8{};
+    for (int it = 0; it < kAhead; ++it) issue_tile(it, max(k_end, 1), key_off);
+  }
+  int n_issued = kAhead;  // tiles whose loads are out (perhaps past n_tiles)
+  // wait until this wave's loads of tile j have landed, leaving the tiles issued
+  // after it (two at most) in flight; Q, the ancestor row and the parent link were
+  // issued before every tile, so they have landed too
+  auto wait_tile = [&](int j) {
+    const int after = n_issued - 1 - j;
+    if (after >= 2) vm_wait<4 * LOADS>();
+    else if (after == 1) vm_wait<2 * LOADS>();
+    else vm_wait<0>();
+  };
+  uint64_t anc_row = 0;  // set once tile 0 and the ancestor rows are in
   f32x16 acc_o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc_o[db] = f32x16{};
@@ -356,61 +403,83 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       const int d = db * 32 + 16 * (g4 & 1) + 4 * (rr & 3);
       voff[db][hl] = key * ROWB + (((d >> 3) ^ kv_swz<CH>(key)) * 16) + ((d >> 2) & 1) * 8;
     }
-  // One 64-key tile.  kMasked: some key of the tile is a tree key or lies past the
-  // request's end, so scores go through the visibility test; the other tiles (all
-  // prompt keys, the bulk of the work) skip it.
-  auto tile = [&](int it, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    // this wave's loads of tile `it` are done once at most (tiles issued after it) x
-    // 2 LOADS operations remain in flight
-    const int ahead = min(n_tiles - 1 - it, kStages - 2);
-    if (ahead >= 1 && it > 0) vm_wait<2 * LOADS>();
-    else vm_wait<0>();  // (the first tile also waits for the Q loads issued after it)
-    lds_barrier();  // every wave's part of tile `it` is in LDS; tile it-1 is consumed
-    if (it + kStages - 1 < n_tiles) issue(it + kStages - 1);
-    const char* sk = sKV[it % kStages][0];
-    const char* sv = sKV[it % kStages][1];
-    const int t0 = k_begin + it * kTile;
-
-    // ---- S^T = K Q^T for this wave's 32 keys: the D/16 operand reads first, then
-    // the MFMAs ----
-    const uint32_t kbase_lds = lds_addr(sk) + kh * 32 * ROWB, vbase_lds = lds_addr(sv) + kh * 32 * ROWB;
-    f32x16 acc_s = f32x16{};
-    static_assert(D == 64 || D == 128, "head_dim");
-    v4i kr[D / 16];
-    {
-      uint32_t ad[D / 16];
+  // The tile loop is software-pipelined: step `it` scores tile it + 1 (the MFMAs of
+  // S^T = K Q^T) while it exponentiates tile it (VALU), then accumulates tile it into
+  // O^T = V^T P^T (MFMAs) while it applies tile it + 1's visibility test and running
+  // max (VALU), so every wave has independent matrix and vector work in flight.  A
+  // step reads K of tile it + 1 and V of tile it from LDS; with kStages = 4 two more
+  // tiles are in flight meanwhile.
+  constexpr int NB = (D / 32 + 3) / 4;  // batches of eight V^T reads per k-step (1 for D <= 128)
+  constexpr int NDB = D / 32;
+  // K operand (this wave's 32 keys of tile j)
+  auto read_k = [&](int j, v4i (&kr)[D / 16]) {
+    const uint32_t kb = lds_addr(sKV[j % kStages][0]) + kh * 32 * ROWB;
+    uint32_t ad[D / 16];
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) ad[j] = kbase_lds + koff[j];
-      if constexpr (D == 128) ds_read_b128_x8(kr, ad);
-      else ds_read_b128_x4(kr, ad);
+    for (int q = 0; q < D / 16; ++q) ad[q] = kb + koff[q];
+    if constexpr (D == 128) ds_read_b128_x8(kr, ad);
+    else ds_read_b128_x4(kr, ad);
+  };
+  // V^T operands of tile j for both k-steps; k-step ks covers keys 16 ks .. 16 ks + 15
+  // of the half in the order sigma(k) = 8 ((k >> 2) & 1) + 4 (k >> 3) + (k & 3) that
+  // the S^T accumulator gives.  D/32 blocks x (lo, hi) reads in batches of 8 (one
+  // batch covers 4 d-blocks)
+  auto read_v = [&](int j, v4s (&va)[2][NB][8]) {
+    const uint32_t vb = lds_addr(sKV[j % kStages][1]) + kh * 32 * ROWB;
+    uint32_t vad[NB][8];
+#pragma unroll
+    for (int bq = 0; bq < NB; ++bq)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int db = (4 * bq + q) % NDB;
+        vad[bq][2 * q] = vb + voff[db][0];
+        vad[bq][2 * q + 1] = vb + voff[db][1];
+      }
+#pragma unroll
+    for (int bq = 0; bq < NB; ++bq) {
+      ds_read_tr16_x8<0>(va[0][bq], vad[bq]);
+      ds_read_tr16_x8<16 * ROWB>(va[1][bq], vad[bq]);
     }
+  };
+  static_assert(D == 64 || D == 128, "head_dim");
+  auto qk = [&](const v4i (&kr)[D / 16]) {
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       bf16x8 kf;
       __builtin_memcpy(&kf, &kr[kk], sizeof(kf));
-      acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
     }
-    // ---- mask, online softmax (lane owns row lane%32; lane^32 holds the other keys
-    // of the half); raw scores, the scale is applied inside the exponent ----
+    return acc;
+  };
+  // Tile j's visibility test and the running max (lane owns row lane % 32; lane ^ 32
+  // holds the other keys of the half).  kMasked: some key of the tile is a tree key
+  // or lies past the request's end; the other tiles (all prompt keys, the bulk of
+  // the work) skip the test.  Raw scores: the scale is applied inside the exponent.
+  auto prep = [&](f32x16& sc, int j, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     float tmax = -INFINITY;
     if constexpr (!kMasked) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, acc_s[e]);
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sc[e]);
     } else {
+      const int t0 = k_begin + j * kTile;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int t = t0 + kh * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int j = t - ctx;  // tree slot
-        const bool vis = t < k_end && (j < 0 || ((anc_row >> (j & 63)) & 1ull));
-        const float sc = vis ? acc_s[e] : -INFINITY;
-        acc_s[e] = sc;
-        tmax = fmaxf(tmax, sc);
+        const int jt = t - ctx;  // tree slot
+        const bool vis = t < k_end && (jt < 0 || ((anc_row >> (jt & 63)) & 1ull));
+        const float v = vis ? sc[e] : -INFINITY;
+        sc[e] = v;
+        tmax = fmaxf(tmax, v);
       }
     }
     tmax = fmaxf(tmax, xor32_f(tmax)) * sl2;
     if (!row_live) tmax = -INFINITY;
     if (__any(tmax > m_run + 8.0f)) {  // raise the reference max (rare after the first tile)
+      // (a side effect keeps this a branch: executed on every tile, the rescale
+      // below would cost more than the rest of the tile's vector work)
+      asm volatile("");
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = (m_new == -INFINITY || m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -418,59 +487,99 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       for (int db = 0; db < D / 32; ++db) acc_o[db] *= alpha;
       m_run = m_new;
     }
+  };
+  // P of a prepared tile (bf16, the two k-steps) and its row sum
+  auto expo = [&](const f32x16& sc, bf16x8 (&pf)[2]) {
     const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;
     float psum = 0.0f;
-    bf16x8 pf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[e], sl2, neg_m));
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[e], sl2, neg_m));
       psum += p;
       pf[e >> 3][e & 7] = (__bf16)p;
     }
     psum += xor32_f(psum);
     l_run += m_run == -INFINITY ? 0.0f : psum;
-    // ---- O^T += V^T P^T over the half's two k-steps; k-step ks covers keys
-    // 16 ks .. 16 ks + 15 of the half in the order sigma(k) = 8 ((k >> 2) & 1) +
-    // 4 (k >> 3) + (k & 3) that the S^T accumulator gives ----
-    // operands of a k-step for every d-block: D/32 blocks x (lo, hi) reads, in
-    // batches of 8 (one batch covers 4 d-blocks)
-    constexpr int NB = (D / 32 + 3) / 4;  // batches per k-step (1 for D <= 128)
-    constexpr int NDB = D / 32;
-    uint32_t vad[NB][8];
+  };
+  auto pv = [&](const v4s (&va)[2][NB][8], const bf16x8 (&pf)[2]) {
 #pragma unroll
-    for (int bq = 0; bq < NB; ++bq)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int db = (4 * bq + q) % NDB;
-        vad[bq][2 * q] = vbase_lds + voff[db][0];
-        vad[bq][2 * q + 1] = vbase_lds + voff[db][1];
-      }
-    v4s va[2][NB][8];
-    auto read_v = [&](auto ks_tag, v4s (&dst)[NB][8]) {
-      constexpr int KS = decltype(ks_tag)::value;
-#pragma unroll
-      for (int bq = 0; bq < NB; ++bq) ds_read_tr16_x8<16 * KS * ROWB>(dst[bq], vad[bq]);
-    };
-    auto pv_step = [&](auto ks_tag) {
-      constexpr int KS = decltype(ks_tag)::value;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const v4s lohi[2] = {va[KS][db / 4][2 * (db % 4)], va[KS][db / 4][2 * (db % 4) + 1]};
+        const v4s lohi[2] = {va[ks][db / 4][2 * (db % 4)], va[ks][db / 4][2 * (db % 4) + 1]};
         bf16x8 vf;
         __builtin_memcpy(&vf, lohi, sizeof(vf));
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[KS], acc_o[db], 0, 0, 0);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc_o[db], 0, 0, 0);
       }
-    };
-    read_v(std::integral_constant<int, 0>{}, va[0]);
-    read_v(std::integral_constant<int, 1>{}, va[1]);
-    pv_step(std::integral_constant<int, 0>{});
-    pv_step(std::integral_constant<int, 1>{});
   };
   // tiles below min(ctx, k_end) hold prompt keys only
   const int n_plain = min(n_tiles, max(0, (min(ctx, k_end) - k_begin) / kTile));
+  wait_tile(0);
+  lds_barrier();  // every wave's part of tile 0 is in LDS, and Q, the links or rows
+  {
+    const uint32_t qb_lds = lds_addr(sKV[kStages - 1][0]) + wr * 32 * ROWB;
+    v4i qr[D / 16];
+    uint32_t ad[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) ad[kk] = qb_lds + koff[kk];
+    if constexpr (D == 128) ds_read_b128_x8(qr, ad);
+    else ds_read_b128_x4(qr, ad);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) __builtin_memcpy(&qf[kk], &qr[kk], sizeof(qf[kk]));
+  }
+  uint64_t anc_raw;
+  if (a.parent) {  // ancestor rows from the parent links, built by every wave
+    const int plink = lane < a.n_max ? ds_read_i32(lds_addr((const char*)s_plink) + 4 * lane) : -1;
+    bool ok;
+    const uint64_t anc_l = tree_ancestors_wave(plink, n, a.n_max, &ok);
+    anc_raw = shfl_u64(anc_l, node_c);
+    row_live = row_live && ok;  // a request that is not a tree gets zero rows
+    if (tid == 0 && !ok && len >= 0 && g == 0 && qb == 0 && s == 0) report(a.status, SPEC_ERR_BAD_TREE);
+  } else {
+    anc_raw = ds_read_u64(lds_addr((const char*)s_ancin) + 8 * node_c);
+  }
+  anc_row = row_live ? anc_raw : 0ull;
+  if (!row_live)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = bf16x8{};
+  f32x16 s_cur = f32x16{};  // scores of the tile being finished, prepared
+  if (n_tiles > 0) {
+    v4i kr[D / 16];
+    read_k(0, kr);
+    s_cur = qk(kr);
+    if (n_plain > 0) prep(s_cur, 0, std::false_type{});
+    else prep(s_cur, 0, std::true_type{});
+  }
+  auto step = [&](int it, auto masked_next) {
+    wait_tile(it + 1);
+    lds_barrier();  // tile it + 1 is in LDS; every wave is done with tile it - 1's stage
+    if (it + kStages - 1 < n_tiles) {
+      issue(it + kStages - 1);
+      ++n_issued;
+    }
+    v4i kr[D / 16];
+    read_k(it + 1, kr);
+    v4s va[2][NB][8];
+    read_v(it, va);
+    const f32x16 s_next0 = qk(kr);
+    bf16x8 pf[2];
+    expo(s_cur, pf);
+    pv(va, pf);
+    f32x16 s_next = s_next0;
+    prep(s_next, it + 1, masked_next);
+    s_cur = s_next;
+  };
   int it = 0;
-  for (; it < n_plain; ++it) tile(it, std::false_type{});
-  for (; it < n_tiles; ++it) tile(it, std::true_type{});
+  for (; it + 1 < n_plain; ++it) step(it, std::false_type{});
+  for (; it + 1 < n_tiles; ++it) step(it, std::true_type{});
+  if (n_tiles > 0) {  // the last tile
+    v4s va[2][NB][8];
+    read_v(it, va);
+    bf16x8 pf[2];
+    expo(s_cur, pf);
+    pv(va, pf);
+  }
+  vm_wait<0>();  // tiles issued past the split's end have landed before LDS is reused
   if (bad_page) report(a.status, SPEC_ERR_BAD_INPUT);
   // ---- merge the two key halves of each row, split by head dimension: the
   // key-half-0 wave finishes dims [0, D/2) and the key-half-1 wave dims [D/2, D).
@@ -514,20 +623,27 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       fin[blk][e + 3] = (lo_half ? acc_o[blk][e + 3] : acc_o[NH + blk][e + 3]) * wa + o.w * wb;
     }
   }
-  // ---- write this split's partials: the wave's 32 rows x D/2 dims go through LDS
-  // (the partner's hand-over area, read by now) so that they leave as whole
-  // 16-byte row pieces ----
+  // ---- write this split's partials (one split: the output rows themselves): the
+  // wave's 32 rows x D/2 dims go through LDS (the partner's hand-over area, read by
+  // now) so that they leave as whole 16-byte row pieces ----
+  const bool direct = a.direct != 0;
+  const int64_t n_rows = (int64_t)a.batch * a.n_max * a.hq;  // rows of one split's partials
   const bool row_out = r < G && node < a.n_max;
-  const int64_t prow = (((int64_t)s * a.batch + b) * a.n_max + node) * a.hq + h;
-  if (kh == 0 && row_out && lane < 32) {
+  const int64_t orow = ((int64_t)b * a.n_max + node) * a.hq + h;
+  const int64_t prow = (int64_t)s * n_rows + orow;
+  if (!direct && kh == 0 && row_out && lane < 32) {
     a.mpart[prow] = m_run;
     a.lpart[prow] = l_run;
   }
+  if (direct && len < 0 && g == 0 && qb == 0 && tid == 0) report(a.status, SPEC_ERR_BAD_INPUT);
   constexpr int HB = D;               // bytes of half a row in bf16
   constexpr int OROW = HB + 16;       // bytes per staged half row (padded)
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the hand-over reads are done
   char* so = reinterpret_cast<char*>(xr);
   {
+    // an output row is zero unless its request is valid, its node exists and (rows
+    // given) its ancestor row holds the node itself
+    const bool keep = !direct || (row_live && ((anc_row >> (node & 63)) & 1ull));
     const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
 #pragma unroll
     for (int db = 0; db < NH; ++db)
@@ -536,7 +652,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
         const int d = db * 32 + 8 * e4 + 4 * (lane >> 5);  // within the half
         bf16x4 o4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(fin[db][4 * e4 + i] * inv_l);
+        for (int i = 0; i < 4; ++i) o4[i] = keep ? (__bf16)(fin[db][4 * e4 + i] * inv_l) : (__bf16)0.0f;
         *reinterpret_cast<bf16x4*>(so + (lane & 31) * OROW + d * 2) = o4;
       }
   }
@@ -551,9 +667,11 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     const int rg = qb * kMfmaRowsPerWg + wr * 32 + rl;
     const int nd2 = rg / hpg;
     if (rg < G && nd2 < a.n_max) {
-      const int64_t prow2 = (((int64_t)s * a.batch + b) * a.n_max + nd2) * a.hq + g * hpg + rg % hpg;
+      const int64_t orow2 = ((int64_t)b * a.n_max + nd2) * a.hq + g * hpg + rg % hpg;
       const int4 v = *reinterpret_cast<const int4*>(so + rl * OROW + (lane % CPR) * 16);
-      *reinterpret_cast<int4*>((char*)a.opart + prow2 * D * 2 + kh * HB + (lane % CPR) * 16) = v;
+      char* dst = (direct ? (char*)a.out + orow2 * D * 2 : (char*)a.opart + ((int64_t)s * n_rows + orow2) * D * 2) +
+                  kh * HB + (lane % CPR) * 16;
+      *reinterpret_cast<int4*>(dst) = v;
     }
   }
 }
@@ -811,6 +929,7 @@ inline size_t attn_ws_bytes(const AttnPlan& p, int32_t batch, int32_t n_max, int
   return 2 * rows * sizeof(float) + rows * D * sizeof(float);  // fp32 partials for fp32 inputs
 }
 
+
 }  // namespace spectree
 
 extern "C" size_t spec_tree_attention_workspace_size(int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
@@ -874,6 +993,8 @@ static int attention_launch(const void* q, const void* k, const void* v, int32_t
   a.lpart = a.mpart + rows;
   a.opart = (void*)(a.lpart + rows);
   a.status = status;
+  a.out = out;
+  a.direct = p.mfma && p.S == 1;  // one split: the output directly, no combine launch
   hipStream_t st = (hipStream_t)stream;
   const dim3 g1((unsigned)grid), blk(256);
   if (p.mfma) {
@@ -894,6 +1015,7 @@ static int attention_launch(const void* q, const void* k, const void* v, int32_t
       hipLaunchKernelGGL((attn_shfl_kernel<64, float>), g1, blk, 0, st, a);
   }
   SPEC_LAUNCH_CHECK();
+  if (a.direct) return SPEC_OK;
   const int64_t out_rows = (int64_t)batch * n_max * hq;
   const dim3 g2((unsigned)((out_rows + 3) / 4));
   if (dtype == SPEC_BF16) {
