@@ -6,10 +6,13 @@ A step is the whole hot path over one input set:
     (target and draft rows at T > 0; spec_tree_softmax at T = 0),
     spec_tree_reject_sample (whose final walk also writes the accepted path, the
     result of spec_accept_path).
-The three calls run in order on one stream.  The attention shares no data with the
-other two, so ``--overlap`` runs it on a second HIP stream, forked from and joined
-back into the timing stream by events; on MI355X that is slower (the attention
-kernel's registers leave no room on its CUs for the other kernels' workgroups).
+The attention shares no data with the other two calls, so it can run on a second HIP
+stream beside them, forked from and joined back into the timing stream by events.
+``--streams auto`` (the default) times a short run of each form before the timed
+region and keeps the faster: at the default workload the three calls in order on one
+stream win (the attention kernel's registers leave no room on its CUs for the other
+kernels' workgroups), at long contexts or large batches the second stream does
+(the attention then outlasts the sampling half).  ``--streams one|two`` fixes it.
 Workload (default): the Llama-3-8B-shaped step -- one request, a 60-node EAGLE-2
 tree (top-k 10, depth 6), 4096 cached tokens, 32 query / 8 KV heads, head_dim 128,
 bf16 KV, fp32 logits over a 128256-token vocabulary, T = 1.  Synthetic, seeded.
@@ -109,9 +112,10 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--overlap", action="store_true",
-                    help="the attention on a second stream beside the logit pass and the sampler (default: the "
-                         "whole step on one stream)")
+    ap.add_argument("--streams", choices=("auto", "one", "two"), default="auto",
+                    help="one: the whole step on one stream; two: the attention on a second stream beside the "
+                         "logit pass and the sampler; auto: time a short run of each, keep the faster")
+    ap.add_argument("--overlap", action="store_true", help="the same as --streams two")
     ap.add_argument("--fork", choices=("start", "after_softmax"), default="start",
                     help="with --overlap: where the second stream branches off, at the step's start or after "
                          "the logit pass")
@@ -675,13 +679,26 @@ def main():
     T = args.temperature if args.config != 3 else None
     inp = synth.make_config(args.config, seed=args.seed, T=T, tree_builder=gpu_tree_builder)
     dev = to_device(inp)
-    step = VerifyStep(dev)
-    if args.overlap:
-        step.overlap(fork=args.fork)  # the attention on a second stream
     big = [k for k in ("q", "k", "v", "tgt_logits", "dft_logits") if k in dev]
     replicas = [{k: dev[k].clone() for k in big} for _ in range(args.replicas)]
     stream = torch.cuda.current_stream()
-    step.compile(replicas, stream)  # the timed steps replay recorded calls: less host time per step
+
+    def make_step(mode):
+        s = VerifyStep(dev)
+        if mode == "two":
+            s.overlap(fork=args.fork)  # the attention on a second stream
+        s.compile(replicas, stream)  # the timed steps replay recorded calls: less host time per step
+        return s
+
+    mode = "two" if args.overlap else args.streams
+    probe = None
+    if mode == "auto":  # a short timed run of each form; the timed region uses the faster
+        probe = {}
+        for m in ("one", "two"):
+            ms, _ = time_steps(make_step(m), replicas, stream, 50, 10)
+            probe[m] = round(ms * 1e3, 2)
+        mode = min(probe, key=probe.get)
+    step = make_step(mode)
 
     # warm-up, the clean timed region, then an instrumented pass with events around
     # every stage of every step
@@ -705,6 +722,8 @@ def main():
     reject_us = time_calls(lambda r: step.reject(None, r["tgt_logits"], r.get("dft_logits")), replicas)
     step_b = attn_b + samp_b
     samp_us = st_mean[2] + st_mean[4] + st_mean[5]
+    # one stream runs the parts in turn; two streams run the attention beside the sampling half
+    crit_us = attn_us + branch_us if step.side is None else max(attn_us, branch_us)
     hd = host_driven(step, replicas, args.steps)
     res = {
         "metric": METRIC,
@@ -757,12 +776,13 @@ def main():
                                               samp_b, branch_us, traffic.get("sampling_branch")),
         },
         # the step's parts, each timed back to back on its own: one stream runs them in
-        # turn; with --overlap the attention runs beside the sampling half
+        # turn; with two streams the attention runs beside the sampling half
         "critical_path": {
             "branch": ("attention, then softmax_pair + reject_sample" if step.side is None else
-                       "softmax_pair + reject_sample (the attention branch runs beside it)"),
-            "us": round(branch_us + (attn_us if step.side is None else 0.0), 2),
-            "share_of_step": round((branch_us + (attn_us if step.side is None else 0.0)) / (ms_per_step * 1e3), 3),
+                       "softmax_pair + reject_sample (the attention branch runs beside it)" if branch_us >= attn_us
+                       else "attention (the sampling half runs beside it)"),
+            "us": round(crit_us, 2),
+            "share_of_step": round(crit_us / (ms_per_step * 1e3), 3),
             "reject_sample_us": round(reject_us, 2), "softmax_pair_us": round(pair_us, 2),
             "sampling_half_us": round(branch_us, 2),
             "attention_call_us": round(attn_us, 2),
@@ -770,6 +790,8 @@ def main():
         # the same replayed steps driven by the host with nothing queued ahead: what a
         # serving loop on this host gets, host issue time included
         "host_driven": hd,
+        # the stream form the timed steps used, and (auto) the short runs that chose it
+        "streams": {"used": mode, "probe_us_per_step": probe},
     }
     acc, first = acceptance_trials(inp, dev, seed=args.seed)
     res["acceptance"] = acc

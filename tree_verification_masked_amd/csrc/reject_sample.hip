@@ -18,31 +18,37 @@
 //
 // Every node is evaluated in parallel (the uniforms are indexed by node and child,
 // so a node's outcome does not depend on how the walk reached it); the walk from
-// the root then only follows the per-node results.  Two launches at T > 0:
-//   plan   one workgroup per node slot: the row statistics of the node's target and
-//          draft rows, merged from the logit pass's chunk partials; the tree's
-//          verdict, the node's children and their tested tokens' p and q (fp64);
-//          the first-child test.  A leaf draws its bonus from p (the chunk that
-//          holds the target is found from the chunk partials and scanned); a node
-//          whose first child is accepted is done; either reports to its request.
-//          A node whose first child is rejected ("active") leaves its plan for the
-//          chain launch.
-//   chain  persistent workgroups, each taking one 4096-token chunk of an active
-//          node at a time, its logits held in registers as exact fixed-point
-//          masses.  The node's chunks follow the sibling chain level by level:
-//          after each rejection every chunk sums, exactly, the masses of its
-//          tokens with p - c q > 0 for the new threshold c, publishes its two sums
-//          as tagged words and reads every other chunk's words of that level, so
-//          all of them hold the same exact W(c) and take the same next step.  When
-//          every child is rejected, the per-chunk sums locate the chunk of the
-//          terminal draw and only that chunk's workgroup scans it.  The node's last
-//          workgroup clears its words and reports the node; the request's last
-//          reported node walks from the root and writes the outputs.
-// The chunks of one node are placed on one XCD (a chunk's workgroups are taken
-// from blockIdx = XCD count * i + x, which the hardware dispatches to one XCD),
-// so their words pass through that XCD's L2; vocabularies above 64 chunks spread a
-// node over the whole device with device-scope words.  Every wait is bounded: a
-// wait that gives up reports SPEC_ERR_TIMEOUT and the call still ends normally.
+// the root then only follows the per-node results.  One launch at T > 0, with a
+// "planner" workgroup and one workgroup per 4096-token chunk for every node slot.
+// Each of them derives the node's plan itself from the inputs: the row statistics
+// of the node's target and draft rows (merged from the logit pass's chunk
+// partials), the tree's verdict, the node's children, their tested tokens' p and q
+// (fp64) and the first-child test.
+//   planner  a leaf draws its bonus from p (the chunk that holds the target is
+//            found from the chunk partials and scanned); a node whose first child
+//            is accepted is done; either is reported to its request here.
+//   chunks   only an internal node keeps them.  Its chunk of both rows is loaded at
+//            once and held in registers as exact fixed-point masses, and the sums
+//            of the first threshold (c = 1, whatever the first test gives) go out
+//            before the plan is known.  When the first child is rejected the
+//            node's chunks follow the sibling chain level by level: after each
+//            rejection every chunk sums, exactly, the masses of its tokens with
+//            p - c q > 0 for the new threshold c, publishes its two sums as tagged
+//            words and reads every other chunk's words of that level, so all of
+//            them hold the same exact W(c) and take the same next step.  When every
+//            child is rejected, the per-chunk sums locate the chunk of the terminal
+//            draw and only that chunk's workgroup scans it.  The node's last chunk
+//            to finish clears its words; a chain node is reported by its chunks.
+// The request's last reported node walks from the root and writes the outputs.
+// The workgroups of one node are placed on one XCD (the node of ordinal o, in group
+// x = o mod nx, takes blockIdx = nx * i + x, which the hardware dispatches to one
+// XCD), so their words pass through that XCD's L2; within a group, blocks of nodes
+// put their planners ahead of their chunks, every request's first node slots first.  Vocabularies above 64 chunks spread a node over
+// the whole device with device-scope words.  A planner never waits, and a node's
+// chunks wait only for each other, so the waits end whenever every chunk of a node
+// can be resident at once (checked on the host from the occupancy); every wait is
+// bounded besides: one that gives up reports SPEC_ERR_TIMEOUT and the call still
+// ends normally.
 // Masses are summed as exact integers: the fp32 unnormalised mass exp((l - m)/T)
 // in [0, 1] is truncated to a multiple of 2^-42 (bit arithmetic, no rounding), so
 // the sums are exact, independent of summation order and bitwise reproducible;
@@ -546,13 +552,18 @@ __device__ inline bool gather_level(const unsigned long long* sl0, int nch, int 
 }
 
 // Workgroup blockIdx = nx i + x serves group x (with nx = the XCD count, the hardware
-// dispatches it to one XCD): the nodes nd = nx g + x, in blocks of nb_blk nodes.  A
-// block's workgroups are first one planner per node (ch = -1: the plan, a leaf's
-// draw, the report of a node that needs no chain; it never waits), then the nch
-// chunks of each node, node by node.  Only the chunks of one node wait, and only for
-// each other; workgroups start in blockIdx order, so the first unfinished node always
-// has all of its chunks started, and every wait ends.
-__device__ inline void chunk_of(int blk, int q_off, int nch, int nx, int nb_blk, int* nd, int* ch) {
+// dispatches it to one XCD): the nodes of ordinal o = nx g + x, in blocks of nb_blk
+// nodes.  Ordinals run over node slots first and requests second (o = n batch + b),
+// so every request's first slots (the root and the nodes nearest it, which hold the
+// long sibling chains; the later slots are mostly leaves) start ahead of the later
+// slots.  A block's workgroups are first one planner per node (ch = -1: the plan, a
+// leaf's draw, the report of a node that needs no chain; it never waits), then the
+// nch chunks of each node, node by node.  Only the chunks of one node wait, and only
+// for each other; workgroups start in blockIdx order, so the first unfinished node
+// always has all of its chunks started, and every wait ends.  *nd = batch n_max for an
+// ordinal past the last node.
+__device__ inline void chunk_of(int blk, int q_off, int nch, int nx, int nb_blk, int batch, int n_max, int* nd,
+                                int* ch) {
   const int x = blk % nx, q = blk / nx + q_off;
   const int per = nb_blk * (nch + 1), blkno = q / per, r = q % per;
   int g, c;
@@ -564,7 +575,8 @@ __device__ inline void chunk_of(int blk, int q_off, int nch, int nx, int nb_blk,
     g = blkno * nb_blk + h / nch;
     c = h % nch;
   }
-  *nd = g * nx + x;
+  const int o = g * nx + x;
+  *nd = o < batch * n_max ? (o % batch) * n_max + o / batch : batch * n_max;
   *ch = c;
 }
 
@@ -585,7 +597,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(RejArgs a, SampWs w
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nch = a.nch, nodes = a.batch * a.n_max;
   int nd, ch;
-  chunk_of((int)blockIdx.x, q_off, nch, nx, nb_blk, &nd, &ch);
+  chunk_of((int)blockIdx.x, q_off, nch, nx, nb_blk, a.batch, a.n_max, &nd, &ch);
   if (nd >= nodes) return;
   const bool planner = ch < 0;
   const int b = nd / a.n_max, n = nd % a.n_max;

@@ -91,11 +91,11 @@ class VerifyStep:
         """Run the attention (after the mask build when it is not folded) on
         ``side_stream`` (a new default-priority stream if None), concurrently with the
         caller's stream.  fork "start": beside softmax and sampling; "after_softmax":
-        beside the sampling only.  On MI355X either is slower than one stream (60-node
-        / 4k step: 64.4 and 69.8 vs 60.6 us per step with the same kernels): the
-        attention kernel's registers leave no room on its CUs for the others'
-        workgroups, so the kernels mostly wait for each other.
-        Returns self."""
+        beside the sampling only.  On MI355X at the 60-node / 4k step either is slower
+        than one stream (the attention kernel's registers leave no room on its CUs for
+        the others' workgroups, so the kernels mostly wait for each other); where the
+        attention outlasts the sampling half (long contexts, large batches) the second
+        stream is faster.  Returns self."""
         assert fork in ("start", "after_softmax")
         if self.with_attention:
             self.side = side_stream if side_stream is not None else torch.cuda.Stream(self.d["parent"].device)
