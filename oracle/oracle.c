@@ -451,7 +451,16 @@ static int eval_node(const verify_in* in, int32_t b, int32_t n, node_ws* ws, int
   const float* us = in->u_sample + (int64_t)b * in->n_max;
   const double eps = ws->eps;
   if (row_probs(lt, V, in->T, ws->p) != 0) return -1;
-  if (row_probs(in->dft + row * V, V, in->Td, ws->q) != 0) return -1;
+  /* [ZS] part C: q is the draft distribution produced at this node and serves only
+     to test this node's children; a leaf has none, so its draft row takes no part
+     (its bonus is drawn from p, part G) and is not read */
+  int has_kids = 0;
+  for (int32_t c = n + 1; c < nb && !has_kids; ++c) has_kids = par[c] == n;
+  if (has_kids) {
+    if (row_probs(in->dft + row * V, V, in->Td, ws->q) != 0) return -1;
+  } else {
+    for (int32_t x = 0; x < V; ++x) ws->q[x] = 0.0;
+  }
   for (int32_t x = 0; x < V; ++x) {
     ws->r[x] = ws->p[x];
     ws->p_lo[x] = ws->p[x] * (1.0 - eps);

@@ -234,6 +234,30 @@ def test_small_temperature_reproduces_greedy():
 
 # ---------------------------------------------------------------- bookkeeping
 
+def test_leaf_draft_rows_take_no_part():
+    """[ZS] part C: the draft distribution produced at a node serves only to test that
+    node's children, and a leaf's bonus is drawn from its target row (part G), so a
+    leaf's draft row takes no part: NaN, +inf or arbitrary values there change no
+    output (every node evaluated), while NaN in the root's draft row, which tests the
+    root's children, makes the request bad."""
+    rng = synth.rng_for(30, 2)
+    p, q = rng.dirichlet(np.ones(16)), rng.dirichlet(np.ones(16))
+    tr = synth.star_trials(rng, p, q, 3, 64, leaf_p=rng.dirichlet(np.ones(16)))
+    ref = _run(tr, mode="all")
+    alt = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in tr.items()}
+    alt["dft_logits"][:, 1, 3] = np.nan
+    alt["dft_logits"][:, 2, :] = np.inf
+    alt["dft_logits"][:, 3] = rng.standard_normal((64, 16)).astype(np.float32)
+    got = _run(alt, mode="all")
+    for k in ("accepted_child", "term_token", "accept_len", "path_nodes", "out_tokens"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert (ref["term_token"][:, 1:] >= 0).all()  # the leaves were evaluated: each drew its bonus
+    alt["dft_logits"][5, 0, 7] = np.nan
+    got = _run(alt, mode="all")
+    assert got["accept_len"][5] == -1 and got["accepted_child"][5, 0] == oracle.BAD_REQUEST
+    assert np.array_equal(np.delete(got["out_tokens"], 5, 0), np.delete(ref["out_tokens"], 5, 0))
+
+
 def test_bad_requests_are_flagged():
     rng = synth.rng_for(30, 1)
     p = rng.dirichlet(np.ones(16))
