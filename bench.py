@@ -129,15 +129,26 @@ def parse():
     return ap.parse_args()
 
 
+def internal_rows(inp):
+    """Node rows whose node has at least one child (the rows whose draft logits the
+    sampler reads: a leaf's draft row takes no part)."""
+    n = 0
+    for b in range(inp["B"]):
+        nb, par = int(inp["n_nodes"][b]), inp["parent"][b]
+        n += len({int(par[c]) for c in range(1, nb)})
+    return n
+
+
 def algorithmic_bytes(inp):
     """Bytes the step must move at least once: KV of every request (prompt + tree),
-    Q and O, the target logits, and the draft logits when T > 0."""
+    Q and O, the target logits of every node row, and at T > 0 the draft logits of
+    the rows of nodes with children."""
     B, n_max, hq, hkv, d = inp["B"], inp["n_max"], inp["hq"], inp["hkv"], inp["d"]
     el = 2 if inp["bf16"] else 4
     kv_tokens = int(np.sum(inp["ctx_len"] + inp["n_nodes"]))
     attn = 2 * kv_tokens * hkv * d * el + 2 * B * n_max * hq * d * el
     logits = B * n_max * inp["V"] * 4
-    sampling = logits * (2 if inp["T"] > 0 else 1)
+    sampling = logits + (internal_rows(inp) * inp["V"] * 4 if inp["T"] > 0 else 0)
     return attn, logits, sampling
 
 

@@ -204,10 +204,22 @@ int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float te
  *                   tgt_argmax (nullable) as spec_tree_softmax defines them.  With
  *                   none, no row merge is launched and both chunk pairs are required
  *                   -- the single vocabulary pass of a verification step.
+ *   the tree        parent [batch, n_max] and n_nodes [batch] (both or neither;
+ *                   rows = batch * n_max node rows, 1 <= n_max <= 64, chunk partials
+ *                   only).  Tree notes, parts C and G: a node's draft distribution
+ *                   only tests its children and a leaf draws from its target row, so
+ *                   the draft partials are computed only for the rows of nodes with
+ *                   at least one child (parent[b, c] == n for some n < c < n_nodes[b]);
+ *                   the other rows' draft partials are left as they were.  The target
+ *                   rows are all computed.  spec_tree_reject_sample reads exactly the
+ *                   draft rows this computes.
+ * Host errors (beyond spec_tree_softmax's): a tree with row statistics, n_max outside
+ * [1, 64] or rows not a multiple of it, only one of parent / n_nodes.
  */
 size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vocab);
 int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
-                           float draft_temperature, int64_t rows, int32_t vocab, float* tgt_max, float* tgt_sumexp,
+                           float draft_temperature, int64_t rows, int32_t vocab, const int32_t* parent,
+                           const int32_t* n_nodes, int32_t n_max, float* tgt_max, float* tgt_sumexp,
                            int32_t* tgt_argmax, float* tgt_chunk_max, double* tgt_chunk_sum, float* dft_max,
                            float* dft_sumexp, float* dft_chunk_max, double* dft_chunk_sum, void* workspace,
                            size_t workspace_bytes, int32_t* status, void* stream);
@@ -230,7 +242,9 @@ int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const flo
  * and chunk inputs, uniforms and workspace may be NULL.
  * T > 0 reads the chunk partials of both arrays (spec_tree_softmax_pair or
  * spec_tree_softmax, same chunking) and merges each row's statistics itself;
- * tgt_max and tgt_argmax are not read.
+ * tgt_max and tgt_argmax are not read.  The draft row of a node without children
+ * takes no part (its draft partials are not read and need not be valid), so
+ * spec_tree_softmax_pair given the tree may skip them.
  * Inputs: tgt_logits, dft_logits fp32 [batch, n_max, vocab]; tokens, parent int32
  * [batch, n_max]; n_nodes int32 [batch]; u_accept, u_sample fp32 [batch, n_max] in
  * [0, 1).
@@ -238,8 +252,9 @@ int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const flo
  * SPEC_NODE_NONE, or SPEC_NODE_NOT_EVALUATED for nodes off the walk;
  * term_token[b,n] = the terminal token of the last node of the walk, else
  * SPEC_NODE_NOT_EVALUATED.  A request with a bad tree, a token outside
- * [0, vocab) or an invalid logit row gets accepted_child[b,0] =
- * SPEC_NODE_BAD_REQUEST and a device error code.
+ * [0, vocab), an invalid target row or an invalid draft row of a node with
+ * children gets accepted_child[b,0] = SPEC_NODE_BAD_REQUEST and a device error
+ * code.
  * path_nodes, out_tokens [batch, n_max] and accept_len [batch] (int32, all three
  * or none, NULL to skip): the accepted path, exactly as spec_accept_path would
  * derive it from accepted_child and term_token, written by the same walk.

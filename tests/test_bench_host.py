@@ -19,7 +19,11 @@ def test_algorithmic_bytes_and_flops_of_the_60_node_step():
     kv = 2 * (4096 + 60) * 8 * 128 * 2            # K and V of every position, bf16
     qo = 2 * 60 * 32 * 128 * 2                    # Q in, O out
     assert attn == kv + qo == 18006016
-    assert logits == 60 * 128256 * 4 and sampling == 2 * logits
+    # the draft rows count only at nodes with children (a leaf's draft row takes no part)
+    par = inp["parent"][0]
+    internal = sum(1 for n in range(60) if (par[n + 1:60] == n).any())
+    assert internal == bench.internal_rows(inp) == 13
+    assert logits == 60 * 128256 * 4 and sampling == logits + internal * 128256 * 4
     assert bench.attention_flops(inp) == 4 * 32 * 128 * 60 * (4096 + 60)
 
 

@@ -170,6 +170,68 @@ def test_softmax_pair_and_chunk_partials(V):
         np.testing.assert_allclose(csm[:, c], ref, rtol=1e-5)
 
 
+def test_softmax_pair_given_the_tree_skips_leaf_draft_rows():
+    """Given the tree, the pair launch computes the draft partials only for the rows
+    of nodes with children (reading 25): those and every target partial equal the
+    launch without the tree bit for bit; the draft partials of leaves and padding
+    slots are left as they were."""
+    say("softmax pair with the tree")
+    rng = np.random.default_rng(5)
+    Bn, n_max, V, T, Td = 3, 8, 10000, 1.0, 0.7
+    parent = np.full((Bn, n_max), -1, np.int32)
+    parent[0] = [-1, 0, 0, 1, 1, 2, 3, 3]
+    parent[1, :5] = [-1, 0, 1, 1, 0]
+    n_nodes = np.array([8, 5, 1], np.int32)
+    R = Bn * n_max
+    tgt = (rng.standard_normal((Bn, n_max, V)) * 3).astype(np.float32)
+    dft = (tgt + rng.standard_normal((Bn, n_max, V))).astype(np.float32)
+    nch = -(-V // B.spec_tree_softmax_chunk())
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, dtype=dt, device="cuda")
+    outs = []
+    for tree in (False, True):
+        cm, cs = z(R, nch), z(R, nch, dt=torch.float64)
+        dcm, dcs = torch.full((R, nch), -7.0, device="cuda"), torch.full((R, nch), -9.0, dtype=torch.float64,
+                                                                        device="cuda")
+        ws = z(B.spec_tree_softmax_pair_workspace_size(R, V), dt=torch.uint8)
+        st = z(1, dt=torch.int32)
+        B.spec_tree_softmax_pair(dev(tgt), T, dev(dft), Td, None, None, None, cm, cs, None, None, ws, status=st,
+                                 dft_chunk_max=dcm, dft_chunk_sum=dcs, parent=dev(parent) if tree else None,
+                                 n_nodes=dev(n_nodes) if tree else None)
+        torch.cuda.synchronize()
+        assert st.item() == 0
+        outs.append([x.cpu().numpy() for x in (cm, cs, dcm, dcs)])
+    (cm0, cs0, dm0, ds0), (cm1, cs1, dm1, ds1) = outs
+    assert np.array_equal(cm0, cm1) and np.array_equal(cs0, cs1)
+    internal = np.zeros(R, bool)
+    for b in range(Bn):
+        for n in range(n_nodes[b]):
+            internal[b * n_max + n] = any(parent[b, c] == n for c in range(n + 1, n_nodes[b]))
+    assert internal.sum() == 6  # nodes 0-3 of request 0 and 0-1 of request 1
+    assert np.array_equal(dm1[internal], dm0[internal]) and np.array_equal(ds1[internal], ds0[internal])
+    assert (dm1[~internal] == -7.0).all() and (ds1[~internal] == -9.0).all()
+
+
+def test_sampling_leaf_draft_rows_take_no_part():
+    """NaN, +inf or unrelated values in the draft rows of leaves change no output and
+    raise no error (reading 25), against the oracle, which reads no such row either."""
+    say("sampling leaf draft rows")
+    inp = support.make_config(2, seed=7, with_kv=False, vocab_override=9000)
+    ref_clean = _sampling_gpu(inp)
+    par, nb = inp["parent"][0], int(inp["n_nodes"][0])
+    leaves = [n for n in range(nb) if not any(par[c] == n for c in range(n + 1, nb))]
+    assert len(leaves) > 20
+    alt = dict(inp, dft_logits=inp["dft_logits"].copy())
+    rng = np.random.default_rng(3)
+    for i, n in enumerate(leaves):
+        alt["dft_logits"][0, n] = (np.nan if i % 3 == 0 else np.inf if i % 3 == 1
+                                   else rng.standard_normal(inp["V"]).astype(np.float32))
+    got = _sampling_gpu(alt)
+    assert got["status"][0] == 0
+    for k in ("accepted_child", "term_token", "path_nodes", "out_tokens", "accept_len"):
+        assert np.array_equal(got[k], ref_clean[k]), k
+    _compare_sampling(got, _oracle_sampling(alt), alt, max_exempt=1)
+
+
 def test_softmax_flags_bad_rows():
     say("softmax bad rows")
     logits = np.zeros((4, 300), np.float32)
@@ -925,13 +987,19 @@ def test_full_step(cfg, T):
     if inp["T"] > 0:
         # the step's logit pass leaves chunk partials only: merged on the host they
         # give the row statistics
+        # give the row statistics; the draft rows only at nodes with children (the
+        # others are left untouched: reading 25)
         ref_d = oracle.softmax(inp["dft_logits"], inp["Td"], want_probs=False)
-        for cm, cs, T_, rf in ((got["tcmax"], got["tcsum"], inp["T"], ref_t), (got["dcmax"], got["dcsum"], inp["Td"],
-                                                                              ref_d)):
-            m = cm.max(axis=1).astype(np.float64)
-            z = (cs * np.exp((cm.astype(np.float64) - m[:, None]) / T_)).sum(axis=1)
-            assert np.array_equal(m, rf["max"])
-            np.testing.assert_allclose(z, rf["sumexp"], rtol=1e-5)
+        internal = np.array([any(inp["parent"][b, c] == n for c in range(n + 1, inp["n_nodes"][b]))
+                             for b in range(inp["B"]) for n in range(inp["n_max"])])
+        every = np.ones_like(internal)
+        for cm, cs, T_, rf, rows in ((got["tcmax"], got["tcsum"], inp["T"], ref_t, every),
+                                     (got["dcmax"], got["dcsum"], inp["Td"], ref_d, internal)):
+            m = cm[rows].max(axis=1).astype(np.float64)
+            z = (cs[rows] * np.exp((cm[rows].astype(np.float64) - m[:, None]) / T_)).sum(axis=1)
+            assert np.array_equal(m, rf["max"][rows])
+            np.testing.assert_allclose(z, rf["sumexp"][rows], rtol=1e-5)
+        assert (got["dcmax"][~internal] == 0).all() and (got["dcsum"][~internal] == 0).all()
     else:
         assert np.array_equal(got["tmax"].astype(np.float64), ref_t["max"])
         assert np.array_equal(got["targ"], ref_t["argmax"])

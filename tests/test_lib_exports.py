@@ -63,9 +63,10 @@ def test_host_errors_softmax(lib):
     assert f(P, 4, 100, 1.0, P, P, P, None, None, None, P, 8, None, None) == -5              # workspace
     assert f(P, 4, 100, 1.0, P, P, P, None, None, None, None, 0, None, None) == -5
     g = lib.spec_tree_softmax_pair
-    #          tl T    dl Td   R  V    tmx tse tam tcm tcs dmx dse dcm dcs ws wsb st s
-    ok_rows = [P, 1.0, P, 1.0, 4, 100, P, P, P, None, None, P, P, None, None, P, 1 << 20, None, None]
-    ok_chunks = [P, 1.0, P, 1.0, 4, 100, None, None, None, P, P, None, None, P, P, P, 1 << 20, None, None]
+    #          tl T    dl Td   R  V    par  nn   nmx tmx tse tam tcm   tcs   dmx dse dcm   dcs   ws wsb      st    s
+    ok_rows = [P, 1.0, P, 1.0, 4, 100, None, None, 0, P, P, P, None, None, P, P, None, None, P, 1 << 20, None, None]
+    ok_chunks = [P, 1.0, P, 1.0, 4, 100, None, None, 0, None, None, None, P, P, None, None, P, P, P, 1 << 20, None,
+                 None]
 
     def pair(base, **kw):
         a = list(base)
@@ -75,12 +76,19 @@ def test_host_errors_softmax(lib):
 
     assert pair(ok_rows, a3=0.0) == -1                      # T_d = 0
     assert pair(ok_rows, a2=None) == -1                     # draft logits
-    assert pair(ok_rows, a16=8) == -5                       # workspace
-    assert pair(ok_rows, a7=None) == -1                     # row outputs all or none
-    assert pair(ok_chunks, a10=None) == -1                  # a chunk pair is both or neither
-    assert pair(ok_chunks, a13=None, a14=None) == -1        # chunk pass only: both pairs needed
-    assert pair(ok_chunks, a8=P) == -1                      # the argmax needs the row merge
-    assert pair(ok_chunks, a16=8) == -5
+    assert pair(ok_rows, a19=8) == -5                       # workspace
+    assert pair(ok_rows, a10=None) == -1                    # row outputs all or none
+    assert pair(ok_chunks, a13=None) == -1                  # a chunk pair is both or neither
+    assert pair(ok_chunks, a16=None, a17=None) == -1        # chunk pass only: both pairs needed
+    assert pair(ok_chunks, a11=P) == -1                     # the argmax needs the row merge
+    assert pair(ok_chunks, a19=8) == -5
+    # the tree: parent and n_nodes both or neither, chunk partials only, rows = batch x n_max
+    assert pair(ok_chunks, a6=P) == -1
+    assert pair(ok_chunks, a7=P, a8=4) == -1
+    assert pair(ok_rows, a6=P, a7=P, a8=4) == -1            # with row statistics
+    assert pair(ok_chunks, a6=P, a7=P, a8=0) == -1          # n_max outside [1, 64]
+    assert pair(ok_chunks, a6=P, a7=P, a8=65) == -1
+    assert pair(ok_chunks, a6=P, a7=P, a8=3) == -1          # 4 rows are not whole requests of 3 nodes
     assert lib.spec_tree_softmax_chunk() == 4096
 
 

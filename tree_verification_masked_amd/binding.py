@@ -47,8 +47,8 @@ _SIGNATURES = {
     "spec_tree_softmax_workspace_size": [_I64, _I32],
     "spec_tree_softmax": [_VP, _I64, _I32, _F32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_tree_softmax_pair_workspace_size": [_I64, _I32],
-    "spec_tree_softmax_pair": [_VP, _F32, _VP, _F32, _I64, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                               _SZ, _VP, _VP],
+    "spec_tree_softmax_pair": [_VP, _F32, _VP, _F32, _I64, _I32, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                               _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_tree_reject_sample_workspace_size": [_I32, _I32, _I32],
     "spec_tree_reject_sample": [_VP, _F32, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32,
                                 _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
@@ -303,12 +303,23 @@ def _check_chunks(cmax, csum, rows, vocab, prefix):
 
 def spec_tree_softmax_pair(tgt_logits, temperature, dft_logits, draft_temperature, tgt_max, tgt_sumexp, tgt_argmax,
                            tgt_chunk_max, tgt_chunk_sum, dft_max, dft_sumexp, workspace, status=None, stream=None,
-                           dft_chunk_max=None, dft_chunk_sum=None):
+                           dft_chunk_max=None, dft_chunk_sum=None, parent=None, n_nodes=None):
     """Row statistics (tgt_max, tgt_sumexp, dft_max, dft_sumexp: all or none; tgt_argmax
     optional) and / or chunk partials of both logit arrays in one launch; with no row
-    statistics only the chunk pass runs (both chunk pairs required)."""
+    statistics only the chunk pass runs (both chunk pairs required).  Given the tree
+    (parent [B, n_max], n_nodes [B]; logits [B, n_max, V]; chunk partials only), the
+    draft partials are computed only for the rows of nodes with children."""
     V = tgt_logits.shape[-1]
     R = tgt_logits.numel() // V
+    n_max = 0
+    if parent is not None or n_nodes is not None:
+        if parent is None or n_nodes is None or parent.dim() != 2:
+            raise ValueError("the tree needs parent [B, n_max] and n_nodes [B]")
+        n_max = parent.shape[1]
+        _check(parent, torch.int32, None, "parent")
+        _check(n_nodes, torch.int32, (parent.shape[0],), "n_nodes")
+        if parent.shape[0] * n_max != R:
+            raise ValueError("the tree's node rows must be the logit rows")
     _check(tgt_logits, torch.float32, None, "tgt_logits")
     _check(dft_logits, torch.float32, tuple(tgt_logits.shape), "dft_logits")
     for t, nm in ((tgt_max, "tgt_max"), (tgt_sumexp, "tgt_sumexp"), (dft_max, "dft_max"), (dft_sumexp, "dft_sumexp")):
@@ -318,8 +329,9 @@ def spec_tree_softmax_pair(tgt_logits, temperature, dft_logits, draft_temperatur
     _check_chunks(dft_chunk_max, dft_chunk_sum, R, V, "dft")
     _check(status, torch.int32, (1,), "status")
     _call("spec_tree_softmax_pair", _ptr(tgt_logits), float(temperature), _ptr(dft_logits), float(draft_temperature),
-          R, V, _ptr(tgt_max), _ptr(tgt_sumexp), _ptr(tgt_argmax), _ptr(tgt_chunk_max), _ptr(tgt_chunk_sum),
-          _ptr(dft_max), _ptr(dft_sumexp), _ptr(dft_chunk_max), _ptr(dft_chunk_sum), _ptr(workspace),
+          R, V, _ptr(parent), _ptr(n_nodes), n_max, _ptr(tgt_max), _ptr(tgt_sumexp), _ptr(tgt_argmax),
+          _ptr(tgt_chunk_max), _ptr(tgt_chunk_sum), _ptr(dft_max), _ptr(dft_sumexp), _ptr(dft_chunk_max),
+          _ptr(dft_chunk_sum), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream))
 
 

@@ -664,7 +664,8 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(RejArgs a, SampWs w
   const uint64_t kids = __ballot(is_kid);
   const int k = __popcll(kids);
   const bool node_ok = verdict == 0 && n < nb;
-  const bool row_ok = s_ok[0] && s_ok[1];
+  // a leaf needs only its target row: its draft row takes no part (parts C and G)
+  const bool row_ok = s_ok[0] && (k == 0 || s_ok[1]);
   const float mt = s_m[0], md = s_m[1];
   const double izt = row_ok ? 1.0 / s_z[0] : 0.0, izd = row_ok ? 1.0 / s_z[1] : 0.0;
   const bool internal = node_ok && row_ok && k > 0;

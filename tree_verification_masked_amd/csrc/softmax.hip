@@ -39,6 +39,11 @@ struct SmSet {
   double* csum;     // [rows, nch]  chunk sums of exp((l - m_c)/T)
   int32_t* carg;    // [rows, nch]  workspace
   int32_t* cbad;    // [rows, nch]  workspace
+  // draft rows of a step given its tree: only the rows of nodes with children are
+  // needed (a leaf's draft row takes no part; tree notes, parts C and G)
+  const int32_t* parent;   // [batch, n_max] or null
+  const int32_t* n_nodes;  // [batch]
+  int32_t n_max;
 };
 
 // Workspace of one logit array: argmax / bad flags per chunk, and the chunk maxima
@@ -95,6 +100,12 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSe
   if (second) blk -= blocks_a;
   const int chunk = (int)(blk % nch);
   const int64_t row = blk / nch;
+  if (S.parent) {  // a node without children (or a padding slot): its row is not needed
+    const int64_t b = row / S.n_max;
+    const int n = (int)(row % S.n_max), nb = S.n_nodes[b];
+    const int par = lane < S.n_max ? S.parent[b * S.n_max + lane] : -2;
+    if (n >= nb || !__ballot(lane > n && lane < nb && par == n)) return;  // the same in every wave
+  }
   const float* src = S.logits + row * (int64_t)vocab;
   const int c0 = chunk * kChunk;
 
@@ -310,7 +321,8 @@ extern "C" size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vo
 }
 
 extern "C" int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
-                                      float draft_temperature, int64_t rows, int32_t vocab, float* tgt_max,
+                                      float draft_temperature, int64_t rows, int32_t vocab, const int32_t* parent,
+                                      const int32_t* n_nodes, int32_t n_max, float* tgt_max,
                                       float* tgt_sumexp, int32_t* tgt_argmax, float* tgt_chunk_max,
                                       double* tgt_chunk_sum, float* dft_max, float* dft_sumexp, float* dft_chunk_max,
                                       double* dft_chunk_sum, void* workspace, size_t workspace_bytes,
@@ -326,11 +338,16 @@ extern "C" int spec_tree_softmax_pair(const float* tgt_logits, float temperature
   if (rows < 1 || vocab < 1) return SPEC_ERR_INVALID_ARG;
   if (!(temperature > 0.0f) || isinf(temperature) || !(draft_temperature > 0.0f) || isinf(draft_temperature))
     return SPEC_ERR_INVALID_ARG;
+  if ((parent == nullptr) != (n_nodes == nullptr)) return SPEC_ERR_INVALID_ARG;  // the tree: both or neither
+  if (parent && (row_out || n_max < 1 || n_max > 64 || rows % n_max)) return SPEC_ERR_INVALID_ARG;
   const size_t one = sm_set_bytes(rows, vocab);
   if (!workspace || workspace_bytes < 2 * one) return SPEC_ERR_WORKSPACE;
   SmSet A = make_set(tgt_logits, rows, temperature, tgt_max, tgt_sumexp, tgt_argmax);
   SmSet B = make_set(dft_logits, rows, draft_temperature, dft_max, dft_sumexp, nullptr);
   sm_set_carve((char*)workspace, rows, vocab, &A, tgt_chunk_max, tgt_chunk_sum);
   sm_set_carve((char*)workspace + one, rows, vocab, &B, dft_chunk_max, dft_chunk_sum);
+  B.parent = parent;
+  B.n_nodes = n_nodes;
+  B.n_max = n_max;
   return launch_stats(A, B, vocab, status, (hipStream_t)stream, row_out);
 }

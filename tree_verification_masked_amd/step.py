@@ -118,9 +118,10 @@ class VerifyStep:
                               stream=stream, parent=d["parent"] if self.fold_mask else None)
 
     def softmax(self, stream=None, tgt=None, dft=None, rows=False):
-        """T > 0: the chunk partials of both logit arrays (one launch); with rows, the
-        row statistics as well (a second, merging launch the sampler does not need).
-        T = 0: the target rows' maximum and argmax."""
+        """T > 0: the chunk partials of both logit arrays (one launch), the draft rows
+        only of nodes with children (the sampler reads no others); with rows, the row
+        statistics of every row as well (a second, merging launch the sampler does not
+        need).  T = 0: the target rows' maximum and argmax."""
         d = self.d
         tgt = d["tgt_logits"] if tgt is None else tgt
         if self.T > 0:
@@ -129,7 +130,8 @@ class VerifyStep:
                                      self.targ if rows else None, self.tcmax, self.tcsum,
                                      self.dmax if rows else None, self.dsum if rows else None, self.sm_ws,
                                      status=self.status, stream=stream, dft_chunk_max=self.dcmax,
-                                     dft_chunk_sum=self.dcsum)
+                                     dft_chunk_sum=self.dcsum, parent=None if rows else d["parent"],
+                                     n_nodes=None if rows else d["n_nodes"])
         else:
             B.spec_tree_softmax(tgt, 0.0, self.tmax, self.tsum, self.targ, self.sm_ws, status=self.status,
                                 stream=stream)
