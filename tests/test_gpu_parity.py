@@ -789,6 +789,7 @@ def _rows_sample(inp, n_rows, rng):
                 rows.add((b, i, int(rng.integers(inp["hq"]))))
         if nb[b] < inp["n_max"]:
             rows.add((b, inp["n_max"] - 1, 0))  # padding row: must be zero
+    n_rows = min(n_rows, inp["B"] * inp["n_max"] * inp["hq"])  # (a small case has fewer rows in all)
     while len(rows) < n_rows:
         b = int(rng.integers(inp["B"]))
         rows.add((b, int(rng.integers(inp["n_max"])), int(rng.integers(inp["hq"]))))
