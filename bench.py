@@ -112,9 +112,11 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--streams", choices=("auto", "one", "two"), default="auto",
-                    help="one: the whole step on one stream; two: the attention on a second stream beside the "
-                         "logit pass and the sampler; auto: time a short run of each, keep the faster")
+    ap.add_argument("--streams", choices=("auto", "one", "two", "step"), default="auto",
+                    help="one: the separate calls on one stream; two: the attention on a second stream beside the "
+                         "logit pass and the sampler; step: the single spec_tree_verify_step call (the attention's "
+                         "split combine inside the logit pass's launch); auto: time a short run of each, keep the "
+                         "fastest")
     ap.add_argument("--overlap", action="store_true", help="the same as --streams two")
     ap.add_argument("--fork", choices=("start", "after_softmax"), default="start",
                     help="with --overlap: where the second stream branches off, at the step's start or after "
@@ -698,6 +700,8 @@ def main():
         s = VerifyStep(dev)
         if mode == "two":
             s.overlap(fork=args.fork)  # the attention on a second stream
+        elif mode == "step":
+            s.one_call()
         s.compile(replicas, stream)  # the timed steps replay recorded calls: less host time per step
         return s
 
@@ -705,7 +709,7 @@ def main():
     probe = None
     if mode == "auto":  # a short timed run of each form; the timed region uses the faster
         probe = {}
-        for m in ("one", "two"):
+        for m in ("one", "two", "step"):
             ms, _ = time_steps(make_step(m), replicas, stream, 50, 10)
             probe[m] = round(ms * 1e3, 2)
         mode = min(probe, key=probe.get)
@@ -753,7 +757,8 @@ def main():
             "workload": synth.CONFIGS[args.config], "batch": inp["B"], "n_nodes": int(inp["n_nodes"].max()),
             "ctx": int(inp["ctx_len"].max()), "hq": inp["hq"], "hkv": inp["hkv"], "head_dim": inp["d"],
             "vocab": inp["V"], "T": inp["T"], "replicas": args.replicas,
-            "launch": "one stream (no graph)" if step.side is None else
+            "launch": "one spec_tree_verify_step call: attention, logit pass with the split combine, sampler "
+                      "(one stream, no graph)" if step.composite else "one stream (no graph)" if step.side is None else
                       ("two streams: the attention (ancestor rows built in its launch) beside softmax + sampling "
                        "(no graph)" if step.fork == "start"
                        else "two streams: the attention beside the sampling, after the logit pass (no graph)"),

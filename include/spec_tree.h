@@ -8,6 +8,8 @@
  *   spec_tree_softmax         per-node vocabulary softmax statistics (target, draft)
  *   spec_tree_reject_sample   lossless tree rejection sampling (or greedy at T = 0)
  *   spec_accept_path          longest accepted root-to-leaf path plus the bonus token
+ *   spec_tree_verify_step     the whole step above in three launches (attention, logit
+ *                             pass with the attention's split combine, sampler)
  *   spec_tree_kv_commit       keep the accepted path's K/V, free the rejected tree slots
  *   spec_tree_build_init      start EAGLE-2 draft trees at their roots
  *   spec_tree_expand          one EAGLE-2 expand round from the frontier's draft rows
@@ -312,6 +314,81 @@ void spec_tree_reject_sample_set_wait_limit(uint32_t polls);
 int spec_accept_path(const int32_t* accepted_child, const int32_t* term_token, const int32_t* tokens,
                      const int32_t* n_nodes, int32_t batch, int32_t n_max, int32_t* path_nodes, int32_t* out_tokens,
                      int32_t* accept_len, int32_t* status, void* stream);
+
+/*
+ * The whole verification step (tree notes, part D.2: the tree-masked target pass,
+ * then the verification of part C over every node's row) in one call, with the
+ * results of spec_tree_attention (given the parent links), spec_tree_softmax_pair
+ * given the tree (T > 0; spec_tree_softmax with row statistics of the target rows
+ * at T = 0) and spec_tree_reject_sample with the path outputs, made by the same
+ * kernels bit for bit.  Three launches instead of four: the attention's split
+ * combine (when its plan has more than one key split) runs as extra workgroups of
+ * the logit pass's launch, after its chunks.  The attention output is therefore
+ * complete only once the whole call has run.
+ * Fields of SpecTreeStepArgs (every pointer a device pointer; sizes and layouts
+ * those of the separate entry points):
+ *   tree      parent, tokens [batch, n_max], n_nodes [batch]
+ *   attention q, k, v, dtype, block_table, page_size, kv_capacity, n_pages,
+ *             ctx_len, hq, hkv, head_dim, max_kv_len, scale, attn_out, and its
+ *             workspace (spec_tree_attention_workspace_size)
+ *   logits    tgt_logits, dft_logits (T > 0) [batch, n_max, vocab]; temperature,
+ *             draft_temperature; T > 0: the chunk partials tgt_chunk_max,
+ *             tgt_chunk_sum, dft_chunk_max, dft_chunk_sum [batch * n_max, nch];
+ *             T = 0: tgt_max, tgt_sumexp, tgt_argmax [batch * n_max]; the logit
+ *             workspace (spec_tree_softmax_pair_workspace_size of batch * n_max rows)
+ *   sampling  u_accept, u_sample (T > 0); accepted_child, term_token, path_nodes,
+ *             out_tokens [batch, n_max], accept_len [batch]; the sampler workspace
+ *             (spec_tree_reject_sample_workspace_size, T > 0)
+ *   status    as for every entry point
+ * Host errors: a null `args`, and those of the three calls; they are checked call by
+ * call, so an error of the logit pass or the sampler can return after the attention
+ * was launched: then its combine has been launched on its own, and the attention
+ * output is complete, but the sampling outputs are not written.
+ */
+typedef struct SpecTreeStepArgs {
+  const int32_t* parent;
+  const int32_t* tokens;
+  const int32_t* n_nodes;
+  int32_t batch, n_max;
+  const void* q;
+  const void* k;
+  const void* v;
+  int32_t dtype;
+  const int32_t* block_table;
+  int32_t page_size, kv_capacity, n_pages;
+  const int32_t* ctx_len;
+  int32_t hq, hkv, head_dim, max_kv_len;
+  float scale;
+  void* attn_out;
+  void* attn_workspace;
+  size_t attn_workspace_bytes;
+  const float* tgt_logits;
+  const float* dft_logits;
+  int32_t vocab;
+  float temperature, draft_temperature;
+  float* tgt_chunk_max;
+  double* tgt_chunk_sum;
+  float* dft_chunk_max;
+  double* dft_chunk_sum;
+  float* tgt_max;
+  float* tgt_sumexp;
+  int32_t* tgt_argmax;
+  void* softmax_workspace;
+  size_t softmax_workspace_bytes;
+  const float* u_accept;
+  const float* u_sample;
+  int32_t* accepted_child;
+  int32_t* term_token;
+  int32_t* path_nodes;
+  int32_t* out_tokens;
+  int32_t* accept_len;
+  void* sample_workspace;
+  size_t sample_workspace_bytes;
+  int32_t* status;
+} SpecTreeStepArgs;
+int spec_tree_verify_step(const SpecTreeStepArgs* args, void* stream);
+/* sizeof(SpecTreeStepArgs) as the library was compiled (a binding's layout check). */
+size_t spec_tree_step_args_size(void);
 
 /*
  * KV commit and rollback after the path (fal.ai page, "EAGLE-4 verification trees

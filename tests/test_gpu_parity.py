@@ -987,7 +987,6 @@ def test_full_step(cfg, T):
     ref_t = oracle.softmax(inp["tgt_logits"], inp["T"], want_probs=False)
     if inp["T"] > 0:
         # the step's logit pass leaves chunk partials only: merged on the host they
-        # give the row statistics
         # give the row statistics; the draft rows only at nodes with children (the
         # others are left untouched: reading 25)
         ref_d = oracle.softmax(inp["dft_logits"], inp["Td"], want_probs=False)
@@ -1013,6 +1012,65 @@ def test_full_step(cfg, T):
     sep = st.results()
     for k in fused:
         assert np.array_equal(fused[k], sep[k]), k
+
+
+_STEP_KEYS = ("attn", "accepted_child", "term_token", "path_nodes", "out_tokens", "accept_len", "status")
+
+
+def _step_keys(T):
+    return _STEP_KEYS + (("tcmax", "tcsum", "dcmax", "dcsum") if T > 0 else ("tmax", "tsum", "targ"))
+
+
+@pytest.mark.parametrize("cfg,T", [(1, 1.0), (2, 1.0), (2, 0.0), (3, None), (4, 1.0), (4, 0.0), (5, 1.0)])
+def test_verify_step_equals_separate_calls(cfg, T):
+    """spec_tree_verify_step (three launches: the attention's split combine runs in
+    the logit pass's launch) gives, bit for bit, what the separate calls give, over
+    consecutive steps on rotated inputs; its first step also against the oracle."""
+    say("verify step", cfg, T)
+    inp = support.make_config(cfg, seed=13, T=T)
+    d = to_device(inp)
+    big = [k for k in ("q", "k", "v", "tgt_logits", "dft_logits") if k in d]
+    reps = [{k: d[k].clone() for k in big} for _ in range(2)]
+    reps[1]["q"].mul_(-1)
+    reps[1]["tgt_logits"].add_(0.25 * torch.randn_like(reps[1]["tgt_logits"]))
+    keys = _step_keys(inp["T"])
+    sep = VerifyStep(d)
+    want = []
+    for r in reps:
+        sep.run(replica=r)
+        want.append({k: v for k, v in sep.results().items() if k in keys})
+    one = VerifyStep(d).one_call()
+    for rnd in range(2):
+        for i, r in enumerate(reps):
+            one.run(replica=r)
+            got = one.results()
+            for k in keys:
+                assert np.array_equal(got[k], want[i][k]), (rnd, i, k)
+    one.run(replica={k: d[k] for k in big})
+    got = one.results()
+    assert got["status"][0] == 0
+    anc_r, _, _, _ = oracle.mask(inp["parent"], inp["n_nodes"])
+    _check_attention(inp, got["attn"], anc_r, n_rows=256, seed=cfg)
+    _compare_sampling(got, _oracle_sampling(inp), inp, max_exempt=max(1, inp["B"] // 4))
+
+
+def test_verify_step_one_split_plan():
+    """A batch whose attention plan has one key split: its workgroups write the output
+    rows, there is no combine, and the logit pass's launch has no extra workgroups."""
+    say("verify step, one split")
+    inp = _custom_attention_case(np.random.default_rng(21), 40, 12, 32, 8, 128, [(41 * i) % 300 for i in range(40)],
+                                 [1 + (7 * i) % 12 for i in range(40)], True)
+    d = to_device(inp)
+    sep = VerifyStep(d)
+    sep.run()
+    want = sep.results()
+    one = VerifyStep(d).one_call()
+    one.run()
+    got = one.results()
+    for k in _step_keys(0.0):
+        assert np.array_equal(got[k], want[k]), k
+    anc_r, _, _, _ = oracle.mask(inp["parent"], inp["n_nodes"])
+    _check_attention(inp, got["attn"], anc_r, n_rows=256)
 
 
 @pytest.mark.parametrize("cfg,fork", [(2, "start"), (2, "after_softmax"), (4, "after_softmax")])
@@ -1049,7 +1107,7 @@ def test_two_stream_step_equals_one_stream_step(cfg, fork):
                 assert np.array_equal(g, want[i][k]), (rnd, i, k)
 
 
-@pytest.mark.parametrize("cfg,overlap", [(2, True), (2, False), (4, True)])
+@pytest.mark.parametrize("cfg,overlap", [(2, True), (2, False), (4, True), (2, "one_call"), (3, "one_call")])
 def test_recorded_step_replay_equals_run(cfg, overlap):
     """VerifyStep.compile() records each replica's library calls; run_fast(i) replays
     them and must give, bit for bit, what run() gives on the same replica."""
@@ -1067,7 +1125,9 @@ def test_recorded_step_replay_equals_run(cfg, overlap):
         ref.run(replica=r)
         want.append({k: v for k, v in ref.results().items() if k in keys})
     st = VerifyStep(d)
-    if overlap:
+    if overlap == "one_call":
+        st.one_call()
+    elif overlap:
         st.overlap()
     st.compile(reps)
     for rnd in range(2):

@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding and header disagree"
@@ -158,6 +158,28 @@ def test_host_errors_reject(lib):
     assert binding.spec_tree_reject_sample_workspace_size(1, 65, 4096) == 0
     ws = binding.spec_tree_reject_sample_workspace_size(1, 60, 128256)
     assert 60 * 4 * 32 * 8 < ws < 128 * 1024  # each node's level words: two levels x 32 chunks x (P, Q)
+
+
+def test_host_errors_verify_step(lib):
+    """The argument struct's layout agrees with the library's, and the composite step
+    refuses bad arguments before launching anything (every case below fails in the
+    attention's checks, the first of the three calls)."""
+    assert binding.spec_tree_step_args_size() == ctypes.sizeof(binding.SpecTreeStepArgs)
+    f = lib.spec_tree_verify_step
+    assert f(None, None) == -1
+    a = binding.SpecTreeStepArgs(parent=P, tokens=P, n_nodes=P, batch=1, n_max=8, q=P, k=P, v=P, dtype=1,
+                                 kv_capacity=4096, ctx_len=P, hq=32, hkv=8, head_dim=128, max_kv_len=4096,
+                                 scale=0.088, attn_out=P, attn_workspace=None, attn_workspace_bytes=0,
+                                 tgt_logits=P, vocab=1000, temperature=1.0, draft_temperature=1.0)
+    assert f(ctypes.addressof(a), None) == -5  # the attention's workspace
+    a.q = None
+    assert f(ctypes.addressof(a), None) == -1
+    a.q = P
+    a.head_dim = 96
+    assert f(ctypes.addressof(a), None) == -2
+    a.head_dim = 128
+    a.parent = None  # the step builds the ancestor rows from the parent links
+    assert f(ctypes.addressof(a), None) == -1
 
 
 def test_host_errors_kv_commit(lib):

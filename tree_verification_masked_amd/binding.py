@@ -54,6 +54,8 @@ _SIGNATURES = {
                                 _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP],
     "spec_tree_reject_sample_set_wait_limit": [ctypes.c_uint32],
     "spec_accept_path": [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
+    "spec_tree_verify_step": [_VP, _VP],  # (const SpecTreeStepArgs*, stream)
+    "spec_tree_step_args_size": [],
     "spec_tree_kv_commit": [_VP, _VP, _I32, _I32, _I64, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
                             _I32, _VP, _VP, _VP, _VP],
     "spec_tree_build_init": [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
@@ -64,6 +66,7 @@ _SIGNATURES = {
     "spec_tree_version": [],
 }
 _RESTYPES = {
+    "spec_tree_step_args_size": _SZ,
     "spec_tree_softmax_chunk": _I32,
     "spec_tree_attention_workspace_size": _SZ,
     "spec_tree_softmax_workspace_size": _SZ,
@@ -201,8 +204,9 @@ def spec_tree_mask_build(parent, n_nodes, anc_mask, child_mask, depth, status=No
 
 def _attention_args(q, k, v, ctx_len, n_nodes, anc_mask, out, hkv, max_kv_len, block_table, page_size, n_pages,
                     scale, status, parent):
-    """The argument list shared by spec_tree_attention and spec_tree_attention_noalloc
-    (everything before their workspace / status arguments), after the checks.  The
+    """The argument list shared by spec_tree_attention, spec_tree_attention_noalloc and
+    the attention fields of spec_tree_verify_step (everything before their workspace /
+    status arguments), after the checks.  The
     ancestor sets come from exactly one of anc_mask and parent."""
     B, n_max, hq, D = q.shape
     if q.dtype == torch.bfloat16:
@@ -377,6 +381,77 @@ def reject_sample_diagnostics(workspace) -> dict:
 
 def spec_tree_reject_sample_set_wait_limit(polls: int) -> None:
     lib().spec_tree_reject_sample_set_wait_limit(int(polls))
+
+
+class SpecTreeStepArgs(ctypes.Structure):
+    """The C struct SpecTreeStepArgs of spec_tree.h, field for field."""
+    _fields_ = [
+        ("parent", _VP), ("tokens", _VP), ("n_nodes", _VP), ("batch", _I32), ("n_max", _I32),
+        ("q", _VP), ("k", _VP), ("v", _VP), ("dtype", _I32), ("block_table", _VP), ("page_size", _I32),
+        ("kv_capacity", _I32), ("n_pages", _I32), ("ctx_len", _VP), ("hq", _I32), ("hkv", _I32), ("head_dim", _I32),
+        ("max_kv_len", _I32), ("scale", _F32), ("attn_out", _VP), ("attn_workspace", _VP),
+        ("attn_workspace_bytes", _SZ), ("tgt_logits", _VP), ("dft_logits", _VP), ("vocab", _I32),
+        ("temperature", _F32), ("draft_temperature", _F32), ("tgt_chunk_max", _VP), ("tgt_chunk_sum", _VP),
+        ("dft_chunk_max", _VP), ("dft_chunk_sum", _VP), ("tgt_max", _VP), ("tgt_sumexp", _VP), ("tgt_argmax", _VP),
+        ("softmax_workspace", _VP), ("softmax_workspace_bytes", _SZ), ("u_accept", _VP), ("u_sample", _VP),
+        ("accepted_child", _VP), ("term_token", _VP), ("path_nodes", _VP), ("out_tokens", _VP), ("accept_len", _VP),
+        ("sample_workspace", _VP), ("sample_workspace_bytes", _SZ), ("status", _VP),
+    ]
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def spec_tree_verify_step(q, k, v, ctx_len, attn_out, attn_workspace, tgt_logits, temperature, tokens, parent,
+                          n_nodes, accepted_child, term_token, path_nodes, out_tokens, accept_len, softmax_workspace,
+                          *, hkv, max_kv_len, block_table=None, page_size=0, n_pages=0, scale=None, dft_logits=None,
+                          draft_temperature=1.0, tgt_chunk_max=None, tgt_chunk_sum=None, dft_chunk_max=None,
+                          dft_chunk_sum=None, tgt_max=None, tgt_sumexp=None, tgt_argmax=None, u_accept=None,
+                          u_sample=None, sample_workspace=None, status=None, stream=None):
+    """The whole step in one call (attention given the parent links, the logit pass
+    with the attention's split combine in its launch, the sampler with the accepted
+    path).  T > 0: the chunk partials, draft logits, uniforms and sampler workspace;
+    T = 0: tgt_max, tgt_sumexp, tgt_argmax.  Returns the argument struct, which must
+    stay alive while a recorded copy of the call may be replayed."""
+    (qp, kp, vp, dtype, btp, page_size, kv_capacity, n_pages, ctxp, nnp, parp, _, B, n_max, hq, hkv, D, max_kv_len,
+     scale, outp) = _attention_args(q, k, v, ctx_len, n_nodes, None, attn_out, hkv, max_kv_len, block_table,
+                                    page_size, n_pages, scale, status, parent)
+    V = tgt_logits.shape[-1]
+    R = B * n_max
+    _check(tgt_logits, torch.float32, (B, n_max, V), "tgt_logits")
+    _check(dft_logits, torch.float32, (B, n_max, V), "dft_logits")
+    for t, nm in ((tokens, "tokens"), (accepted_child, "accepted_child"), (term_token, "term_token"),
+                  (path_nodes, "path_nodes"), (out_tokens, "out_tokens")):
+        _check(t, torch.int32, (B, n_max), nm)
+    _check(accept_len, torch.int32, (B,), "accept_len")
+    _check(u_accept, torch.float32, (B, n_max), "u_accept")
+    _check(u_sample, torch.float32, (B, n_max), "u_sample")
+    _check_rows(tgt_max, torch.float32, R, "tgt_max")
+    _check_rows(tgt_sumexp, torch.float32, R, "tgt_sumexp")
+    _check_rows(tgt_argmax, torch.int32, R, "tgt_argmax")
+    _check_chunks(tgt_chunk_max, tgt_chunk_sum, R, V, "tgt")
+    _check_chunks(dft_chunk_max, dft_chunk_sum, R, V, "dft")
+    a = SpecTreeStepArgs(
+        parent=parp, tokens=_ptr(tokens), n_nodes=nnp, batch=B, n_max=n_max, q=qp, k=kp, v=vp, dtype=dtype,
+        block_table=btp, page_size=page_size, kv_capacity=kv_capacity, n_pages=n_pages, ctx_len=ctxp, hq=hq,
+        hkv=hkv, head_dim=D, max_kv_len=max_kv_len, scale=scale, attn_out=outp, attn_workspace=_ptr(attn_workspace),
+        attn_workspace_bytes=_nbytes(attn_workspace), tgt_logits=_ptr(tgt_logits), dft_logits=_ptr(dft_logits),
+        vocab=V, temperature=float(temperature), draft_temperature=float(draft_temperature),
+        tgt_chunk_max=_ptr(tgt_chunk_max), tgt_chunk_sum=_ptr(tgt_chunk_sum), dft_chunk_max=_ptr(dft_chunk_max),
+        dft_chunk_sum=_ptr(dft_chunk_sum), tgt_max=_ptr(tgt_max), tgt_sumexp=_ptr(tgt_sumexp),
+        tgt_argmax=_ptr(tgt_argmax), softmax_workspace=_ptr(softmax_workspace),
+        softmax_workspace_bytes=_nbytes(softmax_workspace), u_accept=_ptr(u_accept), u_sample=_ptr(u_sample),
+        accepted_child=_ptr(accepted_child), term_token=_ptr(term_token), path_nodes=_ptr(path_nodes),
+        out_tokens=_ptr(out_tokens), accept_len=_ptr(accept_len), sample_workspace=_ptr(sample_workspace),
+        sample_workspace_bytes=_nbytes(sample_workspace), status=_ptr(status))
+    _call("spec_tree_verify_step", ctypes.addressof(a), _stream(stream))
+    return a
+
+
+def spec_tree_step_args_size() -> int:
+    """sizeof(SpecTreeStepArgs) as the library was compiled."""
+    return int(lib().spec_tree_step_args_size())
 
 
 def spec_accept_path(accepted_child, term_token, tokens, n_nodes, path_nodes, out_tokens, accept_len, status=None,

@@ -15,7 +15,8 @@
 // device-wide before signalling; on MI355X that costs more than the extra launch.)
 // One launch can cover two logit arrays (target and draft rows, each with its own
 // temperature).
-#include "common.hpp"
+#include "attn_combine.hpp"
+#include "internal.hpp"
 
 namespace spectree {
 
@@ -88,13 +89,22 @@ __device__ inline void wave_best(float& m, int& a) {
   a = lane63_i(a);
 }
 
-template <bool kVec>
+// kCombD > 0: the workgroups after the chunks finish an attention call's split
+// combine (head size kCombD, element type CombT), one output row per wave.
+template <bool kVec, int kCombD, typename CombT>
 __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSet B, int32_t vocab, int nch,
-                                                                   int32_t* status) {
+                                                                   int32_t* status, AttnArgs comb_args, CombT* comb_out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   int64_t blk = blockIdx.x;
-  const int64_t blocks_a = A.rows * nch;
+  const int64_t blocks_a = A.rows * nch, blocks_ab = (A.rows + B.rows) * nch;
+  if constexpr (kCombD > 0) {
+    if (blk >= blocks_ab) {
+      // four splits per load round: the chunk workgroups' register budget
+      attn_combine_row<kCombD, CombT, 4>(comb_args, comb_out, (blk - blocks_ab) * 4 + wid);
+      return;
+    }
+  }
   const bool second = blk >= blocks_a;
   const SmSet& S = second ? B : A;
   if (second) blk -= blocks_a;
@@ -259,20 +269,37 @@ inline SmSet make_set(const float* logits, int64_t rows, float t, float* mx, flo
   return s;
 }
 
-// The chunk pass, then (merge) the row merge.
+// The chunk pass (followed, in the same launch, by the rows of `comb` when given),
+// then (merge) the row merge.
 inline int launch_stats(const SmSet& A, const SmSet& B, int32_t vocab, int32_t* status, hipStream_t st,
-                        bool merge = true) {
+                        bool merge, const AttnCombine* comb) {
   const int nch = sm_chunks(vocab);
-  const int64_t blocks = (A.rows + B.rows) * nch;
+  AttnCombine c{};
+  if (comb) c = *comb;
+  const int64_t blocks = (A.rows + B.rows) * nch + (c.rows + 3) / 4;
   if (blocks * kSmThreads > 0xffffffffLL) return SPEC_ERR_UNSUPPORTED;  // a dispatch counts work-items in 32 bits
   bool vec = vocab % 4 == 0 && (((uintptr_t)A.logits & 15) == 0);
   if (B.rows) vec = vec && (((uintptr_t)B.logits & 15) == 0);
-  if (vec)
-    hipLaunchKernelGGL(softmax_stats_kernel<true>, dim3((unsigned)blocks), dim3(kSmThreads), 0, st, A, B, vocab, nch,
-                       status);
-  else
-    hipLaunchKernelGGL(softmax_stats_kernel<false>, dim3((unsigned)blocks), dim3(kSmThreads), 0, st, A, B, vocab,
-                       nch, status);
+  const dim3 g((unsigned)blocks), blk(kSmThreads);
+  // the instance without the combine rows keeps the plain pass's registers
+  const int form = c.rows <= 0 ? 0 : c.dtype == SPEC_BF16 ? (c.head_dim == 128 ? 1 : 2) : (c.head_dim == 128 ? 3 : 4);
+  if (vec) {
+    switch (form) {
+      case 0: hipLaunchKernelGGL((softmax_stats_kernel<true, 0, float>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (float*)nullptr); break;
+      case 1: hipLaunchKernelGGL((softmax_stats_kernel<true, 128, __bf16>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (__bf16*)c.out); break;
+      case 2: hipLaunchKernelGGL((softmax_stats_kernel<true, 64, __bf16>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (__bf16*)c.out); break;
+      case 3: hipLaunchKernelGGL((softmax_stats_kernel<true, 128, float>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (float*)c.out); break;
+      default: hipLaunchKernelGGL((softmax_stats_kernel<true, 64, float>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (float*)c.out); break;
+    }
+  } else {
+    switch (form) {
+      case 0: hipLaunchKernelGGL((softmax_stats_kernel<false, 0, float>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (float*)nullptr); break;
+      case 1: hipLaunchKernelGGL((softmax_stats_kernel<false, 128, __bf16>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (__bf16*)c.out); break;
+      case 2: hipLaunchKernelGGL((softmax_stats_kernel<false, 64, __bf16>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (__bf16*)c.out); break;
+      case 3: hipLaunchKernelGGL((softmax_stats_kernel<false, 128, float>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (float*)c.out); break;
+      default: hipLaunchKernelGGL((softmax_stats_kernel<false, 64, float>), g, blk, 0, st, A, B, vocab, nch, status, c.a, (float*)c.out); break;
+    }
+  }
   SPEC_LAUNCH_CHECK();
   if (!merge) return SPEC_OK;  // invalid rows were reported by the chunk pass
   const int64_t rows = A.rows + B.rows;
@@ -290,11 +317,10 @@ extern "C" size_t spec_tree_softmax_workspace_size(int64_t rows, int32_t vocab) 
   return spectree::sm_set_bytes(rows, vocab);
 }
 
-extern "C" int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float temperature,
-                                 float* row_max, float* row_sumexp, int32_t* row_argmax, float* probs,
-                                 float* chunk_max, double* chunk_sum, void* workspace, size_t workspace_bytes,
-                                 int32_t* status, void* stream) {
-  using namespace spectree;
+namespace spectree {
+int softmax_call(const float* logits, int64_t rows, int32_t vocab, float temperature, float* row_max,
+                 float* row_sumexp, int32_t* row_argmax, float* probs, float* chunk_max, double* chunk_sum,
+                 void* workspace, size_t workspace_bytes, int32_t* status, void* stream, const AttnCombine* comb) {
   if (!logits || !row_max || rows < 1 || vocab < 1) return SPEC_ERR_INVALID_ARG;
   if (!(temperature >= 0.0f) || isinf(temperature)) return SPEC_ERR_INVALID_ARG;
   const bool greedy = temperature == 0.0f;
@@ -303,7 +329,7 @@ extern "C" int spec_tree_softmax(const float* logits, int64_t rows, int32_t voca
   SmSet A = make_set(logits, rows, temperature, row_max, row_sumexp, row_argmax);
   sm_set_carve((char*)workspace, rows, vocab, &A, chunk_max, chunk_sum);
   SmSet B{};
-  const int rc = launch_stats(A, B, vocab, status, (hipStream_t)stream);
+  const int rc = launch_stats(A, B, vocab, status, (hipStream_t)stream, true, comb);
   if (rc != SPEC_OK) return rc;
   if (probs && !greedy) {
     if (rows > 65535) return SPEC_ERR_UNSUPPORTED;
@@ -314,20 +340,28 @@ extern "C" int spec_tree_softmax(const float* logits, int64_t rows, int32_t voca
   }
   return SPEC_OK;
 }
+}  // namespace spectree
+
+extern "C" int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float temperature,
+                                 float* row_max, float* row_sumexp, int32_t* row_argmax, float* probs,
+                                 float* chunk_max, double* chunk_sum, void* workspace, size_t workspace_bytes,
+                                 int32_t* status, void* stream) {
+  return spectree::softmax_call(logits, rows, vocab, temperature, row_max, row_sumexp, row_argmax, probs, chunk_max,
+                                chunk_sum, workspace, workspace_bytes, status, stream, nullptr);
+}
 
 extern "C" size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vocab) {
   if (rows < 1 || vocab < 1) return 0;
   return 2 * spectree::sm_set_bytes(rows, vocab);
 }
 
-extern "C" int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
-                                      float draft_temperature, int64_t rows, int32_t vocab, const int32_t* parent,
-                                      const int32_t* n_nodes, int32_t n_max, float* tgt_max,
-                                      float* tgt_sumexp, int32_t* tgt_argmax, float* tgt_chunk_max,
-                                      double* tgt_chunk_sum, float* dft_max, float* dft_sumexp, float* dft_chunk_max,
-                                      double* dft_chunk_sum, void* workspace, size_t workspace_bytes,
-                                      int32_t* status, void* stream) {
-  using namespace spectree;
+namespace spectree {
+int softmax_pair_call(const float* tgt_logits, float temperature, const float* dft_logits, float draft_temperature,
+                      int64_t rows, int32_t vocab, const int32_t* parent, const int32_t* n_nodes, int32_t n_max,
+                      float* tgt_max, float* tgt_sumexp, int32_t* tgt_argmax, float* tgt_chunk_max,
+                      double* tgt_chunk_sum, float* dft_max, float* dft_sumexp, float* dft_chunk_max,
+                      double* dft_chunk_sum, void* workspace, size_t workspace_bytes, int32_t* status, void* stream,
+                      const AttnCombine* comb) {
   if (!tgt_logits || !dft_logits) return SPEC_ERR_INVALID_ARG;
   const bool row_out = tgt_max || tgt_sumexp || dft_max || dft_sumexp;
   if (row_out && !(tgt_max && tgt_sumexp && dft_max && dft_sumexp)) return SPEC_ERR_INVALID_ARG;  // all or none
@@ -349,5 +383,19 @@ extern "C" int spec_tree_softmax_pair(const float* tgt_logits, float temperature
   B.parent = parent;
   B.n_nodes = n_nodes;
   B.n_max = n_max;
-  return launch_stats(A, B, vocab, status, (hipStream_t)stream, row_out);
+  return launch_stats(A, B, vocab, status, (hipStream_t)stream, row_out, comb);
+}
+}  // namespace spectree
+
+extern "C" int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
+                                      float draft_temperature, int64_t rows, int32_t vocab, const int32_t* parent,
+                                      const int32_t* n_nodes, int32_t n_max, float* tgt_max,
+                                      float* tgt_sumexp, int32_t* tgt_argmax, float* tgt_chunk_max,
+                                      double* tgt_chunk_sum, float* dft_max, float* dft_sumexp, float* dft_chunk_max,
+                                      double* dft_chunk_sum, void* workspace, size_t workspace_bytes,
+                                      int32_t* status, void* stream) {
+  return spectree::softmax_pair_call(tgt_logits, temperature, dft_logits, draft_temperature, rows, vocab, parent,
+                                     n_nodes, n_max, tgt_max, tgt_sumexp, tgt_argmax, tgt_chunk_max, tgt_chunk_sum,
+                                     dft_max, dft_sumexp, dft_chunk_max, dft_chunk_sum, workspace, workspace_bytes,
+                                     status, stream, nullptr);
 }

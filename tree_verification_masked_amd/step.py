@@ -10,8 +10,10 @@ and only issues the library calls, in order, on one stream:
     target rows at T = 0) -> spec_tree_reject_sample (which merges each row itself
     and writes the accepted path, the result of spec_accept_path)
 
-With ``fold_mask=False`` the step runs spec_tree_mask_build first and the attention
-reads its ancestor rows.  ``mask()`` and ``path()`` also run the standalone
+With ``one_call()`` the step is the single spec_tree_verify_step call: the same
+kernels in three launches, the attention's split combine running inside the logit
+pass's launch.  With ``fold_mask=False`` the step runs spec_tree_mask_build first
+and the attention reads its ancestor rows.  ``mask()`` and ``path()`` also run the standalone
 spec_tree_mask_build and spec_accept_path calls.
 
 The attention output is not an input of the sampling half (the target logits are
@@ -86,6 +88,7 @@ class VerifyStep:
         self.out_tokens = torch.zeros((Bn, n_max), **i32)
         self.accept_len = torch.zeros(Bn, **i32)
         self.side = None
+        self.composite = False
 
     def overlap(self, side_stream=None, fork="start"):
         """Run the attention (after the mask build when it is not folded) on
@@ -102,6 +105,31 @@ class VerifyStep:
             self.ev_fork, self.ev_join = torch.cuda.Event(), torch.cuda.Event()
             self.fork = fork
         return self
+
+    def one_call(self):
+        """Run the step as one spec_tree_verify_step call (on the caller's stream).
+        Needs the attention from the parent links and no second stream.  Returns self."""
+        assert self.with_attention and self.fold_mask and self.side is None
+        self.composite = True
+        return self
+
+    def verify_step(self, stream=None, replica=None):
+        """spec_tree_verify_step over this step's buffers; returns its argument struct."""
+        d, r = self.d, replica or {}
+        tgt = r.get("tgt_logits", d["tgt_logits"])
+        common = dict(hkv=d["hkv"], max_kv_len=d["max_kv_len"], block_table=d.get("block_table"),
+                      page_size=d.get("page_size", 0), n_pages=d.get("n_pages", 0), status=self.status, stream=stream)
+        if self.T > 0:
+            extra = dict(dft_logits=r.get("dft_logits", d["dft_logits"]), draft_temperature=self.Td,
+                         tgt_chunk_max=self.tcmax, tgt_chunk_sum=self.tcsum, dft_chunk_max=self.dcmax,
+                         dft_chunk_sum=self.dcsum, u_accept=d["u_accept"], u_sample=d["u_sample"],
+                         sample_workspace=self.rj_ws)
+        else:
+            extra = dict(tgt_max=self.tmax, tgt_sumexp=self.tsum, tgt_argmax=self.targ)
+        return B.spec_tree_verify_step(r.get("q", d["q"]), r.get("k", d["k"]), r.get("v", d["v"]), d["ctx_len"],
+                                       self.attn_out, self.attn_ws, tgt, self.T, d["tokens"], d["parent"],
+                                       d["n_nodes"], self.accepted_child, self.term_token, self.path_nodes,
+                                       self.out_tokens, self.accept_len, self.sm_ws, **common, **extra)
 
     # the individual stages -------------------------------------------------
     def mask(self, stream=None):
@@ -164,6 +192,9 @@ class VerifyStep:
         """The whole step.  ``replica`` (optional dict) swaps in another copy of the
         large inputs (q/k/v and logits) so that timed loops can rotate buffers."""
         r = replica or {}
+        if self.composite:
+            self._args = self.verify_step(stream, r)  # (kept alive until the next call)
+            return
         if self.side is not None:
             main = torch.cuda.current_stream() if stream is None else stream
             if self.fork == "after_softmax":
@@ -197,6 +228,7 @@ class VerifyStep:
         self._main = main
         self._plans = []
         self._replicas = list(replicas)  # keeps every recorded address valid
+        self._keep = []
         torch.cuda.synchronize()
         for r in replicas:
             if self.side is not None:
@@ -208,6 +240,10 @@ class VerifyStep:
                     self.softmax(main, r.get("tgt_logits"), r.get("dft_logits"))
                     self.reject(main, r.get("tgt_logits"), r.get("dft_logits"))
                 self._plans.append((list(side_calls), list(main_calls)))
+            elif self.composite:
+                with B.record_calls() as calls:
+                    self._keep.append(self.verify_step(main, r))  # the recorded call points at this struct
+                self._plans.append(([], list(calls)))
             else:
                 with B.record_calls() as calls:
                     self.run(main, r)
