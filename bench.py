@@ -739,6 +739,8 @@ def main():
     samp_us = st_mean[2] + st_mean[4] + st_mean[5]
     # one stream runs the parts in turn; two streams run the attention beside the sampling half
     crit_us = attn_us + branch_us if step.side is None else max(attn_us, branch_us)
+    if step.composite:  # one call on one stream: its three launches in turn are the whole step
+        crit_us = ms_per_step * 1e3
     hd = host_driven(step, replicas, args.steps)
     res = {
         "metric": METRIC,
@@ -771,6 +773,8 @@ def main():
         "step_bytes": step_b,
         "step_gbs": round(step_b / (ms_per_step * 1e-3) / 1e9, 1),
         "step_frac_of_hbm": round(step_b / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        # HBM bytes per single-call step from the counters (null for another form or stale counters)
+        "step_traffic": traffic.get("spec_tree_verify_step") if step.composite else None,
         "attn_gbs": round(attn_b / (attn_us * 1e-6) / 1e9, 1),
         "sampling_gbs": round(samp_b / (samp_us * 1e-6) / 1e9, 1),
         "stage_us": {n: round(float(v), 2) for n, v in zip(names, st_mean) if n != "-"},
@@ -794,7 +798,9 @@ def main():
         # the step's parts, each timed back to back on its own: one stream runs them in
         # turn; with two streams the attention runs beside the sampling half
         "critical_path": {
-            "branch": ("attention, then softmax_pair + reject_sample" if step.side is None else
+            "branch": ("spec_tree_verify_step: the attention kernel, the logit pass with the split combine, the "
+                       "sampler (the whole step)" if step.composite else
+                       "attention, then softmax_pair + reject_sample" if step.side is None else
                        "softmax_pair + reject_sample (the attention branch runs beside it)" if branch_us >= attn_us
                        else "attention (the sampling half runs beside it)"),
             "us": round(crit_us, 2),
