@@ -428,34 +428,32 @@ __global__ __launch_bounds__(64) void greedy_walk_kernel(RejArgs a) {
     else if (tid > 0 && (s_tok[tid] < 0 || s_tok[tid] >= a.vocab)) atomicOr(&s_bad, 2);
   }
   __syncthreads();
-  if (tid == 0) {
-    int verdict = !n_ok || (s_bad & 1) ? SPEC_ERR_BAD_TREE : (s_bad ? SPEC_ERR_BAD_INPUT : 0);
-    int cur = 0;
-    for (int step = 0; verdict == 0 && step < nb; ++step) {
-      if (isnan(s_max[cur])) {
-        verdict = SPEC_ERR_BAD_INPUT;
-        break;
-      }
-      const int am = s_arg[cur];
-      int acc = SPEC_NODE_NONE;
-      for (int c = cur + 1; c < nb; ++c)
-        if (s_par[c] == cur && s_tok[c] == am) {
-          acc = c;
-          break;
-        }
-      s_oacc[cur] = acc;
-      if (acc >= 0) {
-        cur = acc;
-        continue;
-      }
-      s_oterm[cur] = am;
+  // The walk, by the whole wavefront (every value below is the same in all lanes): the
+  // accepted child of node cur is its first child, by index, whose token is cur's
+  // target argmax, found with one ballot over the node slots.
+  int verdict = !n_ok || (s_bad & 1) ? SPEC_ERR_BAD_TREE : (s_bad ? SPEC_ERR_BAD_INPUT : 0);
+  const int my_par = s_par[tid], my_tok = s_tok[tid];
+  int cur = 0;
+  for (int step = 0; verdict == 0 && step < nb; ++step) {
+    if (isnan(s_max[cur])) {
+      verdict = SPEC_ERR_BAD_INPUT;
       break;
     }
-    if (verdict != 0) {
-      for (int i = 0; i < 64; ++i) s_oacc[i] = s_oterm[i] = SPEC_NODE_NOT_EVALUATED;
-      s_oacc[0] = SPEC_NODE_BAD_REQUEST;
-      report(a.status, verdict);
+    const int am = s_arg[cur];
+    const unsigned long long m = __ballot(tid > cur && tid < nb && my_par == cur && my_tok == am);
+    const int acc = m ? __ffsll(m) - 1 : SPEC_NODE_NONE;
+    if (tid == 0) s_oacc[cur] = acc;
+    if (acc >= 0) {
+      cur = acc;
+      continue;
     }
+    if (tid == 0) s_oterm[cur] = am;
+    break;
+  }
+  if (verdict != 0) {
+    s_oacc[tid] = tid == 0 ? SPEC_NODE_BAD_REQUEST : SPEC_NODE_NOT_EVALUATED;
+    s_oterm[tid] = SPEC_NODE_NOT_EVALUATED;
+    if (tid == 0) report(a.status, verdict);
   }
   __syncthreads();
   if (in) {
