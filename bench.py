@@ -554,7 +554,7 @@ def cost_table(args):
                                      "v": vf[:Bn, : ctx + N].clone(), "tgt_logits": pt["tgt_logits"].clone(),
                                      "dft_logits": pt["dft_logits"].clone()})
                 pt.update(q=replicas[0]["q"], k=replicas[0]["k"], v=replicas[0]["v"])
-                step = VerifyStep(pt).overlap()
+                step = VerifyStep(pt).one_call()
                 ms, st = time_steps(step, replicas, stream, args.steps, args.warmup)
                 rows.append({"batch": Bn, "ctx": ctx, "n_nodes": N, "step_us": round(ms * 1e3, 2),
                              "attention_us": round(float(st[1]), 2),
@@ -567,8 +567,9 @@ def cost_table(args):
                 torch.cuda.empty_cache()
     meta = {"what": "verify latency of one tree-verification step (one layer's attention, its ancestor rows built "
                     "from the parent links, + full-vocabulary sampling) on one MI355X, HIP events, inputs resident "
-                    "in HBM; the attention on a second stream beside the logit pass and the sampler; the attention "
-                    "and sampling columns come from a one-stream pass with events around each stage",
+                    "in HBM; the step is the single spec_tree_verify_step call (the attention's split combine in the "
+                    "logit pass's launch); the attention and sampling columns come from a pass of the separate calls "
+                    "with events around each stage",
             "workload": synth.CONFIGS[6], "T": inp["T"], "hq": hq, "hkv": hkv, "head_dim": d, "vocab": V,
             "steps": args.steps, "warmup": args.warmup, "seed": args.seed, "grid": COST_GRID,
             "command": " ".join(["python", "bench.py"] + sys.argv[1:])}
