@@ -217,6 +217,8 @@ int spec_tree_softmax(const float* logits, int64_t rows, int32_t vocab, float te
  *                   draft rows this computes.
  * Host errors (beyond spec_tree_softmax's): a tree with row statistics, n_max outside
  * [1, 64] or rows not a multiple of it, only one of parent / n_nodes.
+ * The workspace query also leaves room, at its end, for the per-request counters
+ * spec_tree_verify_step uses at T = 0 (left at zero by every call).
  */
 size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vocab);
 int spec_tree_softmax_pair(const float* tgt_logits, float temperature, const float* dft_logits,
@@ -323,8 +325,9 @@ int spec_accept_path(const int32_t* accepted_child, const int32_t* term_token, c
  * at T = 0) and spec_tree_reject_sample with the path outputs, made by the same
  * kernels bit for bit.  Three launches instead of four: the attention's split
  * combine (when its plan has more than one key split) runs as extra workgroups of
- * the logit pass's launch, after its chunks.  The attention output is therefore
- * complete only once the whole call has run.
+ * the logit pass's launch, after its chunks; at T = 0 the greedy walk of a request
+ * runs in the row merge's launch, by the wave that merges the request's last row.
+ * The attention output is therefore complete only once the whole call has run.
  * Fields of SpecTreeStepArgs (every pointer a device pointer; sizes and layouts
  * those of the separate entry points):
  *   tree      parent, tokens [batch, n_max], n_nodes [batch]
@@ -340,10 +343,12 @@ int spec_accept_path(const int32_t* accepted_child, const int32_t* term_token, c
  *             out_tokens [batch, n_max], accept_len [batch]; the sampler workspace
  *             (spec_tree_reject_sample_workspace_size, T > 0)
  *   status    as for every entry point
- * Host errors: a null `args`, and those of the three calls; they are checked call by
- * call, so an error of the logit pass or the sampler can return after the attention
- * was launched: then its combine has been launched on its own, and the attention
- * output is complete, but the sampling outputs are not written.
+ * Host errors: a null `args`, and those of the three calls; at T = 0 every check of
+ * the walk comes first (a workspace smaller than the query gives SPEC_ERR_WORKSPACE),
+ * otherwise they are checked call by call, so an error of the logit pass or the
+ * sampler can return after the attention was launched: then its combine has been
+ * launched on its own, and the attention output is complete, but the sampling outputs
+ * are not written.
  */
 typedef struct SpecTreeStepArgs {
   const int32_t* parent;

@@ -56,6 +56,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "greedy_walk.hpp"
 
 namespace spectree {
 
@@ -406,62 +407,7 @@ __device__ inline int pick_chunk(const double* s_chunk, int nch, double u, doubl
 
 
 // T == 0: one wavefront per request follows the target argmax.
-__global__ __launch_bounds__(64) void greedy_walk_kernel(RejArgs a) {
-  __shared__ int s_par[64], s_tok[64], s_arg[64], s_oacc[64], s_oterm[64], s_pn[64], s_ot[64];
-  __shared__ float s_max[64];
-  __shared__ int s_bad, s_len;
-  const int tid = threadIdx.x, b = blockIdx.x;
-  const int64_t base = (int64_t)b * a.n_max;
-  const int nb = a.n_nodes[b];
-  const bool n_ok = nb >= 1 && nb <= a.n_max;
-  const bool in = tid < a.n_max;
-  s_par[tid] = in ? a.parent[base + tid] : -2;
-  s_tok[tid] = in ? a.tokens[base + tid] : 0;
-  s_arg[tid] = in ? a.tgt_argmax[base + tid] : -1;
-  s_max[tid] = in ? a.tgt_max[base + tid] : 0.0f;
-  s_oacc[tid] = s_oterm[tid] = SPEC_NODE_NOT_EVALUATED;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  if (n_ok && tid < nb) {
-    const int p = s_par[tid];
-    if (tid == 0 ? p != -1 : (p < 0 || p >= tid)) atomicOr(&s_bad, 1);
-    else if (tid > 0 && (s_tok[tid] < 0 || s_tok[tid] >= a.vocab)) atomicOr(&s_bad, 2);
-  }
-  __syncthreads();
-  // The walk, by the whole wavefront (every value below is the same in all lanes): the
-  // accepted child of node cur is its first child, by index, whose token is cur's
-  // target argmax, found with one ballot over the node slots.
-  int verdict = !n_ok || (s_bad & 1) ? SPEC_ERR_BAD_TREE : (s_bad ? SPEC_ERR_BAD_INPUT : 0);
-  const int my_par = s_par[tid], my_tok = s_tok[tid];
-  int cur = 0;
-  for (int step = 0; verdict == 0 && step < nb; ++step) {
-    if (isnan(s_max[cur])) {
-      verdict = SPEC_ERR_BAD_INPUT;
-      break;
-    }
-    const int am = s_arg[cur];
-    const unsigned long long m = __ballot(tid > cur && tid < nb && my_par == cur && my_tok == am);
-    const int acc = m ? __ffsll(m) - 1 : SPEC_NODE_NONE;
-    if (tid == 0) s_oacc[cur] = acc;
-    if (acc >= 0) {
-      cur = acc;
-      continue;
-    }
-    if (tid == 0) s_oterm[cur] = am;
-    break;
-  }
-  if (verdict != 0) {
-    s_oacc[tid] = tid == 0 ? SPEC_NODE_BAD_REQUEST : SPEC_NODE_NOT_EVALUATED;
-    s_oterm[tid] = SPEC_NODE_NOT_EVALUATED;
-    if (tid == 0) report(a.status, verdict);
-  }
-  __syncthreads();
-  if (in) {
-    a.accepted_child[base + tid] = s_oacc[tid];
-    a.term_token[base + tid] = s_oterm[tid];
-  }
-  emit_path(a, b, s_oacc, s_oterm, s_tok, nb, s_pn, s_ot, &s_len);
-}
+__global__ __launch_bounds__(64) void greedy_walk_kernel(GreedyArgs g) { greedy_walk_wave<false>(g, blockIdx.x); }
 
 
 // ---------------------------------------------------------------------------
@@ -948,7 +894,9 @@ extern "C" int spec_tree_reject_sample(const float* tgt_logits, float temperatur
   a.status = status;
   hipStream_t st = (hipStream_t)stream;
   if (greedy) {
-    hipLaunchKernelGGL(greedy_walk_kernel, dim3((unsigned)batch), dim3(64), 0, st, a);
+    const GreedyArgs g{parent, tokens, n_nodes, tgt_max, tgt_argmax, n_max, vocab, accepted_child, term_token,
+                       path_nodes, out_tokens, accept_len, status};
+    hipLaunchKernelGGL(greedy_walk_kernel, dim3((unsigned)batch), dim3(64), 0, st, g);
     SPEC_LAUNCH_CHECK();
     return SPEC_OK;
   }

@@ -16,6 +16,7 @@
 // One launch can cover two logit arrays (target and draft rows, each with its own
 // temperature).
 #include "attn_combine.hpp"
+#include "greedy_walk.hpp"
 #include "internal.hpp"
 
 namespace spectree {
@@ -198,8 +199,12 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSe
   }
 }
 
-// One wavefront per row: merge the chunk partials in chunk order.
-__global__ __launch_bounds__(256) void softmax_merge_kernel(SmSet A, SmSet B, int nch, int32_t* status) {
+// One wavefront per row: merge the chunk partials in chunk order.  With a walk (g),
+// the rows of A are a batch of requests' node rows at T = 0: the wave that merges a
+// request's last row (an arrival on req_count, which it leaves at zero) then runs
+// that request's greedy walk.
+__global__ __launch_bounds__(256) void softmax_merge_kernel(SmSet A, SmSet B, int nch, int32_t* status, GreedyArgs g,
+                                                            uint32_t* req_count) {
   const int lane = threadIdx.x & 63;
   int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= A.rows + B.rows) return;
@@ -240,6 +245,18 @@ __global__ __launch_bounds__(256) void softmax_merge_kernel(SmSet A, SmSet B, in
     if (S.row_argmax) S.row_argmax[row] = bad_row ? -1 : a_all;
     if (bad_row) report(status, SPEC_ERR_BAD_INPUT);
   }
+  if (g.accepted_child && !second) {
+    const int b = (int)(row / g.n_max);
+    int last = 0;
+    if (lane == 0) {
+      stores_done();
+      last = pub_arrive(&req_count[b]) == (uint32_t)(g.n_max - 1);
+    }
+    if (__shfl(last, 0)) {
+      if (lane == 0) pub_store(&req_count[b], 0u);
+      greedy_walk_wave<true>(g, b);
+    }
+  }
 }
 
 // probs[r, x] = exp((l - m) / T) / Z, tests only.
@@ -272,7 +289,8 @@ inline SmSet make_set(const float* logits, int64_t rows, float t, float* mx, flo
 // The chunk pass (followed, in the same launch, by the rows of `comb` when given),
 // then (merge) the row merge.
 inline int launch_stats(const SmSet& A, const SmSet& B, int32_t vocab, int32_t* status, hipStream_t st,
-                        bool merge, const AttnCombine* comb) {
+                        bool merge, const AttnCombine* comb, const GreedyArgs* walk = nullptr,
+                        uint32_t* req_count = nullptr) {
   const int nch = sm_chunks(vocab);
   AttnCombine c{};
   if (comb) c = *comb;
@@ -303,7 +321,10 @@ inline int launch_stats(const SmSet& A, const SmSet& B, int32_t vocab, int32_t* 
   SPEC_LAUNCH_CHECK();
   if (!merge) return SPEC_OK;  // invalid rows were reported by the chunk pass
   const int64_t rows = A.rows + B.rows;
-  hipLaunchKernelGGL(softmax_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, A, B, nch, status);
+  GreedyArgs wk{};
+  if (walk) wk = *walk;
+  hipLaunchKernelGGL(softmax_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, A, B, nch, status, wk,
+                     req_count);
   SPEC_LAUNCH_CHECK();
   return SPEC_OK;
 }
@@ -320,7 +341,8 @@ extern "C" size_t spec_tree_softmax_workspace_size(int64_t rows, int32_t vocab) 
 namespace spectree {
 int softmax_call(const float* logits, int64_t rows, int32_t vocab, float temperature, float* row_max,
                  float* row_sumexp, int32_t* row_argmax, float* probs, float* chunk_max, double* chunk_sum,
-                 void* workspace, size_t workspace_bytes, int32_t* status, void* stream, const AttnCombine* comb) {
+                 void* workspace, size_t workspace_bytes, int32_t* status, void* stream, const AttnCombine* comb,
+                 const GreedyArgs* walk, uint32_t* req_count) {
   if (!logits || !row_max || rows < 1 || vocab < 1) return SPEC_ERR_INVALID_ARG;
   if (!(temperature >= 0.0f) || isinf(temperature)) return SPEC_ERR_INVALID_ARG;
   const bool greedy = temperature == 0.0f;
@@ -329,7 +351,7 @@ int softmax_call(const float* logits, int64_t rows, int32_t vocab, float tempera
   SmSet A = make_set(logits, rows, temperature, row_max, row_sumexp, row_argmax);
   sm_set_carve((char*)workspace, rows, vocab, &A, chunk_max, chunk_sum);
   SmSet B{};
-  const int rc = launch_stats(A, B, vocab, status, (hipStream_t)stream, true, comb);
+  const int rc = launch_stats(A, B, vocab, status, (hipStream_t)stream, true, comb, walk, req_count);
   if (rc != SPEC_OK) return rc;
   if (probs && !greedy) {
     if (rows > 65535) return SPEC_ERR_UNSUPPORTED;
@@ -347,12 +369,17 @@ extern "C" int spec_tree_softmax(const float* logits, int64_t rows, int32_t voca
                                  float* chunk_max, double* chunk_sum, void* workspace, size_t workspace_bytes,
                                  int32_t* status, void* stream) {
   return spectree::softmax_call(logits, rows, vocab, temperature, row_max, row_sumexp, row_argmax, probs, chunk_max,
-                                chunk_sum, workspace, workspace_bytes, status, stream, nullptr);
+                                chunk_sum, workspace, workspace_bytes, status, stream, nullptr, nullptr, nullptr);
 }
+
+namespace spectree {
+size_t softmax_pair_counters_offset(int64_t rows, int32_t vocab) { return 2 * sm_set_bytes(rows, vocab); }
+}  // namespace spectree
 
 extern "C" size_t spec_tree_softmax_pair_workspace_size(int64_t rows, int32_t vocab) {
   if (rows < 1 || vocab < 1) return 0;
-  return 2 * spectree::sm_set_bytes(rows, vocab);
+  // two row sets, then the verification step's per-request counters at T = 0
+  return 2 * spectree::sm_set_bytes(rows, vocab) + spectree::align256((size_t)rows * 4);
 }
 
 namespace spectree {
