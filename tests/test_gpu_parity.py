@@ -1054,6 +1054,64 @@ def test_verify_step_equals_separate_calls(cfg, T):
     _compare_sampling(got, _oracle_sampling(inp), inp, max_exempt=max(1, inp["B"] // 4))
 
 
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_verify_step_bad_requests(T):
+    """The single call on a batch with malformed requests (a parent behind its child,
+    a drafted token outside the vocabulary, a NaN in a root's target row): the same
+    outputs and status as the separate calls, the bad requests marked, the others
+    equal to the oracle."""
+    say("verify step, bad requests", T)
+    inp = support.make_config(4, seed=41, T=T, vocab_override=8192)
+    inp["parent"][1, 6] = 9
+    inp["tokens"][3, 2] = inp["V"] + 5
+    inp["tgt_logits"][5, 0, 77] = np.nan
+    d = to_device(inp)
+    sep = VerifyStep(d)
+    sep.run()
+    want = sep.results()
+    one = VerifyStep(d).one_call()
+    one.run()
+    got = one.results()
+    for k in _step_keys(T):  # (the NaN row's chunk maximum is NaN in both)
+        assert np.array_equal(got[k], want[k], equal_nan=got[k].dtype.kind == "f"), k
+    assert got["status"][0] != 0
+    bad = [1, 3, 5]
+    for b in bad:
+        assert got["accept_len"][b] == -1 and got["accepted_child"][b, 0] == B.NODE_BAD_REQUEST, b
+    good = [b for b in range(inp["B"]) if b not in bad]
+    sub = {k: (v[good] if isinstance(v, np.ndarray) and v.shape[:1] == (inp["B"],) else v) for k, v in inp.items()}
+    sub["B"] = len(good)
+    ref = _oracle_sampling(sub)
+    gsub = {k: got[k][good] for k in ("accept_len", "path_nodes", "out_tokens", "accepted_child", "term_token")}
+    _compare_sampling(gsub, ref, sub, max_exempt=2)
+
+
+def test_verify_step_greedy_walk_reads_every_merged_row():
+    """At T = 0 the single call's walk runs in the row merge's launch and reads row
+    statistics that waves on other XCDs stored: 8 requests, three input copies with
+    different target rows, 40 rounds; every round's outputs must equal the separate
+    calls' (whose walk is a launch of its own)."""
+    say("verify step, greedy walk across the merge launch")
+    inp = support.make_config(4, seed=43, T=0.0, vocab_override=16384)
+    d = to_device(inp)
+    reps = [{k: d[k].clone() for k in ("q", "k", "v", "tgt_logits")} for _ in range(3)]
+    for i, r in enumerate(reps[1:]):
+        r["tgt_logits"].add_((1.0 + i) * torch.randn_like(r["tgt_logits"]))
+    keys = ("accepted_child", "term_token", "path_nodes", "out_tokens", "accept_len", "tmax", "targ", "status")
+    sep = VerifyStep(d)
+    want = []
+    for r in reps:
+        sep.run(replica=r)
+        want.append({k: v for k, v in sep.results().items() if k in keys})
+    one = VerifyStep(d).one_call()
+    for rnd in range(40):
+        i = rnd % 3
+        one.run(replica=reps[i])
+        got = {k: getattr(one, k).cpu().numpy() for k in keys}
+        for k in keys:
+            assert np.array_equal(got[k], want[i][k]), (rnd, i, k)
+
+
 def test_verify_step_one_split_plan():
     """A batch whose attention plan has one key split: its workgroups write the output
     rows, there is no combine, and the logit pass's launch has no extra workgroups."""

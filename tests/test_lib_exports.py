@@ -180,6 +180,22 @@ def test_host_errors_verify_step(lib):
     a.head_dim = 128
     a.parent = None  # the step builds the ancestor rows from the parent links
     assert f(ctypes.addressof(a), None) == -1
+    # T = 0: the walk runs in the logit pass's launch, so its arguments are checked
+    # before anything is launched
+    a.parent = P
+    a.temperature = 0.0
+    a.attn_workspace, a.attn_workspace_bytes = P, 1 << 30  # (the attention's checks would pass)
+    assert f(ctypes.addressof(a), None) == -1  # no tgt_max / tgt_argmax / outputs
+    a.tgt_max, a.tgt_argmax, a.accepted_child, a.term_token = P, P, P, P
+    a.path_nodes = P  # the path outputs come together
+    assert f(ctypes.addressof(a), None) == -1
+    a.path_nodes = None
+    assert f(ctypes.addressof(a), None) == -5  # the logit workspace
+    a.softmax_workspace = P
+    a.softmax_workspace_bytes = binding.spec_tree_softmax_pair_workspace_size(8, 1000) - 1
+    assert f(ctypes.addressof(a), None) == -5
+    a.n_max = 65
+    assert f(ctypes.addressof(a), None) == -1
 
 
 def test_host_errors_kv_commit(lib):

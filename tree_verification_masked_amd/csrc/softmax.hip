@@ -239,10 +239,12 @@ __global__ __launch_bounds__(256) void softmax_merge_kernel(SmSet A, SmSet B, in
     z = wave_sum_d(z);
   }
   if (lane == 0) {
+    // agent-scope stores: a walk in this launch (below) may read them from another XCD,
+    // whose L2 a plain store does not reach
     const bool bad_row = b_all || !(m_all > -INFINITY);
-    S.row_max[row] = bad_row ? NAN : m_all;
-    if (S.row_sumexp) S.row_sumexp[row] = bad_row ? NAN : (float)z;
-    if (S.row_argmax) S.row_argmax[row] = bad_row ? -1 : a_all;
+    pub_store(&S.row_max[row], bad_row ? NAN : m_all);
+    if (S.row_sumexp) pub_store(&S.row_sumexp[row], bad_row ? NAN : (float)z);
+    if (S.row_argmax) pub_store(&S.row_argmax[row], bad_row ? -1 : a_all);
     if (bad_row) report(status, SPEC_ERR_BAD_INPUT);
   }
   if (g.accepted_child && !second) {
