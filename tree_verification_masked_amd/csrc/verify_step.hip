@@ -1,11 +1,11 @@
 // The whole verification step in three launches: the tree attention (its split
 // combine deferred), the logit pass with the combine's rows as extra workgroups of
 // the same launch, then the sampler with its walk (at T = 0 the row merge's launch,
-// whose wave that finishes a request's last row walks that request).  Tree-verification notes
-// (zhangshuibai.github.io), "Tree Verification 详解" part D.2: the step is the
-// tree-masked target pass plus the verification of part C over every node's row;
-// the attention output is not an input of the verification, so the combine can
-// finish beside the logit pass.
+// whose wave that finishes a request's last row walks that request).
+// Tree-verification notes (zhangshuibai.github.io), "Tree Verification 详解" part
+// D.2: the step is the tree-masked target pass plus the verification of part C over
+// every node's row; the attention output is not an input of the verification, so
+// the combine can finish beside the logit pass.
 #include "internal.hpp"
 #include "spec_tree.h"
 
@@ -38,13 +38,13 @@ extern "C" int spec_tree_verify_step(const SpecTreeStepArgs* s, void* stream) {
     rc = softmax_call(s->tgt_logits, rows, s->vocab, 0.0f, s->tgt_max, s->tgt_sumexp, s->tgt_argmax, nullptr,
                       nullptr, nullptr, s->softmax_workspace, s->softmax_workspace_bytes, s->status, stream, &comb, &g,
                       counters);
-    if (rc != SPEC_OK) attention_combine_launch(comb, stream);
+    if (rc != SPEC_OK) attention_combine_launch(comb, stream);  // (nothing of that call was launched)
     return rc;
-  } else
-    rc = softmax_pair_call(s->tgt_logits, s->temperature, s->dft_logits, s->draft_temperature, rows, s->vocab,
-                           s->parent, s->n_nodes, s->n_max, nullptr, nullptr, nullptr, s->tgt_chunk_max,
-                           s->tgt_chunk_sum, nullptr, nullptr, s->dft_chunk_max, s->dft_chunk_sum,
-                           s->softmax_workspace, s->softmax_workspace_bytes, s->status, stream, &comb);
+  }
+  rc = softmax_pair_call(s->tgt_logits, s->temperature, s->dft_logits, s->draft_temperature, rows, s->vocab,
+                         s->parent, s->n_nodes, s->n_max, nullptr, nullptr, nullptr, s->tgt_chunk_max,
+                         s->tgt_chunk_sum, nullptr, nullptr, s->dft_chunk_max, s->dft_chunk_sum, s->softmax_workspace,
+                         s->softmax_workspace_bytes, s->status, stream, &comb);
   if (rc != SPEC_OK) {  // nothing of that call was launched: finish the attention on its own
     attention_combine_launch(comb, stream);
     return rc;
