@@ -98,22 +98,24 @@ __global__ __launch_bounds__(kSmThreads) void softmax_stats_kernel(SmSet A, SmSe
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   int64_t blk = blockIdx.x;
-  // Workgroup order: the second set's rows, then the split combine's rows, then the
-  // first set's rows.  Given the tree, a second-set workgroup reads the parent links
-  // before its row, and the combine reads partials another launch wrote; both waits
-  // overlap the first set's streaming behind them.
+  // Workgroup order with a second set: its rows, then the split combine's rows, then
+  // the first set's rows.  Given the tree, a second-set workgroup reads the parent
+  // links before its row, and the combine reads partials another launch wrote; both
+  // waits overlap the first set's streaming behind them.  With one set the combine's
+  // rows come after it.
   const int64_t blocks_a = A.rows * nch, blocks_b = B.rows * nch;
   const int64_t blocks_c = (int64_t)gridDim.x - blocks_a - blocks_b;  // the combine's (0 without it)
+  const int64_t c_begin = blocks_b > 0 ? blocks_b : blocks_a;
   if constexpr (kCombD > 0) {
-    if (blk >= blocks_b && blk < blocks_b + blocks_c) {
+    if (blk >= c_begin && blk < c_begin + blocks_c) {
       // four splits per load round: the chunk workgroups' register budget
-      attn_combine_row<kCombD, CombT, 4>(comb_args, comb_out, (blk - blocks_b) * 4 + wid);
+      attn_combine_row<kCombD, CombT, 4>(comb_args, comb_out, (blk - c_begin) * 4 + wid);
       return;
     }
   }
   const bool second = blk < blocks_b;
   const SmSet& S = second ? B : A;
-  if (!second) blk -= blocks_b + (kCombD > 0 ? blocks_c : 0);
+  if (!second) blk -= blocks_b + (kCombD > 0 && blocks_b > 0 ? blocks_c : 0);
   const int chunk = (int)(blk % nch);
   const int64_t row = blk / nch;
   if (S.parent) {  // a node without children (or a padding slot): its row is not needed
