@@ -413,74 +413,94 @@ __global__ __launch_bounds__(64) void greedy_walk_kernel(GreedyArgs g) { greedy_
 // ---------------------------------------------------------------------------
 // The sampler: one workgroup per (node slot, vocabulary chunk)
 // ---------------------------------------------------------------------------
-// The chain's level step.  level_sums: every thread sums, exactly, the fixed-point
-// masses of its tokens with dp - K dq > 0 (integers below 2^46), each wavefront
-// reduces them (below 2^52, still exact in fp64) into s_ll.  publish_level (wave 0,
-// after a barrier): this chunk's sums (below 2^55) into *P, *Q and, with more than
-// one chunk, out as two words (sum << kTagBits) | level, through this XCD's L2 when
-// the node's chunks share it (local), else device-wide.  gather_level (wave 0): every
-// chunk's words of the level (lane l reads chunks l, l + 64, ...; each wait bounded
-// by wait_limit polls) into s_lp / s_lq, their totals into s_tot; false when a wait
-// gave up.
-__device__ inline void level_sums(const double* dp, const double* dq, double K, long long (*s_ll)[kThreads / 64]) {
+// The chain's level step.  level_push (every wavefront, no barrier): the wavefront
+// sums, exactly, the fixed-point masses of its tokens with dp - K dq > 0 (a thread's
+// below 2^46, the wavefront's below 2^52: exact in fp64), adds them into the
+// workgroup's accumulators of the level's parity (LDS atomics on exact integers, so
+// the order of arrival does not matter) and takes a ticket; the last wavefront to
+// arrive reads the chunk's sums (below 2^55), resets the accumulators and, with
+// more than one chunk, publishes them as two words (sum << kTagBits) | level,
+// through this XCD's L2 when the node's chunks share it (local), else device-wide.
+// gather_level (wave 0): every chunk's words of the level, this chunk's included
+// (lane l reads chunks l, l + 64, ...; each wait bounded by wait_limit polls) into
+// s_lp / s_lq, their totals into s_tot; false when a wait gave up.
+__device__ inline void level_push(const double* dp, const double* dq, double K, unsigned long long* sl0, int nch,
+                                  int ch, int lv, int local, unsigned long long* s_acc, uint32_t* s_cnt,
+                                  long long* s_own) {
   double sp = 0.0, sq = 0.0;
 #pragma unroll
   for (int s2 = 0; s2 < kPer; ++s2) {
-    const bool in = __fma_rn(-K, dq[s2], dp[s2]) > 0.0;
-    sp += in ? dp[s2] : 0.0;
-    sq += in ? dq[s2] : 0.0;
+    const double in = __fma_rn(-K, dq[s2], dp[s2]) > 0.0 ? 1.0 : 0.0;
+    sp = __fma_rn(in, dp[s2], sp);  // exact: integers below 2^53
+    sq = __fma_rn(in, dq[s2], sq);
   }
   sp = wave_sum_d(sp);
   sq = wave_sum_d(sq);
   if ((threadIdx.x & 63) == 0) {
-    s_ll[0][threadIdx.x >> 6] = (long long)sp;
-    s_ll[1][threadIdx.x >> 6] = (long long)sq;
-  }
-}
-__device__ inline void publish_level(long long (*s_ll)[kThreads / 64], unsigned long long* sl0, int nch, int ch,
-                                     int lv, int local, long long* P, long long* Q) {
-  long long Pc = 0, Qc = 0;
-#pragma unroll
-  for (int t = 0; t < kThreads / 64; ++t) {
-    Pc += s_ll[0][t];
-    Qc += s_ll[1][t];
-  }
-  *P = Pc;
-  *Q = Qc;
-  if (nch > 1 && (threadIdx.x & 63) == 0) {
-    unsigned long long* sl = sl0 + (lv & 1) * nch * 2;
-    const unsigned long long wp = ((unsigned long long)Pc << kTagBits) | (unsigned)lv;
-    const unsigned long long wq = ((unsigned long long)Qc << kTagBits) | (unsigned)lv;
-    if (local) {
-      __hip_atomic_store(&sl[2 * ch], wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_store(&sl[2 * ch + 1], wq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else {
-      pub_store(&sl[2 * ch], wp);
-      pub_store(&sl[2 * ch + 1], wq);
+    const int par = lv & 1;
+    __hip_atomic_fetch_add(&s_acc[2 * par], (unsigned long long)(long long)sp, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(&s_acc[2 * par + 1], (unsigned long long)(long long)sq, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t t = __hip_atomic_fetch_add(&s_cnt[par], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (t == kThreads / 64 - 1) {
+      const unsigned long long P = __hip_atomic_load(&s_acc[2 * par], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const unsigned long long Q =
+          __hip_atomic_load(&s_acc[2 * par + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(&s_acc[2 * par], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(&s_acc[2 * par + 1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(&s_cnt[par], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (nch > 1) {
+        unsigned long long* sl = sl0 + par * nch * 2;
+        const unsigned long long wp = (P << kTagBits) | (unsigned)lv;
+        const unsigned long long wq = (Q << kTagBits) | (unsigned)lv;
+        if (local) {
+          __hip_atomic_store(&sl[2 * ch], wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_store(&sl[2 * ch + 1], wq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
+          pub_store(&sl[2 * ch], wp);
+          pub_store(&sl[2 * ch + 1], wq);
+        }
+      } else {  // one chunk: its sums are the node's, handed to the gather through LDS
+        __hip_atomic_store(&s_own[2 * par], (long long)P, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&s_own[2 * par + 1], (long long)Q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&s_cnt[2 + par], (uint32_t)lv, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
     }
   }
 }
-__device__ inline bool gather_level(const unsigned long long* sl0, int nch, int ch, int lv, long long Pc,
-                                    long long Qc, uint32_t wait_limit, long long* s_lp, long long* s_lq,
-                                    long long* s_tot) {
+__device__ inline bool gather_level(const unsigned long long* sl0, int nch, int lv, uint32_t wait_limit, long long* s_lp,
+                                    long long* s_lq, long long* s_tot, const uint32_t* s_cnt, const long long* s_own) {
   const int lane = threadIdx.x & 63;
   const unsigned long long* sl = sl0 + (lv & 1) * nch * 2;
   const unsigned tag = (unsigned)lv;
   long long cp = 0, cq = 0;
   bool ready = true;
-  for (int t = lane; t < nch; t += 64) {
-    long long vp = Pc, vq = Qc;
-    if (t != ch) {
-      unsigned long long xp = pub_load(&sl[2 * t]), xq = pub_load(&sl[2 * t + 1]);
-      for (uint32_t polls = 0; ((xp & 0xffu) != tag || (xq & 0xffu) != tag) && polls < wait_limit; ++polls) {
-        __builtin_amdgcn_s_sleep(1);
-        xp = pub_load(&sl[2 * t]);
-        xq = pub_load(&sl[2 * t + 1]);
-      }
-      ready = ready && (xp & 0xffu) == tag && (xq & 0xffu) == tag;
-      vp = (long long)(xp >> kTagBits);
-      vq = (long long)(xq >> kTagBits);
+  if (nch == 1) {  // the chunk's own sums, once its last wavefront has left them in LDS
+    uint32_t polls = 0;
+    while (__hip_atomic_load(&s_cnt[2 + (lv & 1)], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != (uint32_t)lv &&
+           polls < wait_limit) {
+      __builtin_amdgcn_s_sleep(1);
+      ++polls;
     }
+    ready = polls < wait_limit;
+    if (lane == 0) {
+      s_lp[0] = s_own[2 * (lv & 1)];
+      s_lq[0] = s_own[2 * (lv & 1) + 1];
+      s_tot[0] = s_own[2 * (lv & 1)];
+      s_tot[1] = s_own[2 * (lv & 1) + 1];
+    }
+    return __ballot(!ready) == 0;
+  }
+  for (int t = lane; t < nch; t += 64) {
+    unsigned long long xp = pub_load(&sl[2 * t]), xq = pub_load(&sl[2 * t + 1]);
+    for (uint32_t polls = 0; ((xp & 0xffu) != tag || (xq & 0xffu) != tag) && polls < wait_limit; ++polls) {
+      __builtin_amdgcn_s_sleep(1);
+      xp = pub_load(&sl[2 * t]);
+      xq = pub_load(&sl[2 * t + 1]);
+    }
+    ready = ready && (xp & 0xffu) == tag && (xq & 0xffu) == tag;
+    const long long vp = (long long)(xp >> kTagBits), vq = (long long)(xq >> kTagBits);
     s_lp[t] = vp;
     s_lq[t] = vq;
     cp += vp;
@@ -533,7 +553,9 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(RejArgs a, SampWs w
   __shared__ double s_pch[256], s_chunk[256];
   __shared__ long long s_lp[2][256], s_lq[2][256];  // every chunk's sums at the last two levels
   __shared__ double s_w[16];
-  __shared__ long long s_ll[2][kThreads / 64], s_tot[2];
+  __shared__ long long s_tot[2], s_own[4];
+  __shared__ unsigned long long s_acc[4];  // a level's chunk sums, by level parity
+  __shared__ uint32_t s_cnt[4];            // arrivals by parity; [2 + parity]: the level whose own sums are in s_own
   __shared__ double s_z[2];
   __shared__ float s_m[2];
   __shared__ int s_ok[2], s_nb, s_pick, s_fail, s_done, s_last;
@@ -572,6 +594,10 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(RejArgs a, SampWs w
     s_tok[lane] = tk;
     s_ua[lane] = in ? a.u_accept[base + lane] : 0.0f;
     if (lane == 0) s_fail = 0;
+    if (lane < 4) {
+      s_acc[lane] = 0ull;
+      s_cnt[lane] = 0u;
+    }
     const bool bad_link = live && (lane == 0 ? par != -1 : (par < 0 || par >= lane));
     const bool bad_tok = live && lane > 0 && (tk < 0 || tk >= a.vocab);
     if (!__ballot(bad_link) && !__ballot(bad_tok) && live && lane > 0 && par == n) {
@@ -620,22 +646,20 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(RejArgs a, SampWs w
   // (threshold 1, whatever the first child's test gives) start at once ----
   double dp[kPer], dq[kPer];
   const double kr = izd / izt;  // K = c kr
+  unsigned long long* sl0 = w.slot + (int64_t)nd * 4 * nch;
   if (!planner) {
 #pragma unroll
     for (int s2 = 0; s2 < kPer; ++s2) {
       dp[s2] = (double)fx42(exp_scaled(xl[s2] - mt, a.est));
       dq[s2] = (double)fx42(exp_scaled(xd[s2] - md, a.esd));
     }
-    level_sums(dp, dq, kr, s_ll);
+    level_push(dp, dq, kr, sl0, nch, ch, 1, local, s_acc, s_cnt, s_own);
   }
   // the chunk masses of p
   if (row_ok)
     for (int c = tid; c < nch; c += kThreads) s_pch[c] *= exp(((double)s_cm[c] - (double)mt) * a.inv_t);
   __syncthreads();
-  unsigned long long* sl0 = w.slot + (int64_t)nd * 4 * nch;
-  long long Pc = 0, Qc = 0;  // wave 0: this chunk's sums of the current level
   if (wv == 0) {
-    if (!planner) publish_level(s_ll, sl0, nch, ch, 1, local, &Pc, &Qc);
     // ---- round 2: the children's p and q (fp64) ----
     double px = 0.0, qx = 0.0;
     if (is_kid && row_ok) {
@@ -683,12 +707,8 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(RejArgs a, SampWs w
           if (!zero) {
             // the child just tested was rejected: the threshold after it is c + W
             const double cn = c + W;
-            if (lv > 1) {
-              level_sums(dp, dq, cn * kr, s_ll);
-              __syncthreads();
-              if (wv == 0) publish_level(s_ll, sl0, nch, ch, lv, local, &Pc, &Qc);
-            }
-            if (wv == 0 && !gather_level(sl0, nch, ch, lv, Pc, Qc, wait_limit, s_lp[lv & 1], s_lq[lv & 1], s_tot))
+            if (lv > 1) level_push(dp, dq, cn * kr, sl0, nch, ch, lv, local, s_acc, s_cnt, s_own);
+            if (wv == 0 && !gather_level(sl0, nch, lv, wait_limit, s_lp[lv & 1], s_lq[lv & 1], s_tot, s_cnt, s_own))
               s_fail = 1;
             __syncthreads();
             if (s_fail) {
