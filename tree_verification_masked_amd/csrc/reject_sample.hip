@@ -544,7 +544,9 @@ __device__ inline void chunk_of(int blk, int q_off, int nch, int nx, int nb_blk,
   *ch = c;
 }
 
-__global__ __launch_bounds__(kThreads, 4) void sample_kernel(RejArgs a, SampWs w, uint32_t wait_limit, int nx,
+// Six waves per SIMD: three workgroups per CU (80 VGPRs; a few registers spill to
+// scratch), so more of a batch's chunks are resident at once.
+__global__ __launch_bounds__(kThreads, 6) void sample_kernel(RejArgs a, SampWs w, uint32_t wait_limit, int nx,
                                                              int nb_blk, int q_off, int local) {
   __shared__ int s_par[64], s_tok[64];
   __shared__ float s_ua[64];
